@@ -1,0 +1,554 @@
+"""Pins for the CPU oracle: each test ties an oracle function to something other than itself.
+
+Sources of truth used here: the pages' worked examples (fixtures under tests/golden/, cited there), closed
+forms derived from the ring schedule, brute force over every left-fold order on tiny inputs, exact fp64
+sums with textbook error bounds, and independent library conversions (torch, numpy) for number formats.
+"""
+import itertools
+import math
+import os
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from all_reduce_reduction_ring_amd import inputs
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def _read_fixture(name):
+    rows = {}
+    with open(os.path.join(GOLDEN, name)) as f:
+        for line in f:
+            line = line.strip()
+            if not line or line.startswith("#"):
+                continue
+            key, _, val = line.partition(":")
+            rows[key.strip()] = val.split()
+    return rows
+
+
+def _f32(a):
+    return np.asarray(a, dtype=np.float32)
+
+
+def _bits(a):
+    return np.asarray(a).view(np.uint32) if np.asarray(a).dtype == np.float32 else np.asarray(a)
+
+
+def _fold(vals, order, op="sum"):
+    """Left fold in float32 over the given rank order (numpy scalar arithmetic, one rounding per add)."""
+    acc = np.float32(vals[order[0]])
+    for r in order[1:]:
+        acc = np.float32(acc + np.float32(vals[r]))
+    return acc
+
+
+def _ring_start(e, lo):
+    """Chunk index of element e under the balanced split."""
+    return int(np.searchsorted(lo, e, side="right") - 1)
+
+
+# ---------------------------------------------------------------- worked examples from the pages
+
+
+@pytest.mark.parametrize("algo", ["ring", "fused", "rhd"])
+@pytest.mark.parametrize("dtype", [oracle.I32, oracle.F32])
+def test_worked_example(algo, dtype):
+    fx = _read_fixture("worked_example.txt")
+    npd = oracle.NP_DTYPE[dtype]
+    xs = [np.array([int(v) for v in fx[f"rank {r}"]], dtype=npd) for r in range(4)]
+    want = np.array([int(v) for v in fx["result"]], dtype=npd)
+    fn = {"ring": oracle.ring_allreduce, "fused": oracle.fused_allreduce, "rhd": oracle.rhd_allreduce}[algo]
+    outs = fn(xs, dtype, oracle.SUM)
+    assert len(outs) == 4
+    for o in outs:
+        np.testing.assert_array_equal(o, want)
+
+
+def test_worked_example_ring_chunk_owners():
+    # count=2 < N=4: chunks {0}, {1}, {}, {}; element 0 is folded from rank 0, element 1 from rank 1, and
+    # after reduce-scatter rank 3 owns chunk 0 and rank 0 owns chunk 1.
+    fx = _read_fixture("worked_example.txt")
+    xs = [np.array([int(v) for v in fx[f"rank {r}"]], dtype=np.float32) for r in range(4)]
+    lo = oracle.chunk_bounds(2, 4)
+    np.testing.assert_array_equal(lo, [0, 1, 2, 2, 2])
+    st = oracle.ring_rs_state(xs, oracle.F32, oracle.SUM)
+    assert st[3].view(np.float32)[0] == 1111.0
+    assert st[0].view(np.float32)[1] == 2222.0
+
+
+def test_allgather_example():
+    fx = _read_fixture("allgather_example.txt")
+    sym = {k.split()[1]: int(v[0]) for k, v in fx.items() if k.startswith("symbol")}
+    parts = [np.array([sym[fx[f"rank {r}"][0]]], dtype=np.int32) for r in range(4)]
+    want = np.array([sym[s] for s in fx["result"]], dtype=np.int32)
+    for o in oracle.allgather(parts, oracle.I32):
+        np.testing.assert_array_equal(o, want)
+
+
+def test_reduce_scatter_two_rank_example():
+    fx = _read_fixture("reduce_scatter_two_rank.txt")
+    xs = [np.array([int(v) for v in fx[f"rank {r}"]], dtype=np.int32) for r in range(2)]
+    outs = oracle.reduce_scatter(xs, oracle.I32, oracle.SUM)
+    np.testing.assert_array_equal(outs[0], np.array([int(v) for v in fx["rank 0 holds"]]))
+    np.testing.assert_array_equal(outs[1], np.array([int(v) for v in fx["rank 1 holds"]]))
+    np.testing.assert_array_equal(np.concatenate(outs), np.array([int(v) for v in fx["reduced"]]))
+
+
+# ---------------------------------------------------------------- invariants
+
+
+@pytest.mark.parametrize("n,count", [(1, 5), (2, 7), (3, 10), (4, 1), (5, 33), (8, 1000), (7, 6)])
+@pytest.mark.parametrize("dtype", [oracle.F32, oracle.BF16, oracle.F16, oracle.I32])
+def test_outputs_identical_and_rs_ag_is_ar(n, count, dtype):
+    kind = {oracle.F32: "uniform_f32", oracle.BF16: "uniform_bf16", oracle.F16: "uniform_f16",
+            oracle.I32: "int32"}[dtype]
+    xs = inputs.rank_inputs(kind, n, count, cfg=90)
+    for op in (oracle.SUM, oracle.AVG, oracle.MIN, oracle.MAX):
+        outs = oracle.ring_allreduce(xs, dtype, op)
+        for o in outs[1:]:
+            np.testing.assert_array_equal(o.view(np.uint8), outs[0].view(np.uint8))
+        parts = oracle.reduce_scatter(xs, dtype, op)
+        gathered = oracle.allgather(parts, dtype)
+        for g in gathered:
+            np.testing.assert_array_equal(g.view(np.uint8), outs[0].view(np.uint8))
+
+
+def test_in_place_matches_out_of_place():
+    xs = inputs.rank_inputs("uniform_f32", 5, 103, cfg=91)
+    want = oracle.ring_allreduce(xs, oracle.F32, oracle.SUM)
+    bufs = [x.copy() for x in xs]
+    rc = oracle.lib().oracle_ring_allreduce(oracle._ptrs(bufs), oracle._ptrs(bufs), 5, 103, oracle.F32, oracle.SUM)
+    assert rc == 0
+    for b, w in zip(bufs, want):
+        np.testing.assert_array_equal(b.view(np.uint32), w.view(np.uint32))
+
+
+# ---------------------------------------------------------------- integer brute force (unique answer)
+
+
+@pytest.mark.parametrize("n", [1, 2, 3, 4, 5, 6])
+@pytest.mark.parametrize("count", [1, 4, 13])
+def test_int32_brute_force_all_ops(n, count):
+    xs = inputs.rank_inputs("int32", n, count, cfg=92, extra=(count,))
+    big = np.array([[int(v) for v in x] for x in xs], dtype=object)
+    s = [(sum(int(big[r, e]) for r in range(n)) + (1 << 31)) % (1 << 32) - (1 << 31) for e in range(count)]
+    want = {
+        oracle.SUM: s,
+        oracle.AVG: [int(v / n) if v >= 0 else -int(-v / n) for v in s],  # C division truncates toward 0
+        oracle.MIN: [min(int(big[r, e]) for r in range(n)) for e in range(count)],
+        oracle.MAX: [max(int(big[r, e]) for r in range(n)) for e in range(count)],
+    }
+    # the exact-integer trunc above must use integer arithmetic, not float
+    want[oracle.AVG] = [abs(v) // n * (1 if v >= 0 else -1) for v in s]
+    for op, w in want.items():
+        for algo in (oracle.ring_allreduce, oracle.fused_allreduce):
+            for o in algo(xs, oracle.I32, op):
+                np.testing.assert_array_equal(o, np.array(w, dtype=np.int32))
+        if n & (n - 1) == 0:
+            for o in oracle.rhd_allreduce(xs, oracle.I32, op):
+                np.testing.assert_array_equal(o, np.array(w, dtype=np.int32))
+
+
+# ---------------------------------------------------------------- ring order (fp32)
+
+
+@pytest.mark.parametrize("n,count", [(2, 9), (3, 10), (4, 1000), (5, 12), (7, 50), (8, 4099), (16, 300)])
+def test_ring_equals_closed_form_fold_from_chunk_rank(n, count):
+    """Ring schedule (rank i sends chunk (i-s) mod N at round s) => chunk c is folded starting at rank c."""
+    xs = inputs.rank_inputs("uniform_f32", n, count, cfg=93)
+    lo = oracle.chunk_bounds(count, n)
+    got = oracle.ring_allreduce(xs, oracle.F32, oracle.SUM)[0]
+    want = np.empty(count, dtype=np.float32)
+    for c in range(n):
+        acc = xs[c][lo[c]:lo[c + 1]].copy()
+        for k in range(1, n):
+            acc = (acc + xs[(c + k) % n][lo[c]:lo[c + 1]]).astype(np.float32)
+        want[lo[c]:lo[c + 1]] = acc
+    np.testing.assert_array_equal(got.view(np.uint32), want.view(np.uint32))
+
+
+@pytest.mark.parametrize("n,count", [(3, 9), (4, 8), (5, 15), (8, 64)])
+def test_ownership_after_reduce_scatter(n, count):
+    xs = inputs.rank_inputs("uniform_f32", n, count, cfg=94)
+    lo = oracle.chunk_bounds(count, n)
+    st = oracle.ring_rs_state(xs, oracle.F32, oracle.SUM)
+    for i in range(n):
+        c = (i + 1) % n
+        acc = xs[c][lo[c]:lo[c + 1]].copy()
+        for k in range(1, n):
+            acc = (acc + xs[(c + k) % n][lo[c]:lo[c + 1]]).astype(np.float32)
+        np.testing.assert_array_equal(st[i][lo[c]:lo[c + 1]], acc.view(np.uint32))
+
+
+def _order_revealing(n, count, shift):
+    """V1 (shift 0): in chunk c, x_c = 2^24, x_{c+1} = -2^24, x_{c-1} = 1, zero elsewhere.
+    V2 (shift 1): the same pattern moved one rank left: x_{c-1} = 2^24, x_c = -2^24, x_{c-2} = 1.
+    A left fold starting at rank a returns 1 iff the 1 is added after +2^24 and -2^24 have cancelled, or
+    before the big values meet. For V1 that happens iff a in {c, c+1}; for V2 iff a in {c-1, c}."""
+    lo = oracle.chunk_bounds(count, n)
+    xs = [np.zeros(count, dtype=np.float32) for _ in range(n)]
+    for c in range(n):
+        sl = slice(lo[c], lo[c + 1])
+        base = (c - shift) % n
+        xs[base][sl] = 2.0 ** 24
+        xs[(base + 1) % n][sl] = -(2.0 ** 24)
+        xs[(base - 1) % n][sl] = 1.0
+    return xs, lo
+
+
+@pytest.mark.parametrize("n", [3, 4, 5, 6, 8])
+def test_order_revealing_vectors_pin_ring_start(n):
+    count = 3 * n + 1
+    for shift in (0, 1):
+        xs, lo = _order_revealing(n, count, shift)
+        got = oracle.ring_allreduce(xs, oracle.F32, oracle.SUM)[0]
+        for e in range(count):
+            c = _ring_start(e, lo)
+            vals = [xs[r][e] for r in range(n)]
+            starts_giving_one = {a for a in range(n)
+                                 if _fold(vals, [(a + k) % n for k in range(n)]) == np.float32(1.0)}
+            expect = {c, (c + 1) % n} if shift == 0 else {(c - 1) % n, c}
+            assert starts_giving_one == expect
+            assert got[e] == np.float32(1.0)
+    # The rank-order fold (reduce at root 0) is a different association: it fails on middle chunks.
+    xs, lo = _order_revealing(n, count, 0)
+    fused = oracle.fused_allreduce(xs, oracle.F32, oracle.SUM)[0]
+    xs2, _ = _order_revealing(n, count, 1)
+    fused2 = oracle.fused_allreduce(xs2, oracle.F32, oracle.SUM)[0]
+    middle = [e for e in range(count) if 1 <= _ring_start(e, lo) <= n - 2]
+    assert any(fused[e] != 1.0 or fused2[e] != 1.0 for e in middle)
+
+
+@pytest.mark.parametrize("n", [2, 3, 4, 5])
+def test_brute_force_every_order(n):
+    """Every oracle element is one of the N! left folds, and exactly the cyclic fold from the chunk's rank."""
+    count = 2 * n + 1
+    xs = inputs.rank_inputs("uniform_f32", n, count, cfg=95, extra=(n,))
+    xs = [x * np.float32(2.0 ** (3 * r)) for r, x in enumerate(xs)]  # spread magnitudes: orders disagree
+    lo = oracle.chunk_bounds(count, n)
+    ring = oracle.ring_allreduce(xs, oracle.F32, oracle.SUM)[0]
+    fused = oracle.fused_allreduce(xs, oracle.F32, oracle.SUM)[0]
+    for e in range(count):
+        vals = [xs[r][e] for r in range(n)]
+        folds = {perm: _fold(vals, perm) for perm in itertools.permutations(range(n))}
+        assert ring[e] in set(folds.values())
+        c = _ring_start(e, lo)
+        assert ring[e] == folds[tuple((c + k) % n for k in range(n))]
+        assert fused[e] == folds[tuple(range(n))]
+
+
+@pytest.mark.parametrize("n", [2, 4, 8])
+def test_error_bound_against_exact_sum(n):
+    """Values on the 2^-24 grid: fp64 sums of <= 8 of them are exact. Recursive summation error is bounded by
+    gamma_{N-1} * sum|x| with gamma_k = k u / (1 - k u), u = 2^-24 (Higham, Accuracy and Stability of
+    Numerical Algorithms, ch. 4)."""
+    count = 100_003
+    xs = inputs.rank_inputs("uniform_f32", n, count, cfg=96)
+    exact = np.sum(np.array(xs, dtype=np.float64), axis=0)
+    abss = np.sum(np.abs(np.array(xs, dtype=np.float64)), axis=0)
+    u = 2.0 ** -24
+    gamma = (n - 1) * u / (1 - (n - 1) * u)
+    for fn in (oracle.ring_allreduce, oracle.fused_allreduce, oracle.rhd_allreduce):
+        got = fn(xs, oracle.F32, oracle.SUM)[0].astype(np.float64)
+        assert np.all(np.abs(got - exact) <= gamma * abss)
+
+
+# ---------------------------------------------------------------- avg, min, max rules
+
+
+@pytest.mark.parametrize("n", [2, 3, 5, 6, 7, 8])
+def test_avg_is_sum_then_one_fp32_division(n):
+    xs = inputs.rank_inputs("uniform_f32", n, 517, cfg=97)
+    s = oracle.ring_allreduce(xs, oracle.F32, oracle.SUM)[0]
+    a = oracle.ring_allreduce(xs, oracle.F32, oracle.AVG)[0]
+    np.testing.assert_array_equal(a.view(np.uint32), (s / np.float32(n)).astype(np.float32).view(np.uint32))
+    # integer-valued inputs: the sum is exact, so avg is the correctly rounded quotient
+    ints = [np.round(x * 100).astype(np.float32) for x in xs]
+    a2 = oracle.ring_allreduce(ints, oracle.F32, oracle.AVG)[0]
+    exact = np.sum(np.array(ints, dtype=np.float64), axis=0) / n
+    np.testing.assert_array_equal(a2, exact.astype(np.float32))
+
+
+def test_min_max_rules():
+    n, count = 5, 1001
+    xs = inputs.rank_inputs("uniform_f32", n, count, cfg=98)
+    for fn in (oracle.ring_allreduce, oracle.fused_allreduce):
+        np.testing.assert_array_equal(fn(xs, oracle.F32, oracle.MIN)[0], np.min(np.array(xs), axis=0))
+        np.testing.assert_array_equal(fn(xs, oracle.F32, oracle.MAX)[0], np.max(np.array(xs), axis=0))
+    # signed zeros: -0 orders below +0; any NaN gives the canonical quiet NaN
+    z = [np.array([0.0, -0.0, 1.0, np.nan], np.float32), np.array([-0.0, 0.0, np.nan, 2.0], np.float32)]
+    mn = oracle.ring_allreduce(z, oracle.F32, oracle.MIN)[0].view(np.uint32)
+    mx = oracle.ring_allreduce(z, oracle.F32, oracle.MAX)[0].view(np.uint32)
+    np.testing.assert_array_equal(mn, [0x80000000, 0x80000000, 0x7FC00000, 0x7FC00000])
+    np.testing.assert_array_equal(mx, [0x00000000, 0x00000000, 0x7FC00000, 0x7FC00000])
+
+
+# ---------------------------------------------------------------- RHD tree and fused order
+
+
+def _xor_tree(vals, n):
+    """Halving with partner distance N/2 first pairs (i, i+N/2), then pairs of pairs at N/4, and so on."""
+    level = [np.float32(v) for v in vals]
+    while len(level) > 1:
+        h = len(level) // 2
+        level = [np.float32(level[i] + level[i + h]) for i in range(h)]
+    return level[0]
+
+
+@pytest.mark.parametrize("n", [2, 4, 8, 16])
+def test_rhd_equals_xor_tree(n):
+    count = 257
+    xs = inputs.rank_inputs("uniform_f32", n, count, cfg=99)
+    xs = [x * np.float32(2.0 ** (2 * (r % 5))) for r, x in enumerate(xs)]
+    got = oracle.rhd_allreduce(xs, oracle.F32, oracle.SUM)
+    for o in got[1:]:
+        np.testing.assert_array_equal(o.view(np.uint32), got[0].view(np.uint32))
+    for e in range(count):
+        assert got[0][e] == _xor_tree([xs[r][e] for r in range(n)], n)
+    if n == 8:  # written out: ((x0+x4)+(x2+x6)) + ((x1+x5)+(x3+x7))
+        e = 11
+        v = [np.float32(xs[r][e]) for r in range(8)]
+        f = np.float32
+        assert got[0][e] == f(f(f(v[0] + v[4]) + f(v[2] + v[6])) + f(f(v[1] + v[5]) + f(v[3] + v[7])))
+
+
+def test_rhd_rejects_non_power_of_two():
+    xs = inputs.rank_inputs("uniform_f32", 3, 10, cfg=99)
+    with pytest.raises(RuntimeError):
+        oracle.rhd_allreduce(xs, oracle.F32, oracle.SUM)
+
+
+# ---------------------------------------------------------------- number formats vs library conversions
+
+
+def _special_f32():
+    vals = [0.0, -0.0, 1.0, -1.0, np.inf, -np.inf, 1e-45, -1e-45, 1.1754942e-38, 1.17549435e-38,
+            3.4028235e38, -3.4028235e38, 65504.0, 65519.0, 65520.0, 6.0e-8, 2.98e-8, 448.0, 464.0, 0.0078125]
+    rng = np.random.default_rng(7)
+    pats = rng.integers(0, 1 << 32, 400_000, dtype=np.uint64).astype(np.uint32)
+    # ties: bit patterns whose dropped low bits are exactly half-way, for bf16 (16 bits) and f16 (13 bits)
+    ties16 = (pats & np.uint32(0xFFFF0000)) | np.uint32(0x8000)
+    ties13 = (pats & np.uint32(0xFFFFE000)) | np.uint32(0x1000)
+    allv = np.concatenate([np.array(vals, np.float32).view(np.uint32), pats, ties16, ties13])
+    f = allv.view(np.float32)
+    return f[~np.isnan(f)]
+
+
+def test_bf16_matches_torch_conversion():
+    x = _special_f32()
+    want = torch.from_numpy(x.copy()).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    np.testing.assert_array_equal(oracle.f32_to_bf16(x), want)
+    assert oracle.f32_to_bf16(np.array([np.nan], np.float32))[0] == 0x7FC0
+    h = np.arange(1 << 16, dtype=np.uint32).astype(np.uint16)
+    back = torch.from_numpy(h.view(np.int16).copy()).view(torch.bfloat16).float().numpy()
+    got = oracle.bf16_to_f32(h)
+    ok = ~np.isnan(back)
+    np.testing.assert_array_equal(got[ok].view(np.uint32), back[ok].view(np.uint32))
+    assert np.all(np.isnan(got[~ok]))
+
+
+def test_f16_matches_numpy_conversion():
+    x = _special_f32()
+    with np.errstate(over="ignore"):
+        want = x.astype(np.float16).view(np.uint16)
+    np.testing.assert_array_equal(oracle.f32_to_f16(x), want)
+    h = np.arange(1 << 16, dtype=np.uint32).astype(np.uint16)
+    back = h.view(np.float16).astype(np.float32)
+    got = oracle.f16_to_f32(h)
+    ok = ~np.isnan(back)
+    np.testing.assert_array_equal(got[ok].view(np.uint32), back[ok].view(np.uint32))
+    assert np.all(np.isnan(got[~ok]))
+
+
+def test_e4m3_fixed_points():
+    with open(os.path.join(GOLDEN, "e4m3_points.txt")) as f:
+        rows = [ln.split() for ln in f if ln.strip() and not ln.startswith("#")]
+    codes = np.array([int(r[0], 16) for r in rows], dtype=np.uint8)
+    vals = np.array([float(r[1]) for r in rows], dtype=np.float32)
+    dec = oracle.e4m3_to_f32(codes)
+    for c, v, d in zip(codes, vals, dec):
+        if np.isnan(v):
+            assert np.isnan(d)
+        else:
+            assert d.view(np.uint32) == v.view(np.uint32), hex(c)
+            assert oracle.f32_to_e4m3(np.array([v]))[0] == c
+
+
+def test_e4m3_decode_all_codes_matches_torch():
+    codes = np.arange(256, dtype=np.uint8)
+    want = torch.from_numpy(codes.copy()).view(torch.float8_e4m3fn).float().numpy()
+    got = oracle.e4m3_to_f32(codes)
+    ok = ~np.isnan(want)
+    np.testing.assert_array_equal(got[ok].view(np.uint32), want[ok].view(np.uint32))
+    assert np.all(np.isnan(got[~ok])) and (~ok).sum() == 2
+
+
+def test_e4m3_encode_matches_torch_below_464():
+    vals = oracle.e4m3_to_f32(np.arange(256, dtype=np.uint8))
+    fin = np.unique(vals[np.isfinite(vals)])
+    mids = (fin[:-1].astype(np.float64) + fin[1:]) / 2  # exact midpoints between neighbours
+    mids = mids.astype(np.float32)
+    near = np.concatenate([mids, np.nextafter(mids, np.float32(np.inf)), np.nextafter(mids, np.float32(-np.inf)),
+                           fin, np.float32(2.0) ** np.arange(-14, -5, dtype=np.float32)])
+    rng = np.random.default_rng(11)
+    rnd = (rng.standard_normal(300_000) * rng.choice([1e-4, 1e-2, 1, 50], 300_000)).astype(np.float32)
+    x = np.concatenate([near, rnd, -near])
+    x = x[np.abs(x) < 464.0]
+    want = torch.from_numpy(x.copy()).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+    np.testing.assert_array_equal(oracle.f32_to_e4m3(x), want)
+
+
+def test_e4m3_saturates_and_maps_nan():
+    x = np.array([464.0, 500.0, 1e30, np.inf, -464.0, -np.inf, np.nan], np.float32)
+    np.testing.assert_array_equal(oracle.f32_to_e4m3(x), [0x7E, 0x7E, 0x7E, 0x7E, 0xFE, 0xFE, 0x7F])
+
+
+# ---------------------------------------------------------------- fp8 block codec and compressed ring
+
+
+def _q_block_lib(v):
+    """Independent restatement with numpy + torch's e4m3 conversion (valid while |v*inv| < 464)."""
+    v = np.asarray(v, np.float32)
+    amax = np.float32(np.max(np.abs(v))) if v.size else np.float32(0)
+    if amax == 0:
+        inv, scale = np.float32(1), np.float32(1)
+    else:
+        inv, scale = np.float32(448) / amax, amax / np.float32(448)
+    codes = torch.from_numpy((v * inv).astype(np.float32)).to(torch.float8_e4m3fn)
+    return codes.view(torch.uint8).numpy(), scale, codes.float().numpy()
+
+
+def _qdq_lib(v):
+    out = np.empty_like(np.asarray(v, np.float32))
+    for s in range(0, len(v), 128):
+        _, scale, dec = _q_block_lib(v[s:s + 128])
+        out[s:s + 128] = (dec * scale).astype(np.float32)
+    return out
+
+
+def test_fp8_quant_matches_library_restatement():
+    x = inputs.normal_f32((5, 0), 128 * 37 + 55, 1.0)
+    x[::97] *= np.float32(100)
+    codes, scales = oracle.fp8_quant(x, oracle.F32)
+    for b in range(len(scales)):
+        c, s, _ = _q_block_lib(x[b * 128:(b + 1) * 128])
+        np.testing.assert_array_equal(codes[b * 128:(b + 1) * 128], c)
+        assert scales[b] == s
+    deq = oracle.fp8_dequant(codes, scales, oracle.F32)
+    np.testing.assert_array_equal(deq, _qdq_lib(x))
+    # error bound: half a spacing of the block's E4M3 grid, i.e. <= 2^-4 |v| in the normal range and
+    # <= 2^-10 * scale below it
+    sc = np.repeat(scales, 128)[: x.size]
+    err = np.abs(deq.astype(np.float64) - x)
+    assert np.all(err <= np.maximum(np.abs(x) * 2.0 ** -4, sc * 2.0 ** -10) * (1 + 2 ** -20))
+
+
+def test_fp8_quant_round_trip_of_codes_and_zero_block():
+    vals = oracle.e4m3_to_f32(np.arange(256, dtype=np.uint8))
+    fin = vals[np.isfinite(vals)]
+    blk = np.resize(fin, 128).astype(np.float32)
+    blk[0] = 448.0  # amax = 448 -> inv = scale = 1
+    codes, scales = oracle.fp8_quant(blk, oracle.F32)
+    assert scales[0] == 1.0
+    np.testing.assert_array_equal(oracle.e4m3_to_f32(codes).view(np.uint32), blk.view(np.uint32))
+    codes, scales = oracle.fp8_quant(np.zeros(130, np.float32), oracle.F32)
+    assert np.all(codes == 0) and np.all(scales == 1.0)
+
+
+def test_fp8_ring_single_rank_is_quant_dequant():
+    x = inputs.normal_bf16((5, 1), 1000)
+    got = oracle.fp8_ring_allreduce([x], oracle.BF16, oracle.SUM)[0]
+    xf = torch.from_numpy(x.view(np.int16).copy()).view(torch.bfloat16).float().numpy()
+    want = inputs.f32_to_bf16_bits_lib(_qdq_lib(xf))
+    np.testing.assert_array_equal(got, want)
+
+
+def test_fp8_ring_two_ranks_closed_form():
+    """N=2: chunk 0 = bf16(deq(Q(deq(Q(x0)) + x1))), chunk 1 = bf16(deq(Q(deq(Q(x1)) + x0)))."""
+    count = 128 * 6 + 40
+    xs = inputs.rank_inputs("outlier_bf16", 2, count, cfg=5, extra=(77,))
+    got = oracle.fp8_ring_allreduce(xs, oracle.BF16, oracle.SUM)
+    f = [torch.from_numpy(x.view(np.int16).copy()).view(torch.bfloat16).float().numpy() for x in xs]
+    lo = oracle.chunk_bounds(count, 2)
+    want = np.empty(count, np.float32)
+    for c in range(2):
+        sl = slice(lo[c], lo[c + 1])
+        part = (_qdq_lib(f[c][sl]) + f[1 - c][sl]).astype(np.float32)
+        want[sl] = _qdq_lib(part)
+    want_b = inputs.f32_to_bf16_bits_lib(want)
+    for o in got:
+        np.testing.assert_array_equal(o, want_b)
+
+
+def test_fp8_ring_accuracy_vs_exact():
+    """Reported bound: each of the N-1 hops and the final quantization adds <= 1/16 relative of the block
+    scale's grid; compare the eight-rank result with the exact fp64 sum."""
+    n, count = 8, 128 * 64
+    xs = inputs.rank_inputs("outlier_bf16", n, count, cfg=5, extra=(78,))
+    got = oracle.fp8_ring_allreduce(xs, oracle.BF16, oracle.SUM)[0]
+    f = np.array([oracle.bf16_to_f32(x) for x in xs], dtype=np.float64)
+    exact = f.sum(axis=0)
+    g = oracle.bf16_to_f32(got).astype(np.float64)
+    blk_amax = np.repeat(np.abs(f).sum(axis=0).reshape(-1, 128).max(axis=1), 128)
+    assert np.all(np.abs(g - exact) <= n * blk_amax * 2.0 ** -4)
+
+
+# ---------------------------------------------------------------- buckets
+
+
+def test_bucket_plan_hand_example():
+    # cap 64 B, fp32 (16 B groups = 4 elements), N = 2 -> bucket counts rounded to 8 elements.
+    numels = [3, 5, 40, 1, 0, 2, 9]
+    b, off, cnt = oracle.bucket_plan(numels, 4, 2, 64)
+    # t0: pad 4 -> bucket 0 [0,4); t1: pad 8 -> fill 12*4=48 <= 64 -> [4,12); t2: pad 40 -> would exceed,
+    # new bucket 1 [0,40) (oversize, alone); t3: bucket 1 is over cap -> bucket 2 [0,4); t4: empty tensor at
+    # offset 4; t5: pad 4 -> [4,8); t6: pad 12 -> 8+12=20 elements = 80 B > 64 -> bucket 3 [0,12).
+    np.testing.assert_array_equal(b, [0, 0, 1, 2, 2, 2, 3])
+    np.testing.assert_array_equal(off, [0, 4, 0, 0, 4, 4, 0])
+    np.testing.assert_array_equal(cnt, [16, 40, 8, 16])
+
+
+def test_bucket_plan_properties_full_size():
+    sizes = inputs.bucket_sizes()
+    n, cap = 8, 25 << 20
+    b, off, cnt = oracle.bucket_plan(sizes, 4, n, cap)
+    assert np.all(np.diff(b) >= 0) and b[0] == 0 and b[-1] == len(cnt) - 1
+    assert np.all(off % 4 == 0) and np.all(cnt % (4 * n) == 0)
+    for k in range(len(cnt)):
+        ts = np.where(b == k)[0]
+        ends = off[ts] + sizes[ts]
+        assert np.all(ends <= cnt[k])
+        assert np.all(off[ts][1:] >= ends[:-1])  # disjoint, in order
+        if len(ts) > 1:
+            assert (off[ts[-1]] + (sizes[ts[-1]] + 3) // 4 * 4) * 4 <= cap
+        else:
+            pass  # a singleton may exceed the cap
+    big = sizes * 4 > cap
+    assert np.all([np.sum(b == b[t]) == 1 for t in np.where(big)[0]])
+
+
+def test_bucketed_allreduce_equals_per_tensor_exact():
+    """Integer-valued fp32 tensors: every association is exact, so the bucketed avg equals sum/N per tensor."""
+    n = 4
+    sizes = [5, 1, 300, 17, 4096, 2, 999]
+    rng = np.random.default_rng(3)
+    ts = [[rng.integers(-50, 50, s).astype(np.float32) for s in sizes] for _ in range(n)]
+    outs = oracle.bucketed_allreduce(ts, oracle.F32, oracle.AVG, cap_bytes=2048)
+    for t, s in enumerate(sizes):
+        exact = np.sum(np.array([ts[r][t] for r in range(n)], np.float64), axis=0) / n
+        for r in range(n):
+            np.testing.assert_array_equal(outs[r][t], exact.astype(np.float32))
+    # and it equals packing by hand + the ring oracle on each bucket
+    b, off, cnt = oracle.bucket_plan(sizes, 4, n, 2048)
+    for k in range(len(cnt)):
+        flat = [np.zeros(cnt[k], np.float32) for _ in range(n)]
+        for t in np.where(b == k)[0]:
+            for r in range(n):
+                flat[r][off[t]:off[t] + sizes[t]] = ts[r][t]
+        red = oracle.ring_allreduce(flat, oracle.F32, oracle.AVG)
+        for t in np.where(b == k)[0]:
+            np.testing.assert_array_equal(outs[0][t], red[0][off[t]:off[t] + sizes[t]])
