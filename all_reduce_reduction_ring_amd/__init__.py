@@ -1,0 +1,273 @@
+"""Python binding of libar, the MI355X ring all-reduce library (ctypes over the in-tree ``libar.so``).
+
+The binding only marshals arguments: torch tensors become device pointers, the current torch stream becomes
+the hipStream_t, and a non-zero ar_status becomes an :class:`ArError`. Every step of the all-reduce runs in
+the library's HIP kernels. There is no CPU fallback: if ``libar.so`` is missing or cannot be loaded, every
+call raises.
+
+Entry points (same names as ``include/ar.h``): ar_allreduce, ar_allreduce_ws, ar_allreduce_workspace_size,
+ar_bucket_plan, ar_bucket_pack, ar_bucket_unpack, ar_fp8_quant, ar_fp8_dequant, ar_status_string,
+ar_last_call, ar_version. Helpers: make_copy_descs, BucketedAllReduce.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import numpy as np
+
+__all__ = [
+    "AR_OK", "AR_ERR_INVALID", "AR_ERR_UNSUPPORTED", "AR_ERR_ALIAS", "AR_ERR_WORKSPACE", "AR_ERR_HIP",
+    "AR_F32", "AR_BF16", "AR_F16", "AR_I32", "AR_SUM", "AR_AVG", "AR_MIN", "AR_MAX",
+    "AR_ALGO_RING", "AR_ALGO_FUSED", "AR_ALGO_RHD", "AR_ALGO_RING_STEPWISE", "AR_ALGO_RHD_STEPWISE",
+    "AR_ALGO_RING_FP8", "AR_MAX_RANKS", "AR_FP8_BLOCK", "ArError", "lib", "lib_path",
+    "ar_allreduce", "ar_allreduce_ws", "ar_allreduce_workspace_size", "ar_bucket_plan", "ar_bucket_pack",
+    "ar_bucket_unpack", "ar_fp8_quant", "ar_fp8_dequant", "ar_status_string", "ar_last_call", "ar_version",
+    "make_copy_descs", "BucketedAllReduce", "dtype_code",
+]
+
+AR_OK, AR_ERR_INVALID, AR_ERR_UNSUPPORTED, AR_ERR_ALIAS, AR_ERR_WORKSPACE, AR_ERR_HIP = 0, 1, 2, 3, 4, 5
+AR_F32, AR_BF16, AR_F16, AR_I32 = 0, 1, 2, 3
+AR_SUM, AR_AVG, AR_MIN, AR_MAX = 0, 1, 2, 3
+AR_ALGO_RING, AR_ALGO_FUSED, AR_ALGO_RHD, AR_ALGO_RING_STEPWISE, AR_ALGO_RHD_STEPWISE, AR_ALGO_RING_FP8 = range(6)
+AR_MAX_RANKS = 64
+AR_FP8_BLOCK = 128
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_LIB_PATH = os.path.join(_HERE, "libar.so")
+_lib = None
+
+
+class ArError(RuntimeError):
+    def __init__(self, status: int, entry: str):
+        self.status = status
+        super().__init__(f"{entry}: {ar_status_string(status)}")
+
+
+class _CallRecord(ctypes.Structure):
+    _fields_ = [("seq", ctypes.c_uint64), ("entry", ctypes.c_char_p), ("nranks", ctypes.c_int),
+                ("dtype", ctypes.c_int), ("op", ctypes.c_int), ("algo", ctypes.c_int), ("status", ctypes.c_int),
+                ("count", ctypes.c_size_t)]
+
+
+def lib_path() -> str:
+    return _LIB_PATH
+
+
+def lib():
+    """Load libar.so (built in-tree by build.py). Raises if it is missing: there is no fallback path."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(_LIB_PATH):
+            raise RuntimeError(f"libar.so not found at {_LIB_PATH}; build it first "
+                               "(python -c 'import __graft_entry__ as g; g.build()')")
+        L = ctypes.CDLL(_LIB_PATH)
+        vp, sz, i32 = ctypes.c_void_p, ctypes.c_size_t, ctypes.c_int
+        L.ar_allreduce.argtypes = [vp, vp, i32, sz, i32, i32, i32, vp]
+        L.ar_allreduce_ws.argtypes = [vp, vp, i32, sz, i32, i32, i32, vp, sz, vp]
+        L.ar_allreduce_workspace_size.argtypes = [i32, sz, i32, i32, i32, ctypes.POINTER(sz)]
+        L.ar_bucket_plan.argtypes = [vp, i32, i32, i32, sz, vp, vp, vp, ctypes.POINTER(i32)]
+        L.ar_bucket_pack.argtypes = [vp, i32, i32, vp]
+        L.ar_bucket_unpack.argtypes = [vp, i32, i32, vp]
+        L.ar_fp8_quant.argtypes = [vp, i32, sz, vp, vp, vp]
+        L.ar_fp8_dequant.argtypes = [vp, vp, sz, vp, i32, vp]
+        L.ar_status_string.argtypes = [i32]
+        L.ar_status_string.restype = ctypes.c_char_p
+        L.ar_last_call.argtypes = [ctypes.POINTER(_CallRecord)]
+        for name in ("ar_allreduce", "ar_allreduce_ws", "ar_allreduce_workspace_size", "ar_bucket_plan",
+                     "ar_bucket_pack", "ar_bucket_unpack", "ar_fp8_quant", "ar_fp8_dequant", "ar_last_call",
+                     "ar_version"):
+            getattr(L, name).restype = i32
+        _lib = L
+    return _lib
+
+
+# ------------------------------------------------------------------------------------------ marshalling
+def dtype_code(t) -> int:
+    import torch
+    codes = {torch.float32: AR_F32, torch.bfloat16: AR_BF16, torch.float16: AR_F16, torch.int32: AR_I32}
+    if t not in codes:
+        raise TypeError(f"unsupported dtype {t}; expected float32, bfloat16, float16 or int32")
+    return codes[t]
+
+
+def _stream(stream):
+    import torch
+    if stream is None:
+        return ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+    if isinstance(stream, int):
+        return ctypes.c_void_p(stream)
+    return ctypes.c_void_p(stream.cuda_stream)
+
+
+def _check(rc: int, entry: str):
+    if rc != AR_OK:
+        raise ArError(rc, entry)
+
+
+def _rank_arrays(ins, outs):
+    if len(ins) != len(outs) or not ins:
+        raise ValueError("ins and outs must be non-empty lists of the same length (one tensor per rank)")
+    t0 = ins[0]
+    for t in list(ins) + list(outs):
+        # every rank must call with the same count and dtype; one call enforces it
+        if t.dtype != t0.dtype or t.numel() != t0.numel() or t.device != t0.device:
+            raise ValueError("all rank tensors must share dtype, element count and device")
+        if not t.is_contiguous():
+            raise ValueError("rank tensors must be contiguous")
+        if t.device.type != "cuda":
+            raise ValueError("rank tensors must be GPU tensors")
+    n = len(ins)
+    arr_in = (ctypes.c_void_p * n)(*[t.data_ptr() for t in ins])
+    arr_out = (ctypes.c_void_p * n)(*[t.data_ptr() for t in outs])
+    return arr_in, arr_out, n, t0.numel(), dtype_code(t0.dtype)
+
+
+def ar_allreduce(ins, outs, op=AR_SUM, algo=AR_ALGO_RING, stream=None):
+    """All-reduce ins[r] -> outs[r] for every rank r (outs[r] may be ins[r])."""
+    arr_in, arr_out, n, count, dt = _rank_arrays(ins, outs)
+    _check(lib().ar_allreduce(arr_in, arr_out, n, count, dt, op, algo, _stream(stream)), "ar_allreduce")
+
+
+def ar_allreduce_workspace_size(nranks, count, dtype, op, algo) -> int:
+    out = ctypes.c_size_t(0)
+    _check(lib().ar_allreduce_workspace_size(nranks, count, dtype, op, algo, ctypes.byref(out)),
+           "ar_allreduce_workspace_size")
+    return out.value
+
+
+def ar_allreduce_ws(ins, outs, op=AR_SUM, algo=AR_ALGO_RING, workspace=None, stream=None):
+    """ar_allreduce with a caller workspace tensor (any dtype, contiguous, on the same GPU)."""
+    arr_in, arr_out, n, count, dt = _rank_arrays(ins, outs)
+    wp = ctypes.c_void_p(workspace.data_ptr()) if workspace is not None else ctypes.c_void_p(0)
+    wb = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    _check(lib().ar_allreduce_ws(arr_in, arr_out, n, count, dt, op, algo, wp, wb, _stream(stream)),
+           "ar_allreduce_ws")
+
+
+def ar_bucket_plan(numels, dtype, nranks, cap_bytes=25 << 20):
+    """Host-only plan; returns (bucket_of int32[T], offset_of int64[T], bucket_count int64[nbuckets])."""
+    numels = np.ascontiguousarray(numels, dtype=np.int64)
+    nt = numels.size
+    bucket_of = np.zeros(max(nt, 1), np.int32)
+    offset_of = np.zeros(max(nt, 1), np.int64)
+    bcount = np.zeros(max(nt, 1), np.int64)
+    nb = ctypes.c_int(0)
+    _check(lib().ar_bucket_plan(numels.ctypes.data, nt, dtype, nranks, cap_bytes, bucket_of.ctypes.data,
+                                offset_of.ctypes.data, bcount.ctypes.data, ctypes.byref(nb)), "ar_bucket_plan")
+    return bucket_of[:nt], offset_of[:nt], bcount[: nb.value]
+
+
+def make_copy_descs(tasks, device):
+    """tasks: iterable of (src_ptr, dst_ptr, numel, zero_pad_after) -> device int64 tensor [ndescs, 4]
+    laid out as ar_copy_desc (two pointers, two int64)."""
+    import torch
+    host = np.array(list(tasks), dtype=np.uint64).reshape(-1, 4).view(np.int64)
+    return torch.from_numpy(host).to(device)
+
+
+def ar_bucket_pack(descs, dtype, stream=None):
+    _check(lib().ar_bucket_pack(ctypes.c_void_p(descs.data_ptr()), descs.shape[0], dtype, _stream(stream)),
+           "ar_bucket_pack")
+
+
+def ar_bucket_unpack(descs, dtype, stream=None):
+    _check(lib().ar_bucket_unpack(ctypes.c_void_p(descs.data_ptr()), descs.shape[0], dtype, _stream(stream)),
+           "ar_bucket_unpack")
+
+
+def ar_fp8_quant(x, codes, scales, stream=None):
+    """x: float32/bfloat16 GPU tensor; codes: uint8[numel]; scales: float32[ceil(numel/128)]."""
+    if codes.numel() < x.numel() or scales.numel() < (x.numel() + AR_FP8_BLOCK - 1) // AR_FP8_BLOCK:
+        raise ValueError("codes/scales too small")
+    _check(lib().ar_fp8_quant(ctypes.c_void_p(x.data_ptr()), dtype_code(x.dtype), x.numel(),
+                              ctypes.c_void_p(codes.data_ptr()), ctypes.c_void_p(scales.data_ptr()),
+                              _stream(stream)), "ar_fp8_quant")
+
+
+def ar_fp8_dequant(codes, scales, out, stream=None):
+    if codes.numel() < out.numel() or scales.numel() < (out.numel() + AR_FP8_BLOCK - 1) // AR_FP8_BLOCK:
+        raise ValueError("codes/scales too small")
+    _check(lib().ar_fp8_dequant(ctypes.c_void_p(codes.data_ptr()), ctypes.c_void_p(scales.data_ptr()), out.numel(),
+                                ctypes.c_void_p(out.data_ptr()), dtype_code(out.dtype), _stream(stream)),
+           "ar_fp8_dequant")
+
+
+def ar_status_string(status: int) -> str:
+    return lib().ar_status_string(status).decode()
+
+
+def ar_last_call():
+    rec = _CallRecord()
+    if lib().ar_last_call(ctypes.byref(rec)) != AR_OK:
+        return None
+    return {"seq": rec.seq, "entry": rec.entry.decode() if rec.entry else None, "nranks": rec.nranks,
+            "count": rec.count, "dtype": rec.dtype, "op": rec.op, "algo": rec.algo, "status": rec.status}
+
+
+def ar_version() -> int:
+    return lib().ar_version()
+
+
+# ------------------------------------------------------------------------------------------ bucketing
+class BucketedAllReduce:
+    """DDP-style bucketed all-reduce of per-rank tensor lists: pack every rank's tensors into its bucket
+    buffer (one launch), all-reduce each bucket with the ring kernel, unpack to per-tensor outputs (one
+    launch). The plan and descriptor tables are built once; bucket buffers are torch allocations."""
+
+    def __init__(self, ins, outs, op=AR_AVG, algo=AR_ALGO_RING, cap_bytes=25 << 20):
+        import torch
+        self.n = len(ins)
+        self.nt = len(ins[0])
+        if any(len(x) != self.nt for x in list(ins) + list(outs)):
+            raise ValueError("every rank needs the same number of tensors")
+        for t in range(self.nt):
+            _rank_arrays([ins[r][t] for r in range(self.n)], [outs[r][t] for r in range(self.n)])
+        t00 = ins[0][0]
+        self.dtype = dtype_code(t00.dtype)
+        self.op, self.algo = op, algo
+        numels = [ins[0][t].numel() for t in range(self.nt)]
+        self.bucket_of, self.offset_of, self.bucket_count = ar_bucket_plan(numels, self.dtype, self.n, cap_bytes)
+        self.bucket_start = np.concatenate([[0], np.cumsum(self.bucket_count)]).astype(np.int64)
+        total = int(self.bucket_start[-1])
+        self.buffers = [torch.empty(total, dtype=t00.dtype, device=t00.device) for _ in range(self.n)]
+        es = t00.element_size()
+        g = 16 // es
+        pack, unpack = [], []
+        for r in range(self.n):
+            base = self.buffers[r].data_ptr()
+            for t in range(self.nt):
+                b = int(self.bucket_of[t])
+                off = int(self.bucket_start[b] + self.offset_of[t])
+                numel = numels[t]
+                # zero pad up to the next tensor's start (or the bucket's end)
+                nxt = t + 1
+                end = (int(self.bucket_start[b] + self.offset_of[nxt])
+                       if nxt < self.nt and int(self.bucket_of[nxt]) == b else int(self.bucket_start[b + 1]))
+                pad = end - off - numel
+                assert pad >= 0 and pad < max(g * self.n, g) + g * self.n
+                pack.append((ins[r][t].data_ptr(), base + off * es, numel, pad))
+                unpack.append((base + off * es, outs[r][t].data_ptr(), numel, 0))
+        self.pack_descs = make_copy_descs(pack, t00.device)
+        self.unpack_descs = make_copy_descs(unpack, t00.device)
+        self.views = [[self.buffers[r][int(self.bucket_start[b]):int(self.bucket_start[b + 1])]
+                       for r in range(self.n)] for b in range(len(self.bucket_count))]
+
+    @property
+    def nbuckets(self):
+        return len(self.bucket_count)
+
+    def pack(self, stream=None):
+        ar_bucket_pack(self.pack_descs, self.dtype, stream)
+
+    def reduce(self, stream=None):
+        for v in self.views:
+            ar_allreduce(v, v, self.op, self.algo, stream)
+
+    def unpack(self, stream=None):
+        ar_bucket_unpack(self.unpack_descs, self.dtype, stream)
+
+    def __call__(self, stream=None):
+        self.pack(stream)
+        self.reduce(stream)
+        self.unpack(stream)

@@ -1,0 +1,250 @@
+// ar_api.hip -- the C ABI of libar: argument validation, dispatch to the kernels, the per-thread last-call
+// record. Nothing here allocates device memory or synchronises the stream.
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <atomic>
+#include <cstdint>
+#include <cstring>
+#include <mutex>
+
+#include "ar.h"
+#include "ar_internal.h"
+
+namespace ar {
+
+int cu_count() {
+  static std::atomic<int> cache[64];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0) dev = 0;
+  const int slot = dev < 64 ? dev : 63;
+  int v = cache[slot].load(std::memory_order_relaxed);
+  if (v <= 0) {
+    if (hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || v <= 0) v = 256;
+    cache[slot].store(v, std::memory_order_relaxed);
+  }
+  return v;
+}
+
+}  // namespace ar
+
+namespace {
+
+thread_local ar_call_record g_last;
+thread_local bool g_has_last = false;
+thread_local uint64_t g_seq = 0;
+
+int finish(const char* entry, int nranks, size_t count, int dtype, int op, int algo, int status) {
+  g_last.seq = ++g_seq;
+  g_last.entry = entry;
+  g_last.nranks = nranks;
+  g_last.count = count;
+  g_last.dtype = dtype;
+  g_last.op = op;
+  g_last.algo = algo;
+  g_last.status = status;
+  g_has_last = true;
+  return status;
+}
+
+int esize_of(int dtype) { return (dtype == AR_BF16 || dtype == AR_F16) ? 2 : 4; }
+bool valid_dtype(int d) { return d >= AR_F32 && d <= AR_I32; }
+bool valid_op(int o) { return o >= AR_SUM && o <= AR_MAX; }
+bool valid_algo(int a) { return a >= AR_ALGO_RING && a <= AR_ALGO_RING_FP8; }
+bool is_pow2(int n) { return n > 0 && (n & (n - 1)) == 0; }
+
+size_t workspace_bytes(int nranks, size_t count, int dtype, int algo) {
+  const bool stepwise = algo == AR_ALGO_RING_STEPWISE || algo == AR_ALGO_RHD_STEPWISE;
+  if (!stepwise || esize_of(dtype) == 4 || nranks < 2) return 0;
+  return static_cast<size_t>(nranks) * static_cast<size_t>(ar::stepwise_ws_stride(static_cast<int64_t>(count))) * 4;
+}
+
+struct Range {
+  uintptr_t lo, hi;
+};
+
+// Overlap among [p, p + bytes) ranges; sorted by start, any overlap shows up between neighbours.
+bool any_overlap(Range* r, int m) {
+  std::sort(r, r + m, [](const Range& a, const Range& b) { return a.lo < b.lo; });
+  for (int k = 1; k < m; ++k)
+    if (r[k].lo < r[k - 1].hi) return true;
+  return false;
+}
+
+int allreduce_impl(const char* entry, const void* const* in_bufs, void* const* out_bufs, int nranks, size_t count,
+                   int dtype, int op, int algo, void* workspace, size_t ws_bytes, void* stream) {
+  auto done = [&](int st) { return finish(entry, nranks, count, dtype, op, algo, st); };
+  if (!valid_dtype(dtype) || !valid_op(op) || !valid_algo(algo)) return done(AR_ERR_INVALID);
+  if (nranks < 1 || nranks > AR_MAX_RANKS) return done(AR_ERR_INVALID);
+  if (algo == AR_ALGO_RHD || algo == AR_ALGO_RHD_STEPWISE) {
+    if (!is_pow2(nranks)) return done(AR_ERR_UNSUPPORTED);
+  }
+  if (algo == AR_ALGO_RING_FP8) {
+    if ((dtype != AR_F32 && dtype != AR_BF16) || (op != AR_SUM && op != AR_AVG)) return done(AR_ERR_UNSUPPORTED);
+  }
+  if (count == 0) return done(AR_OK);
+  if (!in_bufs || !out_bufs) return done(AR_ERR_INVALID);
+  const size_t es = static_cast<size_t>(esize_of(dtype));
+  if (count > (SIZE_MAX / 2) / es) return done(AR_ERR_INVALID);
+  const size_t bytes = count * es;
+  Range ranges[2 * AR_MAX_RANKS + 1];
+  int m = 0;
+  bool vec = true;
+  for (int r = 0; r < nranks; ++r) {
+    if (!in_bufs[r] || !out_bufs[r]) return done(AR_ERR_INVALID);
+    const uintptr_t i = reinterpret_cast<uintptr_t>(in_bufs[r]), o = reinterpret_cast<uintptr_t>(out_bufs[r]);
+    if (i > UINTPTR_MAX - bytes || o > UINTPTR_MAX - bytes) return done(AR_ERR_INVALID);
+    ranges[m++] = Range{i, i + bytes};
+    if (o != i) ranges[m++] = Range{o, o + bytes};
+    if ((i | o) & 15u) vec = false;
+  }
+  const size_t need = workspace_bytes(nranks, count, dtype, algo);
+  if (need > 0) {
+    if (!workspace || ws_bytes < need) return done(AR_ERR_WORKSPACE);
+    const uintptr_t w = reinterpret_cast<uintptr_t>(workspace);
+    if (w & 255u) return done(AR_ERR_INVALID);
+    ranges[m++] = Range{w, w + need};
+  }
+  if (any_overlap(ranges, m)) return done(AR_ERR_ALIAS);
+
+  ar::RankPtrs p;
+  std::memset(&p, 0, sizeof(p));
+  for (int r = 0; r < nranks; ++r) {
+    p.in[r] = in_bufs[r];
+    p.out[r] = out_bufs[r];
+  }
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const int64_t n64 = static_cast<int64_t>(count);
+  hipError_t e = hipSuccess;
+  if (nranks == 1 && algo != AR_ALGO_RING_FP8) {
+    e = ar::launch_collapsed(p, 1, n64, dtype, op, AR_ALGO_RING, vec, s);
+  } else {
+    switch (algo) {
+      case AR_ALGO_RING:
+      case AR_ALGO_FUSED:
+      case AR_ALGO_RHD: e = ar::launch_collapsed(p, nranks, n64, dtype, op, algo, vec, s); break;
+      case AR_ALGO_RING_STEPWISE:
+        e = ar::launch_ring_stepwise(p, nranks, n64, dtype, op, static_cast<float*>(workspace), vec, s);
+        break;
+      case AR_ALGO_RHD_STEPWISE:
+        e = ar::launch_rhd_stepwise(p, nranks, n64, dtype, op, static_cast<float*>(workspace), vec, s);
+        break;
+      case AR_ALGO_RING_FP8: e = ar::launch_fp8_ring(p, nranks, n64, dtype, op, vec, s); break;
+      default: return done(AR_ERR_INVALID);
+    }
+  }
+  return done(e == hipSuccess ? AR_OK : AR_ERR_HIP);
+}
+
+}  // namespace
+
+extern "C" {
+
+int ar_version(void) { return AR_VERSION; }
+
+const char* ar_status_string(int status) {
+  switch (status) {
+    case AR_OK: return "AR_OK: success";
+    case AR_ERR_INVALID: return "AR_ERR_INVALID: invalid argument";
+    case AR_ERR_UNSUPPORTED: return "AR_ERR_UNSUPPORTED: unsupported combination of algorithm, dtype, op or rank count";
+    case AR_ERR_ALIAS: return "AR_ERR_ALIAS: rank buffers overlap (only exact in-place is allowed)";
+    case AR_ERR_WORKSPACE: return "AR_ERR_WORKSPACE: workspace missing or too small";
+    case AR_ERR_HIP: return "AR_ERR_HIP: HIP runtime error at launch";
+    default: return "unknown ar_status";
+  }
+}
+
+int ar_last_call(ar_call_record* rec) {
+  if (!rec || !g_has_last) return AR_ERR_INVALID;
+  *rec = g_last;
+  return AR_OK;
+}
+
+int ar_allreduce_workspace_size(int nranks, size_t count, int dtype, int op, int algo, size_t* bytes) {
+  if (!bytes || !valid_dtype(dtype) || !valid_op(op) || !valid_algo(algo) || nranks < 1 || nranks > AR_MAX_RANKS)
+    return AR_ERR_INVALID;
+  *bytes = workspace_bytes(nranks, count, dtype, algo);
+  return AR_OK;
+}
+
+int ar_allreduce(const void* const* in_bufs, void* const* out_bufs, int nranks, size_t count, int dtype, int op,
+                 int algo, void* stream) {
+  return allreduce_impl("ar_allreduce", in_bufs, out_bufs, nranks, count, dtype, op, algo, nullptr, 0, stream);
+}
+
+int ar_allreduce_ws(const void* const* in_bufs, void* const* out_bufs, int nranks, size_t count, int dtype, int op,
+                    int algo, void* workspace, size_t ws_bytes, void* stream) {
+  return allreduce_impl("ar_allreduce_ws", in_bufs, out_bufs, nranks, count, dtype, op, algo, workspace, ws_bytes,
+                        stream);
+}
+
+int ar_bucket_plan(const int64_t* numels, int ntensors, int dtype, int nranks, size_t cap_bytes, int32_t* bucket_of,
+                   int64_t* offset_of, int64_t* bucket_count, int* nbuckets) {
+  auto done = [&](int st) { return finish("ar_bucket_plan", nranks, static_cast<size_t>(ntensors), dtype, -1, -1, st); };
+  if (ntensors < 0 || !valid_dtype(dtype) || nranks < 1 || nranks > AR_MAX_RANKS || cap_bytes == 0 || !nbuckets)
+    return done(AR_ERR_INVALID);
+  if (ntensors > 0 && (!numels || !bucket_of || !offset_of || !bucket_count)) return done(AR_ERR_INVALID);
+  const int64_t es = esize_of(dtype);
+  const int64_t g = 16 / es;                 // elements per 16-byte group
+  const int64_t unit = g * nranks;           // bucket length granularity: N chunks of whole groups
+  // Bounds keep every product below INT64_MAX: numel * es <= INT64_MAX/4 and cap <= INT64_MAX/4.
+  const int64_t cap = cap_bytes > static_cast<size_t>(INT64_MAX / 4) ? INT64_MAX / 4 : static_cast<int64_t>(cap_bytes);
+  for (int t = 0; t < ntensors; ++t)
+    if (numels[t] < 0 || numels[t] > (INT64_MAX / 4) / es) return done(AR_ERR_INVALID);
+  int b = -1;
+  int64_t fill = 0;
+  for (int t = 0; t < ntensors; ++t) {
+    const int64_t len = (numels[t] + g - 1) / g * g;
+    const bool over = fill > 0 && (fill + len) * es > cap;
+    if (b < 0 || over) {
+      if (b >= 0) bucket_count[b] = (fill + unit - 1) / unit * unit;
+      ++b;
+      fill = 0;
+    }
+    bucket_of[t] = b;
+    offset_of[t] = fill;
+    fill += len;
+  }
+  if (b >= 0) bucket_count[b] = (fill + unit - 1) / unit * unit;
+  *nbuckets = b + 1;
+  return done(AR_OK);
+}
+
+static int batched_copy(const char* entry, const ar_copy_desc* d_descs, int ndescs, int dtype, void* stream) {
+  auto done = [&](int st) { return finish(entry, 0, static_cast<size_t>(ndescs), dtype, -1, -1, st); };
+  if (ndescs < 0 || !valid_dtype(dtype)) return done(AR_ERR_INVALID);
+  if (ndescs == 0) return done(AR_OK);
+  if (!d_descs) return done(AR_ERR_INVALID);
+  hipError_t e = ar::launch_batched_copy(d_descs, ndescs, esize_of(dtype), static_cast<hipStream_t>(stream));
+  return done(e == hipSuccess ? AR_OK : AR_ERR_HIP);
+}
+
+int ar_bucket_pack(const ar_copy_desc* d_descs, int ndescs, int dtype, void* stream) {
+  return batched_copy("ar_bucket_pack", d_descs, ndescs, dtype, stream);
+}
+
+int ar_bucket_unpack(const ar_copy_desc* d_descs, int ndescs, int dtype, void* stream) {
+  return batched_copy("ar_bucket_unpack", d_descs, ndescs, dtype, stream);
+}
+
+int ar_fp8_quant(const void* in, int in_dtype, size_t count, uint8_t* codes, float* scales, void* stream) {
+  auto done = [&](int st) { return finish("ar_fp8_quant", 1, count, in_dtype, -1, -1, st); };
+  if (in_dtype != AR_F32 && in_dtype != AR_BF16) return done(AR_ERR_INVALID);
+  if (count == 0) return done(AR_OK);
+  if (!in || !codes || !scales || count > static_cast<size_t>(INT64_MAX / 8)) return done(AR_ERR_INVALID);
+  hipError_t e = ar::launch_fp8_quant(in, in_dtype, static_cast<int64_t>(count), codes, scales,
+                                      static_cast<hipStream_t>(stream));
+  return done(e == hipSuccess ? AR_OK : AR_ERR_HIP);
+}
+
+int ar_fp8_dequant(const uint8_t* codes, const float* scales, size_t count, void* out, int out_dtype, void* stream) {
+  auto done = [&](int st) { return finish("ar_fp8_dequant", 1, count, out_dtype, -1, -1, st); };
+  if (out_dtype != AR_F32 && out_dtype != AR_BF16) return done(AR_ERR_INVALID);
+  if (count == 0) return done(AR_OK);
+  if (!codes || !scales || !out || count > static_cast<size_t>(INT64_MAX / 8)) return done(AR_ERR_INVALID);
+  hipError_t e = ar::launch_fp8_dequant(codes, scales, static_cast<int64_t>(count), out, out_dtype,
+                                        static_cast<hipStream_t>(stream));
+  return done(e == hipSuccess ? AR_OK : AR_ERR_HIP);
+}
+
+}  // extern "C"

@@ -1,0 +1,288 @@
+// ar_collapsed.hip -- one-pass all-reduce kernels: ring order, rank order (reduce + broadcast) and the
+// recursive halving-doubling tree.
+//
+// Ring order (jisaku.com glossary "AllReduce（オールリデュース）", section Ring-AllReduceの仕組み; astro-wiki
+// "AllReduce", section Ring AllReduce, phases 阶段一 and 阶段二): with reduce-scatter round s sending chunk
+// (i-s) mod N from rank i to rank i+1, the partial of chunk c starts at rank c and picks up ranks c+1, c+2,
+// ... in turn; the owner finishes it and all-gather copies it everywhere. On one GPU nothing has to move
+// between the rounds, so each thread carries the partial of its 16-byte slot in registers through all N
+// ranks in exactly that order, applies the owner epilogue and stores the finished slot to all N ranks:
+// N reads + N writes per element, the minimum HBM traffic, bit-identical to the literal rounds.
+//
+// Rank order (same glossary, section AllReduceの基本動作: Reduce + Broadcast): the same pass with every
+// chunk folded from rank 0.
+//
+// Halving-doubling (glossary algorithm table, Recursive Halving-Doubling; astro-wiki section 其他 AllReduce
+// 算法, Rabenseifner row): halving step j pairs ranks N >> (j+1) apart, so every element ends as the pairwise
+// tree combining ranks N/2 apart first; the pass evaluates that tree in registers.
+//
+// Layout: grid.y = chunk c (ring/fused) or 1 (tree); grid.x strides over the chunk's 16-byte slots. A chunk
+// whose start or end is not slot-aligned has its few edge elements done element-wise by block x = 0.
+#include "ar_device.h"
+#include "ar_internal.h"
+
+namespace ar {
+namespace {
+
+constexpr int kThreads = 256;
+
+struct CollapsedArgs {
+  RankPtrs p;
+  int64_t count;
+  int64_t q;  // count / nchunks
+  int64_t r;  // count % nchunks
+  int n;      // ranks
+  int rot;    // 1: chunk c folds from rank c (ring); 0: from rank 0
+  int vec;    // 1: all buffers 16-byte aligned
+};
+
+// ------------------------------------------------------------------------------------------ fold orders
+// Ring / rank order for one slot at byte offset `off`: x[start], x[start+1], ... (mod n).
+template <int DT, int OP, int NR>
+__device__ __forceinline__ u32x4 ring_slot(const CollapsedArgs& a, int start, int64_t off) {
+  using S = Slot<DT>;
+  using Acc = typename S::Acc;
+  constexpr int V = S::V;
+  Acc acc[V], t[V];
+  if constexpr (NR > 0) {
+    u32x4 x[NR];
+#pragma unroll
+    for (int k = 0; k < NR; ++k) {
+      int r = start + k;
+      r = r >= NR ? r - NR : r;
+      x[k] = ld16(static_cast<const char*>(a.p.in[r]) + off);
+    }
+    S::unpack(x[0], acc);
+#pragma unroll
+    for (int k = 1; k < NR; ++k) {
+      S::unpack(x[k], t);
+#pragma unroll
+      for (int e = 0; e < V; ++e) acc[e] = combine<OP>(acc[e], t[e]);
+    }
+  } else {
+    const int n = a.n;
+    S::unpack(ld16(static_cast<const char*>(a.p.in[start]) + off), acc);
+    int k = 1;
+    for (; k + 3 < n; k += 4) {
+      u32x4 x[4];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        int r = start + k + j;
+        r = r >= n ? r - n : r;
+        x[j] = ld16(static_cast<const char*>(a.p.in[r]) + off);
+      }
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        S::unpack(x[j], t);
+#pragma unroll
+        for (int e = 0; e < V; ++e) acc[e] = combine<OP>(acc[e], t[e]);
+      }
+    }
+    for (; k < n; ++k) {
+      int r = start + k;
+      r = r >= n ? r - n : r;
+      S::unpack(ld16(static_cast<const char*>(a.p.in[r]) + off), t);
+#pragma unroll
+      for (int e = 0; e < V; ++e) acc[e] = combine<OP>(acc[e], t[e]);
+    }
+  }
+  const int n = NR > 0 ? NR : a.n;
+#pragma unroll
+  for (int e = 0; e < V; ++e) acc[e] = finalize<OP>(acc[e], n);
+  return S::pack(acc);
+}
+
+// Pairwise tree over ranks OFF, OFF+STRIDE, OFF+2*STRIDE, ... (NR of them): tree(evens) (+) tree(odds).
+// At the top (STRIDE 1, OFF 0) this is the halving tree: N=8 gives ((x0+x4)+(x2+x6))+((x1+x5)+(x3+x7)).
+template <int DT, int OP, int NR, int STRIDE, int OFF>
+__device__ __forceinline__ void tree_fold(const CollapsedArgs& a, int64_t off, typename Traits<DT>::Acc (&acc)[Traits<DT>::kVec]) {
+  using S = Slot<DT>;
+  if constexpr (NR == 1) {
+    S::unpack(ld16(static_cast<const char*>(a.p.in[OFF]) + off), acc);
+  } else {
+    typename Traits<DT>::Acc b[Traits<DT>::kVec];
+    tree_fold<DT, OP, NR / 2, STRIDE * 2, OFF>(a, off, acc);
+    tree_fold<DT, OP, NR / 2, STRIDE * 2, OFF + STRIDE>(a, off, b);
+#pragma unroll
+    for (int e = 0; e < Traits<DT>::kVec; ++e) acc[e] = combine<OP>(acc[e], b[e]);
+  }
+}
+
+template <int DT, int OP, int NR>
+__device__ __forceinline__ u32x4 tree_slot(const CollapsedArgs& a, int64_t off) {
+  using S = Slot<DT>;
+  typename S::Acc acc[S::V];
+  tree_fold<DT, OP, NR, 1, 0>(a, off, acc);
+#pragma unroll
+  for (int e = 0; e < S::V; ++e) acc[e] = finalize<OP>(acc[e], NR);
+  return S::pack(acc);
+}
+
+// Element-wise versions for slot edges and unaligned buffers.
+template <int DT, int OP>
+__device__ __forceinline__ uint32_t ring_elem(const CollapsedArgs& a, int start, int64_t e) {
+  const int n = a.n;
+  auto acc = widen<DT>(load_elem<DT>(a.p.in[start], e));
+  for (int k = 1; k < n; ++k) {
+    int r = start + k;
+    r = r >= n ? r - n : r;
+    acc = combine<OP>(acc, widen<DT>(load_elem<DT>(a.p.in[r], e)));
+  }
+  return narrow<DT>(finalize<OP>(acc, n));
+}
+
+// Tree for runtime n (power of two): the halving tree evaluated as a binary counter over the leaves in
+// bit-reversed rank order (leaf j is rank bitrev(j)); each completed pair of equal-height subtrees merges.
+template <int DT, int OP>
+__device__ __forceinline__ uint32_t tree_elem(const CollapsedArgs& a, int64_t e) {
+  using Acc = typename Traits<DT>::Acc;
+  const int n = a.n;
+  int k = 0;
+  while ((1 << k) < n) ++k;
+  Acc stack[7];
+  int height[7];
+  int sp = 0;
+  for (int j = 0; j < n; ++j) {
+    int rev = 0;
+    for (int b = 0; b < k; ++b) rev |= ((j >> b) & 1) << (k - 1 - b);
+    Acc v = widen<DT>(load_elem<DT>(a.p.in[rev], e));
+    int h = 0;
+    while (sp > 0 && height[sp - 1] == h) {
+      v = combine<OP>(stack[sp - 1], v);
+      --sp;
+      ++h;
+    }
+    stack[sp] = v;
+    height[sp] = h;
+    ++sp;
+  }
+  return narrow<DT>(finalize<OP>(stack[0], n));
+}
+
+template <int DT, int OP, int NR, bool TREE>
+__device__ __forceinline__ void edge_elem(const CollapsedArgs& a, int start, int64_t e) {
+  uint32_t b = TREE ? tree_elem<DT, OP>(a, e) : ring_elem<DT, OP>(a, start, e);
+  const int n = NR > 0 ? NR : a.n;
+  for (int r = 0; r < n; ++r) store_elem<DT>(a.p.out[r], e, b);
+}
+
+// ------------------------------------------------------------------------------------------ kernel
+template <int DT, int OP, int NR, int U, bool TREE>
+__global__ __launch_bounds__(kThreads) void collapsed_kernel(CollapsedArgs a) {
+  constexpr int V = Traits<DT>::kVec;
+  const int c = blockIdx.y;
+  const int start = a.rot ? c : 0;
+  const int64_t lo = chunk_lo(a.q, a.r, c), hi = chunk_lo(a.q, a.r, c + 1);
+  const int64_t stride = static_cast<int64_t>(gridDim.x) * kThreads;
+  const int n = NR > 0 ? NR : a.n;
+
+  if (!a.vec) {
+    for (int64_t e = lo + static_cast<int64_t>(blockIdx.x) * kThreads + threadIdx.x; e < hi; e += stride)
+      edge_elem<DT, OP, NR, TREE>(a, start, e);
+    return;
+  }
+
+  const int64_t vlo = (lo + V - 1) / V, vhi = hi / V;
+  int64_t v = vlo + static_cast<int64_t>(blockIdx.x) * kThreads + threadIdx.x;
+  auto slot = [&](int64_t vv) -> u32x4 {
+    if constexpr (TREE) return tree_slot<DT, OP, NR>(a, vv * 16);
+    else return ring_slot<DT, OP, NR>(a, start, vv * 16);
+  };
+  for (; v + (U - 1) * stride < vhi; v += U * stride) {
+    u32x4 w[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) w[u] = slot(v + u * stride);
+#pragma unroll
+    for (int u = 0; u < U; ++u)
+      for (int r = 0; r < n; ++r) st16(static_cast<char*>(a.p.out[r]) + (v + u * stride) * 16, w[u]);
+  }
+  for (; v < vhi; v += stride) {
+    u32x4 w = slot(v);
+    for (int r = 0; r < n; ++r) st16(static_cast<char*>(a.p.out[r]) + v * 16, w);
+  }
+
+  if (blockIdx.x == 0) {
+    int64_t h1 = vlo * V, t0 = vhi * V;
+    if (vlo >= vhi) {  // no whole aligned slot inside the chunk
+      h1 = hi;
+      t0 = hi;
+    }
+    for (int64_t e = lo + threadIdx.x; e < h1; e += kThreads) edge_elem<DT, OP, NR, TREE>(a, start, e);
+    for (int64_t e = t0 + threadIdx.x; e < hi; e += kThreads) edge_elem<DT, OP, NR, TREE>(a, start, e);
+  }
+}
+
+// ------------------------------------------------------------------------------------------ launch
+template <int DT, int OP, int NR, int U, bool TREE>
+hipError_t launch_one(CollapsedArgs& a, int nchunks, hipStream_t s) {
+  constexpr int V = Traits<DT>::kVec;
+  const int64_t per_chunk = a.q + 1;
+  const int64_t slots = a.vec ? (per_chunk + V - 1) / V : per_chunk;
+  int64_t want = (slots + static_cast<int64_t>(kThreads) * U - 1) / (static_cast<int64_t>(kThreads) * U);
+  int64_t cap = (static_cast<int64_t>(cu_count()) * 8 + nchunks - 1) / nchunks;
+  if (cap < 1) cap = 1;
+  int64_t bx = want < cap ? want : cap;
+  if (bx < 1) bx = 1;
+  dim3 grid(static_cast<unsigned>(bx), static_cast<unsigned>(nchunks));
+  hipLaunchKernelGGL((collapsed_kernel<DT, OP, NR, U, TREE>), grid, dim3(kThreads), 0, s, a);
+  return hipGetLastError();
+}
+
+template <int DT, int OP>
+hipError_t dispatch_n(CollapsedArgs& a, int algo, hipStream_t s) {
+  const int n = a.n;
+  if (algo == AR_ALGO_RHD && n > 1) {
+    switch (n) {
+      case 2: return launch_one<DT, OP, 2, 2, true>(a, 1, s);
+      case 4: return launch_one<DT, OP, 4, 2, true>(a, 1, s);
+      case 8: return launch_one<DT, OP, 8, 2, true>(a, 1, s);
+      case 16: return launch_one<DT, OP, 16, 1, true>(a, 1, s);
+      case 32: return launch_one<DT, OP, 32, 1, true>(a, 1, s);
+      case 64: return launch_one<DT, OP, 64, 1, true>(a, 1, s);
+      default: return hipErrorInvalidValue;
+    }
+  }
+  switch (n) {
+    case 2: return launch_one<DT, OP, 2, 2, false>(a, n, s);
+    case 4: return launch_one<DT, OP, 4, 2, false>(a, n, s);
+    case 8: return launch_one<DT, OP, 8, 2, false>(a, n, s);
+    case 16: return launch_one<DT, OP, 16, 1, false>(a, n, s);
+    default: return launch_one<DT, OP, 0, 1, false>(a, n, s);
+  }
+}
+
+template <int DT>
+hipError_t dispatch_op(CollapsedArgs& a, int op, int algo, hipStream_t s) {
+  switch (op) {
+    case AR_SUM: return dispatch_n<DT, AR_SUM>(a, algo, s);
+    case AR_AVG: return dispatch_n<DT, AR_AVG>(a, algo, s);
+    case AR_MIN: return dispatch_n<DT, AR_MIN>(a, algo, s);
+    case AR_MAX: return dispatch_n<DT, AR_MAX>(a, algo, s);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+}  // namespace
+
+hipError_t launch_collapsed(const RankPtrs& p, int n, int64_t count, int dtype, int op, int algo, bool vec,
+                            hipStream_t s) {
+  CollapsedArgs a;
+  a.p = p;
+  a.count = count;
+  a.n = n;
+  a.vec = vec ? 1 : 0;
+  const bool tree = algo == AR_ALGO_RHD && n > 1;
+  const int nchunks = tree ? 1 : n;
+  a.q = count / nchunks;
+  a.r = count % nchunks;
+  a.rot = algo == AR_ALGO_RING ? 1 : 0;
+  switch (dtype) {
+    case AR_F32: return dispatch_op<AR_F32>(a, op, algo, s);
+    case AR_BF16: return dispatch_op<AR_BF16>(a, op, algo, s);
+    case AR_F16: return dispatch_op<AR_F16>(a, op, algo, s);
+    case AR_I32: return dispatch_op<AR_I32>(a, op, algo, s);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+}  // namespace ar

@@ -1,0 +1,159 @@
+// ar_device.h -- device-side element arithmetic shared by the libar kernels (gfx950, wave64).
+//
+// Element values in flight: fp32 for F32/BF16/F16 (16-bit inputs widen exactly), uint32 for I32 (sums
+// wrap modulo 2^32). Outputs round once, to nearest even, into the storage type; NaN rounds to the
+// canonical quiet NaN of the target type. Build with -ffp-contract=off: every float operation below must
+// stay one IEEE operation.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "ar.h"
+
+namespace ar {
+
+// Native 4 x 32-bit vector (one 16-byte slot); element k is v[k].
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+constexpr uint32_t kNaN32 = 0x7FC00000u;
+constexpr uint32_t kNaNBF16 = 0x7FC0u;
+constexpr uint32_t kNaNF16 = 0x7E00u;
+
+// ------------------------------------------------------------------------------------------ type traits
+// kVec: elements per 16-byte vector slot.
+template <int DT> struct Traits;
+template <> struct Traits<AR_F32> { using Acc = float; static constexpr int kVec = 4; static constexpr int kSize = 4; };
+template <> struct Traits<AR_BF16> { using Acc = float; static constexpr int kVec = 8; static constexpr int kSize = 2; };
+template <> struct Traits<AR_F16> { using Acc = float; static constexpr int kVec = 8; static constexpr int kSize = 2; };
+template <> struct Traits<AR_I32> { using Acc = uint32_t; static constexpr int kVec = 4; static constexpr int kSize = 4; };
+
+__device__ __forceinline__ bool is_nan(float f) { return (__float_as_uint(f) & 0x7FFFFFFFu) > 0x7F800000u; }
+
+// fp32 -> bf16 bits: round to nearest even on the upper 16 bits of the binary32 pattern.
+__device__ __forceinline__ uint32_t bf16_bits(float f) {
+  uint32_t u = __float_as_uint(f);
+  if ((u & 0x7FFFFFFFu) > 0x7F800000u) return kNaNBF16;
+  u += 0x7FFFu + ((u >> 16) & 1u);
+  return u >> 16;
+}
+__device__ __forceinline__ float bf16_value(uint32_t h) { return __uint_as_float(h << 16); }
+
+// fp32 <-> binary16 through the hardware conversions (round to nearest even, denormals kept).
+__device__ __forceinline__ uint32_t f16_bits(float f) {
+  if (is_nan(f)) return kNaNF16;
+  _Float16 h = static_cast<_Float16>(f);
+  return __builtin_bit_cast(uint16_t, h);
+}
+__device__ __forceinline__ float f16_value(uint32_t h) {
+  return static_cast<float>(__builtin_bit_cast(_Float16, static_cast<uint16_t>(h)));
+}
+
+// Storage element (as raw bits) -> value in flight.
+template <int DT> __device__ __forceinline__ typename Traits<DT>::Acc widen(uint32_t bits);
+template <> __device__ __forceinline__ float widen<AR_F32>(uint32_t b) { return __uint_as_float(b); }
+template <> __device__ __forceinline__ float widen<AR_BF16>(uint32_t b) { return bf16_value(b); }
+template <> __device__ __forceinline__ float widen<AR_F16>(uint32_t b) { return f16_value(b); }
+template <> __device__ __forceinline__ uint32_t widen<AR_I32>(uint32_t b) { return b; }
+
+template <int DT> __device__ __forceinline__ uint32_t narrow(typename Traits<DT>::Acc v);
+template <> __device__ __forceinline__ uint32_t narrow<AR_F32>(float v) { return __float_as_uint(v); }
+template <> __device__ __forceinline__ uint32_t narrow<AR_BF16>(float v) { return bf16_bits(v); }
+template <> __device__ __forceinline__ uint32_t narrow<AR_F16>(float v) { return f16_bits(v); }
+template <> __device__ __forceinline__ uint32_t narrow<AR_I32>(uint32_t v) { return v; }
+
+// ------------------------------------------------------------------------------------------ reduction ops
+// min/max on floats: NaN-propagating to the canonical NaN; equal operands differ only for +-0, where the
+// bitwise OR (min) gives -0 and the AND (max) gives +0.
+__device__ __forceinline__ float min_rule(float a, float b) {
+  if (is_nan(a) || is_nan(b)) return __uint_as_float(kNaN32);
+  if (a < b) return a;
+  if (b < a) return b;
+  return __uint_as_float(__float_as_uint(a) | __float_as_uint(b));
+}
+__device__ __forceinline__ float max_rule(float a, float b) {
+  if (is_nan(a) || is_nan(b)) return __uint_as_float(kNaN32);
+  if (a > b) return a;
+  if (b > a) return b;
+  return __uint_as_float(__float_as_uint(a) & __float_as_uint(b));
+}
+
+// acc: the partial arriving along the ring; loc: the receiving rank's own value.
+template <int OP> __device__ __forceinline__ float combine(float acc, float loc) {
+  if constexpr (OP == AR_MIN) return min_rule(acc, loc);
+  else if constexpr (OP == AR_MAX) return max_rule(acc, loc);
+  else return acc + loc;
+}
+template <int OP> __device__ __forceinline__ uint32_t combine(uint32_t acc, uint32_t loc) {
+  if constexpr (OP == AR_MIN) return static_cast<uint32_t>(min(static_cast<int32_t>(acc), static_cast<int32_t>(loc)));
+  else if constexpr (OP == AR_MAX) return static_cast<uint32_t>(max(static_cast<int32_t>(acc), static_cast<int32_t>(loc)));
+  else return acc + loc;
+}
+
+// Owner epilogue: avg divides once by N.
+template <int OP> __device__ __forceinline__ float finalize(float v, int n) {
+  if constexpr (OP == AR_AVG) return v / static_cast<float>(n);
+  else return v;
+}
+template <int OP> __device__ __forceinline__ uint32_t finalize(uint32_t v, int n) {
+  if constexpr (OP == AR_AVG) return static_cast<uint32_t>(static_cast<int32_t>(v) / n);
+  else return v;
+}
+
+// ------------------------------------------------------------------------------------------ 16-byte slots
+// A slot is kVec consecutive elements held as a u32x4 of storage bits.
+template <int DT> struct Slot {
+  using Acc = typename Traits<DT>::Acc;
+  static constexpr int V = Traits<DT>::kVec;
+
+  __device__ __forceinline__ static void unpack(const u32x4& w, Acc (&a)[V]) {
+    const uint32_t ws[4] = {w[0], w[1], w[2], w[3]};
+    if constexpr (Traits<DT>::kSize == 4) {
+#pragma unroll
+      for (int k = 0; k < 4; ++k) a[k] = widen<DT>(ws[k]);
+    } else {
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        a[2 * k] = widen<DT>(ws[k] & 0xFFFFu);
+        a[2 * k + 1] = widen<DT>(ws[k] >> 16);
+      }
+    }
+  }
+  __device__ __forceinline__ static u32x4 pack(const Acc (&a)[V]) {
+    uint32_t ws[4];
+    if constexpr (Traits<DT>::kSize == 4) {
+#pragma unroll
+      for (int k = 0; k < 4; ++k) ws[k] = narrow<DT>(a[k]);
+    } else {
+#pragma unroll
+      for (int k = 0; k < 4; ++k) ws[k] = narrow<DT>(a[2 * k]) | (narrow<DT>(a[2 * k + 1]) << 16);
+    }
+    u32x4 v;
+    v[0] = ws[0]; v[1] = ws[1]; v[2] = ws[2]; v[3] = ws[3];
+    return v;
+  }
+};
+
+// Scalar element access by element index on raw storage.
+template <int DT> __device__ __forceinline__ uint32_t load_elem(const void* base, int64_t e) {
+  if constexpr (Traits<DT>::kSize == 4) return static_cast<const uint32_t*>(base)[e];
+  else return static_cast<const uint16_t*>(base)[e];
+}
+template <int DT> __device__ __forceinline__ void store_elem(void* base, int64_t e, uint32_t bits) {
+  if constexpr (Traits<DT>::kSize == 4) static_cast<uint32_t*>(base)[e] = bits;
+  else static_cast<uint16_t*>(base)[e] = static_cast<uint16_t>(bits);
+}
+
+// Streaming 16-byte loads and stores. Each element is read once and written once per call, so the data
+// is marked non-temporal to keep it from displacing anything useful in the caches.
+__device__ __forceinline__ u32x4 ld16(const void* p) {
+  return __builtin_nontemporal_load(static_cast<const u32x4*>(p));
+}
+__device__ __forceinline__ void st16(void* p, const u32x4& v) {
+  __builtin_nontemporal_store(v, static_cast<u32x4*>(p));
+}
+
+// Balanced chunk split: chunk c = [c*q + min(c, r), ...) with q = count / N, r = count % N.
+__device__ __forceinline__ int64_t chunk_lo(int64_t q, int64_t r, int64_t c) { return c * q + (c < r ? c : r); }
+
+}  // namespace ar

@@ -1,0 +1,41 @@
+// ar_internal.h -- launchers shared between the libar host layer and its kernel files.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "ar.h"
+
+namespace ar {
+
+// Rank buffer table passed by value in the kernel arguments (1 KiB; fits the 4 KiB kernarg limit).
+struct RankPtrs {
+  const void* in[AR_MAX_RANKS];
+  void* out[AR_MAX_RANKS];
+};
+
+// Number of compute units of the current device (cached per device id).
+int cu_count();
+
+// One-pass kernels. algo: AR_ALGO_RING (chunk c folds from rank c), AR_ALGO_FUSED (folds from rank 0) or
+// AR_ALGO_RHD (pairwise XOR tree, n a power of two). vec: every buffer is 16-byte aligned.
+hipError_t launch_collapsed(const RankPtrs& p, int n, int64_t count, int dtype, int op, int algo, bool vec,
+                            hipStream_t s);
+
+// Round-per-launch schedules. ws: fp32 partial mirror (n * ws_stride floats) for 16-bit types, else null.
+int64_t stepwise_ws_stride(int64_t count);
+hipError_t launch_ring_stepwise(const RankPtrs& p, int n, int64_t count, int dtype, int op, float* ws, bool vec,
+                                hipStream_t s);
+hipError_t launch_rhd_stepwise(const RankPtrs& p, int n, int64_t count, int dtype, int op, float* ws, bool vec,
+                               hipStream_t s);
+
+// Batched copy with zero padding (bucket pack/unpack).
+hipError_t launch_batched_copy(const ar_copy_desc* d_descs, int ndescs, int esize, hipStream_t s);
+
+// FP8 E4M3 block codec and the compressed ring.
+hipError_t launch_fp8_quant(const void* in, int dtype, int64_t count, uint8_t* codes, float* scales, hipStream_t s);
+hipError_t launch_fp8_dequant(const uint8_t* codes, const float* scales, int64_t count, void* out, int dtype,
+                              hipStream_t s);
+hipError_t launch_fp8_ring(const RankPtrs& p, int n, int64_t count, int dtype, int op, bool vec, hipStream_t s);
+
+}  // namespace ar

@@ -1,0 +1,192 @@
+/*
+ * ar.h -- C ABI of libar, the ring all-reduce library for AMD Instinct MI355X (gfx950).
+ *
+ * N "ranks" are N separate device buffers on one GPU. One call takes all N buffers, so every rank always
+ * calls with the same element count and dtype (the pages stress that a mismatch there hangs or corrupts a
+ * real collective: vasteelab "All-Reduce・All-Gather・All-to-Allとは？…", section "rankとcommunicatorを先に
+ * 理解する").
+ *
+ * Pages cited below (title, then section):
+ *   [G] jisaku.com glossary, "AllReduce（オールリデュース）"
+ *   [V] vasteelab, "All-Reduce・All-Gather・All-to-Allとは？LLM分散推論のGPU通信を整理する"
+ *   [I] intelion.cloud encyclopedia, "All-Reduce"
+ *   [W] astro-wiki, "AllReduce"
+ *   [P] wikiprompt, "All-reduce"
+ *
+ * Conventions for every entry point:
+ *   - Return value: an ar_status (AR_OK == 0). Nothing throws across the ABI.
+ *   - Device pointers are plain device addresses (hipMalloc / PyTorch CUDA tensors). "Host array" means
+ *     memory the call reads on the host during the call only; it may be freed as soon as the call returns.
+ *   - `stream` is a hipStream_t passed as void*; NULL means the null stream. Work is enqueued on it and the
+ *     call returns without synchronising; a fault inside a kernel surfaces at the caller's next sync.
+ *   - The library allocates no device memory. Entry points that need scratch take a caller workspace.
+ *   - Arguments are validated on the host before anything is enqueued; on any error nothing is enqueued.
+ *   - Element types: AR_F32 (binary32), AR_BF16 (bfloat16), AR_F16 (binary16), AR_I32 (two's complement).
+ *     Floating-point sums are accumulated in fp32: bf16/f16 inputs are widened exactly, partial sums stay
+ *     fp32 between ring hops and are rounded once (to nearest even) into the output type. int32 sums wrap
+ *     modulo 2^32.
+ *   - AR_AVG is the sum divided by N once, by the owner of each finished chunk: one fp32 IEEE division by
+ *     (float)N; for int32, C division truncating toward zero ([W] "在 DDP 中的角色"; [P] "在分布式训练中的作用").
+ *   - AR_MIN / AR_MAX on floats: any NaN gives the quiet NaN 0x7FC00000 (bf16 0x7FC0, f16 0x7E00), and -0
+ *     orders below +0. Rounding to bf16/f16 maps every NaN to those same canonical patterns.
+ *   - All calls are re-entrant. The only state is a per-thread record of the last call (ar_last_call).
+ */
+#ifndef AR_H
+#define AR_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define AR_VERSION 10000   /* major*10000 + minor*100 + patch */
+#define AR_MAX_RANKS 64
+#define AR_FP8_BLOCK 128   /* elements per E4M3 scaling block */
+
+enum ar_status {
+    AR_OK = 0,
+    AR_ERR_INVALID = 1,     /* bad enum, nranks outside 1..AR_MAX_RANKS, NULL pointer where one is needed */
+    AR_ERR_UNSUPPORTED = 2, /* valid but unsupported combination (see each entry point) */
+    AR_ERR_ALIAS = 3,       /* buffers overlap other than exact in-place (in_bufs[r] == out_bufs[r]) */
+    AR_ERR_WORKSPACE = 4,   /* the algorithm needs a workspace and none, or too small a one, was given */
+    AR_ERR_HIP = 5          /* the HIP runtime reported an error at launch */
+};
+
+enum ar_dtype { AR_F32 = 0, AR_BF16 = 1, AR_F16 = 2, AR_I32 = 3 };
+enum ar_op { AR_SUM = 0, AR_AVG = 1, AR_MIN = 2, AR_MAX = 3 };
+
+/* Algorithms. All of them return, on every rank, the same element-wise reduction; they differ in the
+ * order in which floating-point partials are associated, and in how many passes over HBM they take.
+ *
+ * AR_ALGO_RING ([G] "Ring-AllReduceの仕組み"; [W] "Ring AllReduce", 阶段一 Reduce-Scatter and 阶段二
+ *   All-Gather): the buffer is split into N balanced chunks (chunk c has count/N + 1 elements when
+ *   c < count%N, else count/N). Reduce-scatter round s sends chunk (i-s) mod N from rank i to rank i+1,
+ *   which combines it with its own copy; after N-1 rounds rank i owns finished chunk (i+1) mod N, which is
+ *   therefore the fold x_c (+) x_{c+1} (+) ... (+) x_{c+N-1} (indices mod N) for chunk c. The owner applies
+ *   the epilogue (avg, rounding) and N-1 all-gather rounds copy the finished chunks to every rank. On one
+ *   GPU the rounds collapse into a single pass that keeps the in-flight partial in registers: each element
+ *   is read once from every rank, folded in exactly the ring's order, and written once to every rank.
+ *   Bit-identical to the literal ring.
+ * AR_ALGO_FUSED ([G] "AllReduceの基本動作": Reduce then Broadcast; [W] 朴素方法与瓶颈): one pass, every
+ *   element folded in rank order 0..N-1 and written to all ranks. Chunk-agnostic.
+ * AR_ALGO_RHD ([G] algorithm table, Recursive Halving-Doubling; [W] "其他 AllReduce 算法", Rabenseifner row;
+ *   [P] "算法与实现"): N must be a power of two. Halving step j pairs rank i with i XOR (N >> (j+1));
+ *   doubling reverses the steps. Every element ends as the pairwise tree that first combines ranks N/2
+ *   apart, then N/4 apart, ..., e.g. N=8: ((x0+x4)+(x2+x6))+((x1+x5)+(x3+x7)). Collapsed into one pass.
+ * AR_ALGO_RING_STEPWISE / AR_ALGO_RHD_STEPWISE: the same schedules executed one round per kernel launch,
+ *   with partials passing through HBM (2(N-1) launches for the ring, 2 log2 N for RHD). Bit-identical to
+ *   the collapsed forms. For bf16/f16 the fp32 partials need a workspace (ar_allreduce_ws).
+ * AR_ALGO_RING_FP8 ([G] NCCL feature list, FP8 AllReduce, and "勾配圧縮技術", FP8 quantization;
+ *   [V] "data typeと圧縮は品質だけの問題ではない"): the ring where every reduce-scatter message is the
+ *   sender's fp32 partial quantized to OCP E4M3 codes with one fp32 scale per 128-element block (blocks
+ *   tile each chunk from its start). The receiver adds the dequantized message to its own full-precision
+ *   value. The owner quantizes its finished chunk once; all-gather forwards those codes and scales, and
+ *   every rank writes round(dequant(codes)). Block quantization: amax = max |v| over the block (NaN
+ *   ignored); inv = 448/amax and scale = amax/448 (fp32 divisions); amax == 0, or an infinite inv, gives
+ *   inv = scale = 1; code = E4M3(v*inv) rounded to nearest even and saturated to +-448; NaN -> 0x7F;
+ *   dequant = value(code) * scale. dtype AR_F32 or AR_BF16, op AR_SUM or AR_AVG. Codes never reach HBM.
+ */
+enum ar_algo {
+    AR_ALGO_RING = 0,
+    AR_ALGO_FUSED = 1,
+    AR_ALGO_RHD = 2,
+    AR_ALGO_RING_STEPWISE = 3,
+    AR_ALGO_RHD_STEPWISE = 4,
+    AR_ALGO_RING_FP8 = 5
+};
+
+/* All-reduce of N rank buffers ([P] opening definition: every process contributes a buffer, buffers are
+ * combined element-wise and the result is copied back to all; [V] "All-Reduceは全rankの値を集約して全rankへ返す").
+ *   in_bufs, out_bufs: host arrays of nranks device pointers, each to `count` elements of `dtype`.
+ *     out_bufs[r] may equal in_bufs[r] (in place); any other overlap among the 2N ranges -> AR_ERR_ALIAS.
+ *   count == 0 returns AR_OK and enqueues nothing. nranks == 1 copies (avg divides by 1).
+ *   Alignment: any. A 16-byte vector path is used where every pointer is 16-byte aligned.
+ * Errors: AR_ERR_INVALID (enum, nranks, NULL), AR_ERR_UNSUPPORTED (RHD with N not a power of two; FP8
+ *   with a dtype other than F32/BF16 or an op other than SUM/AVG), AR_ERR_ALIAS, AR_ERR_WORKSPACE (the
+ *   stepwise algorithms on bf16/f16 need ar_allreduce_ws), AR_ERR_HIP. */
+int ar_allreduce(const void* const* in_bufs, void* const* out_bufs, int nranks, size_t count, int dtype, int op,
+                 int algo, void* stream);
+
+/* Bytes of device workspace ar_allreduce_ws needs for this call (0 when none). Host only, no HIP call. */
+int ar_allreduce_workspace_size(int nranks, size_t count, int dtype, int op, int algo, size_t* bytes);
+
+/* ar_allreduce with a caller workspace: `workspace` is a device pointer to at least
+ * ar_allreduce_workspace_size() bytes, 256-byte aligned, disjoint from every rank buffer; its contents on
+ * entry do not matter and are clobbered. A NULL workspace is accepted when 0 bytes are needed. */
+int ar_allreduce_ws(const void* const* in_bufs, void* const* out_bufs, int nranks, size_t count, int dtype, int op,
+                    int algo, void* workspace, size_t ws_bytes, void* stream);
+
+/* ------------------------------------------------------------------------------------------------ */
+/* Bucketing ([G] "パフォーマンスチューニング": many small gradient tensors are packed into one bucket, 25 MB
+ * by default, and all-reduced together; [V] "communicationとcomputeを重ねる条件": buckets that are too small
+ * cost launches and latency, too large ones delay the first transfer). */
+
+/* One batched-copy task: copy `numel` elements from src to dst, then write `zero_pad_after` zero elements
+ * at dst + numel. Pointers are device addresses; element size is given by the call's dtype. */
+typedef struct ar_copy_desc {
+    const void* src;
+    void* dst;
+    int64_t numel;
+    int64_t zero_pad_after;
+} ar_copy_desc;
+
+/* Host-only greedy bucket plan over tensors in index order. Each tensor occupies its numel rounded up to a
+ * 16-byte multiple. The open bucket is closed when it is non-empty and the next tensor would push it past
+ * cap_bytes, so a tensor larger than the cap sits alone. A bucket's element count is its filled length
+ * rounded up to a multiple of nranks * (16 / element size), so its N chunks start on 16-byte boundaries.
+ *   numels: host array [ntensors]. Outputs (host arrays, caller-allocated): bucket_of[ntensors] (int32),
+ *   offset_of[ntensors] (elements from the bucket's start), bucket_count[ntensors] (only the first
+ *   *nbuckets entries are written), *nbuckets.
+ * Errors: AR_ERR_INVALID (NULLs, negative numel, ntensors < 0, cap 0, bad dtype or nranks). */
+int ar_bucket_plan(const int64_t* numels, int ntensors, int dtype, int nranks, size_t cap_bytes,
+                   int32_t* bucket_of, int64_t* offset_of, int64_t* bucket_count, int* nbuckets);
+
+/* Execute `ndescs` copy tasks in one launch. d_descs is a DEVICE array of ar_copy_desc (ranks x tensors of
+ * copies do not fit in kernel arguments); it must stay valid until the work completes on `stream`.
+ * pack: per-tensor -> bucket (with zero pads); unpack: bucket -> per-tensor. The two calls execute the same
+ * task semantics; they are separate names for the two directions. Destinations must not overlap each
+ * other or any source. ndescs == 0 enqueues nothing. Errors: AR_ERR_INVALID, AR_ERR_HIP. */
+int ar_bucket_pack(const ar_copy_desc* d_descs, int ndescs, int dtype, void* stream);
+int ar_bucket_unpack(const ar_copy_desc* d_descs, int ndescs, int dtype, void* stream);
+
+/* ------------------------------------------------------------------------------------------------ */
+/* FP8 E4M3 block codec (the quantization AR_ALGO_RING_FP8 applies on every hop; format: OCP 8-bit
+ * floating point, E4M3, bias 7, largest finite 448, NaN = S.1111.111).
+ *   ar_fp8_quant: blocks of AR_FP8_BLOCK elements tile [0, count) from the start (the last may be
+ *     partial). in: device, count elements of in_dtype (AR_F32 or AR_BF16). codes: device uint8[count].
+ *     scales: device float[ceil(count / AR_FP8_BLOCK)].
+ *   ar_fp8_dequant: out[e] = round(value(codes[e]) * scales[e / AR_FP8_BLOCK]) into out_dtype (F32|BF16).
+ * Errors: AR_ERR_INVALID (NULL, dtype), AR_ERR_HIP. count == 0 enqueues nothing. */
+int ar_fp8_quant(const void* in, int in_dtype, size_t count, uint8_t* codes, float* scales, void* stream);
+int ar_fp8_dequant(const uint8_t* codes, const float* scales, size_t count, void* out, int out_dtype, void* stream);
+
+/* ------------------------------------------------------------------------------------------------ */
+/* Diagnostics ([V] "hangをtimeoutだけで再起動しない": keep the last collective entered, its sequence number,
+ * shape and dtype, and the error before it). */
+
+/* Static text for a status code (never NULL). */
+const char* ar_status_string(int status);
+
+typedef struct ar_call_record {
+    uint64_t seq;       /* per-thread count of calls that reached validation */
+    const char* entry;  /* static name of the entry point */
+    int nranks;
+    int dtype;
+    int op;
+    int algo;
+    int status;
+    size_t count;
+} ar_call_record;
+
+/* Copies this thread's last call record into *rec. AR_ERR_INVALID if rec is NULL or no call was made yet. */
+int ar_last_call(ar_call_record* rec);
+
+/* AR_VERSION of the built library. */
+int ar_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* AR_H */

@@ -1,0 +1,156 @@
+"""CPU-only checks of the C ABI: the library loads, exports every declared symbol, its enums agree with the
+binding, and argument validation returns before anything is launched (no GPU needed)."""
+import ctypes
+import os
+import re
+
+import numpy as np
+import pytest
+
+import all_reduce_reduction_ring_amd as ar
+import oracle
+from all_reduce_reduction_ring_amd import inputs
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "ar.h")
+
+
+def _header():
+    with open(HEADER) as f:
+        return f.read()
+
+
+def _declared_functions():
+    text = re.sub(r"/\*.*?\*/", "", _header(), flags=re.S)
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?\w+\s*\*?\s*(ar_\w+)\s*\(", text, flags=re.M)))
+
+
+def test_library_exports_every_declared_function():
+    names = _declared_functions()
+    assert {"ar_allreduce", "ar_allreduce_ws", "ar_allreduce_workspace_size", "ar_bucket_plan", "ar_bucket_pack",
+            "ar_bucket_unpack", "ar_fp8_quant", "ar_fp8_dequant", "ar_status_string", "ar_last_call",
+            "ar_version"} <= set(names)
+    L = ctypes.CDLL(ar.lib_path())
+    for n in names:
+        assert hasattr(L, n), n
+
+
+def test_binding_constants_match_header():
+    text = _header()
+    for name, val in re.findall(r"\b(AR_[A-Z0-9_]+)\s*=\s*(\d+)", text):
+        assert getattr(ar, name) == int(val), name
+    assert ar.AR_MAX_RANKS == int(re.search(r"#define AR_MAX_RANKS (\d+)", text).group(1))
+    assert ar.AR_FP8_BLOCK == int(re.search(r"#define AR_FP8_BLOCK (\d+)", text).group(1))
+    assert ar.ar_version() == int(re.search(r"#define AR_VERSION (\d+)", text).group(1))
+
+
+def test_status_strings():
+    for s in range(6):
+        assert ar.ar_status_string(s).startswith(["AR_OK", "AR_ERR_INVALID", "AR_ERR_UNSUPPORTED", "AR_ERR_ALIAS",
+                                                  "AR_ERR_WORKSPACE", "AR_ERR_HIP"][s])
+    assert "unknown" in ar.ar_status_string(99)
+
+
+def _call(n, count, dtype=ar.AR_F32, op=ar.AR_SUM, algo=ar.AR_ALGO_RING, ins=None, outs=None, ws=None, wsb=0):
+    """Call with fake device addresses; only valid for argument combinations that fail validation."""
+    L = ar.lib()
+    es = 2 if dtype in (ar.AR_BF16, ar.AR_F16) else 4
+    span = max(count * es, 1)
+    ins = ins if ins is not None else [0x10000000 + 2 * r * ((span + 4095) // 4096 * 4096) for r in range(max(n, 1))]
+    outs = outs if outs is not None else [p + (span + 4095) // 4096 * 4096 for p in ins]
+    ai = (ctypes.c_void_p * len(ins))(*ins)
+    ao = (ctypes.c_void_p * len(outs))(*outs)
+    return L.ar_allreduce_ws(ai, ao, n, count, dtype, op, algo, ctypes.c_void_p(ws or 0), wsb, None)
+
+
+def test_invalid_arguments():
+    assert _call(2, 10, dtype=7) == ar.AR_ERR_INVALID
+    assert _call(2, 10, op=9) == ar.AR_ERR_INVALID
+    assert _call(2, 10, algo=6) == ar.AR_ERR_INVALID
+    assert _call(0, 10) == ar.AR_ERR_INVALID
+    assert _call(65, 10) == ar.AR_ERR_INVALID
+    assert _call(2, 10, ins=[0x1000, 0]) == ar.AR_ERR_INVALID
+    L = ar.lib()
+    assert L.ar_allreduce(None, None, 2, 10, 0, 0, 0, None) == ar.AR_ERR_INVALID
+    # count == 0 is a no-op even with no buffers at all
+    assert L.ar_allreduce(None, None, 2, 0, 0, 0, 0, None) == ar.AR_OK
+
+
+def test_unsupported_combinations():
+    assert _call(3, 10, algo=ar.AR_ALGO_RHD) == ar.AR_ERR_UNSUPPORTED
+    assert _call(6, 10, algo=ar.AR_ALGO_RHD_STEPWISE) == ar.AR_ERR_UNSUPPORTED
+    assert _call(4, 10, dtype=ar.AR_I32, algo=ar.AR_ALGO_RING_FP8) == ar.AR_ERR_UNSUPPORTED
+    assert _call(4, 10, dtype=ar.AR_F16, algo=ar.AR_ALGO_RING_FP8) == ar.AR_ERR_UNSUPPORTED
+    assert _call(4, 10, op=ar.AR_MAX, algo=ar.AR_ALGO_RING_FP8) == ar.AR_ERR_UNSUPPORTED
+
+
+def test_alias_detection():
+    base = 0x20000000
+    # in-place is fine; any other overlap is rejected
+    assert _call(2, 256, ins=[base, base + 1024], outs=[base + 512, base + 4096]) == ar.AR_ERR_ALIAS
+    assert _call(2, 256, ins=[base, base], outs=[base + 8192, base + 16384]) == ar.AR_ERR_ALIAS
+    assert _call(2, 256, ins=[base, base + 4096], outs=[base + 4096, base]) == ar.AR_ERR_ALIAS
+    assert _call(2, 256, ins=[base, base + 1020], outs=[base, base + 1020]) == ar.AR_ERR_ALIAS
+
+
+def test_workspace_rules():
+    need = ar.ar_allreduce_workspace_size(8, 1000, ar.AR_BF16, ar.AR_SUM, ar.AR_ALGO_RING_STEPWISE)
+    assert need == 8 * 1024 * 4
+    assert ar.ar_allreduce_workspace_size(8, 1000, ar.AR_F32, ar.AR_SUM, ar.AR_ALGO_RING_STEPWISE) == 0
+    assert ar.ar_allreduce_workspace_size(8, 1000, ar.AR_BF16, ar.AR_SUM, ar.AR_ALGO_RING) == 0
+    assert _call(8, 1000, dtype=ar.AR_BF16, algo=ar.AR_ALGO_RING_STEPWISE) == ar.AR_ERR_WORKSPACE
+    assert _call(8, 1000, dtype=ar.AR_BF16, algo=ar.AR_ALGO_RHD_STEPWISE, ws=0x7000000000, wsb=need - 1) \
+        == ar.AR_ERR_WORKSPACE
+    assert _call(8, 1000, dtype=ar.AR_BF16, algo=ar.AR_ALGO_RING_STEPWISE, ws=0x7000000010, wsb=need) \
+        == ar.AR_ERR_INVALID  # not 256-byte aligned
+    # a workspace overlapping a rank buffer
+    assert _call(2, 1000, dtype=ar.AR_BF16, algo=ar.AR_ALGO_RING_STEPWISE, ins=[0x10000000, 0x10010000],
+                 outs=[0x10020000, 0x10030000], ws=0x10030000, wsb=need) == ar.AR_ERR_ALIAS
+
+
+def test_last_call_record():
+    _call(2, 10, dtype=7)
+    r1 = ar.ar_last_call()
+    _call(3, 10, algo=ar.AR_ALGO_RHD)
+    r2 = ar.ar_last_call()
+    assert r2["seq"] == r1["seq"] + 1
+    assert r2["entry"] == "ar_allreduce_ws" and r2["nranks"] == 3 and r2["status"] == ar.AR_ERR_UNSUPPORTED
+    assert r2["algo"] == ar.AR_ALGO_RHD and r2["count"] == 10
+
+
+def test_codec_and_copy_validation():
+    L = ar.lib()
+    assert L.ar_fp8_quant(None, ar.AR_I32, 10, None, None, None) == ar.AR_ERR_INVALID
+    assert L.ar_fp8_quant(None, ar.AR_F32, 0, None, None, None) == ar.AR_OK
+    assert L.ar_fp8_quant(None, ar.AR_F32, 10, None, None, None) == ar.AR_ERR_INVALID
+    assert L.ar_fp8_dequant(None, None, 10, None, ar.AR_F16, None) == ar.AR_ERR_INVALID
+    assert L.ar_bucket_pack(None, 0, ar.AR_F32, None) == ar.AR_OK
+    assert L.ar_bucket_pack(None, 3, ar.AR_F32, None) == ar.AR_ERR_INVALID
+    assert L.ar_bucket_unpack(None, -1, ar.AR_F32, None) == ar.AR_ERR_INVALID
+
+
+@pytest.mark.parametrize("n", [1, 2, 8, 16])
+@pytest.mark.parametrize("dtype,es", [(ar.AR_F32, 4), (ar.AR_BF16, 2)])
+def test_bucket_plan_matches_oracle(n, dtype, es):
+    sizes = inputs.bucket_sizes()
+    for cap in (25 << 20, 1 << 20, 4096):
+        got = ar.ar_bucket_plan(sizes, dtype, n, cap)
+        want = oracle.bucket_plan(sizes, es, n, cap)
+        for g, w in zip(got, want):
+            np.testing.assert_array_equal(g, w)
+    rng = np.random.default_rng(n)
+    for _ in range(20):
+        sz = rng.integers(0, 5000, rng.integers(0, 40))
+        got = ar.ar_bucket_plan(sz, dtype, n, 8192)
+        want = oracle.bucket_plan(sz, es, n, 8192)
+        for g, w in zip(got, want):
+            np.testing.assert_array_equal(g, w)
+
+
+def test_bucket_plan_validation():
+    with pytest.raises(ar.ArError):
+        ar.ar_bucket_plan([1, -2], ar.AR_F32, 2, 100)
+    with pytest.raises(ar.ArError):
+        ar.ar_bucket_plan([1, 2], ar.AR_F32, 2, 0)
+    b, o, c = ar.ar_bucket_plan([], ar.AR_F32, 2, 100)
+    assert len(b) == 0 and len(c) == 0
