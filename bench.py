@@ -1,0 +1,346 @@
+#!/usr/bin/env python3
+"""Benchmark of the ring all-reduce on one MI355X.
+
+Headline workload (one "step" = one all-reduce): N = 8 simulated ranks, each a separate HBM buffer of
+134,217,728 bf16 gradients (256 MiB), values bf16(z * 1e-3) with z ~ N(0, 1); sum in fp32 in ring order
+(chunk c folded from rank c), divided by 8, rounded once to bf16 and written to all 8 rank buffers.
+
+Reported: busbw (the JSON "value") = algbw * 2(N-1)/N with algbw = S / t and S the per-rank bytes
+(astro-wiki "AllReduce", section 通信量分析: each GPU sends 2(N-1)/N of its data); achieved HBM bandwidth
+of the kernel = algorithmic bytes (N reads + N writes of S) / kernel time, against the 8 TB/s peak; the
+CPU oracle timed on this host on the same inputs; and, beside the headline, every other step of the path
+(rank-order and halving-doubling one-pass kernels, the round-per-launch schedules, bucketing with 25 MiB
+buckets over 300 tensors, the fp8 codec and compressed ring) with its own algorithmic-bytes roofline.
+
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--headline-only] [--copy-calibration]
+"""
+from __future__ import annotations
+
+import argparse
+import concurrent.futures
+import ctypes
+import hashlib
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "busbw & achieved HBM GB/s (% of peak) vs message size, N=8 ranks, fp32/bf16"
+PEAK_HBM_GBPS = 8000.0
+N_RANKS = 8
+COUNT = 134_217_728
+GB = 1e9
+
+
+def _sources_digest(names):
+    h = hashlib.sha256()
+    for n in names:
+        with open(os.path.join(ROOT, "all_reduce_reduction_ring_amd", "csrc", n), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()
+
+
+def _load_traffic(kernel_key, sources):
+    """HBM bytes per launch from the committed rocprofv3 counter summary, if it was taken on this exact
+    kernel source; otherwise None."""
+    path = os.path.join(ROOT, "profiles", "hbm_counters.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        data = json.load(f)
+    ent = data.get(kernel_key)
+    if not ent or ent.get("sources_sha256") != _sources_digest(sources):
+        return None
+    return ent.get("hbm_bytes_per_launch")
+
+
+class Timer:
+    """Per-call kernel time with HIP events recorded on the stream the library launches on."""
+
+    def __init__(self, torch):
+        self.torch = torch
+        self.ms = []
+
+    def run(self, fn, reps):
+        torch = self.torch
+        stream = torch.cuda.current_stream()
+        evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(reps)]
+        for a, b in evs:
+            a.record(stream)
+            fn()
+            b.record(stream)
+        torch.cuda.synchronize()
+        self.ms = [a.elapsed_time(b) for a, b in evs]
+        return self.ms
+
+
+def log(msg):
+    print(f"bench: {msg}", file=sys.stderr, flush=True)
+
+
+def _gen_parallel(fn, items, workers=16):
+    with concurrent.futures.ThreadPoolExecutor(max_workers=workers) as ex:
+        return list(ex.map(fn, items))
+
+
+def _upload(torch, arrays, dtype, dev):
+    out = []
+    for a in arrays:
+        t = torch.from_numpy(a.view(np.int16) if a.dtype == np.uint16 else a)
+        out.append(t.to(dev, non_blocking=False).view(dtype))
+    return out
+
+
+def stats_us(ms):
+    a = np.array(ms) * 1e3
+    return {"p50": float(np.percentile(a, 50)), "p95": float(np.percentile(a, 95)),
+            "p99": float(np.percentile(a, 99)), "mean": float(a.mean())}
+
+
+def bus_factor(n):
+    return 2.0 * (n - 1) / n
+
+
+def headline(torch, ar, inputs, args, dev):
+    """Generate the 8 rank buffers, warm up, time exactly K steps."""
+    log("generating the headline inputs")
+    host = _gen_parallel(lambda r: inputs.normal_bf16((2, r), COUNT), range(N_RANKS))
+    ins = _upload(torch, host, torch.bfloat16, dev)
+    log("timing the headline")
+    outs = [torch.empty_like(t) for t in ins]
+    step = lambda: ar.ar_allreduce(ins, outs, ar.AR_AVG, ar.AR_ALGO_RING)
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    timer = Timer(torch)
+    t0 = time.perf_counter()
+    timer.run(step, args.steps)  # synchronises at the end
+    wall = time.perf_counter() - t0
+    return host, ins, outs, timer.ms, wall
+
+
+def copy_ceiling(torch, ins, outs, reps=10):
+    """A plain device copy moving the same bytes (N*S read + N*S written)."""
+    src = torch.cat([t.view(-1) for t in ins])
+    dst = torch.empty_like(src)
+    dst.copy_(src)
+    torch.cuda.synchronize()
+    ms = Timer(torch).run(lambda: dst.copy_(src), reps)
+    nbytes = 2 * src.numel() * src.element_size()
+    del src, dst
+    return nbytes / (np.mean(ms) * 1e-3) / GB
+
+
+def cpu_baseline(host, budget_s=10.0, max_reps=5):
+    """The oracle's literal ring on the headline inputs, repeated until ~budget_s of CPU time."""
+    import oracle as _o
+    reps, t_total = 0, 0.0
+    while reps < max_reps and (t_total < budget_s or reps == 0):
+        t0 = time.perf_counter()
+        _o.ring_allreduce(host, _o.BF16, _o.AVG)
+        t_total += time.perf_counter() - t0
+        reps += 1
+    t = t_total / reps
+    S = COUNT * 2
+    return {"value": S / t / GB * bus_factor(N_RANKS), "unit": "GB/s", "cores": _o.num_threads(), "kind": "oracle",
+            "sample": f"the full headline workload (8 ranks x {COUNT} bf16, avg), literal ring rounds in C, "
+                      f"{reps} repetition(s), {t:.2f} s each"}
+
+
+def ring_bytes(n, count, es):
+    return 2 * n * count * es
+
+
+def stepwise_ring_bytes(n, count, es, acc):
+    """Reduce-scatter round s: every rank reads the incoming partial and its own chunk and writes the new
+    partial (inputs at s = 0, outputs at the last round); all-gather: read + write a chunk per rank."""
+    chunk = count / n
+    total = 0.0
+    for s in range(n - 1):
+        msg = es if s == 0 else acc
+        dst = es if s == n - 2 else acc
+        total += n * chunk * (msg + es + dst)
+    total += (n - 1) * n * chunk * 2 * es
+    return total
+
+
+def stepwise_rhd_bytes(n, count, es, acc):
+    k = int(np.log2(n))
+    total = 0.0
+    for j in range(k):
+        part = count / 2 ** (j + 1)
+        rd = es if j == 0 else acc
+        wr = es if j == k - 1 else acc
+        total += n * part * (2 * rd + wr)
+    for j in range(k):
+        total += n * (count / 2 ** (j + 1)) * 2 * es
+    return total
+
+
+def row_entry(name, ms, alg_bytes, S, n, extra=None):
+    t = float(np.mean(ms)) * 1e-3
+    e = {"us": stats_us(ms), "algbw_GBps": S / t / GB, "busbw_GBps": S / t / GB * bus_factor(n),
+         "hbm_GBps": alg_bytes / t / GB, "frac_of_peak": alg_bytes / t / GB / PEAK_HBM_GBPS,
+         "alg_bytes": alg_bytes}
+    if extra:
+        e.update(extra)
+    return e
+
+
+def other_rows(torch, ar, inputs, ins, outs, dev, reps):
+    """Every other step of the path, timed beside the headline."""
+    rows = {}
+    S = COUNT * 2
+    timer = Timer(torch)
+    log("timing the other rows")
+    for name, algo in (("fused_reduce_broadcast", ar.AR_ALGO_FUSED), ("rhd_tree", ar.AR_ALGO_RHD)):
+        fn = lambda: ar.ar_allreduce(ins, outs, ar.AR_AVG, algo)
+        fn()
+        rows[name] = row_entry(name, timer.run(fn, reps), ring_bytes(N_RANKS, COUNT, 2), S, N_RANKS)
+    ws = torch.empty(ar.ar_allreduce_workspace_size(N_RANKS, COUNT, ar.AR_BF16, ar.AR_AVG, ar.AR_ALGO_RING_STEPWISE),
+                     dtype=torch.uint8, device=dev)
+    for name, algo, fb in (("ring_stepwise", ar.AR_ALGO_RING_STEPWISE, stepwise_ring_bytes),
+                           ("rhd_stepwise", ar.AR_ALGO_RHD_STEPWISE, stepwise_rhd_bytes)):
+        fn = lambda: ar.ar_allreduce_ws(ins, outs, ar.AR_AVG, algo, ws)
+        fn()
+        rows[name] = row_entry(name, timer.run(fn, max(3, reps // 2)), fb(N_RANKS, COUNT, 2, 4), S, N_RANKS,
+                               {"launches": 2 * (N_RANKS - 1) if algo == ar.AR_ALGO_RING_STEPWISE else 6})
+    del ws
+    torch.cuda.empty_cache()
+
+    log("fp8 rows")
+    # fp8 compressed ring: 8 ranks x 67,108,864 bf16 with 0.1% outliers x100, blocks of 128
+    n8 = 67_108_864
+    h8 = _gen_parallel(lambda r: inputs.outlier_bf16((5, r), n8), range(N_RANKS))
+    i8 = _upload(torch, h8, torch.bfloat16, dev)
+    o8 = [torch.empty_like(t) for t in i8]
+    fn = lambda: ar.ar_allreduce(i8, o8, ar.AR_SUM, ar.AR_ALGO_RING_FP8)
+    fn()
+    rows["fp8_ring"] = row_entry("fp8_ring", timer.run(fn, reps), ring_bytes(N_RANKS, n8, 2), n8 * 2, N_RANKS,
+                                 {"count": n8, "wire_bytes_per_element": 1 + 4 / 128})
+    codes = torch.empty(n8, dtype=torch.uint8, device=dev)
+    scales = torch.empty(n8 // 128, dtype=torch.float32, device=dev)
+    fn = lambda: ar.ar_fp8_quant(i8[0], codes, scales)
+    fn()
+    qb = n8 * 2 + n8 + n8 // 128 * 4
+    rows["fp8_quant"] = row_entry("fp8_quant", timer.run(fn, reps), qb, n8 * 2, 1, {"count": n8})
+    fn = lambda: ar.ar_fp8_dequant(codes, scales, o8[0])
+    fn()
+    rows["fp8_dequant"] = row_entry("fp8_dequant", timer.run(fn, reps), qb, n8 * 2, 1, {"count": n8})
+    del i8, o8, codes, scales, h8
+    torch.cuda.empty_cache()
+
+    log("bucket row")
+    # bucketing: 300 fp32 tensors per rank, log-uniform sizes in [1K, 16M], 25 MiB buckets, sum then /8.
+    sizes = inputs.bucket_sizes()
+    g = torch.Generator(device=dev)
+    g.manual_seed(3)
+    bins = [[torch.randn(int(s), generator=g, device=dev, dtype=torch.float32).mul_(1e-2) for s in sizes]
+            for _ in range(N_RANKS)]
+    bouts = [[torch.empty_like(t) for t in r] for r in bins]
+    bar = ar.BucketedAllReduce(bins, bouts, op=ar.AR_AVG, cap_bytes=25 << 20)
+    bar()
+    torch.cuda.synchronize()
+    s_tot = int(np.sum(sizes)) * 4
+    b_tot = int(np.sum(bar.bucket_count)) * 4
+    phases = {}
+    for name, fn in (("pack", bar.pack), ("allreduce", bar.reduce), ("unpack", bar.unpack)):
+        phases[name] = stats_us(timer.run(fn, max(3, reps // 2)))
+    ms = timer.run(bar, max(3, reps // 2))
+    # pack: read the tensors, write the buckets with pads; ring: N reads + N writes of every bucket;
+    # unpack: read and write the tensor elements
+    alg = N_RANKS * (s_tot + b_tot) + 2 * N_RANKS * b_tot + 2 * N_RANKS * s_tot
+    rows["buckets"] = row_entry("buckets", ms, alg, s_tot, N_RANKS,
+                                {"tensors": len(sizes), "buckets": bar.nbuckets, "bytes_per_rank": s_tot,
+                                 "launches": 2 + bar.nbuckets, "phases_us": phases,
+                                 "data": "torch GPU generator, normal(0, 1e-2)"})
+    del bins, bouts, bar
+    torch.cuda.empty_cache()
+    return rows
+
+
+def main():
+    p = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=20)
+    p.add_argument("--warmup", type=int, default=5)
+    p.add_argument("--headline-only", action="store_true", help="time the headline only (for profiler runs)")
+    p.add_argument("--copy-calibration", action="store_true",
+                   help="run only a plain 2 GiB device copy, the reference for HBM counter scaling")
+    args = p.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py: this build runs on one GPU; --gpus {args.gpus} is not supported (the N ranks are "
+              "simulated as separate buffers on one MI355X)", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    import all_reduce_reduction_ring_amd as ar
+    from all_reduce_reduction_ring_amd import inputs
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(2)
+    dev = torch.device("cuda:0")
+    ar.lib()
+
+    if args.copy_calibration:
+        src = torch.empty(1 << 30, dtype=torch.int16, device=dev).fill_(1)
+        dst = torch.empty_like(src)
+        for _ in range(args.warmup + args.steps):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_calibration": {"bytes_read_per_launch": 2 << 30, "bytes_written_per_launch": 2 << 30,
+                                               "launches": args.warmup + args.steps}}))
+        return
+
+    host, ins, outs, ms, wall = headline(torch, ar, inputs, args, dev)
+    S = COUNT * 2
+    t_kernel = float(np.mean(ms)) * 1e-3
+    algbw = S / t_kernel / GB
+    alg_bytes = ring_bytes(N_RANKS, COUNT, 2)
+    achieved = alg_bytes / t_kernel / GB
+    sources = ["ar_collapsed.hip", "ar_device.h"]
+    traffic = _load_traffic("collapsed_kernel<bf16,avg,8>", sources)
+    result = {
+        "metric": METRIC,
+        "value": algbw * bus_factor(N_RANKS),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": wall / args.steps * 1e3,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "config": {"workload": "ring all-reduce, N=8 simulated ranks (separate HBM buffers), 134,217,728 bf16 "
+                               "per rank (256 MiB), fp32 sum in ring order, /8, bf16 out to all 8",
+                   "nranks": N_RANKS, "count_per_rank": COUNT, "storage": "bf16", "op": "avg", "algo": "ring"},
+        "algbw_GBps": algbw,
+        "busbw_GBps": algbw * bus_factor(N_RANKS),
+        "hbm_GBps": achieved,
+        "kernel_us": stats_us(ms),
+        "roofline": {"bound": "hbm", "achieved": achieved, "peak": PEAK_HBM_GBPS, "unit": "GB/s",
+                     "frac": achieved / PEAK_HBM_GBPS,
+                     "traffic": traffic},
+    }
+    if not args.headline_only:
+        result["copy_ceiling_GBps"] = copy_ceiling(torch, ins, outs)
+        result["rows"] = other_rows(torch, ar, inputs, ins, outs, dev, reps=max(5, args.steps // 2))
+        del ins, outs
+        torch.cuda.empty_cache()
+        log("timing the CPU oracle")
+        result["cpu_baseline"] = cpu_baseline(host)
+    print(json.dumps(result))
+
+
+if __name__ == "__main__":
+    main()
