@@ -26,6 +26,15 @@ namespace {
 
 constexpr int kThreads = 256;
 
+// Launch shape, measured on MI355X: HBM3E streams writes best with few concurrent writers, while reads need
+// bytes in flight. Each thread keeps about eight independent 16-byte loads in flight (U slots x N ranks,
+// U = 8/N for small N), and the grid is a small number of 256-thread workgroups per CU in total (split over
+// the chunks): one for N = 8, more where a thread has fewer loads in flight or writes fewer streams.
+template <int NR> constexpr int slots_per_thread() { return (NR > 0 && NR < 8) ? 8 / NR : 1; }
+template <int NR> constexpr int blocks_per_cu() {
+  return NR == 8 ? 1 : NR == 2 ? 2 : (NR == 4 || NR == 16) ? 4 : 8;
+}
+
 struct CollapsedArgs {
   RankPtrs p;
   int64_t count;
@@ -216,10 +225,11 @@ __global__ __launch_bounds__(kThreads) void collapsed_kernel(CollapsedArgs a) {
 template <int DT, int OP, int NR, int U, bool TREE>
 hipError_t launch_one(CollapsedArgs& a, int nchunks, hipStream_t s) {
   constexpr int V = Traits<DT>::kVec;
+  constexpr int kBlocksPerCU = blocks_per_cu<NR>();
   const int64_t per_chunk = a.q + 1;
   const int64_t slots = a.vec ? (per_chunk + V - 1) / V : per_chunk;
   int64_t want = (slots + static_cast<int64_t>(kThreads) * U - 1) / (static_cast<int64_t>(kThreads) * U);
-  int64_t cap = (static_cast<int64_t>(cu_count()) * 8 + nchunks - 1) / nchunks;
+  int64_t cap = (static_cast<int64_t>(cu_count()) * kBlocksPerCU + nchunks - 1) / nchunks;
   if (cap < 1) cap = 1;
   int64_t bx = want < cap ? want : cap;
   if (bx < 1) bx = 1;
@@ -233,9 +243,9 @@ hipError_t dispatch_n(CollapsedArgs& a, int algo, hipStream_t s) {
   const int n = a.n;
   if (algo == AR_ALGO_RHD && n > 1) {
     switch (n) {
-      case 2: return launch_one<DT, OP, 2, 2, true>(a, 1, s);
-      case 4: return launch_one<DT, OP, 4, 2, true>(a, 1, s);
-      case 8: return launch_one<DT, OP, 8, 2, true>(a, 1, s);
+      case 2: return launch_one<DT, OP, 2, slots_per_thread<2>(), true>(a, 1, s);
+      case 4: return launch_one<DT, OP, 4, slots_per_thread<4>(), true>(a, 1, s);
+      case 8: return launch_one<DT, OP, 8, slots_per_thread<8>(), true>(a, 1, s);
       case 16: return launch_one<DT, OP, 16, 1, true>(a, 1, s);
       case 32: return launch_one<DT, OP, 32, 1, true>(a, 1, s);
       case 64: return launch_one<DT, OP, 64, 1, true>(a, 1, s);
@@ -243,9 +253,9 @@ hipError_t dispatch_n(CollapsedArgs& a, int algo, hipStream_t s) {
     }
   }
   switch (n) {
-    case 2: return launch_one<DT, OP, 2, 2, false>(a, n, s);
-    case 4: return launch_one<DT, OP, 4, 2, false>(a, n, s);
-    case 8: return launch_one<DT, OP, 8, 2, false>(a, n, s);
+    case 2: return launch_one<DT, OP, 2, slots_per_thread<2>(), false>(a, n, s);
+    case 4: return launch_one<DT, OP, 4, slots_per_thread<4>(), false>(a, n, s);
+    case 8: return launch_one<DT, OP, 8, slots_per_thread<8>(), false>(a, n, s);
     case 16: return launch_one<DT, OP, 16, 1, false>(a, n, s);
     default: return launch_one<DT, OP, 0, 1, false>(a, n, s);
   }

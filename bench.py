@@ -265,6 +265,49 @@ def other_rows(torch, ar, inputs, ins, outs, dev, reps):
     return rows
 
 
+def sweep(torch, ar, dev, out_path, reps=20, max_log2=30):
+    """Message-size sweep: N = 8 fp32 ranks, sum, 8 B ... 1 GiB per rank, ring vs halving-doubling vs rank order
+    vs the round-per-launch schedules. Below 1 GiB of total traffic, ceil(1 GiB / (2 N S)) buffer sets (at most
+    64) are rotated so that no call finds its data in the 256 MB last-level cache. One JSON line per point."""
+    algos = [("ring", ar.AR_ALGO_RING), ("rhd", ar.AR_ALGO_RHD), ("fused", ar.AR_ALGO_FUSED),
+             ("ring_stepwise", ar.AR_ALGO_RING_STEPWISE), ("rhd_stepwise", ar.AR_ALGO_RHD_STEPWISE)]
+    n = N_RANKS
+    g = torch.Generator(device=dev)
+    lines = []
+    with open(out_path, "w") as f:
+        for lg in range(3, max_log2 + 1):
+            S = 1 << lg
+            count = S // 4
+            sets = int(min(64, max(1, -(-(1 << 30) // (2 * n * S)))))
+            g.manual_seed(4000 + lg)
+            bufs = [([torch.rand(count, generator=g, device=dev).mul_(2).sub_(1) for _ in range(n)],
+                     [torch.empty(count, device=dev) for _ in range(n)]) for _ in range(sets)]
+            for name, algo in algos:
+                k = [0]
+
+                def call():
+                    i, o = bufs[k[0] % sets]
+                    k[0] += 1
+                    ar.ar_allreduce(i, o, ar.AR_SUM, algo)
+
+                for _ in range(3):
+                    call()
+                ms = Timer(torch).run(call, reps)
+                t = float(np.median(ms)) * 1e-3
+                alg = ring_bytes(n, count, 4) if "stepwise" not in name else (
+                    stepwise_ring_bytes(n, count, 4, 4) if name == "ring_stepwise" else stepwise_rhd_bytes(n, count, 4, 4))
+                rec = {"bytes_per_rank": S, "algo": name, "us_p50": t * 1e6, "us": stats_us(ms),
+                       "algbw_GBps": S / t / GB, "busbw_GBps": S / t / GB * bus_factor(n),
+                       "hbm_GBps": alg / t / GB, "frac_of_peak": alg / t / GB / PEAK_HBM_GBPS, "buffer_sets": sets}
+                f.write(json.dumps(rec) + "\n")
+                f.flush()
+                lines.append(rec)
+            log(f"sweep {S} B done")
+            del bufs
+            torch.cuda.empty_cache()
+    return lines
+
+
 def main():
     p = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     p.add_argument("--gpus", type=int, default=1)
@@ -273,6 +316,8 @@ def main():
     p.add_argument("--headline-only", action="store_true", help="time the headline only (for profiler runs)")
     p.add_argument("--copy-calibration", action="store_true",
                    help="run only a plain 2 GiB device copy, the reference for HBM counter scaling")
+    p.add_argument("--sweep", metavar="OUT.jsonl", help="run only the message-size sweep, one JSON line per point")
+    p.add_argument("--sweep-max-log2", type=int, default=30)
     args = p.parse_args()
     if args.gpus != 1:
         print(f"bench.py: this build runs on one GPU; --gpus {args.gpus} is not supported (the N ranks are "
@@ -289,6 +334,10 @@ def main():
         sys.exit(2)
     dev = torch.device("cuda:0")
     ar.lib()
+
+    if args.sweep:
+        sweep(torch, ar, dev, args.sweep, max_log2=args.sweep_max_log2)
+        return
 
     if args.copy_calibration:
         src = torch.empty(1 << 30, dtype=torch.int16, device=dev).fill_(1)

@@ -1,0 +1,129 @@
+"""GPU parity at the workloads' full sizes, in the launch configuration the benchmark times, against the oracle.
+
+- headline: 8 ranks x 134,217,728 bf16 (256 MiB each), fp32 ring-order sum, /8, bf16 out: every element of
+  every rank, bit for bit.
+- compressed ring: 8 ranks x 67,108,864 bf16 with 0.1% outliers x100, E4M3 blocks of 128: every element.
+- largest sweep point: 8 ranks x 268,435,456 fp32 (1 GiB each): ring and ring-stepwise, every element; the
+  rank-order and halving-doubling variants (which do not depend on chunk positions) on 2^20 sampled elements,
+  for which the oracle is evaluated on exactly those elements.
+- buckets: 300 fp32 tensors per rank (log-uniform 1K..16M elements, 2.07 GB per rank), 25 MiB buckets, avg:
+  every tensor of every rank.
+"""
+import concurrent.futures
+
+import numpy as np
+import pytest
+import torch
+
+import all_reduce_reduction_ring_amd as ar
+import oracle
+from all_reduce_reduction_ring_amd import inputs
+from gpu_util import DEV
+
+pytestmark = pytest.mark.gpu
+
+
+def _par(fn, items):
+    with concurrent.futures.ThreadPoolExecutor(max_workers=16) as ex:
+        return list(ex.map(fn, items))
+
+
+def _up(arrs, tdt):
+    return [torch.from_numpy(a.view(np.int16) if a.dtype == np.uint16 else a).to(DEV).view(tdt) for a in arrs]
+
+
+def _down_bits(t):
+    bits = torch.int16 if t.element_size() == 2 else torch.int32
+    return t.view(bits).cpu().numpy().view(np.uint16 if t.element_size() == 2 else np.uint32)
+
+
+def _same_on_all_ranks(outs):
+    for o in outs[1:]:
+        assert torch.equal(o.view(torch.int16 if o.element_size() == 2 else torch.int32),
+                           outs[0].view(torch.int16 if o.element_size() == 2 else torch.int32))
+
+
+@pytest.mark.timeout(600)
+def test_headline_eight_ranks_256MiB_bf16_avg():
+    n, count = 8, 134_217_728
+    host = _par(lambda r: inputs.normal_bf16((2, r), count), range(n))
+    ins = _up(host, torch.bfloat16)
+    outs = [torch.empty_like(t) for t in ins]
+    ar.ar_allreduce(ins, outs, ar.AR_AVG, ar.AR_ALGO_RING)
+    torch.cuda.synchronize()
+    del ins
+    want = oracle.ring_allreduce(host, oracle.BF16, oracle.AVG)
+    _same_on_all_ranks(outs)
+    for r in range(n):
+        np.testing.assert_array_equal(_down_bits(outs[r]), want[r])
+
+
+@pytest.mark.timeout(600)
+def test_fp8_ring_eight_ranks_128MiB_bf16():
+    n, count = 8, 67_108_864
+    host = _par(lambda r: inputs.outlier_bf16((5, r), count), range(n))
+    ins = _up(host, torch.bfloat16)
+    outs = [torch.empty_like(t) for t in ins]
+    ar.ar_allreduce(ins, outs, ar.AR_SUM, ar.AR_ALGO_RING_FP8)
+    torch.cuda.synchronize()
+    del ins
+    want = oracle.fp8_ring_allreduce(host, oracle.BF16, oracle.SUM)
+    _same_on_all_ranks(outs)
+    np.testing.assert_array_equal(_down_bits(outs[0]), want[0])
+    np.testing.assert_array_equal(_down_bits(outs[n - 1]), want[n - 1])
+    # reported, not gated: error of the compressed sum against the exact sum, relative to the block scale
+    exact = np.zeros(count, np.float64)
+    for h in host:
+        exact += oracle.bf16_to_f32(h)
+    got = oracle.bf16_to_f32(want[0]).astype(np.float64)
+    print(f"fp8 ring: max |err| = {np.max(np.abs(got - exact)):.3e}, mean |exact| = {np.mean(np.abs(exact)):.3e}")
+
+
+@pytest.mark.timeout(900)
+def test_sweep_largest_point_one_GiB_per_rank():
+    n, count = 8, 268_435_456
+    host = _par(lambda r: inputs.uniform_pm1((4, r, 30), count), range(n))
+    ins = _up(host, torch.float32)
+    outs = [torch.empty_like(t) for t in ins]
+    want = oracle.ring_allreduce(host, oracle.F32, oracle.SUM)
+    for algo in (ar.AR_ALGO_RING, ar.AR_ALGO_RING_STEPWISE):
+        for o in outs:
+            o.fill_(float("nan"))
+        ar.ar_allreduce(ins, outs, ar.AR_SUM, algo)
+        torch.cuda.synchronize()
+        _same_on_all_ranks(outs)
+        np.testing.assert_array_equal(_down_bits(outs[0]), want[0].view(np.uint32))
+        np.testing.assert_array_equal(_down_bits(outs[5]), want[5].view(np.uint32))
+    del want
+    rng = np.random.default_rng(44)
+    idx = np.unique(np.concatenate([rng.integers(0, count, 1 << 20), np.arange(1000), np.arange(count - 1000, count)]))
+    sub = [h[idx] for h in host]
+    for algo, fn in ((ar.AR_ALGO_FUSED, oracle.fused_allreduce), (ar.AR_ALGO_RHD, oracle.rhd_allreduce),
+                     (ar.AR_ALGO_RHD_STEPWISE, oracle.rhd_allreduce)):
+        ar.ar_allreduce(ins, outs, ar.AR_SUM, algo)
+        torch.cuda.synchronize()
+        _same_on_all_ranks(outs)
+        w = fn(sub, oracle.F32, oracle.SUM)[0].view(np.uint32)
+        got = outs[3][torch.from_numpy(idx).to(DEV)]
+        np.testing.assert_array_equal(_down_bits(got), w)
+
+
+@pytest.mark.timeout(900)
+def test_buckets_300_tensors_full_size():
+    n = 8
+    sizes = inputs.bucket_sizes()
+    host = _par(lambda r: inputs.bucket_tensors(r, sizes), range(n))
+    ins = [[torch.from_numpy(t).to(DEV) for t in host[r]] for r in range(n)]
+    outs = [[torch.empty_like(t) for t in ins[r]] for r in range(n)]
+    bar = ar.BucketedAllReduce(ins, outs, op=ar.AR_AVG, cap_bytes=25 << 20)
+    bo, oo, bc = oracle.bucket_plan(sizes, 4, n, 25 << 20)
+    np.testing.assert_array_equal(bar.bucket_of, bo)
+    np.testing.assert_array_equal(bar.offset_of, oo)
+    np.testing.assert_array_equal(bar.bucket_count, bc)
+    bar()
+    torch.cuda.synchronize()
+    del ins, bar
+    want = oracle.bucketed_allreduce(host, oracle.F32, oracle.AVG, cap_bytes=25 << 20)
+    for r in range(n):
+        for t in range(len(sizes)):
+            np.testing.assert_array_equal(_down_bits(outs[r][t]), want[r][t].view(np.uint32))
