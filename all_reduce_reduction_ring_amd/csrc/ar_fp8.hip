@@ -24,32 +24,37 @@ constexpr int kThreads = 256;
 constexpr int kBlock = AR_FP8_BLOCK;  // 128
 constexpr int kPerLane = 8;
 
-// Nearest E4M3 value to v (ties to even), saturated to +-448; NaN stays NaN. Adding c = 2^(e+20), where
-// 2^e is the binade of |v| (at least 2^-6, the subnormal spacing region), makes the fp32 sum's last place
-// equal to E4M3's spacing 2^(e-3) there, so the sum rounds |v| to E4M3 precision; subtracting c is exact.
-__device__ __forceinline__ float e4m3_round(float v) {
-  const float a = fminf(fabsf(v), 448.0f);
-  const uint32_t eb = max(__float_as_uint(a) & 0x7F800000u, 0x3C800000u);
-  const float c = __uint_as_float(eb + (20u << 23));
-  const float r = (a + c) - c;
-  const float sr = __uint_as_float(__float_as_uint(r) | (__float_as_uint(v) & 0x80000000u));
-  return is_nan(v) ? __uint_as_float(kNaN32) : sr;
+// E4M3 conversions use gfx950's OCP-format instructions: v_cvt_pk_fp8_f32 (two fp32 -> two codes, round to
+// nearest even) and v_cvt_pk_f32_fp8 (two codes -> two exact fp32). They are not saturating: |v| >= 464 and
+// +-inf would become NaN codes. The encoder never sees such values: a block's values are multiplied by
+// inv = RN(448 / amax) with |v| <= amax, so |v * inv| <= 448 (1 + 2^-23)^2 < 464, which rounds to at most 448;
+// the fallbacks (inv = 1 only for amax < 448 / FLT_MAX, inv = 0 for an infinite amax) keep that true or give
+// NaN, which stays NaN. Over every fp32 input below 464 in magnitude these instructions round exactly as
+// nearest-even E4M3 with saturation does.
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+
+// Round-trip four values through E4M3: returns value(code(v)), codes packed in *codes (byte k = value k).
+__device__ __forceinline__ void e4m3_round4(const float* v, float* r, uint32_t* codes) {
+  int w = __builtin_amdgcn_cvt_pk_fp8_f32(v[0], v[1], 0, false);
+  w = __builtin_amdgcn_cvt_pk_fp8_f32(v[2], v[3], w, true);
+  const f32x2 lo = __builtin_amdgcn_cvt_pk_f32_fp8(w, false), hi = __builtin_amdgcn_cvt_pk_f32_fp8(w, true);
+  r[0] = lo[0];
+  r[1] = lo[1];
+  r[2] = hi[0];
+  r[3] = hi[1];
+  *codes = static_cast<uint32_t>(w);
 }
 
-// Code of an E4M3 value r (the output of e4m3_round).
-__device__ __forceinline__ uint32_t e4m3_code(float r) {
-  if (is_nan(r)) return 0x7Fu;
-  const uint32_t s = (__float_as_uint(r) >> 24) & 0x80u;
-  const float a = fabsf(r);
-  const uint32_t mag = a < 0.015625f ? static_cast<uint32_t>(a * 512.0f) : ((__float_as_uint(a) >> 20) - (120u << 3));
-  return s | mag;
-}
-
-__device__ __forceinline__ float e4m3_value(uint32_t code) {
-  const uint32_t mag = code & 0x7Fu;
-  if (mag == 0x7Fu) return __uint_as_float(kNaN32);
-  const float v = mag < 8u ? static_cast<float>(mag) * 0.001953125f : __uint_as_float((mag << 20) + (120u << 23));
-  return __uint_as_float(__float_as_uint(v) | ((code & 0x80u) << 24));
+// A NaN value encodes as 0x7F whatever its sign (the hardware may set the sign bit).
+__device__ __forceinline__ uint32_t canonical_nan_codes(uint32_t w) {
+  uint32_t out = 0;
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    uint32_t b = (w >> (8 * k)) & 0xFFu;
+    b = (b & 0x7Fu) == 0x7Fu ? 0x7Fu : b;
+    out |= b << (8 * k);
+  }
+  return out;
 }
 
 // Max over the 16 lanes of a row of non-negative, non-NaN floats (their bit patterns order as integers).
@@ -66,26 +71,19 @@ struct BlockScale {
   float inv, scale;
 };
 
-// Block scale from the lane's valid values (invalid lanes pass nvalid = 0). All 64 lanes must call it.
-__device__ __forceinline__ BlockScale block_scale(const float (&v)[kPerLane], int nvalid) {
+// Block scale. Elements past the end of the data are held as zeros, so they never raise the amax; a NaN
+// never compares greater, so it never counts. All 64 lanes of the wave must call it (DPP).
+__device__ __forceinline__ BlockScale block_scale(const float (&v)[kPerLane]) {
   float m = 0.0f;
 #pragma unroll
   for (int k = 0; k < kPerLane; ++k) {
     const float a = fabsf(v[k]);
-    const float an = (k < nvalid && !is_nan(a)) ? a : 0.0f;
-    m = an > m ? an : m;
+    m = a > m ? a : m;
   }
   const float amax = row16_max(m);
-  BlockScale s{1.0f, 1.0f};
-  if (amax > 0.0f) {
-    s.inv = 448.0f / amax;
-    s.scale = amax / 448.0f;
-    if (__builtin_isinf(s.inv)) {
-      s.inv = 1.0f;
-      s.scale = 1.0f;
-    }
-  }
-  return s;
+  const float inv = 448.0f / amax, scale = amax / 448.0f;  // amax == 0 gives inv = inf: replaced below
+  const bool unit = !(amax > 0.0f) || __builtin_isinf(inv);
+  return BlockScale{unit ? 1.0f : inv, unit ? 1.0f : scale};
 }
 
 // Load 8 consecutive elements starting at element e0 (nvalid of them exist) as fp32.
@@ -146,18 +144,23 @@ __global__ __launch_bounds__(kThreads) void quant_kernel(const void* in, int64_t
     const int nvalid = nv <= 0 ? 0 : (nv >= kPerLane ? kPerLane : static_cast<int>(nv));
     float v[kPerLane];
     load8<DT>(in, e0, nvalid, vec != 0, v);
-    const BlockScale s = block_scale(v, nvalid);
-    uint32_t c[kPerLane];
+    const BlockScale s = block_scale(v);
+    float q[kPerLane], r[kPerLane];
 #pragma unroll
-    for (int k = 0; k < kPerLane; ++k) c[k] = e4m3_code(e4m3_round(v[k] * s.inv));
+    for (int k = 0; k < kPerLane; ++k) q[k] = v[k] * s.inv;
+    uint32_t w0, w1;
+    e4m3_round4(q, r, &w0);
+    e4m3_round4(q + 4, r + 4, &w1);
+    w0 = canonical_nan_codes(w0);
+    w1 = canonical_nan_codes(w1);
     if (vec && nvalid == kPerLane) {
       typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
       u32x2 p;
-      p[0] = c[0] | (c[1] << 8) | (c[2] << 16) | (c[3] << 24);
-      p[1] = c[4] | (c[5] << 8) | (c[6] << 16) | (c[7] << 24);
+      p[0] = w0;
+      p[1] = w1;
       __builtin_nontemporal_store(p, reinterpret_cast<u32x2*>(codes + e0));
     } else {
-      for (int k = 0; k < nvalid; ++k) codes[e0 + k] = static_cast<uint8_t>(c[k]);
+      for (int k = 0; k < nvalid; ++k) codes[e0 + k] = static_cast<uint8_t>(((k < 4 ? w0 : w1) >> (8 * (k & 3))) & 0xFFu);
     }
     if (l16 == 0 && blk < nblocks) scales[blk] = s.scale;
   }
@@ -173,9 +176,25 @@ __global__ __launch_bounds__(kThreads) void dequant_kernel(const uint8_t* codes,
     const int64_t e0 = g * kPerLane;
     const int nvalid = count - e0 >= kPerLane ? kPerLane : static_cast<int>(count - e0);
     const float sc = scales[e0 / kBlock];
+    uint32_t w[2] = {0, 0};
+    if (vec && nvalid == kPerLane) {
+      typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+      const u32x2 p = __builtin_nontemporal_load(reinterpret_cast<const u32x2*>(codes + e0));
+      w[0] = p[0];
+      w[1] = p[1];
+    } else {
+      for (int k = 0; k < nvalid; ++k) w[k >> 2] |= static_cast<uint32_t>(codes[e0 + k]) << (8 * (k & 3));
+    }
     float v[kPerLane];
 #pragma unroll
-    for (int k = 0; k < kPerLane; ++k) v[k] = k < nvalid ? e4m3_value(codes[e0 + k]) * sc : 0.0f;
+    for (int h = 0; h < 2; ++h) {
+      const f32x2 lo = __builtin_amdgcn_cvt_pk_f32_fp8(static_cast<int>(w[h]), false);
+      const f32x2 hi = __builtin_amdgcn_cvt_pk_f32_fp8(static_cast<int>(w[h]), true);
+      v[4 * h] = lo[0] * sc;
+      v[4 * h + 1] = lo[1] * sc;
+      v[4 * h + 2] = hi[0] * sc;
+      v[4 * h + 3] = hi[1] * sc;
+    }
     store8<DT>(out, e0, nvalid, vec != 0, v);
   }
 }
@@ -184,60 +203,120 @@ __global__ __launch_bounds__(kThreads) void dequant_kernel(const uint8_t* codes,
 struct Fp8RingArgs {
   RankPtrs p;
   int64_t count, q, r;
-  int64_t nb_a;   // blocks per chunk of q+1 elements (chunks c < r)
-  int64_t nb_b;   // blocks per chunk of q elements
-  int64_t total;  // total blocks over all chunks
+  int64_t nb_a, nb_b;  // blocks per chunk of q+1 elements (chunks c < r) and of q elements
+  int64_t wt_a, wt_b;  // wave tasks (4 blocks each, never spanning two chunks) per such chunk
+  int64_t tasks;       // total wave tasks
   int n;
   int vec;
+};
+
+// One hop: the sender's partial p goes out as E4M3 codes + block scale and comes back as d * scale; the
+// receiver adds its own full-precision value.
+__device__ __forceinline__ void hop(float (&p)[kPerLane], const float (&own)[kPerLane]) {
+  const BlockScale s = block_scale(p);
+  float q[kPerLane], d[kPerLane];
+  uint32_t unused;
+#pragma unroll
+  for (int e = 0; e < kPerLane; ++e) q[e] = p[e] * s.inv;
+  e4m3_round4(q, d, &unused);
+  e4m3_round4(q + 4, d + 4, &unused);
+#pragma unroll
+  for (int e = 0; e < kPerLane; ++e) p[e] = d[e] * s.scale + own[e];
+}
+
+template <int OP>
+__device__ __forceinline__ void finish(float (&p)[kPerLane], int n) {
+#pragma unroll
+  for (int e = 0; e < kPerLane; ++e) p[e] = finalize<OP>(p[e], n);
+  const BlockScale s = block_scale(p);
+  float q[kPerLane], d[kPerLane];
+  uint32_t unused;
+#pragma unroll
+  for (int e = 0; e < kPerLane; ++e) q[e] = p[e] * s.inv;
+  e4m3_round4(q, d, &unused);
+  e4m3_round4(q + 4, d + 4, &unused);
+#pragma unroll
+  for (int e = 0; e < kPerLane; ++e) p[e] = d[e] * s.scale;
+}
+
+// 8 elements of a 16-byte bf16 slot, or of two fp32 slots, already loaded.
+template <int DT> struct Raw8;
+template <> struct Raw8<AR_BF16> {
+  u32x4 w;
+  __device__ __forceinline__ void load(const void* base, int64_t e0) { w = ld16(static_cast<const uint16_t*>(base) + e0); }
+  __device__ __forceinline__ void widen8(float (&v)[kPerLane]) const { Slot<AR_BF16>::unpack(w, v); }
+};
+template <> struct Raw8<AR_F32> {
+  u32x4 a, b;
+  __device__ __forceinline__ void load(const void* base, int64_t e0) {
+    a = ld16(static_cast<const float*>(base) + e0);
+    b = ld16(static_cast<const float*>(base) + e0 + 4);
+  }
+  __device__ __forceinline__ void widen8(float (&v)[kPerLane]) const {
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      v[k] = __uint_as_float(a[k]);
+      v[k + 4] = __uint_as_float(b[k]);
+    }
+  }
 };
 
 template <int DT, int OP, int NR>
 __global__ __launch_bounds__(kThreads) void fp8_ring_kernel(Fp8RingArgs a) {
   const int lane = threadIdx.x & 63, row = lane >> 4, l16 = lane & 15;
   const int n = NR > 0 ? NR : a.n;
-  const int64_t wave = (static_cast<int64_t>(blockIdx.x) * kThreads + threadIdx.x) >> 6;
   const int64_t nwaves = (static_cast<int64_t>(gridDim.x) * kThreads) >> 6;
-  for (int64_t w = wave; w * 4 < a.total; w += nwaves) {
-    const int64_t gb = w * 4 + row;
-    // locate chunk c and the block within it
-    int64_t c = 0, bic = 0;
-    if (gb < a.r * a.nb_a) {
-      c = gb / a.nb_a;
-      bic = gb - c * a.nb_a;
-    } else if (a.nb_b > 0) {
-      const int64_t g2 = gb - a.r * a.nb_a;
-      c = a.r + g2 / a.nb_b;
-      bic = g2 - (c - a.r) * a.nb_b;
-    }
-    if (gb >= a.total) {  // lanes past the last block: no elements, but keep a valid rank index
-      c = 0;
-      bic = 0;
+  const int64_t wave0 = static_cast<int64_t>(blockIdx.x) * (kThreads >> 6) + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  for (int64_t w = wave0; w < a.tasks; w += nwaves) {
+    // wave task -> chunk c (uniform across the wave) and its first block
+    int64_t c, t;
+    if (w < a.r * a.wt_a) {
+      c = w / a.wt_a;
+      t = w - c * a.wt_a;
+    } else {
+      const int64_t w2 = w - a.r * a.wt_a;
+      c = a.r + w2 / a.wt_b;
+      t = w2 - (c - a.r) * a.wt_b;
     }
     const int64_t lo = chunk_lo(a.q, a.r, c), hi = chunk_lo(a.q, a.r, c + 1);
+    const int64_t bic = t * 4 + row;
     const int64_t e0 = lo + bic * kBlock + l16 * kPerLane;
     const int64_t bend = lo + (bic + 1) * kBlock < hi ? lo + (bic + 1) * kBlock : hi;
-    const int64_t nv = gb < a.total ? bend - e0 : 0;
+    const int64_t nv = bend - e0;
     const int nvalid = nv <= 0 ? 0 : (nv >= kPerLane ? kPerLane : static_cast<int>(nv));
-    const bool vec = a.vec != 0;
     const int start = static_cast<int>(c);
-
     float p[kPerLane];
-    load8<DT>(a.p.in[start], e0, nvalid, vec, p);
-    for (int k = 1; k < n; ++k) {
-      int rr = start + k;
-      rr = rr >= n ? rr - n : rr;
-      float own[kPerLane];
-      load8<DT>(a.p.in[rr], e0, nvalid, vec, own);
-      const BlockScale s = block_scale(p, nvalid);  // the message that crosses the hop
+    if (NR > 0 && a.vec && __all(nvalid == kPerLane)) {
+      // every lane holds 8 in-range, aligned elements: issue all N loads before any arithmetic
+      Raw8<DT> raw[NR > 0 ? NR : 1];
 #pragma unroll
-      for (int e = 0; e < kPerLane; ++e) p[e] = e4m3_round(p[e] * s.inv) * s.scale + own[e];
+      for (int k = 0; k < NR; ++k) {
+        int rr = start + k;
+        rr = rr >= NR ? rr - NR : rr;
+        raw[k].load(a.p.in[rr], e0);
+      }
+      raw[0].widen8(p);
+#pragma unroll
+      for (int k = 1; k < NR; ++k) {
+        float own[kPerLane];
+        raw[k].widen8(own);
+        hop(p, own);
+      }
+      finish<OP>(p, NR);
+#pragma unroll
+      for (int r = 0; r < NR; ++r) store8<DT>(a.p.out[r], e0, kPerLane, true, p);
+    } else {
+      load8<DT>(a.p.in[start], e0, nvalid, a.vec != 0, p);
+      for (int k = 1; k < n; ++k) {
+        int rr = start + k;
+        rr = rr >= n ? rr - n : rr;
+        float own[kPerLane];
+        load8<DT>(a.p.in[rr], e0, nvalid, a.vec != 0, own);
+        hop(p, own);
+      }
+      finish<OP>(p, n);
+      for (int r = 0; r < n; ++r) store8<DT>(a.p.out[r], e0, nvalid, a.vec != 0, p);
     }
-#pragma unroll
-    for (int e = 0; e < kPerLane; ++e) p[e] = finalize<OP>(p[e], n);
-    const BlockScale s = block_scale(p, nvalid);
-#pragma unroll
-    for (int e = 0; e < kPerLane; ++e) p[e] = e4m3_round(p[e] * s.inv) * s.scale;
-    for (int r = 0; r < n; ++r) store8<DT>(a.p.out[r], e0, nvalid, vec, p);
   }
 }
 
@@ -251,7 +330,7 @@ int grid_for_waves(int64_t waves) {
 
 template <int DT, int OP>
 hipError_t ring_n(Fp8RingArgs& a, hipStream_t s) {
-  const int g = grid_for_waves((a.total + 3) / 4);
+  const int g = grid_for_waves(a.tasks);
   switch (a.n) {
     case 8: hipLaunchKernelGGL((fp8_ring_kernel<DT, OP, 8>), dim3(g), dim3(kThreads), 0, s, a); break;
     case 4: hipLaunchKernelGGL((fp8_ring_kernel<DT, OP, 4>), dim3(g), dim3(kThreads), 0, s, a); break;
@@ -296,7 +375,9 @@ hipError_t launch_fp8_ring(const RankPtrs& p, int n, int64_t count, int dtype, i
   a.r = count % n;
   a.nb_a = (a.q + 1 + kBlock - 1) / kBlock;
   a.nb_b = (a.q + kBlock - 1) / kBlock;
-  a.total = a.r * a.nb_a + (n - a.r) * a.nb_b;
+  a.wt_a = (a.nb_a + 3) / 4;
+  a.wt_b = (a.nb_b + 3) / 4;
+  a.tasks = a.r * a.wt_a + (n - a.r) * a.wt_b;
   // 16-byte slots of 8 elements need every chunk start on an 8-element boundary
   a.vec = (vec && a.r == 0 && a.q % kPerLane == 0) ? 1 : 0;
   if (dtype == AR_BF16) return op == AR_AVG ? ring_n<AR_BF16, AR_AVG>(a, s) : ring_n<AR_BF16, AR_SUM>(a, s);

@@ -127,3 +127,37 @@ def test_buckets_300_tensors_full_size():
     for r in range(n):
         for t in range(len(sizes)):
             np.testing.assert_array_equal(_down_bits(outs[r][t]), want[r][t].view(np.uint32))
+
+
+@pytest.mark.timeout(900)
+def test_fp8_encoder_exhaustive_every_fp32_up_to_448():
+    """Every fp32 bit pattern with |v| <= 448 (both signs, subnormals included) goes through ar_fp8_quant in
+    blocks of 128 led by 448, so each block's scale is 1 and the encoder sees the raw values; every code must
+    equal the oracle's. Together with the scale rule (|v * inv| < 464) this covers every value the compressed
+    ring can quantize."""
+    lim = int(np.float32(448.0).view(np.uint32))
+    slab = 127 << 20
+    for start in range(0, lim + 1, slab):
+        pats = np.arange(start, min(start + slab, lim + 1), dtype=np.uint32)
+        for sign in (0, 0x80000000):
+            v = (pats | np.uint32(sign)).view(np.float32)
+            nb = -(-v.size // 127)
+            body = np.zeros(nb * 127, np.float32)
+            body[: v.size] = v
+            x = np.empty((nb, 128), np.float32)
+            x[:, 0] = 448.0
+            x[:, 1:] = body.reshape(nb, 127)
+            x = x.reshape(-1)
+            assert np.array_equal(x.reshape(nb, 128)[:, 1:].reshape(-1)[: v.size].view(np.uint32), v.view(np.uint32))
+            xd = torch.from_numpy(x).to(DEV)
+            codes = torch.empty(x.size, dtype=torch.uint8, device=DEV)
+            scales = torch.empty(nb, dtype=torch.float32, device=DEV)
+            ar.ar_fp8_quant(xd, codes, scales)
+            torch.cuda.synchronize()
+            wc, ws = oracle.fp8_quant(x, oracle.F32)
+            assert np.all(ws == 1.0)
+            got = codes.cpu().numpy()
+            if not np.array_equal(got, wc):
+                bad = np.nonzero(got != wc)[0][:5]
+                raise AssertionError(f"codes differ at inputs {x[bad].view(np.uint32)}: got {got[bad]} want {wc[bad]}")
+            del xd, codes, scales
