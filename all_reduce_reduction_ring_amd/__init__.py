@@ -6,7 +6,7 @@ the library's HIP kernels. There is no CPU fallback: if ``libar.so`` is missing 
 call raises.
 
 Entry points (same names as ``include/ar.h``): ar_allreduce, ar_allreduce_ws, ar_allreduce_workspace_size,
-ar_bucket_plan, ar_bucket_pack, ar_bucket_unpack, ar_fp8_quant, ar_fp8_dequant, ar_status_string,
+ar_allreduce_buckets, ar_bucket_plan, ar_bucket_pack, ar_bucket_unpack, ar_fp8_quant, ar_fp8_dequant, ar_status_string,
 ar_last_call, ar_version. Helpers: make_copy_descs, BucketedAllReduce.
 """
 from __future__ import annotations
@@ -21,7 +21,8 @@ __all__ = [
     "AR_F32", "AR_BF16", "AR_F16", "AR_I32", "AR_SUM", "AR_AVG", "AR_MIN", "AR_MAX",
     "AR_ALGO_RING", "AR_ALGO_FUSED", "AR_ALGO_RHD", "AR_ALGO_RING_STEPWISE", "AR_ALGO_RHD_STEPWISE",
     "AR_ALGO_RING_FP8", "AR_MAX_RANKS", "AR_FP8_BLOCK", "ArError", "lib", "lib_path",
-    "ar_allreduce", "ar_allreduce_ws", "ar_allreduce_workspace_size", "ar_bucket_plan", "ar_bucket_pack",
+    "ar_allreduce", "ar_allreduce_ws", "ar_allreduce_workspace_size", "ar_allreduce_buckets", "ar_bucket_plan",
+    "ar_bucket_pack",
     "ar_bucket_unpack", "ar_fp8_quant", "ar_fp8_dequant", "ar_status_string", "ar_last_call", "ar_version",
     "make_copy_descs", "BucketedAllReduce", "dtype_code",
 ]
@@ -66,6 +67,7 @@ def lib():
         L.ar_allreduce.argtypes = [vp, vp, i32, sz, i32, i32, i32, vp]
         L.ar_allreduce_ws.argtypes = [vp, vp, i32, sz, i32, i32, i32, vp, sz, vp]
         L.ar_allreduce_workspace_size.argtypes = [i32, sz, i32, i32, i32, ctypes.POINTER(sz)]
+        L.ar_allreduce_buckets.argtypes = [vp, vp, i32, vp, i32, i32, i32, i32, vp]
         L.ar_bucket_plan.argtypes = [vp, i32, i32, i32, sz, vp, vp, vp, ctypes.POINTER(i32)]
         L.ar_bucket_pack.argtypes = [vp, i32, i32, vp]
         L.ar_bucket_unpack.argtypes = [vp, i32, i32, vp]
@@ -74,7 +76,8 @@ def lib():
         L.ar_status_string.argtypes = [i32]
         L.ar_status_string.restype = ctypes.c_char_p
         L.ar_last_call.argtypes = [ctypes.POINTER(_CallRecord)]
-        for name in ("ar_allreduce", "ar_allreduce_ws", "ar_allreduce_workspace_size", "ar_bucket_plan",
+        for name in ("ar_allreduce", "ar_allreduce_ws", "ar_allreduce_workspace_size", "ar_allreduce_buckets",
+                     "ar_bucket_plan",
                      "ar_bucket_pack", "ar_bucket_unpack", "ar_fp8_quant", "ar_fp8_dequant", "ar_last_call",
                      "ar_version"):
             getattr(L, name).restype = i32
@@ -143,6 +146,16 @@ def ar_allreduce_ws(ins, outs, op=AR_SUM, algo=AR_ALGO_RING, workspace=None, str
     wb = workspace.numel() * workspace.element_size() if workspace is not None else 0
     _check(lib().ar_allreduce_ws(arr_in, arr_out, n, count, dt, op, algo, wp, wb, _stream(stream)),
            "ar_allreduce_ws")
+
+
+def ar_allreduce_buckets(flat_ins, flat_outs, bucket_count, op=AR_SUM, algo=AR_ALGO_RING, stream=None):
+    """All-reduce every bucket of the flat per-rank tensors in one launch (bucket_count: the plan's counts)."""
+    arr_in, arr_out, n, total, dt = _rank_arrays(flat_ins, flat_outs)
+    counts = np.ascontiguousarray(bucket_count, dtype=np.int64)
+    if int(counts.sum()) > total:
+        raise ValueError("the buckets do not fit in the flat tensors")
+    _check(lib().ar_allreduce_buckets(arr_in, arr_out, n, counts.ctypes.data, counts.size, dt, op, algo,
+                                      _stream(stream)), "ar_allreduce_buckets")
 
 
 def ar_bucket_plan(numels, dtype, nranks, cap_bytes=25 << 20):
@@ -261,6 +274,11 @@ class BucketedAllReduce:
         ar_bucket_pack(self.pack_descs, self.dtype, stream)
 
     def reduce(self, stream=None):
+        """Every bucket in one launch (per-bucket rings, bit-identical to one ar_allreduce per bucket)."""
+        ar_allreduce_buckets(self.buffers, self.buffers, self.bucket_count, self.op, self.algo, stream)
+
+    def reduce_per_bucket(self, stream=None):
+        """One ar_allreduce launch per bucket."""
         for v in self.views:
             ar_allreduce(v, v, self.op, self.algo, stream)
 

@@ -210,6 +210,48 @@ int ar_bucket_plan(const int64_t* numels, int ntensors, int dtype, int nranks, s
   return done(AR_OK);
 }
 
+int ar_allreduce_buckets(const void* const* flat_in, void* const* flat_out, int nranks, const int64_t* bucket_count,
+                         int nbuckets, int dtype, int op, int algo, void* stream) {
+  size_t total = 0;
+  auto done = [&](int st) { return finish("ar_allreduce_buckets", nranks, total, dtype, op, algo, st); };
+  if (!valid_dtype(dtype) || !valid_op(op) || !valid_algo(algo)) return done(AR_ERR_INVALID);
+  if (nranks < 1 || nranks > AR_MAX_RANKS || nbuckets < 0) return done(AR_ERR_INVALID);
+  if (algo != AR_ALGO_RING && algo != AR_ALGO_FUSED && algo != AR_ALGO_RHD) return done(AR_ERR_UNSUPPORTED);
+  if (algo == AR_ALGO_RHD && !is_pow2(nranks)) return done(AR_ERR_UNSUPPORTED);
+  if (nbuckets == 0) return done(AR_OK);
+  if (!bucket_count || !flat_in || !flat_out) return done(AR_ERR_INVALID);
+  const int64_t es = esize_of(dtype);
+  const int64_t unit = static_cast<int64_t>(nranks) * (16 / es);
+  for (int b = 0; b < nbuckets; ++b) {
+    const int64_t c = bucket_count[b];
+    if (c < 0 || c % unit != 0 || c > (INT64_MAX / 4) / es) return done(AR_ERR_INVALID);
+    if (static_cast<size_t>(c) > (SIZE_MAX / 4) / static_cast<size_t>(es) - total) return done(AR_ERR_INVALID);
+    total += static_cast<size_t>(c);
+  }
+  if (total == 0) return done(AR_OK);
+  const size_t bytes = total * static_cast<size_t>(es);
+  Range ranges[2 * AR_MAX_RANKS];
+  int m = 0;
+  for (int r = 0; r < nranks; ++r) {
+    if (!flat_in[r] || !flat_out[r]) return done(AR_ERR_INVALID);
+    const uintptr_t i = reinterpret_cast<uintptr_t>(flat_in[r]), o = reinterpret_cast<uintptr_t>(flat_out[r]);
+    if ((i | o) & 15u) return done(AR_ERR_INVALID);
+    if (i > UINTPTR_MAX - bytes || o > UINTPTR_MAX - bytes) return done(AR_ERR_INVALID);
+    ranges[m++] = Range{i, i + bytes};
+    if (o != i) ranges[m++] = Range{o, o + bytes};
+  }
+  if (any_overlap(ranges, m)) return done(AR_ERR_ALIAS);
+  ar::RankPtrs p;
+  std::memset(&p, 0, sizeof(p));
+  for (int r = 0; r < nranks; ++r) {
+    p.in[r] = flat_in[r];
+    p.out[r] = flat_out[r];
+  }
+  const int a = nranks == 1 ? AR_ALGO_RING : algo;
+  hipError_t e = ar::launch_segments(p, nranks, bucket_count, nbuckets, dtype, op, a, static_cast<hipStream_t>(stream));
+  return done(e == hipSuccess ? AR_OK : AR_ERR_HIP);
+}
+
 static int batched_copy(const char* entry, const ar_copy_desc* d_descs, int ndescs, int dtype, void* stream) {
   auto done = [&](int st) { return finish(entry, 0, static_cast<size_t>(ndescs), dtype, -1, -1, st); };
   if (ndescs < 0 || !valid_dtype(dtype)) return done(AR_ERR_INVALID);

@@ -16,8 +16,14 @@ namespace {
 
 constexpr int kThreads = 256;
 constexpr int kBatch = 256;
-constexpr int kTileBytes = 16384;
-constexpr int kSlotsPerThread = kTileBytes / 16 / kThreads;  // 4
+#ifndef AR_COPY_TILE_BYTES
+#define AR_COPY_TILE_BYTES 16384
+#endif
+#ifndef AR_COPY_BLOCKS_PER_CU
+#define AR_COPY_BLOCKS_PER_CU 8
+#endif
+constexpr int kTileBytes = AR_COPY_TILE_BYTES;
+constexpr int kSlotsPerThread = kTileBytes / 16 / kThreads;
 
 __device__ __forceinline__ void copy_elems(const ar_copy_desc& d, int64_t e0, int64_t e1, int es) {
   for (int64_t e = e0 + threadIdx.x; e < e1; e += kThreads) {
@@ -106,7 +112,7 @@ __global__ __launch_bounds__(kThreads) void batched_copy_kernel(const ar_copy_de
 }  // namespace
 
 hipError_t launch_batched_copy(const ar_copy_desc* d_descs, int ndescs, int esize, hipStream_t s) {
-  const int blocks = cu_count() * 8;
+  const int blocks = cu_count() * AR_COPY_BLOCKS_PER_CU;
   hipLaunchKernelGGL(batched_copy_kernel, dim3(blocks), dim3(kThreads), 0, s, d_descs, ndescs, esize);
   return hipGetLastError();
 }

@@ -272,7 +272,148 @@ hipError_t dispatch_op(CollapsedArgs& a, int op, int algo, hipStream_t s) {
   }
 }
 
+// ------------------------------------------------------------------------------------------ segments
+// Many buckets in one launch. Segment s occupies elements [start_s, start_s + count_s) of every rank's flat
+// buffer, count_s a multiple of N * (16 / element size), so each of its N chunks is whole 16-byte slots. Each
+// segment is reduced exactly as a one-segment call would reduce it: chunk c of segment s folds from rank c.
+// The work is cut into tiles of kThreads * U slots of one chunk; tile_pre holds the running tile count per
+// segment, and tile t goes to block t mod G.
+constexpr int kMaxSegments = 64;  // per launch; keeps the arguments under the 4 KiB kernel-argument limit
+
+struct SegmentArgs {
+  CollapsedArgs f;                     // rank table, n, fold order
+  int64_t start[kMaxSegments];         // first element of the segment
+  int64_t chunk_slots[kMaxSegments];   // 16-byte slots per chunk
+  int64_t tile_pre[kMaxSegments + 1];  // tiles before segment s
+  int nseg;
+};
+
+template <int DT, int OP, int NR, int U, bool TREE>
+__global__ __launch_bounds__(kThreads) void segment_kernel(SegmentArgs a) {
+  constexpr int V = Traits<DT>::kVec;
+  constexpr int64_t TS = static_cast<int64_t>(kThreads) * U;
+  const int n = NR > 0 ? NR : a.f.n;
+  const int64_t total = a.tile_pre[a.nseg];
+  int s = 0;
+  for (int64_t t = blockIdx.x; t < total; t += gridDim.x) {
+    while (a.tile_pre[s + 1] <= t) ++s;  // tiles are visited in increasing order, so s only moves forward
+    const int64_t lt = t - a.tile_pre[s];
+    const int c = static_cast<int>(lt % n);
+    const int64_t k = lt / n;
+    const int64_t v0 = a.start[s] / V + c * a.chunk_slots[s];  // first slot of chunk c
+    const int64_t vend = v0 + a.chunk_slots[s];
+    const int start = a.f.rot ? c : 0;
+    int64_t v = v0 + k * TS + threadIdx.x;
+    u32x4 w[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int64_t vv = v + u * kThreads;
+      if (vv < vend) {
+        if constexpr (TREE) w[u] = tree_slot<DT, OP, NR>(a.f, vv * 16);
+        else w[u] = ring_slot<DT, OP, NR>(a.f, start, vv * 16);
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int64_t vv = v + u * kThreads;
+      if (vv < vend)
+        for (int r = 0; r < n; ++r) st16(static_cast<char*>(a.f.p.out[r]) + vv * 16, w[u]);
+    }
+  }
+}
+
+template <int DT, int OP, int NR, int U, bool TREE>
+hipError_t launch_segments(SegmentArgs& a, hipStream_t s) {
+  constexpr int kBlocksPerCU = blocks_per_cu<NR>();
+  const int64_t total = a.tile_pre[a.nseg];
+  int64_t g = static_cast<int64_t>(cu_count()) * kBlocksPerCU;
+  if (g > total) g = total;
+  if (g < 1) g = 1;
+  hipLaunchKernelGGL((segment_kernel<DT, OP, NR, U, TREE>), dim3(static_cast<unsigned>(g)), dim3(kThreads), 0, s, a);
+  return hipGetLastError();
+}
+
+template <int DT, int OP>
+hipError_t segments_n(SegmentArgs& a, int algo, hipStream_t s) {
+  const int n = a.f.n;
+  if (algo == AR_ALGO_RHD && n > 1) {
+    switch (n) {
+      case 2: return launch_segments<DT, OP, 2, slots_per_thread<2>(), true>(a, s);
+      case 4: return launch_segments<DT, OP, 4, slots_per_thread<4>(), true>(a, s);
+      case 8: return launch_segments<DT, OP, 8, slots_per_thread<8>(), true>(a, s);
+      case 16: return launch_segments<DT, OP, 16, 1, true>(a, s);
+      case 32: return launch_segments<DT, OP, 32, 1, true>(a, s);
+      case 64: return launch_segments<DT, OP, 64, 1, true>(a, s);
+      default: return hipErrorInvalidValue;
+    }
+  }
+  switch (n) {
+    case 2: return launch_segments<DT, OP, 2, slots_per_thread<2>(), false>(a, s);
+    case 4: return launch_segments<DT, OP, 4, slots_per_thread<4>(), false>(a, s);
+    case 8: return launch_segments<DT, OP, 8, slots_per_thread<8>(), false>(a, s);
+    case 16: return launch_segments<DT, OP, 16, 1, false>(a, s);
+    default: return launch_segments<DT, OP, 0, 1, false>(a, s);
+  }
+}
+
+template <int DT>
+hipError_t segments_op(SegmentArgs& a, int op, int algo, hipStream_t s) {
+  switch (op) {
+    case AR_SUM: return segments_n<DT, AR_SUM>(a, algo, s);
+    case AR_AVG: return segments_n<DT, AR_AVG>(a, algo, s);
+    case AR_MIN: return segments_n<DT, AR_MIN>(a, algo, s);
+    case AR_MAX: return segments_n<DT, AR_MAX>(a, algo, s);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+static_assert(sizeof(SegmentArgs) <= 4096, "kernel arguments must fit in 4 KiB");
+
 }  // namespace
+
+hipError_t launch_segments(const RankPtrs& p, int n, const int64_t* counts, int nseg, int dtype, int op, int algo,
+                           hipStream_t s) {
+  const int V = (dtype == AR_BF16 || dtype == AR_F16) ? 8 : 4;
+  const int tree = algo == AR_ALGO_RHD && n > 1;
+  const int U = (n > 0 && n < 8 && (tree ? true : (n == 2 || n == 4))) ? 8 / n : 1;
+  const int64_t TS = static_cast<int64_t>(kThreads) * U;
+  int64_t start = 0;
+  int done = 0;
+  while (done < nseg) {
+    SegmentArgs a;
+    a.f.p = p;
+    a.f.count = 0;
+    a.f.q = 0;
+    a.f.r = 0;
+    a.f.n = n;
+    a.f.rot = algo == AR_ALGO_RING ? 1 : 0;
+    a.f.vec = 1;
+    int m = 0;
+    a.tile_pre[0] = 0;
+    while (done + m < nseg && m < kMaxSegments) {
+      const int64_t cnt = counts[done + m];
+      a.start[m] = start;
+      a.chunk_slots[m] = cnt / n / V;
+      a.tile_pre[m + 1] = a.tile_pre[m] + static_cast<int64_t>(n) * ((a.chunk_slots[m] + TS - 1) / TS);
+      start += cnt;
+      ++m;
+    }
+    a.nseg = m;
+    hipError_t e = hipSuccess;
+    if (a.tile_pre[m] > 0) {
+      switch (dtype) {
+        case AR_F32: e = segments_op<AR_F32>(a, op, algo, s); break;
+        case AR_BF16: e = segments_op<AR_BF16>(a, op, algo, s); break;
+        case AR_F16: e = segments_op<AR_F16>(a, op, algo, s); break;
+        case AR_I32: e = segments_op<AR_I32>(a, op, algo, s); break;
+        default: e = hipErrorInvalidValue;
+      }
+    }
+    if (e != hipSuccess) return e;
+    done += m;
+  }
+  return hipSuccess;
+}
 
 hipError_t launch_collapsed(const RankPtrs& p, int n, int64_t count, int dtype, int op, int algo, bool vec,
                             hipStream_t s) {

@@ -22,6 +22,10 @@ int cu_count();
 hipError_t launch_collapsed(const RankPtrs& p, int n, int64_t count, int dtype, int op, int algo, bool vec,
                             hipStream_t s);
 
+// Many buckets of flat per-rank buffers in as few launches as possible (each count a multiple of N slots).
+hipError_t launch_segments(const RankPtrs& p, int n, const int64_t* counts, int nseg, int dtype, int op, int algo,
+                           hipStream_t s);
+
 // Round-per-launch schedules. ws: fp32 partial mirror (n * ws_stride floats) for 16-bit types, else null.
 int64_t stepwise_ws_stride(int64_t count);
 hipError_t launch_ring_stepwise(const RankPtrs& p, int n, int64_t count, int dtype, int op, float* ws, bool vec,

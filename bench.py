@@ -193,16 +193,34 @@ def row_entry(name, ms, alg_bytes, S, n, extra=None):
     return e
 
 
-def other_rows(torch, ar, inputs, ins, outs, dev, reps):
-    """Every other step of the path, timed beside the headline."""
+def oracle_time(fn, *args):
+    """Wall time of one call of an oracle routine (its OpenMP threads on this host's cores)."""
+    t0 = time.perf_counter()
+    fn(*args)
+    return time.perf_counter() - t0
+
+
+def cpu_row(t, S, n, sample):
+    """The oracle's rate for a row, in the row's own units (algbw and busbw from S per-rank bytes)."""
+    import oracle as _o
+    return {"s": t, "algbw_GBps": S / t / GB, "busbw_GBps": S / t / GB * bus_factor(n), "cores": _o.num_threads(),
+            "sample": sample}
+
+
+def other_rows(torch, ar, inputs, ins, outs, dev, reps, host):
+    """Every other step of the path, timed beside the headline, each with the oracle timed on this host."""
+    import oracle as _o
     rows = {}
     S = COUNT * 2
     timer = Timer(torch)
     log("timing the other rows")
-    for name, algo in (("fused_reduce_broadcast", ar.AR_ALGO_FUSED), ("rhd_tree", ar.AR_ALGO_RHD)):
+    for name, algo, ofn in (("fused_reduce_broadcast", ar.AR_ALGO_FUSED, _o.fused_allreduce),
+                            ("rhd_tree", ar.AR_ALGO_RHD, _o.rhd_allreduce)):
         fn = lambda: ar.ar_allreduce(ins, outs, ar.AR_AVG, algo)
         fn()
         rows[name] = row_entry(name, timer.run(fn, reps), ring_bytes(N_RANKS, COUNT, 2), S, N_RANKS)
+        rows[name]["cpu_oracle"] = cpu_row(oracle_time(ofn, host, _o.BF16, _o.AVG), S, N_RANKS,
+                                           "the full headline workload, one call")
     ws = torch.empty(ar.ar_allreduce_workspace_size(N_RANKS, COUNT, ar.AR_BF16, ar.AR_AVG, ar.AR_ALGO_RING_STEPWISE),
                      dtype=torch.uint8, device=dev)
     for name, algo, fb in (("ring_stepwise", ar.AR_ALGO_RING_STEPWISE, stepwise_ring_bytes),
@@ -210,7 +228,9 @@ def other_rows(torch, ar, inputs, ins, outs, dev, reps):
         fn = lambda: ar.ar_allreduce_ws(ins, outs, ar.AR_AVG, algo, ws)
         fn()
         rows[name] = row_entry(name, timer.run(fn, max(3, reps // 2)), fb(N_RANKS, COUNT, 2, 4), S, N_RANKS,
-                               {"launches": 2 * (N_RANKS - 1) if algo == ar.AR_ALGO_RING_STEPWISE else 6})
+                               {"launches": 2 * (N_RANKS - 1) if algo == ar.AR_ALGO_RING_STEPWISE else 6,
+                                "cpu_oracle": "same computation as the ring (cpu_baseline) and rhd_tree oracle "
+                                              "timings: the oracle executes the rounds literally"})
     del ws
     torch.cuda.empty_cache()
 
@@ -224,12 +244,16 @@ def other_rows(torch, ar, inputs, ins, outs, dev, reps):
     fn()
     rows["fp8_ring"] = row_entry("fp8_ring", timer.run(fn, reps), ring_bytes(N_RANKS, n8, 2), n8 * 2, N_RANKS,
                                  {"count": n8, "wire_bytes_per_element": 1 + 4 / 128})
+    rows["fp8_ring"]["cpu_oracle"] = cpu_row(oracle_time(_o.fp8_ring_allreduce, h8, _o.BF16, _o.SUM), n8 * 2, N_RANKS,
+                                             "the full 8 x 67,108,864 bf16 workload, one call")
     codes = torch.empty(n8, dtype=torch.uint8, device=dev)
     scales = torch.empty(n8 // 128, dtype=torch.float32, device=dev)
     fn = lambda: ar.ar_fp8_quant(i8[0], codes, scales)
     fn()
     qb = n8 * 2 + n8 + n8 // 128 * 4
     rows["fp8_quant"] = row_entry("fp8_quant", timer.run(fn, reps), qb, n8 * 2, 1, {"count": n8})
+    rows["fp8_quant"]["cpu_oracle"] = cpu_row(oracle_time(_o.fp8_quant, h8[0], _o.BF16), n8 * 2, 1,
+                                              "one rank's 67,108,864 bf16, one call")
     fn = lambda: ar.ar_fp8_dequant(codes, scales, o8[0])
     fn()
     rows["fp8_dequant"] = row_entry("fp8_dequant", timer.run(fn, reps), qb, n8 * 2, 1, {"count": n8})
@@ -258,11 +282,35 @@ def other_rows(torch, ar, inputs, ins, outs, dev, reps):
     alg = N_RANKS * (s_tot + b_tot) + 2 * N_RANKS * b_tot + 2 * N_RANKS * s_tot
     rows["buckets"] = row_entry("buckets", ms, alg, s_tot, N_RANKS,
                                 {"tensors": len(sizes), "buckets": bar.nbuckets, "bytes_per_rank": s_tot,
-                                 "launches": 2 + bar.nbuckets, "phases_us": phases,
+                                 "launches": 3, "phases_us": phases,
                                  "data": "torch GPU generator, normal(0, 1e-2)"})
     del bins, bouts, bar
     torch.cuda.empty_cache()
+    k = 60  # oracle sample: the first 60 tensors of every rank, drawn as in the tests
+    hb = _gen_parallel(lambda r: inputs.bucket_tensors(r, sizes[:k]), range(N_RANKS))
+    s_k = int(np.sum(sizes[:k])) * 4
+    rows["buckets"]["cpu_oracle"] = cpu_row(oracle_time(_o.bucketed_allreduce, hb, _o.F32, _o.AVG, 25 << 20), s_k,
+                                            N_RANKS, f"the first {k} of the 300 tensors ({s_k} bytes per rank): "
+                                                     "plan, pack, per-bucket literal rings, unpack")
     return rows
+
+
+def graph_time_us(torch, call, calls, replays=5):
+    """Per-call device time of `calls` back-to-back calls captured in one HIP graph (no host launch cost)."""
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        call()  # warm on the capture stream
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        for _ in range(calls):
+            call()
+    g.replay()
+    torch.cuda.synchronize()
+    ms = Timer(torch).run(g.replay, replays)
+    return float(np.median(ms)) * 1e3 / calls
 
 
 def sweep(torch, ar, dev, out_path, reps=20, max_log2=30):
@@ -294,11 +342,16 @@ def sweep(torch, ar, dev, out_path, reps=20, max_log2=30):
                     call()
                 ms = Timer(torch).run(call, reps)
                 t = float(np.median(ms)) * 1e-3
+                graph_us = None
+                if S <= (16 << 20):
+                    # device time per call: 100 calls captured in one HIP graph, replayed
+                    graph_us = graph_time_us(torch, call, 100)
                 alg = ring_bytes(n, count, 4) if "stepwise" not in name else (
                     stepwise_ring_bytes(n, count, 4, 4) if name == "ring_stepwise" else stepwise_rhd_bytes(n, count, 4, 4))
                 rec = {"bytes_per_rank": S, "algo": name, "us_p50": t * 1e6, "us": stats_us(ms),
                        "algbw_GBps": S / t / GB, "busbw_GBps": S / t / GB * bus_factor(n),
-                       "hbm_GBps": alg / t / GB, "frac_of_peak": alg / t / GB / PEAK_HBM_GBPS, "buffer_sets": sets}
+                       "hbm_GBps": alg / t / GB, "frac_of_peak": alg / t / GB / PEAK_HBM_GBPS, "buffer_sets": sets,
+                       "graph_us_per_call": graph_us}
                 f.write(json.dumps(rec) + "\n")
                 f.flush()
                 lines.append(rec)
@@ -383,7 +436,7 @@ def main():
     }
     if not args.headline_only:
         result["copy_ceiling_GBps"] = copy_ceiling(torch, ins, outs)
-        result["rows"] = other_rows(torch, ar, inputs, ins, outs, dev, reps=max(5, args.steps // 2))
+        result["rows"] = other_rows(torch, ar, inputs, ins, outs, dev, reps=max(5, args.steps // 2), host=host)
         del ins, outs
         torch.cuda.empty_cache()
         log("timing the CPU oracle")

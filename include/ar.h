@@ -143,6 +143,20 @@ typedef struct ar_copy_desc {
 int ar_bucket_plan(const int64_t* numels, int ntensors, int dtype, int nranks, size_t cap_bytes,
                    int32_t* bucket_of, int64_t* offset_of, int64_t* bucket_count, int* nbuckets);
 
+/* All-reduce every bucket of N flat per-rank buffers in one launch (per-bucket rings without a launch per
+ * bucket). Bucket b occupies elements [sum_{b'<b} bucket_count[b'], ... + bucket_count[b]) of every rank's
+ * buffer, and is reduced exactly as ar_allreduce would reduce it alone: same balanced chunks, same fold
+ * order, same epilogue, so the results are bit-identical to one ar_allreduce call per bucket.
+ *   flat_in, flat_out: host arrays of nranks device pointers, 16-byte aligned, each to the sum of the
+ *     bucket counts; flat_out[r] may equal flat_in[r]; no other overlap.
+ *   bucket_count: host array [nbuckets]; every count must be a multiple of nranks * (16 / element size), as
+ *     ar_bucket_plan produces, so every chunk starts on a 16-byte boundary.
+ *   algo: AR_ALGO_RING, AR_ALGO_FUSED or AR_ALGO_RHD.
+ * Errors: AR_ERR_INVALID (enums, NULLs, misaligned pointers, a count that is negative or not such a
+ * multiple), AR_ERR_UNSUPPORTED (another algorithm; RHD with N not a power of two), AR_ERR_ALIAS, AR_ERR_HIP. */
+int ar_allreduce_buckets(const void* const* flat_in, void* const* flat_out, int nranks, const int64_t* bucket_count,
+                         int nbuckets, int dtype, int op, int algo, void* stream);
+
 /* Execute `ndescs` copy tasks in one launch. d_descs is a DEVICE array of ar_copy_desc (ranks x tensors of
  * copies do not fit in kernel arguments); it must stay valid until the work completes on `stream`.
  * pack: per-tensor -> bucket (with zero pads); unpack: bucket -> per-tensor. The two calls execute the same

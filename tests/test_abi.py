@@ -154,3 +154,25 @@ def test_bucket_plan_validation():
         ar.ar_bucket_plan([1, 2], ar.AR_F32, 2, 0)
     b, o, c = ar.ar_bucket_plan([], ar.AR_F32, 2, 100)
     assert len(b) == 0 and len(c) == 0
+
+
+def test_allreduce_buckets_validation():
+    L = ar.lib()
+    base = 0x30000000
+    counts = np.array([64, 32], dtype=np.int64)
+    ai = (ctypes.c_void_p * 2)(base, base + (1 << 20))
+    ao = (ctypes.c_void_p * 2)(base + (2 << 20), base + (3 << 20))
+    call = lambda c, n=2, dt=ar.AR_F32, op=ar.AR_SUM, algo=ar.AR_ALGO_RING, i=ai, o=ao: \
+        L.ar_allreduce_buckets(i, o, n, np.ascontiguousarray(c, np.int64).ctypes.data, len(c), dt, op, algo, None)
+    assert call(np.array([], np.int64)) == ar.AR_OK
+    assert call(counts, algo=ar.AR_ALGO_RING_STEPWISE) == ar.AR_ERR_UNSUPPORTED
+    assert call(counts, algo=ar.AR_ALGO_RING_FP8) == ar.AR_ERR_UNSUPPORTED
+    assert call(counts, n=3, algo=ar.AR_ALGO_RHD,
+                i=(ctypes.c_void_p * 3)(base, base + (1 << 20), base + (4 << 20)),
+                o=(ctypes.c_void_p * 3)(base + (2 << 20), base + (3 << 20), base + (5 << 20))) == ar.AR_ERR_UNSUPPORTED
+    assert call(np.array([64, 12], np.int64)) == ar.AR_ERR_INVALID  # not a multiple of N * 4 fp32 elements
+    assert call(np.array([64, -8], np.int64)) == ar.AR_ERR_INVALID
+    assert call(np.array([8], np.int64), dt=ar.AR_BF16) == ar.AR_ERR_INVALID  # bf16 needs multiples of N * 8
+    assert call(counts, i=(ctypes.c_void_p * 2)(base + 4, base + (1 << 20))) == ar.AR_ERR_INVALID  # misaligned
+    assert call(counts, o=(ctypes.c_void_p * 2)(base + 256, base + (3 << 20))) == ar.AR_ERR_ALIAS
+    assert call(counts, dt=9) == ar.AR_ERR_INVALID

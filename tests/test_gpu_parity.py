@@ -337,3 +337,69 @@ def test_fp8_ring_matches_oracle(n, count):
                     _f32_bits_equal_nan_aware(g, w)
             else:
                 assert_bitwise(got, want, f"fp8 ring n={n} count={count} dt={dt}")
+
+
+@pytest.mark.parametrize("n", [1, 2, 3, 5, 8])
+@pytest.mark.parametrize("dt", [ar.AR_F32, ar.AR_BF16, ar.AR_I32])
+def test_allreduce_buckets_equals_one_call_per_bucket(n, dt):
+    """One launch over many buckets (more than one launch's worth of segments, some empty) gives exactly the
+    bits of one ar_allreduce per bucket, in place and out of place, for every op and one-pass algorithm."""
+    unit = n * (16 // (2 if dt == ar.AR_BF16 else 4))
+    rng = np.random.default_rng(n * 10 + dt)
+    counts = (rng.integers(0, 40, 150) * unit).astype(np.int64)
+    counts[[3, 77]] = 0
+    counts[5] = unit * 3001
+    total = int(counts.sum())
+    xs = _inputs(dt, n, total, 20)
+    starts = np.concatenate([[0], np.cumsum(counts)])
+    algos = [ar.AR_ALGO_RING, ar.AR_ALGO_FUSED] + ([ar.AR_ALGO_RHD] if n & (n - 1) == 0 else [])
+    for algo in algos:
+        for op in OPS:
+            want_flat = [np.empty(total, dtype=NP_BITS[dt]) for _ in range(n)]
+            for b in range(len(counts)):
+                if counts[b] == 0:
+                    continue
+                seg = [x.view(NP_BITS[dt])[starts[b]:starts[b + 1]] for x in xs]
+                got_b = expect([s.view(xs[0].dtype) for s in seg], dt, op, algo)
+                for r in range(n):
+                    want_flat[r][starts[b]:starts[b + 1]] = got_b[r]
+            ins = [to_dev(x, dt)[1] for x in xs]
+            outs = [empty_like_dev(total, dt)[1] for _ in range(n)]
+            ar.ar_allreduce_buckets(ins, outs, counts, op, algo)
+            torch.cuda.synchronize()
+            assert_bitwise([from_dev(o, dt) for o in outs], want_flat, f"buckets n={n} op={op} algo={algo}")
+            ar.ar_allreduce_buckets(ins, ins, counts, op, algo)  # in place
+            torch.cuda.synchronize()
+            assert_bitwise([from_dev(o, dt) for o in ins], want_flat, f"buckets in place n={n} op={op}")
+
+
+@pytest.mark.parametrize("algo", [ar.AR_ALGO_RING, ar.AR_ALGO_RHD, ar.AR_ALGO_RING_STEPWISE, ar.AR_ALGO_RING_FP8])
+def test_hip_graph_capture_replays_match_eager(algo):
+    """Calls captured in a HIP graph replay to the eager result, every replay, with eager work in between."""
+    n, count = 8, 50_003
+    dt = ar.AR_BF16
+    xs = inputs.rank_inputs("normal_bf16", n, count, cfg=31)
+    ins = [to_dev(x, dt)[1] for x in xs]
+    outs = [empty_like_dev(count, dt)[1] for _ in range(n)]
+    need = ar.ar_allreduce_workspace_size(n, count, dt, ar.AR_SUM, algo)
+    ws = torch.empty(need, dtype=torch.uint8, device=DEV) if need else None
+    call = lambda: ar.ar_allreduce_ws(ins, outs, ar.AR_SUM, algo, ws)
+    call()
+    torch.cuda.synchronize()
+    eager = [from_dev(o, dt) for o in outs]
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        call()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        call()
+    for rep in range(4):
+        for o in outs:
+            o.view(torch.int16).fill_(-1)  # eager work between replays
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert_bitwise([from_dev(o, dt) for o in outs], eager, f"graph replay {rep} algo={algo}")
