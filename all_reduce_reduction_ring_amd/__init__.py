@@ -6,7 +6,7 @@ the library's HIP kernels. There is no CPU fallback: if ``libar.so`` is missing 
 call raises.
 
 Entry points (same names as ``include/ar.h``): ar_allreduce, ar_allreduce_ws, ar_allreduce_workspace_size,
-ar_allreduce_buckets, ar_bucket_plan, ar_bucket_pack, ar_bucket_unpack, ar_fp8_quant, ar_fp8_dequant, ar_status_string,
+ar_allreduce_buckets, ar_allreduce_tensors, ar_bucket_plan, ar_bucket_pack, ar_bucket_unpack, ar_fp8_quant, ar_fp8_dequant, ar_status_string,
 ar_last_call, ar_version. Helpers: make_copy_descs, BucketedAllReduce.
 """
 from __future__ import annotations
@@ -21,7 +21,8 @@ __all__ = [
     "AR_F32", "AR_BF16", "AR_F16", "AR_I32", "AR_SUM", "AR_AVG", "AR_MIN", "AR_MAX",
     "AR_ALGO_RING", "AR_ALGO_FUSED", "AR_ALGO_RHD", "AR_ALGO_RING_STEPWISE", "AR_ALGO_RHD_STEPWISE",
     "AR_ALGO_RING_FP8", "AR_MAX_RANKS", "AR_FP8_BLOCK", "ArError", "lib", "lib_path",
-    "ar_allreduce", "ar_allreduce_ws", "ar_allreduce_workspace_size", "ar_allreduce_buckets", "ar_bucket_plan",
+    "ar_allreduce", "ar_allreduce_ws", "ar_allreduce_workspace_size", "ar_allreduce_buckets",
+    "ar_allreduce_tensors", "ar_bucket_plan",
     "ar_bucket_pack",
     "ar_bucket_unpack", "ar_fp8_quant", "ar_fp8_dequant", "ar_status_string", "ar_last_call", "ar_version",
     "make_copy_descs", "BucketedAllReduce", "dtype_code",
@@ -68,6 +69,7 @@ def lib():
         L.ar_allreduce_ws.argtypes = [vp, vp, i32, sz, i32, i32, i32, vp, sz, vp]
         L.ar_allreduce_workspace_size.argtypes = [i32, sz, i32, i32, i32, ctypes.POINTER(sz)]
         L.ar_allreduce_buckets.argtypes = [vp, vp, i32, vp, i32, i32, i32, i32, vp]
+        L.ar_allreduce_tensors.argtypes = [vp, vp, vp, i32, i32, i32, i32, i32, vp]
         L.ar_bucket_plan.argtypes = [vp, i32, i32, i32, sz, vp, vp, vp, ctypes.POINTER(i32)]
         L.ar_bucket_pack.argtypes = [vp, i32, i32, vp]
         L.ar_bucket_unpack.argtypes = [vp, i32, i32, vp]
@@ -77,7 +79,7 @@ def lib():
         L.ar_status_string.restype = ctypes.c_char_p
         L.ar_last_call.argtypes = [ctypes.POINTER(_CallRecord)]
         for name in ("ar_allreduce", "ar_allreduce_ws", "ar_allreduce_workspace_size", "ar_allreduce_buckets",
-                     "ar_bucket_plan",
+                     "ar_allreduce_tensors", "ar_bucket_plan",
                      "ar_bucket_pack", "ar_bucket_unpack", "ar_fp8_quant", "ar_fp8_dequant", "ar_last_call",
                      "ar_version"):
             getattr(L, name).restype = i32
@@ -156,6 +158,15 @@ def ar_allreduce_buckets(flat_ins, flat_outs, bucket_count, op=AR_SUM, algo=AR_A
         raise ValueError("the buckets do not fit in the flat tensors")
     _check(lib().ar_allreduce_buckets(arr_in, arr_out, n, counts.ctypes.data, counts.size, dt, op, algo,
                                       _stream(stream)), "ar_allreduce_buckets")
+
+
+def ar_allreduce_tensors(descs, in_ptrs, out_ptrs, ntensors, nranks, dtype, op=AR_AVG, algo=AR_ALGO_RING,
+                         stream=None):
+    """descs: device int64 tensor [ntensors, 4] laid out as ar_tensor_desc; in_ptrs/out_ptrs: device int64
+    tensors [ntensors * nranks] of device addresses (entry t * nranks + r)."""
+    _check(lib().ar_allreduce_tensors(ctypes.c_void_p(descs.data_ptr()), ctypes.c_void_p(in_ptrs.data_ptr()),
+                                      ctypes.c_void_p(out_ptrs.data_ptr()), ntensors, nranks, dtype, op, algo,
+                                      _stream(stream)), "ar_allreduce_tensors")
 
 
 def ar_bucket_plan(numels, dtype, nranks, cap_bytes=25 << 20):
@@ -263,6 +274,18 @@ class BucketedAllReduce:
                 unpack.append((base + off * es, outs[r][t].data_ptr(), numel, 0))
         self.pack_descs = make_copy_descs(pack, t00.device)
         self.unpack_descs = make_copy_descs(unpack, t00.device)
+        # the fused path: one descriptor per tensor (numel, offset in its bucket, bucket count / N) and the
+        # [tensor, rank] pointer tables
+        import torch as _t
+        tdesc = np.zeros((self.nt, 4), np.int64)
+        for t in range(self.nt):
+            b = int(self.bucket_of[t])
+            tdesc[t] = (numels[t], int(self.offset_of[t]), int(self.bucket_count[b]) // self.n, 0)
+        self.tensor_descs = _t.from_numpy(tdesc).to(t00.device)
+        iptr = np.array([[ins[r][t].data_ptr() for r in range(self.n)] for t in range(self.nt)], np.uint64)
+        optr = np.array([[outs[r][t].data_ptr() for r in range(self.n)] for t in range(self.nt)], np.uint64)
+        self.in_ptrs = _t.from_numpy(iptr.reshape(-1).view(np.int64)).to(t00.device)
+        self.out_ptrs = _t.from_numpy(optr.reshape(-1).view(np.int64)).to(t00.device)
         self.views = [[self.buffers[r][int(self.bucket_start[b]):int(self.bucket_start[b + 1])]
                        for r in range(self.n)] for b in range(len(self.bucket_count))]
 
@@ -284,6 +307,12 @@ class BucketedAllReduce:
 
     def unpack(self, stream=None):
         ar_bucket_unpack(self.unpack_descs, self.dtype, stream)
+
+    def fused(self, stream=None):
+        """The whole bucketed all-reduce in one launch, reading and writing the tensors in place of the buckets
+        (same bits as pack + reduce + unpack)."""
+        ar_allreduce_tensors(self.tensor_descs, self.in_ptrs, self.out_ptrs, self.nt, self.n, self.dtype, self.op,
+                             self.algo, stream)
 
     def __call__(self, stream=None):
         self.pack(stream)

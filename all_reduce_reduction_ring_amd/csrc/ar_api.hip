@@ -252,6 +252,23 @@ int ar_allreduce_buckets(const void* const* flat_in, void* const* flat_out, int 
   return done(e == hipSuccess ? AR_OK : AR_ERR_HIP);
 }
 
+int ar_allreduce_tensors(const ar_tensor_desc* d_descs, const void* const* d_in, void* const* d_out, int ntensors,
+                         int nranks, int dtype, int op, int algo, void* stream) {
+  auto done = [&](int st) {
+    return finish("ar_allreduce_tensors", nranks, static_cast<size_t>(ntensors < 0 ? 0 : ntensors), dtype, op, algo, st);
+  };
+  if (!valid_dtype(dtype) || !valid_op(op) || !valid_algo(algo)) return done(AR_ERR_INVALID);
+  if (nranks < 1 || nranks > AR_MAX_RANKS || ntensors < 0) return done(AR_ERR_INVALID);
+  if (algo != AR_ALGO_RING && algo != AR_ALGO_FUSED && algo != AR_ALGO_RHD) return done(AR_ERR_UNSUPPORTED);
+  if (algo == AR_ALGO_RHD && !is_pow2(nranks)) return done(AR_ERR_UNSUPPORTED);
+  if (ntensors == 0) return done(AR_OK);
+  if (!d_descs || !d_in || !d_out) return done(AR_ERR_INVALID);
+  const int a = nranks == 1 ? AR_ALGO_RING : algo;
+  hipError_t e = ar::launch_tensors(d_descs, d_in, d_out, ntensors, nranks, dtype, op, a,
+                                    static_cast<hipStream_t>(stream));
+  return done(e == hipSuccess ? AR_OK : AR_ERR_HIP);
+}
+
 static int batched_copy(const char* entry, const ar_copy_desc* d_descs, int ndescs, int dtype, void* stream) {
   auto done = [&](int st) { return finish(entry, 0, static_cast<size_t>(ndescs), dtype, -1, -1, st); };
   if (ndescs < 0 || !valid_dtype(dtype)) return done(AR_ERR_INVALID);

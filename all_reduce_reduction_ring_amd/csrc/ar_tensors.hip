@@ -1,0 +1,264 @@
+// ar_tensors.hip -- bucketed all-reduce without buckets in memory.
+//
+// Bucketing (jisaku.com glossary "AllReduce（オールリデュース）", section パフォーマンスチューニング; vasteelab
+// "All-Reduce・All-Gather・All-to-Allとは？…", section communicationとcomputeを重ねる条件) packs many gradient
+// tensors into one bucket and all-reduces the bucket with the ring. The ring result of an element depends only
+// on the element's position in its bucket: position p falls in chunk c = p / (bucket count / N), and chunk c is
+// folded starting at rank c. So every rank's tensors can be read where they are and the results written
+// straight to the per-tensor outputs, each element folded in exactly the order the bucket ring would use: the
+// same bits as pack -> ring per bucket -> unpack, with N reads + N writes per element instead of three times
+// that. (Bucket pads are zeros that never mix with other elements, so they need not exist.)
+//
+// Work: tiles of 256 16-byte slots of one tensor, dealt out round-robin over a grid sized to the GPU (tile g to
+// block g mod G). Each block stages 256 tensor descriptors at a time in LDS and prefix-sums their tile counts.
+// A tile normally lies inside one bucket chunk, so the rank rotation is uniform across the block; a tile
+// that crosses a chunk boundary is processed as uniform sub-ranges.
+#include "ar_device.h"
+#include "ar_internal.h"
+
+namespace ar {
+namespace {
+
+constexpr int kThreads = 256;
+constexpr int kBatch = 256;
+
+struct TensorArgs {
+  const ar_tensor_desc* descs;
+  const void* const* in;  // [ntensors * n], rank-minor
+  void* const* out;       // [ntensors * n]
+  int ntensors;
+  int n;
+  int rot;  // 1: ring order; 0: rank order from 0
+};
+
+template <int NR> constexpr int tensor_blocks_per_cu() { return NR == 8 ? 2 : 4; }
+
+// Fold of one 16-byte slot at byte offset `off` over the tensor's rank pointers, starting at rank `start`.
+template <int DT, int OP, int NR, bool TREE>
+__device__ __forceinline__ u32x4 fold_slot(const void* const* ip, int n, int start, int64_t off) {
+  using S = Slot<DT>;
+  using Acc = typename S::Acc;
+  constexpr int V = S::V;
+  Acc acc[V], t[V];
+  if constexpr (NR > 0) {
+    u32x4 x[NR];
+#pragma unroll
+    for (int k = 0; k < NR; ++k) {
+      int r = TREE ? k : start + k;
+      r = r >= NR ? r - NR : r;
+      x[k] = ld16(static_cast<const char*>(ip[r]) + off);
+    }
+    if constexpr (TREE) {
+      // halving tree: combine ranks N/2 apart, then N/4, ... (level by level over the rank-ordered loads)
+      Acc lv[NR][V];
+#pragma unroll
+      for (int k = 0; k < NR; ++k) S::unpack(x[k], lv[k]);
+#pragma unroll
+      for (int h = NR / 2; h >= 1; h /= 2)
+#pragma unroll
+        for (int k = 0; k < h; ++k)
+#pragma unroll
+          for (int e = 0; e < V; ++e) lv[k][e] = combine<OP>(lv[k][e], lv[k + h][e]);
+#pragma unroll
+      for (int e = 0; e < V; ++e) acc[e] = lv[0][e];
+    } else {
+      S::unpack(x[0], acc);
+#pragma unroll
+      for (int k = 1; k < NR; ++k) {
+        S::unpack(x[k], t);
+#pragma unroll
+        for (int e = 0; e < V; ++e) acc[e] = combine<OP>(acc[e], t[e]);
+      }
+    }
+  } else {
+    S::unpack(ld16(static_cast<const char*>(ip[start]) + off), acc);
+    for (int k = 1; k < n; ++k) {
+      int r = start + k;
+      r = r >= n ? r - n : r;
+      S::unpack(ld16(static_cast<const char*>(ip[r]) + off), t);
+#pragma unroll
+      for (int e = 0; e < V; ++e) acc[e] = combine<OP>(acc[e], t[e]);
+    }
+  }
+  const int nn = NR > 0 ? NR : n;
+#pragma unroll
+  for (int e = 0; e < V; ++e) acc[e] = finalize<OP>(acc[e], nn);
+  return S::pack(acc);
+}
+
+// One element (tensor tails and unaligned tensors). The tree order for a runtime n uses the stack form.
+template <int DT, int OP, bool TREE>
+__device__ __forceinline__ uint32_t fold_elem(const void* const* ip, int n, int start, int64_t e) {
+  using Acc = typename Traits<DT>::Acc;
+  if (TREE) {
+    int k = 0;
+    while ((1 << k) < n) ++k;
+    Acc stack[7];
+    int height[7];
+    int sp = 0;
+    for (int j = 0; j < n; ++j) {
+      int rev = 0;
+      for (int b = 0; b < k; ++b) rev |= ((j >> b) & 1) << (k - 1 - b);
+      Acc v = widen<DT>(load_elem<DT>(ip[rev], e));
+      int h = 0;
+      while (sp > 0 && height[sp - 1] == h) {
+        v = combine<OP>(stack[sp - 1], v);
+        --sp;
+        ++h;
+      }
+      stack[sp] = v;
+      height[sp] = h;
+      ++sp;
+    }
+    return narrow<DT>(finalize<OP>(stack[0], n));
+  }
+  Acc acc = widen<DT>(load_elem<DT>(ip[start], e));
+  for (int k = 1; k < n; ++k) {
+    int r = start + k;
+    r = r >= n ? r - n : r;
+    acc = combine<OP>(acc, widen<DT>(load_elem<DT>(ip[r], e)));
+  }
+  return narrow<DT>(finalize<OP>(acc, n));
+}
+
+template <int DT, int OP, int NR, bool TREE>
+__global__ __launch_bounds__(kThreads) void tensor_kernel(TensorArgs a) {
+  constexpr int V = Traits<DT>::kVec;
+  constexpr int64_t TE = static_cast<int64_t>(kThreads) * V;  // elements per tile
+  __shared__ int64_t s_numel[kBatch], s_off[kBatch], s_clen[kBatch], pre[kBatch];
+  const int n = NR > 0 ? NR : a.n;
+  const int64_t G = gridDim.x, b = blockIdx.x;
+  const int t = threadIdx.x;
+  int64_t base = 0;
+  for (int b0 = 0; b0 < a.ntensors; b0 += kBatch) {
+    const int m = a.ntensors - b0 < kBatch ? a.ntensors - b0 : kBatch;
+    int64_t nt = 0;
+    if (t < m) {
+      const ar_tensor_desc d = a.descs[b0 + t];
+      s_numel[t] = d.numel;
+      s_off[t] = d.bucket_offset;
+      s_clen[t] = d.chunk_len;
+      nt = d.numel > 0 ? (d.numel + TE - 1) / TE : 0;
+    }
+    pre[t] = nt;
+    __syncthreads();
+    for (int off = 1; off < kBatch; off <<= 1) {
+      const int64_t v = t >= off ? pre[t - off] : 0;
+      __syncthreads();
+      pre[t] += v;
+      __syncthreads();
+    }
+    const int64_t batch_tiles = pre[kBatch - 1];
+    for (int64_t g = base + ((b - base % G) % G + G) % G; g < base + batch_tiles; g += G) {
+      const int64_t lt = g - base;
+      int lo = 0, hi = m - 1;
+      while (lo < hi) {
+        const int mid = (lo + hi) >> 1;
+        if (pre[mid] > lt) hi = mid;
+        else lo = mid + 1;
+      }
+      const int ti = __builtin_amdgcn_readfirstlane(b0 + lo);
+      const int64_t numel = s_numel[lo], boff = s_off[lo], clen = s_clen[lo];
+      const int64_t e0 = (lt - (lo > 0 ? pre[lo - 1] : 0)) * TE;
+      const int64_t e1 = e0 + TE < numel ? e0 + TE : numel;
+      const void* const* ip = a.in + static_cast<int64_t>(ti) * n;
+      void* const* op = a.out + static_cast<int64_t>(ti) * n;
+      uintptr_t anyp = 0;
+      for (int r = 0; r < n; ++r) anyp |= reinterpret_cast<uintptr_t>(ip[r]) | reinterpret_cast<uintptr_t>(op[r]);
+      // the tree order for a runtime rank count is evaluated per element
+      const bool vec = (anyp & 15u) == 0 && !(TREE && NR == 0);
+      // uniform sub-ranges [s0, s1) of the tile that lie in one bucket chunk
+      int64_t s0 = e0;
+      while (s0 < e1) {
+        int start = 0;
+        int64_t s1 = e1;
+        if (!TREE && a.rot && clen > 0) {
+          int64_t c = (boff + s0) / clen;
+          c = c < 0 ? 0 : (c < n ? c : n - 1);
+          start = static_cast<int>(c);
+          const int64_t bnd = (c + 1) * clen - boff;  // next chunk boundary, in tensor elements
+          s1 = bnd < e1 ? bnd : e1;
+          if (s1 <= s0) s1 = e1;  // only a malformed descriptor gets here; always make progress
+        }
+        // whole slots (tile starts and, for a valid plan, chunk boundaries are slot-aligned); the tensor's
+        // tail, and any sub-range that does not start on a slot, go element by element
+        const bool vsub = vec && (s0 % V) == 0;
+        const int64_t v0 = s0 / V, v1 = vsub ? s1 / V : v0;
+        const int64_t v = v0 + t;
+        if (v < v1) {
+          const u32x4 w = fold_slot<DT, OP, NR, TREE>(ip, n, start, v * 16);
+          for (int r = 0; r < n; ++r) st16(static_cast<char*>(op[r]) + v * 16, w);
+        }
+        const int64_t tail0 = vsub ? v1 * V : s0;
+        for (int64_t e = tail0 + t; e < s1; e += kThreads) {
+          const uint32_t bits = fold_elem<DT, OP, TREE>(ip, n, start, e);
+          for (int r = 0; r < n; ++r) store_elem<DT>(op[r], e, bits);
+        }
+        s0 = s1;
+      }
+    }
+    base += batch_tiles;
+    __syncthreads();
+  }
+}
+
+template <int DT, int OP, int NR, bool TREE>
+hipError_t launch_t(const TensorArgs& a, hipStream_t s) {
+  const int g = cu_count() * tensor_blocks_per_cu<NR>();
+  hipLaunchKernelGGL((tensor_kernel<DT, OP, NR, TREE>), dim3(g), dim3(kThreads), 0, s, a);
+  return hipGetLastError();
+}
+
+template <int DT, int OP>
+hipError_t tensors_n(const TensorArgs& a, int algo, hipStream_t s) {
+  const bool tree = algo == AR_ALGO_RHD && a.n > 1;
+  if (tree) {
+    switch (a.n) {
+      case 2: return launch_t<DT, OP, 2, true>(a, s);
+      case 4: return launch_t<DT, OP, 4, true>(a, s);
+      case 8: return launch_t<DT, OP, 8, true>(a, s);
+      case 16: return launch_t<DT, OP, 16, true>(a, s);
+      default: return launch_t<DT, OP, 0, true>(a, s);
+    }
+  }
+  switch (a.n) {
+    case 2: return launch_t<DT, OP, 2, false>(a, s);
+    case 4: return launch_t<DT, OP, 4, false>(a, s);
+    case 8: return launch_t<DT, OP, 8, false>(a, s);
+    case 16: return launch_t<DT, OP, 16, false>(a, s);
+    default: return launch_t<DT, OP, 0, false>(a, s);
+  }
+}
+
+template <int DT>
+hipError_t tensors_op(const TensorArgs& a, int op, int algo, hipStream_t s) {
+  switch (op) {
+    case AR_SUM: return tensors_n<DT, AR_SUM>(a, algo, s);
+    case AR_AVG: return tensors_n<DT, AR_AVG>(a, algo, s);
+    case AR_MIN: return tensors_n<DT, AR_MIN>(a, algo, s);
+    case AR_MAX: return tensors_n<DT, AR_MAX>(a, algo, s);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+}  // namespace
+
+hipError_t launch_tensors(const ar_tensor_desc* d_descs, const void* const* d_in, void* const* d_out, int ntensors,
+                          int n, int dtype, int op, int algo, hipStream_t s) {
+  TensorArgs a;
+  a.descs = d_descs;
+  a.in = d_in;
+  a.out = d_out;
+  a.ntensors = ntensors;
+  a.n = n;
+  a.rot = algo == AR_ALGO_RING ? 1 : 0;
+  switch (dtype) {
+    case AR_F32: return tensors_op<AR_F32>(a, op, algo, s);
+    case AR_BF16: return tensors_op<AR_BF16>(a, op, algo, s);
+    case AR_F16: return tensors_op<AR_F16>(a, op, algo, s);
+    case AR_I32: return tensors_op<AR_I32>(a, op, algo, s);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+}  // namespace ar

@@ -284,6 +284,12 @@ def other_rows(torch, ar, inputs, ins, outs, dev, reps, host):
                                 {"tensors": len(sizes), "buckets": bar.nbuckets, "bytes_per_rank": s_tot,
                                  "launches": 3, "phases_us": phases,
                                  "data": "torch GPU generator, normal(0, 1e-2)"})
+    # the same bucketed all-reduce read and written in place of the buckets: N reads + N writes per element
+    bar.fused()
+    torch.cuda.synchronize()
+    rows["buckets_fused"] = row_entry("buckets_fused", timer.run(bar.fused, max(3, reps // 2)), 2 * N_RANKS * s_tot,
+                                      s_tot, N_RANKS, {"tensors": len(sizes), "launches": 1,
+                                                       "same_bits_as": "buckets (pack + per-bucket ring + unpack)"})
     del bins, bouts, bar
     torch.cuda.empty_cache()
     k = 60  # oracle sample: the first 60 tensors of every rank, drawn as in the tests

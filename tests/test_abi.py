@@ -176,3 +176,18 @@ def test_allreduce_buckets_validation():
     assert call(counts, i=(ctypes.c_void_p * 2)(base + 4, base + (1 << 20))) == ar.AR_ERR_INVALID  # misaligned
     assert call(counts, o=(ctypes.c_void_p * 2)(base + 256, base + (3 << 20))) == ar.AR_ERR_ALIAS
     assert call(counts, dt=9) == ar.AR_ERR_INVALID
+
+
+def test_allreduce_tensors_validation():
+    L = ar.lib()
+    fake = ctypes.c_void_p(0x40000000)
+    call = lambda nt=3, n=2, dt=ar.AR_F32, op=ar.AR_SUM, algo=ar.AR_ALGO_RING, d=fake, i=fake, o=fake: \
+        L.ar_allreduce_tensors(d, i, o, nt, n, dt, op, algo, None)
+    assert call(nt=0) == ar.AR_OK
+    assert call(nt=-1) == ar.AR_ERR_INVALID
+    assert call(n=0) == ar.AR_ERR_INVALID
+    assert call(dt=5) == ar.AR_ERR_INVALID
+    assert call(d=None) == ar.AR_ERR_INVALID
+    assert call(algo=ar.AR_ALGO_RING_STEPWISE) == ar.AR_ERR_UNSUPPORTED
+    assert call(algo=ar.AR_ALGO_RING_FP8) == ar.AR_ERR_UNSUPPORTED
+    assert call(n=6, algo=ar.AR_ALGO_RHD) == ar.AR_ERR_UNSUPPORTED

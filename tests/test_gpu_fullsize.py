@@ -7,7 +7,7 @@
   rank-order and halving-doubling variants (which do not depend on chunk positions) on 2^20 sampled elements,
   for which the oracle is evaluated on exactly those elements.
 - buckets: 300 fp32 tensors per rank (log-uniform 1K..16M elements, 2.07 GB per rank), 25 MiB buckets, avg:
-  every tensor of every rank.
+  every tensor of every rank, through pack + per-bucket rings + unpack and through the fused tensor path.
 """
 import concurrent.futures
 
@@ -122,11 +122,16 @@ def test_buckets_300_tensors_full_size():
     np.testing.assert_array_equal(bar.bucket_count, bc)
     bar()
     torch.cuda.synchronize()
-    del ins, bar
+    outs_fused = [[torch.empty_like(t) for t in ins[r]] for r in range(n)]
+    bar_fused = ar.BucketedAllReduce(ins, outs_fused, op=ar.AR_AVG, cap_bytes=25 << 20)
+    bar_fused.fused()
+    torch.cuda.synchronize()
+    del ins, bar, bar_fused
     want = oracle.bucketed_allreduce(host, oracle.F32, oracle.AVG, cap_bytes=25 << 20)
     for r in range(n):
         for t in range(len(sizes)):
             np.testing.assert_array_equal(_down_bits(outs[r][t]), want[r][t].view(np.uint32))
+            np.testing.assert_array_equal(_down_bits(outs_fused[r][t]), want[r][t].view(np.uint32))
 
 
 @pytest.mark.timeout(900)
