@@ -6,7 +6,7 @@ the library's HIP kernels. There is no CPU fallback: if ``libar.so`` is missing 
 call raises.
 
 Entry points (same names as ``include/ar.h``): ar_allreduce, ar_allreduce_ws, ar_allreduce_workspace_size,
-ar_allreduce_buckets, ar_allreduce_tensors, ar_bucket_plan, ar_bucket_pack, ar_bucket_unpack, ar_fp8_quant, ar_fp8_dequant, ar_status_string,
+ar_allreduce_buckets, ar_allreduce_tensors, ar_reduce_scatter, ar_all_gather, ar_bucket_plan, ar_bucket_pack, ar_bucket_unpack, ar_fp8_quant, ar_fp8_dequant, ar_status_string,
 ar_last_call, ar_version. Helpers: make_copy_descs, BucketedAllReduce.
 """
 from __future__ import annotations
@@ -22,7 +22,7 @@ __all__ = [
     "AR_ALGO_RING", "AR_ALGO_FUSED", "AR_ALGO_RHD", "AR_ALGO_RING_STEPWISE", "AR_ALGO_RHD_STEPWISE",
     "AR_ALGO_RING_FP8", "AR_MAX_RANKS", "AR_FP8_BLOCK", "ArError", "lib", "lib_path",
     "ar_allreduce", "ar_allreduce_ws", "ar_allreduce_workspace_size", "ar_allreduce_buckets",
-    "ar_allreduce_tensors", "ar_bucket_plan",
+    "ar_allreduce_tensors", "ar_reduce_scatter", "ar_all_gather", "chunk_bounds", "ar_bucket_plan",
     "ar_bucket_pack",
     "ar_bucket_unpack", "ar_fp8_quant", "ar_fp8_dequant", "ar_status_string", "ar_last_call", "ar_version",
     "make_copy_descs", "BucketedAllReduce", "dtype_code",
@@ -70,6 +70,8 @@ def lib():
         L.ar_allreduce_workspace_size.argtypes = [i32, sz, i32, i32, i32, ctypes.POINTER(sz)]
         L.ar_allreduce_buckets.argtypes = [vp, vp, i32, vp, i32, i32, i32, i32, vp]
         L.ar_allreduce_tensors.argtypes = [vp, vp, vp, i32, i32, i32, i32, i32, vp]
+        L.ar_reduce_scatter.argtypes = [vp, vp, i32, sz, i32, i32, vp]
+        L.ar_all_gather.argtypes = [vp, vp, i32, sz, i32, vp]
         L.ar_bucket_plan.argtypes = [vp, i32, i32, i32, sz, vp, vp, vp, ctypes.POINTER(i32)]
         L.ar_bucket_pack.argtypes = [vp, i32, i32, vp]
         L.ar_bucket_unpack.argtypes = [vp, i32, i32, vp]
@@ -79,9 +81,8 @@ def lib():
         L.ar_status_string.restype = ctypes.c_char_p
         L.ar_last_call.argtypes = [ctypes.POINTER(_CallRecord)]
         for name in ("ar_allreduce", "ar_allreduce_ws", "ar_allreduce_workspace_size", "ar_allreduce_buckets",
-                     "ar_allreduce_tensors", "ar_bucket_plan",
-                     "ar_bucket_pack", "ar_bucket_unpack", "ar_fp8_quant", "ar_fp8_dequant", "ar_last_call",
-                     "ar_version"):
+                     "ar_allreduce_tensors", "ar_reduce_scatter", "ar_all_gather", "ar_bucket_plan", "ar_bucket_pack",
+                     "ar_bucket_unpack", "ar_fp8_quant", "ar_fp8_dequant", "ar_last_call", "ar_version"):
             getattr(L, name).restype = i32
         _lib = L
     return _lib
@@ -167,6 +168,40 @@ def ar_allreduce_tensors(descs, in_ptrs, out_ptrs, ntensors, nranks, dtype, op=A
     _check(lib().ar_allreduce_tensors(ctypes.c_void_p(descs.data_ptr()), ctypes.c_void_p(in_ptrs.data_ptr()),
                                       ctypes.c_void_p(out_ptrs.data_ptr()), ntensors, nranks, dtype, op, algo,
                                       _stream(stream)), "ar_allreduce_tensors")
+
+
+def chunk_bounds(count, nranks):
+    """The balanced split: chunk c = [lo[c], lo[c+1]) with count//N + 1 elements for c < count % N."""
+    q, r = divmod(count, nranks)
+    return [c * q + min(c, r) for c in range(nranks + 1)]
+
+
+def _ptr(t):
+    return t.data_ptr() if t is not None and t.numel() > 0 else 0
+
+
+def ar_reduce_scatter(ins, outs, op=AR_SUM, stream=None):
+    """ins: N full tensors; outs[c]: a tensor of chunk c's length (the balanced split) receiving chunk c."""
+    n, count = len(ins), ins[0].numel()
+    lo = chunk_bounds(count, n)
+    if len(outs) != n or any(o is not None and o.numel() != lo[c + 1] - lo[c] for c, o in enumerate(outs)):
+        raise ValueError("outs[c] must hold exactly chunk c of the balanced split")
+    arr_in = (ctypes.c_void_p * n)(*[t.data_ptr() for t in ins])
+    arr_out = (ctypes.c_void_p * n)(*[_ptr(o) for o in outs])
+    _check(lib().ar_reduce_scatter(arr_in, arr_out, n, count, dtype_code(ins[0].dtype), op, _stream(stream)),
+           "ar_reduce_scatter")
+
+
+def ar_all_gather(ins, outs, stream=None):
+    """ins[r]: rank r's chunk (the balanced split of the outputs' length); outs: N full tensors."""
+    n, count = len(outs), outs[0].numel()
+    lo = chunk_bounds(count, n)
+    if len(ins) != n or any(i is not None and i.numel() != lo[c + 1] - lo[c] for c, i in enumerate(ins)):
+        raise ValueError("ins[r] must hold exactly chunk r of the balanced split")
+    arr_in = (ctypes.c_void_p * n)(*[_ptr(i) for i in ins])
+    arr_out = (ctypes.c_void_p * n)(*[t.data_ptr() for t in outs])
+    _check(lib().ar_all_gather(arr_in, arr_out, n, count, dtype_code(outs[0].dtype), _stream(stream)),
+           "ar_all_gather")
 
 
 def ar_bucket_plan(numels, dtype, nranks, cap_bytes=25 << 20):

@@ -20,7 +20,7 @@ BUILD = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "libar.so")
 ARCH = "gfx950"
 
-SOURCES = ["ar_api.hip", "ar_collapsed.hip", "ar_stepwise.hip", "ar_bucket.hip", "ar_fp8.hip", "ar_tensors.hip"]
+SOURCES = ["ar_api.hip", "ar_collapsed.hip", "ar_stepwise.hip", "ar_bucket.hip", "ar_fp8.hip", "ar_tensors.hip", "ar_rsag.hip"]
 
 CFLAGS = [
     f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC", "-ffp-contract=off",

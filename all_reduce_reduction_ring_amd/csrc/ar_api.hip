@@ -136,9 +136,60 @@ int allreduce_impl(const char* entry, const void* const* in_bufs, void* const* o
   return done(e == hipSuccess ? AR_OK : AR_ERR_HIP);
 }
 
+// Shared validation of reduce-scatter / all-gather: `full` are the N buffers of `count` elements, `part` the N
+// chunk buffers; a chunk buffer placed at its own chunk inside its rank's full buffer is the in-place form.
+int rsag_impl(const char* entry, const void* const* full, const void* const* part, int nranks, size_t count,
+              int dtype, int op, bool is_rs, void* const* writable_full, void* const* writable_part, void* stream) {
+  auto done = [&](int st) { return finish(entry, nranks, count, dtype, op, -1, st); };
+  if (!valid_dtype(dtype) || (is_rs && !valid_op(op))) return done(AR_ERR_INVALID);
+  if (nranks < 1 || nranks > AR_MAX_RANKS) return done(AR_ERR_INVALID);
+  if (count == 0) return done(AR_OK);
+  if (!full || !part) return done(AR_ERR_INVALID);
+  const size_t es = static_cast<size_t>(esize_of(dtype));
+  if (count > (SIZE_MAX / 2) / es) return done(AR_ERR_INVALID);
+  const size_t bytes = count * es;
+  const size_t q = count / nranks, rr = count % nranks;
+  Range ranges[2 * AR_MAX_RANKS];
+  int m = 0;
+  bool vec = true;
+  for (int r = 0; r < nranks; ++r) {
+    const size_t lo = r * q + (static_cast<size_t>(r) < rr ? r : rr), len = q + (static_cast<size_t>(r) < rr ? 1 : 0);
+    const uintptr_t f = reinterpret_cast<uintptr_t>(full[r]), c = reinterpret_cast<uintptr_t>(part[r]);
+    if (!f) return done(AR_ERR_INVALID);
+    if (len > 0 && !c) return done(AR_ERR_INVALID);
+    if (f > UINTPTR_MAX - bytes || (c && c > UINTPTR_MAX - len * es)) return done(AR_ERR_INVALID);
+    ranges[m++] = Range{f, f + bytes};
+    if (len > 0 && c != f + lo * es) ranges[m++] = Range{c, c + len * es};
+    if ((f | c) & 15u) vec = false;
+  }
+  if (any_overlap(ranges, m)) return done(AR_ERR_ALIAS);
+  ar::RankPtrs p;
+  std::memset(&p, 0, sizeof(p));
+  for (int r = 0; r < nranks; ++r) {
+    p.in[r] = is_rs ? full[r] : part[r];
+    p.out[r] = is_rs ? writable_part[r] : writable_full[r];
+  }
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  hipError_t e = is_rs ? ar::launch_reduce_scatter(p, nranks, static_cast<int64_t>(count), dtype, op, vec, s)
+                       : ar::launch_all_gather(p, nranks, static_cast<int64_t>(count), static_cast<int>(es), vec, s);
+  return done(e == hipSuccess ? AR_OK : AR_ERR_HIP);
+}
+
 }  // namespace
 
 extern "C" {
+
+int ar_reduce_scatter(const void* const* in_bufs, void* const* out_bufs, int nranks, size_t count, int dtype, int op,
+                      void* stream) {
+  return rsag_impl("ar_reduce_scatter", in_bufs, const_cast<const void* const*>(out_bufs), nranks, count, dtype, op,
+                   true, nullptr, out_bufs, stream);
+}
+
+int ar_all_gather(const void* const* in_bufs, void* const* out_bufs, int nranks, size_t count, int dtype,
+                  void* stream) {
+  return rsag_impl("ar_all_gather", const_cast<const void* const*>(out_bufs), in_bufs, nranks, count, dtype, AR_SUM,
+                   false, out_bufs, nullptr, stream);
+}
 
 int ar_version(void) { return AR_VERSION; }
 

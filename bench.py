@@ -183,9 +183,11 @@ def stepwise_rhd_bytes(n, count, es, acc):
     return total
 
 
-def row_entry(name, ms, alg_bytes, S, n, extra=None):
+def row_entry(name, ms, alg_bytes, S, n, extra=None, factor=None):
+    """factor: busbw / algbw; 2(N-1)/N for an all-reduce (default), (N-1)/N for reduce-scatter and all-gather."""
     t = float(np.mean(ms)) * 1e-3
-    e = {"us": stats_us(ms), "algbw_GBps": S / t / GB, "busbw_GBps": S / t / GB * bus_factor(n),
+    f = bus_factor(n) if factor is None else factor
+    e = {"us": stats_us(ms), "algbw_GBps": S / t / GB, "busbw_GBps": S / t / GB * f,
          "hbm_GBps": alg_bytes / t / GB, "frac_of_peak": alg_bytes / t / GB / PEAK_HBM_GBPS,
          "alg_bytes": alg_bytes}
     if extra:
@@ -221,6 +223,20 @@ def other_rows(torch, ar, inputs, ins, outs, dev, reps, host):
         rows[name] = row_entry(name, timer.run(fn, reps), ring_bytes(N_RANKS, COUNT, 2), S, N_RANKS)
         rows[name]["cpu_oracle"] = cpu_row(oracle_time(ofn, host, _o.BF16, _o.AVG), S, N_RANKS,
                                            "the full headline workload, one call")
+    # the two halves on their own: reduce-scatter (N reads + 1 write per element) and all-gather (1 read + N writes)
+    lo = ar.chunk_bounds(COUNT, N_RANKS)
+    parts = [torch.empty(lo[c + 1] - lo[c], dtype=torch.bfloat16, device=dev) for c in range(N_RANKS)]
+    fn = lambda: ar.ar_reduce_scatter(ins, parts, ar.AR_AVG)
+    fn()
+    rows["reduce_scatter"] = row_entry("reduce_scatter", timer.run(fn, reps), (N_RANKS + 1) * S, S, N_RANKS,
+                                       factor=(N_RANKS - 1) / N_RANKS)
+    rows["reduce_scatter"]["cpu_oracle"] = cpu_row(oracle_time(_o.reduce_scatter, host, _o.BF16, _o.AVG), S, N_RANKS,
+                                                   "the full headline workload, one call")
+    fn = lambda: ar.ar_all_gather(parts, outs)
+    fn()
+    rows["all_gather"] = row_entry("all_gather", timer.run(fn, reps), (N_RANKS + 1) * S, S, N_RANKS,
+                                   factor=(N_RANKS - 1) / N_RANKS)
+    del parts
     ws = torch.empty(ar.ar_allreduce_workspace_size(N_RANKS, COUNT, ar.AR_BF16, ar.AR_AVG, ar.AR_ALGO_RING_STEPWISE),
                      dtype=torch.uint8, device=dev)
     for name, algo, fb in (("ring_stepwise", ar.AR_ALGO_RING_STEPWISE, stepwise_ring_bytes),

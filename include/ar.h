@@ -109,6 +109,25 @@ enum ar_algo {
 int ar_allreduce(const void* const* in_bufs, void* const* out_bufs, int nranks, size_t count, int dtype, int op,
                  int algo, void* stream);
 
+/* Reduce-scatter ([V] "Reduce-Scatterは集約後の結果をrankへ分ける"; [W] primitives table; [P] "变体与相关操作"): rank c
+ * receives chunk c (the balanced split) of the element-wise reduction. Chunk c is folded starting at rank c,
+ * the ring's own order, with the same epilogue as ar_allreduce, so ar_reduce_scatter followed by
+ * ar_all_gather equals AR_ALGO_RING bit for bit.
+ *   in_bufs: host array of nranks device pointers to `count` elements each.
+ *   out_bufs: host array; out_bufs[c] points to the count/N (+1 when c < count%N) elements of chunk c; it may
+ *     be NULL when that chunk is empty. In place: out_bufs[c] == in_bufs[c] + (start of chunk c); any other
+ *     overlap -> AR_ERR_ALIAS. Errors as ar_allreduce. */
+int ar_reduce_scatter(const void* const* in_bufs, void* const* out_bufs, int nranks, size_t count, int dtype, int op,
+                      void* stream);
+
+/* All-gather ([V] "All-Gatherは分割dataを連結して全rankへ配る"; [W] primitives table): rank r contributes chunk r of
+ * the balanced split of `count`; every rank receives all chunks in rank order.
+ *   in_bufs: host array; in_bufs[r] points to chunk r's elements (NULL allowed when it is empty).
+ *   out_bufs: host array of nranks device pointers to `count` elements each. In place:
+ *     in_bufs[r] == out_bufs[r] + (start of chunk r); any other overlap -> AR_ERR_ALIAS. */
+int ar_all_gather(const void* const* in_bufs, void* const* out_bufs, int nranks, size_t count, int dtype,
+                  void* stream);
+
 /* Bytes of device workspace ar_allreduce_ws needs for this call (0 when none). Host only, no HIP call. */
 int ar_allreduce_workspace_size(int nranks, size_t count, int dtype, int op, int algo, size_t* bytes);
 

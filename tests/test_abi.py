@@ -191,3 +191,23 @@ def test_allreduce_tensors_validation():
     assert call(algo=ar.AR_ALGO_RING_STEPWISE) == ar.AR_ERR_UNSUPPORTED
     assert call(algo=ar.AR_ALGO_RING_FP8) == ar.AR_ERR_UNSUPPORTED
     assert call(n=6, algo=ar.AR_ALGO_RHD) == ar.AR_ERR_UNSUPPORTED
+
+
+def test_reduce_scatter_all_gather_validation():
+    L = ar.lib()
+    base = 0x50000000
+    full = (ctypes.c_void_p * 2)(base, base + (1 << 20))
+    part = (ctypes.c_void_p * 2)(base + (2 << 20), base + (3 << 20))
+    assert L.ar_reduce_scatter(full, part, 2, 0, ar.AR_F32, ar.AR_SUM, None) == ar.AR_OK
+    assert L.ar_reduce_scatter(full, part, 0, 10, ar.AR_F32, ar.AR_SUM, None) == ar.AR_ERR_INVALID
+    assert L.ar_reduce_scatter(full, part, 2, 10, ar.AR_F32, 7, None) == ar.AR_ERR_INVALID
+    assert L.ar_all_gather(part, full, 2, 10, 9, None) == ar.AR_ERR_INVALID
+    # a chunk buffer overlapping another rank's full buffer
+    bad = (ctypes.c_void_p * 2)(base + (1 << 20) + 64, base + (3 << 20))
+    assert L.ar_reduce_scatter(full, bad, 2, 1000, ar.AR_F32, ar.AR_SUM, None) == ar.AR_ERR_ALIAS
+    assert L.ar_all_gather(bad, full, 2, 1000, ar.AR_F32, None) == ar.AR_ERR_ALIAS
+    # NULL for an empty chunk is fine at validation (count 1, N 2: chunk 1 is empty); NULL full buffer is not
+    nul = (ctypes.c_void_p * 2)(base + (2 << 20), 0)
+    nfull = (ctypes.c_void_p * 2)(base, 0)
+    assert L.ar_reduce_scatter(nfull, nul, 2, 1, ar.AR_F32, ar.AR_SUM, None) == ar.AR_ERR_INVALID
+    assert L.ar_all_gather((ctypes.c_void_p * 2)(0, 0), full, 2, 1, ar.AR_F32, None) == ar.AR_ERR_INVALID

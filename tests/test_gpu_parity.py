@@ -443,3 +443,60 @@ def test_fused_tensor_path_equals_pack_reduce_unpack(n, dt):
                             bad = np.nonzero(g != w)[0][:5]
                             raise AssertionError(f"n={n} dt={dt} cap={cap} algo={algo} op={op} rank {r} tensor {t} "
                                                  f"(numel {sizes[t]}): first differences at {bad}")
+
+
+def _chunks(x_np, lo):
+    return [x_np[lo[c]:lo[c + 1]] for c in range(len(lo) - 1)]
+
+
+@pytest.mark.parametrize("n", [1, 2, 3, 4, 5, 8])
+@pytest.mark.parametrize("count", [1, 7, 64, 4099, 65536])
+@pytest.mark.parametrize("dt", [ar.AR_F32, ar.AR_BF16, ar.AR_I32])
+def test_reduce_scatter_and_all_gather_match_oracle(n, count, dt):
+    xs = _inputs(dt, n, count, 50)
+    lo = ar.chunk_bounds(count, n)
+    tdt = {ar.AR_F32: torch.float32, ar.AR_BF16: torch.bfloat16, ar.AR_I32: torch.int32}[dt]
+    for op in OPS:
+        ins = [to_dev(x, dt)[1] for x in xs]
+        outs = [torch.empty(lo[c + 1] - lo[c], dtype=tdt, device=DEV) for c in range(n)]
+        ar.ar_reduce_scatter(ins, outs, op)
+        torch.cuda.synchronize()
+        want = oracle.reduce_scatter(xs, ORACLE_DT[dt], ORACLE_OP[op])
+        for c in range(n):
+            np.testing.assert_array_equal(from_dev(outs[c], dt), np.asarray(want[c]).view(NP_BITS[dt]))
+        # all-gather of the reduced chunks reproduces the ring all-reduce bit for bit
+        full = [empty_like_dev(count, dt)[1] for _ in range(n)]
+        ar.ar_all_gather(outs, full)
+        torch.cuda.synchronize()
+        ring = expect(xs, dt, op, ar.AR_ALGO_RING)
+        assert_bitwise([from_dev(f, dt) for f in full], ring, f"RS then AG n={n} count={count} op={op}")
+    # all-gather against the oracle with arbitrary parts
+    parts = _chunks(xs[0].view(NP_BITS[dt]), lo)
+    pin = [to_dev(p.view(xs[0].dtype), dt)[1] if p.size else None for p in parts]
+    full = [empty_like_dev(count, dt)[1] for _ in range(n)]
+    ar.ar_all_gather(pin, full)
+    torch.cuda.synchronize()
+    want = oracle.allgather([p.view(xs[0].dtype) for p in parts], ORACLE_DT[dt])
+    assert_bitwise([from_dev(f, dt) for f in full], [np.asarray(w).view(NP_BITS[dt]) for w in want], "all-gather")
+
+
+def test_reduce_scatter_all_gather_page_examples_and_in_place():
+    # two-rank reduce-scatter halves and the four-rank all-gather placement (tests/golden fixtures)
+    ins = [torch.tensor(v, dtype=torch.int32, device=DEV) for v in ([1, 2, 3, 4], [10, 20, 30, 40])]
+    outs = [torch.empty(2, dtype=torch.int32, device=DEV) for _ in range(2)]
+    ar.ar_reduce_scatter(ins, outs)
+    assert outs[0].tolist() == [11, 22] and outs[1].tolist() == [33, 44]
+    parts = [torch.tensor([v], dtype=torch.int32, device=DEV) for v in (65, 66, 67, 68)]
+    full = [torch.zeros(4, dtype=torch.int32, device=DEV) for _ in range(4)]
+    ar.ar_all_gather(parts, full)
+    assert all(f.tolist() == [65, 66, 67, 68] for f in full)
+    # in place: each rank's chunk lives at its own position in its full buffer
+    n, count = 8, 80_000
+    xs = _inputs(ar.AR_F32, n, count, 51)
+    lo = ar.chunk_bounds(count, n)
+    bufs = [to_dev(x, ar.AR_F32)[1] for x in xs]
+    ar.ar_reduce_scatter(bufs, [bufs[c][lo[c]:lo[c + 1]] for c in range(n)], ar.AR_SUM)
+    ar.ar_all_gather([bufs[c][lo[c]:lo[c + 1]] for c in range(n)], bufs)
+    torch.cuda.synchronize()
+    assert_bitwise([from_dev(b, ar.AR_F32) for b in bufs], expect(xs, ar.AR_F32, ar.AR_SUM, ar.AR_ALGO_RING),
+                   "in-place RS + AG")
