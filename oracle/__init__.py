@@ -44,7 +44,7 @@ def lib():
         vp, i64, i32 = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int
         pp = ctypes.POINTER(ctypes.c_void_p)
         for name in ("oracle_ring_allreduce", "oracle_fused_allreduce", "oracle_rhd_allreduce",
-                     "oracle_reduce_scatter", "oracle_fp8_ring_allreduce"):
+                     "oracle_tree_allreduce", "oracle_reduce_scatter", "oracle_fp8_ring_allreduce"):
             getattr(L, name).argtypes = [pp, pp, i32, i64, i32, i32]
             getattr(L, name).restype = i32
         L.oracle_ring_rs_state.argtypes = [pp, pp, i32, i64, i32, i32]
@@ -109,6 +109,11 @@ def fused_allreduce(xs, dtype=F32, op=SUM):
 def rhd_allreduce(xs, dtype=F32, op=SUM):
     """Recursive halving then recursive doubling, executed literally (N a power of two)."""
     return _collective("oracle_rhd_allreduce", xs, dtype, op)
+
+
+def tree_allreduce(xs, dtype=F32, op=SUM):
+    """Binomial-tree reduce to rank 0 (rank i takes rank i + 2^j at step j), then binomial broadcast."""
+    return _collective("oracle_tree_allreduce", xs, dtype, op)
 
 
 def fp8_ring_allreduce(xs, dtype=BF16, op=SUM):

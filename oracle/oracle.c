@@ -477,6 +477,41 @@ int oracle_rhd_allreduce(const void* const* ins, void* const* outs, int n, int64
     return OR_OK;
 }
 
+/* Binomial-tree all-reduce, literally ([P] "算法与实现": tree-based all-reduce merges data level by level over
+ * a binomial or k-ary tree; [G] algorithm table, Tree-AllReduce; [W] "其他 AllReduce 算法"). Reduce to rank 0:
+ * at step j every rank i with i % 2^(j+1) == 0 receives the partial of rank i + 2^j (when that rank exists)
+ * and combines it into its own, the receiver's partial on the left. Rank 0 applies the epilogue, then a
+ * binomial broadcast copies the result back down the same tree. */
+int oracle_tree_allreduce(const void* const* ins, void* const* outs, int n, int64_t count, int dt, int op) {
+    if (check_common(n, count, dt, op)) return OR_BAD;
+    if (count == 0) return OR_OK;
+    int isint = dt == OT_I32, es = esize_of(dt);
+    uint32_t** w = alloc_work(n, count);
+    if (!w) return OR_NOMEM;
+    widen_all(w, ins, n, count, dt);
+    int top = 0;
+    for (int j = 0; (1 << j) < n; ++j) {
+        for (int i = 0; i < n; i += 2 << j) {
+            int src = i + (1 << j);
+            if (src >= n) continue;
+            uint32_t* dst = w[i];
+            const uint32_t* m = w[src];
+#pragma omp parallel for schedule(static)
+            for (int64_t e = 0; e < count; ++e) dst[e] = combine(dst[e], m[e], isint, op);
+        }
+        top = j + 1;
+    }
+    for (int64_t e = 0; e < count; ++e) narrow_store(outs[0], dt, e, finalize(w[0][e], isint, op, n));
+    /* broadcast back down: step j from the top, rank i (i % 2^(j+1) == 0) sends to i + 2^j */
+    for (int j = top - 1; j >= 0; --j)
+        for (int i = 0; i < n; i += 2 << j) {
+            int d = i + (1 << j);
+            if (d < n) memcpy(outs[d], outs[i], (size_t)count * es);
+        }
+    free_work(w, n);
+    return OR_OK;
+}
+
 /* ------------------------------------------------------------------------------------------------ */
 /* FP8 block codec and the compressed ring.                                                          */
 /* ------------------------------------------------------------------------------------------------ */

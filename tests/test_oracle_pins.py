@@ -552,3 +552,53 @@ def test_bucketed_allreduce_equals_per_tensor_exact():
         red = oracle.ring_allreduce(flat, oracle.F32, oracle.AVG)
         for t in np.where(b == k)[0]:
             np.testing.assert_array_equal(outs[0][t], red[0][off[t]:off[t] + sizes[t]])
+
+
+# ---------------------------------------------------------------- binomial tree
+
+
+def _binomial_closed(vals):
+    """T(lo, n) = T(lo, h) (+) T(lo + h, n - h), h the largest power of two below n (written independently of the
+    oracle's message passing: the shape a binomial reduce to rank 0 produces)."""
+    def t(lo, n):
+        if n == 1:
+            return np.float32(vals[lo])
+        h = 1
+        while h * 2 < n:
+            h *= 2
+        return np.float32(t(lo, h) + t(lo + h, n - h))
+    return t(0, len(vals))
+
+
+@pytest.mark.parametrize("n", [1, 2, 3, 4, 5, 6, 7, 8, 13, 16])
+def test_tree_equals_binomial_closed_form(n):
+    count = 301
+    xs = inputs.rank_inputs("uniform_f32", n, count, cfg=70)
+    xs = [x * np.float32(2.0 ** (3 * (r % 6))) for r, x in enumerate(xs)]
+    got = oracle.tree_allreduce(xs, oracle.F32, oracle.SUM)
+    for o in got[1:]:
+        np.testing.assert_array_equal(o.view(np.uint32), got[0].view(np.uint32))
+    for e in range(count):
+        assert got[0][e] == _binomial_closed([xs[r][e] for r in range(n)])
+    if n == 8:  # written out: ((x0+x1)+(x2+x3))+((x4+x5)+(x6+x7))
+        f = np.float32
+        v = [f(xs[r][7]) for r in range(8)]
+        assert got[0][7] == f(f(f(v[0] + v[1]) + f(v[2] + v[3])) + f(f(v[4] + v[5]) + f(v[6] + v[7])))
+    if n == 5:  # ((x0+x1)+(x2+x3))+x4
+        f = np.float32
+        v = [f(xs[r][3]) for r in range(5)]
+        assert got[0][3] == f(f(f(v[0] + v[1]) + f(v[2] + v[3])) + v[4])
+
+
+def test_tree_worked_example_and_integer_ops():
+    fx = _read_fixture("worked_example.txt")
+    for dt, npd in ((oracle.I32, np.int32), (oracle.F32, np.float32)):
+        xs = [np.array([int(v) for v in fx[f"rank {r}"]], dtype=npd) for r in range(4)]
+        for o in oracle.tree_allreduce(xs, dt, oracle.SUM):
+            np.testing.assert_array_equal(o, np.array([int(v) for v in fx["result"]], dtype=npd))
+    xs = inputs.rank_inputs("int32", 7, 33, cfg=71)
+    ring = oracle.ring_allreduce(xs, oracle.I32, oracle.SUM)[0]
+    for op in (oracle.SUM, oracle.AVG, oracle.MIN, oracle.MAX):
+        np.testing.assert_array_equal(oracle.tree_allreduce(xs, oracle.I32, op)[0],
+                                      oracle.ring_allreduce(xs, oracle.I32, op)[0])
+    assert ring.dtype == np.int32
