@@ -6,8 +6,8 @@ the library's HIP kernels. There is no CPU fallback: if ``libar.so`` is missing 
 call raises.
 
 Entry points (same names as ``include/ar.h``): ar_allreduce, ar_allreduce_ws, ar_allreduce_workspace_size,
-ar_allreduce_buckets, ar_allreduce_tensors, ar_reduce_scatter, ar_all_gather, ar_bucket_plan, ar_bucket_pack, ar_bucket_unpack, ar_fp8_quant, ar_fp8_dequant, ar_status_string,
-ar_last_call, ar_version. Helpers: make_copy_descs, BucketedAllReduce.
+ar_allreduce_buckets, ar_allreduce_tensors, ar_reduce_scatter, ar_all_gather, ar_bucket_plan, ar_bucket_pack,
+ar_bucket_unpack, ar_fp8_quant, ar_fp8_dequant, ar_auto_algo, ar_status_string, ar_last_call, ar_version. Helpers: make_copy_descs, BucketedAllReduce.
 """
 from __future__ import annotations
 
@@ -20,7 +20,8 @@ __all__ = [
     "AR_OK", "AR_ERR_INVALID", "AR_ERR_UNSUPPORTED", "AR_ERR_ALIAS", "AR_ERR_WORKSPACE", "AR_ERR_HIP",
     "AR_F32", "AR_BF16", "AR_F16", "AR_I32", "AR_SUM", "AR_AVG", "AR_MIN", "AR_MAX",
     "AR_ALGO_RING", "AR_ALGO_FUSED", "AR_ALGO_RHD", "AR_ALGO_RING_STEPWISE", "AR_ALGO_RHD_STEPWISE",
-    "AR_ALGO_RING_FP8", "AR_MAX_RANKS", "AR_FP8_BLOCK", "ArError", "lib", "lib_path",
+    "AR_ALGO_RING_FP8", "AR_ALGO_TREE", "AR_ALGO_TREE_STEPWISE", "AR_ALGO_AUTO", "AR_AUTO_STEP_NS",
+    "AR_AUTO_LINK_GBPS", "AR_MAX_RANKS", "AR_FP8_BLOCK", "ArError", "lib", "lib_path", "ar_auto_algo",
     "ar_allreduce", "ar_allreduce_ws", "ar_allreduce_workspace_size", "ar_allreduce_buckets",
     "ar_allreduce_tensors", "ar_reduce_scatter", "ar_all_gather", "chunk_bounds", "ar_bucket_plan",
     "ar_bucket_pack",
@@ -32,6 +33,8 @@ AR_OK, AR_ERR_INVALID, AR_ERR_UNSUPPORTED, AR_ERR_ALIAS, AR_ERR_WORKSPACE, AR_ER
 AR_F32, AR_BF16, AR_F16, AR_I32 = 0, 1, 2, 3
 AR_SUM, AR_AVG, AR_MIN, AR_MAX = 0, 1, 2, 3
 AR_ALGO_RING, AR_ALGO_FUSED, AR_ALGO_RHD, AR_ALGO_RING_STEPWISE, AR_ALGO_RHD_STEPWISE, AR_ALGO_RING_FP8 = range(6)
+AR_ALGO_TREE, AR_ALGO_TREE_STEPWISE, AR_ALGO_AUTO = 6, 7, 8
+AR_AUTO_STEP_NS, AR_AUTO_LINK_GBPS = 1000, 153
 AR_MAX_RANKS = 64
 AR_FP8_BLOCK = 128
 
@@ -77,12 +80,14 @@ def lib():
         L.ar_bucket_unpack.argtypes = [vp, i32, i32, vp]
         L.ar_fp8_quant.argtypes = [vp, i32, sz, vp, vp, vp]
         L.ar_fp8_dequant.argtypes = [vp, vp, sz, vp, i32, vp]
+        L.ar_auto_algo.argtypes = [i32, sz, i32]
         L.ar_status_string.argtypes = [i32]
         L.ar_status_string.restype = ctypes.c_char_p
         L.ar_last_call.argtypes = [ctypes.POINTER(_CallRecord)]
         for name in ("ar_allreduce", "ar_allreduce_ws", "ar_allreduce_workspace_size", "ar_allreduce_buckets",
                      "ar_allreduce_tensors", "ar_reduce_scatter", "ar_all_gather", "ar_bucket_plan", "ar_bucket_pack",
-                     "ar_bucket_unpack", "ar_fp8_quant", "ar_fp8_dequant", "ar_last_call", "ar_version"):
+                     "ar_bucket_unpack", "ar_fp8_quant", "ar_fp8_dequant", "ar_last_call", "ar_version",
+                     "ar_auto_algo"):
             getattr(L, name).restype = i32
         _lib = L
     return _lib
@@ -250,6 +255,14 @@ def ar_fp8_dequant(codes, scales, out, stream=None):
     _check(lib().ar_fp8_dequant(ctypes.c_void_p(codes.data_ptr()), ctypes.c_void_p(scales.data_ptr()), out.numel(),
                                 ctypes.c_void_p(out.data_ptr()), dtype_code(out.dtype), _stream(stream)),
            "ar_fp8_dequant")
+
+
+def ar_auto_algo(nranks, count, dtype) -> int:
+    """The algorithm AR_ALGO_AUTO runs for this shape (AR_ALGO_TREE or AR_ALGO_RING)."""
+    a = lib().ar_auto_algo(nranks, count, dtype)
+    if a < 0:
+        raise ArError(-a, "ar_auto_algo")
+    return a
 
 
 def ar_status_string(status: int) -> str:

@@ -50,11 +50,27 @@ int finish(const char* entry, int nranks, size_t count, int dtype, int op, int a
 int esize_of(int dtype) { return (dtype == AR_BF16 || dtype == AR_F16) ? 2 : 4; }
 bool valid_dtype(int d) { return d >= AR_F32 && d <= AR_I32; }
 bool valid_op(int o) { return o >= AR_SUM && o <= AR_MAX; }
-bool valid_algo(int a) { return a >= AR_ALGO_RING && a <= AR_ALGO_RING_FP8; }
+bool valid_algo(int a) { return a >= AR_ALGO_RING && a <= AR_ALGO_AUTO; }
 bool is_pow2(int n) { return n > 0 && (n & (n - 1)) == 0; }
 
+// Cost table of the tree and the ring (time = steps * alpha + bytes per rank / bandwidth): the tree wins iff
+// bytes < N (N - 1 - L) alpha B, L = ceil(log2 N). alpha [ns] * B [GB/s] is bytes.
+int auto_algo(int nranks, size_t count, int dtype) {
+  int levels = 0;
+  while ((1 << levels) < nranks) ++levels;
+  const int64_t spare_steps = static_cast<int64_t>(nranks) - 1 - levels;
+  if (spare_steps <= 0) return AR_ALGO_RING;
+  const uint64_t threshold = static_cast<uint64_t>(nranks) * static_cast<uint64_t>(spare_steps) *
+                             static_cast<uint64_t>(AR_AUTO_STEP_NS) * static_cast<uint64_t>(AR_AUTO_LINK_GBPS);
+  const uint64_t es = static_cast<uint64_t>(esize_of(dtype));
+  // count * es < threshold, without overflow: count < ceil(threshold / es)
+  return static_cast<uint64_t>(count) < (threshold + es - 1) / es ? AR_ALGO_TREE : AR_ALGO_RING;
+}
+
 size_t workspace_bytes(int nranks, size_t count, int dtype, int algo) {
-  const bool stepwise = algo == AR_ALGO_RING_STEPWISE || algo == AR_ALGO_RHD_STEPWISE;
+  if (algo == AR_ALGO_AUTO) algo = auto_algo(nranks, count, dtype);
+  const bool stepwise =
+      algo == AR_ALGO_RING_STEPWISE || algo == AR_ALGO_RHD_STEPWISE || algo == AR_ALGO_TREE_STEPWISE;
   if (!stepwise || esize_of(dtype) == 4 || nranks < 2) return 0;
   return static_cast<size_t>(nranks) * static_cast<size_t>(ar::stepwise_ws_stride(static_cast<int64_t>(count))) * 4;
 }
@@ -76,6 +92,7 @@ int allreduce_impl(const char* entry, const void* const* in_bufs, void* const* o
   auto done = [&](int st) { return finish(entry, nranks, count, dtype, op, algo, st); };
   if (!valid_dtype(dtype) || !valid_op(op) || !valid_algo(algo)) return done(AR_ERR_INVALID);
   if (nranks < 1 || nranks > AR_MAX_RANKS) return done(AR_ERR_INVALID);
+  if (algo == AR_ALGO_AUTO) algo = auto_algo(nranks, count, dtype);  // recorded as the algorithm that ran
   if (algo == AR_ALGO_RHD || algo == AR_ALGO_RHD_STEPWISE) {
     if (!is_pow2(nranks)) return done(AR_ERR_UNSUPPORTED);
   }
@@ -122,12 +139,16 @@ int allreduce_impl(const char* entry, const void* const* in_bufs, void* const* o
     switch (algo) {
       case AR_ALGO_RING:
       case AR_ALGO_FUSED:
-      case AR_ALGO_RHD: e = ar::launch_collapsed(p, nranks, n64, dtype, op, algo, vec, s); break;
+      case AR_ALGO_RHD:
+      case AR_ALGO_TREE: e = ar::launch_collapsed(p, nranks, n64, dtype, op, algo, vec, s); break;
       case AR_ALGO_RING_STEPWISE:
         e = ar::launch_ring_stepwise(p, nranks, n64, dtype, op, static_cast<float*>(workspace), vec, s);
         break;
       case AR_ALGO_RHD_STEPWISE:
         e = ar::launch_rhd_stepwise(p, nranks, n64, dtype, op, static_cast<float*>(workspace), vec, s);
+        break;
+      case AR_ALGO_TREE_STEPWISE:
+        e = ar::launch_tree_stepwise(p, nranks, n64, dtype, op, static_cast<float*>(workspace), vec, s);
         break;
       case AR_ALGO_RING_FP8: e = ar::launch_fp8_ring(p, nranks, n64, dtype, op, vec, s); break;
       default: return done(AR_ERR_INVALID);
@@ -211,6 +232,11 @@ int ar_last_call(ar_call_record* rec) {
   return AR_OK;
 }
 
+int ar_auto_algo(int nranks, size_t count, int dtype) {
+  if (!valid_dtype(dtype) || nranks < 1 || nranks > AR_MAX_RANKS) return -AR_ERR_INVALID;
+  return auto_algo(nranks, count, dtype);
+}
+
 int ar_allreduce_workspace_size(int nranks, size_t count, int dtype, int op, int algo, size_t* bytes) {
   if (!bytes || !valid_dtype(dtype) || !valid_op(op) || !valid_algo(algo) || nranks < 1 || nranks > AR_MAX_RANKS)
     return AR_ERR_INVALID;
@@ -267,7 +293,8 @@ int ar_allreduce_buckets(const void* const* flat_in, void* const* flat_out, int 
   auto done = [&](int st) { return finish("ar_allreduce_buckets", nranks, total, dtype, op, algo, st); };
   if (!valid_dtype(dtype) || !valid_op(op) || !valid_algo(algo)) return done(AR_ERR_INVALID);
   if (nranks < 1 || nranks > AR_MAX_RANKS || nbuckets < 0) return done(AR_ERR_INVALID);
-  if (algo != AR_ALGO_RING && algo != AR_ALGO_FUSED && algo != AR_ALGO_RHD) return done(AR_ERR_UNSUPPORTED);
+  if (algo != AR_ALGO_RING && algo != AR_ALGO_FUSED && algo != AR_ALGO_RHD && algo != AR_ALGO_TREE)
+    return done(AR_ERR_UNSUPPORTED);
   if (algo == AR_ALGO_RHD && !is_pow2(nranks)) return done(AR_ERR_UNSUPPORTED);
   if (nbuckets == 0) return done(AR_OK);
   if (!bucket_count || !flat_in || !flat_out) return done(AR_ERR_INVALID);
@@ -310,7 +337,8 @@ int ar_allreduce_tensors(const ar_tensor_desc* d_descs, const void* const* d_in,
   };
   if (!valid_dtype(dtype) || !valid_op(op) || !valid_algo(algo)) return done(AR_ERR_INVALID);
   if (nranks < 1 || nranks > AR_MAX_RANKS || ntensors < 0) return done(AR_ERR_INVALID);
-  if (algo != AR_ALGO_RING && algo != AR_ALGO_FUSED && algo != AR_ALGO_RHD) return done(AR_ERR_UNSUPPORTED);
+  if (algo != AR_ALGO_RING && algo != AR_ALGO_FUSED && algo != AR_ALGO_RHD && algo != AR_ALGO_TREE)
+    return done(AR_ERR_UNSUPPORTED);
   if (algo == AR_ALGO_RHD && !is_pow2(nranks)) return done(AR_ERR_UNSUPPORTED);
   if (ntensors == 0) return done(AR_OK);
   if (!d_descs || !d_in || !d_out) return done(AR_ERR_INVALID);

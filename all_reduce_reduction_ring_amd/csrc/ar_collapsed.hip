@@ -16,7 +16,13 @@
 // 算法, Rabenseifner row): halving step j pairs ranks N >> (j+1) apart, so every element ends as the pairwise
 // tree combining ranks N/2 apart first; the pass evaluates that tree in registers.
 //
-// Layout: grid.y = chunk c (ring/fused) or 1 (tree); grid.x strides over the chunk's 16-byte slots. A chunk
+// Binomial tree (wikiprompt "All-reduce", section 算法与实现: tree-based all-reduce over a binomial tree;
+// glossary algorithm table, Tree-AllReduce): reduce step j has rank i (i % 2^(j+1) == 0) take rank i + 2^j's
+// partial, so every element ends as T(0, N) with T(lo, n) = T(lo, h) (+) T(lo + h, n - h), h the largest
+// power of two below n. The blocks of N's binary expansion are perfect trees over consecutive ranks, largest
+// first, folded right to left; the pass evaluates that in registers for any N.
+//
+// Layout: grid.y = chunk c (ring/fused) or 1 (trees); grid.x strides over the chunk's 16-byte slots. A chunk
 // whose start or end is not slot-aligned has its few edge elements done element-wise by block x = 0.
 #include "ar_device.h"
 #include "ar_internal.h"
@@ -34,6 +40,9 @@ template <int NR> constexpr int slots_per_thread() { return (NR > 0 && NR < 8) ?
 template <int NR> constexpr int blocks_per_cu() {
   return NR == 8 ? 1 : NR == 2 ? 2 : (NR == 4 || NR == 16) ? 4 : 8;
 }
+
+// Fold shapes: rank order (ring and fused, from rank `start`), the halving tree, the binomial tree.
+enum Shape { kLinear = 0, kHalving = 1, kBinomial = 2 };
 
 struct CollapsedArgs {
   RankPtrs p;
@@ -127,6 +136,24 @@ __device__ __forceinline__ u32x4 tree_slot(const CollapsedArgs& a, int64_t off) 
   return S::pack(acc);
 }
 
+// Binomial fold of one slot / one element (the fold itself lives with the other device helpers).
+template <int DT, int OP, int NR>
+__device__ __forceinline__ u32x4 binomial_slot(const CollapsedArgs& a, int64_t off) {
+  using S = Slot<DT>;
+  const int n = NR > 0 ? NR : a.n;
+  typename S::Acc acc[S::V];
+  binomial_fold<DT, OP, NR>(a.p.in, n, off, acc);
+#pragma unroll
+  for (int e = 0; e < S::V; ++e) acc[e] = finalize<OP>(acc[e], n);
+  return S::pack(acc);
+}
+
+template <int DT, int OP, int NR>
+__device__ __forceinline__ uint32_t binomial_elem(const CollapsedArgs& a, int64_t e) {
+  const int n = NR > 0 ? NR : a.n;
+  return narrow<DT>(finalize<OP>(binomial_fold_elem<DT, OP, NR>(a.p.in, n, e), n));
+}
+
 // Element-wise versions for slot edges and unaligned buffers.
 template <int DT, int OP>
 __device__ __forceinline__ uint32_t ring_elem(const CollapsedArgs& a, int start, int64_t e) {
@@ -168,15 +195,25 @@ __device__ __forceinline__ uint32_t tree_elem(const CollapsedArgs& a, int64_t e)
   return narrow<DT>(finalize<OP>(stack[0], n));
 }
 
-template <int DT, int OP, int NR, bool TREE>
+template <int DT, int OP, int NR, int SHAPE>
 __device__ __forceinline__ void edge_elem(const CollapsedArgs& a, int start, int64_t e) {
-  uint32_t b = TREE ? tree_elem<DT, OP>(a, e) : ring_elem<DT, OP>(a, start, e);
+  uint32_t b;
+  if constexpr (SHAPE == kHalving) b = tree_elem<DT, OP>(a, e);
+  else if constexpr (SHAPE == kBinomial) b = binomial_elem<DT, OP, NR>(a, e);
+  else b = ring_elem<DT, OP>(a, start, e);
   const int n = NR > 0 ? NR : a.n;
   for (int r = 0; r < n; ++r) store_elem<DT>(a.p.out[r], e, b);
 }
 
+template <int DT, int OP, int NR, int SHAPE>
+__device__ __forceinline__ u32x4 fold_slot(const CollapsedArgs& a, int start, int64_t off) {
+  if constexpr (SHAPE == kHalving) return tree_slot<DT, OP, NR>(a, off);
+  else if constexpr (SHAPE == kBinomial) return binomial_slot<DT, OP, NR>(a, off);
+  else return ring_slot<DT, OP, NR>(a, start, off);
+}
+
 // ------------------------------------------------------------------------------------------ kernel
-template <int DT, int OP, int NR, int U, bool TREE>
+template <int DT, int OP, int NR, int U, int SHAPE>
 __global__ __launch_bounds__(kThreads) void collapsed_kernel(CollapsedArgs a) {
   constexpr int V = Traits<DT>::kVec;
   const int c = blockIdx.y;
@@ -187,26 +224,22 @@ __global__ __launch_bounds__(kThreads) void collapsed_kernel(CollapsedArgs a) {
 
   if (!a.vec) {
     for (int64_t e = lo + static_cast<int64_t>(blockIdx.x) * kThreads + threadIdx.x; e < hi; e += stride)
-      edge_elem<DT, OP, NR, TREE>(a, start, e);
+      edge_elem<DT, OP, NR, SHAPE>(a, start, e);
     return;
   }
 
   const int64_t vlo = (lo + V - 1) / V, vhi = hi / V;
   int64_t v = vlo + static_cast<int64_t>(blockIdx.x) * kThreads + threadIdx.x;
-  auto slot = [&](int64_t vv) -> u32x4 {
-    if constexpr (TREE) return tree_slot<DT, OP, NR>(a, vv * 16);
-    else return ring_slot<DT, OP, NR>(a, start, vv * 16);
-  };
   for (; v + (U - 1) * stride < vhi; v += U * stride) {
     u32x4 w[U];
 #pragma unroll
-    for (int u = 0; u < U; ++u) w[u] = slot(v + u * stride);
+    for (int u = 0; u < U; ++u) w[u] = fold_slot<DT, OP, NR, SHAPE>(a, start, (v + u * stride) * 16);
 #pragma unroll
     for (int u = 0; u < U; ++u)
       for (int r = 0; r < n; ++r) st16(static_cast<char*>(a.p.out[r]) + (v + u * stride) * 16, w[u]);
   }
   for (; v < vhi; v += stride) {
-    u32x4 w = slot(v);
+    u32x4 w = fold_slot<DT, OP, NR, SHAPE>(a, start, v * 16);
     for (int r = 0; r < n; ++r) st16(static_cast<char*>(a.p.out[r]) + v * 16, w);
   }
 
@@ -216,13 +249,13 @@ __global__ __launch_bounds__(kThreads) void collapsed_kernel(CollapsedArgs a) {
       h1 = hi;
       t0 = hi;
     }
-    for (int64_t e = lo + threadIdx.x; e < h1; e += kThreads) edge_elem<DT, OP, NR, TREE>(a, start, e);
-    for (int64_t e = t0 + threadIdx.x; e < hi; e += kThreads) edge_elem<DT, OP, NR, TREE>(a, start, e);
+    for (int64_t e = lo + threadIdx.x; e < h1; e += kThreads) edge_elem<DT, OP, NR, SHAPE>(a, start, e);
+    for (int64_t e = t0 + threadIdx.x; e < hi; e += kThreads) edge_elem<DT, OP, NR, SHAPE>(a, start, e);
   }
 }
 
 // ------------------------------------------------------------------------------------------ launch
-template <int DT, int OP, int NR, int U, bool TREE>
+template <int DT, int OP, int NR, int U, int SHAPE>
 hipError_t launch_one(CollapsedArgs& a, int nchunks, hipStream_t s) {
   constexpr int V = Traits<DT>::kVec;
   constexpr int kBlocksPerCU = blocks_per_cu<NR>();
@@ -234,7 +267,7 @@ hipError_t launch_one(CollapsedArgs& a, int nchunks, hipStream_t s) {
   int64_t bx = want < cap ? want : cap;
   if (bx < 1) bx = 1;
   dim3 grid(static_cast<unsigned>(bx), static_cast<unsigned>(nchunks));
-  hipLaunchKernelGGL((collapsed_kernel<DT, OP, NR, U, TREE>), grid, dim3(kThreads), 0, s, a);
+  hipLaunchKernelGGL((collapsed_kernel<DT, OP, NR, U, SHAPE>), grid, dim3(kThreads), 0, s, a);
   return hipGetLastError();
 }
 
@@ -243,21 +276,30 @@ hipError_t dispatch_n(CollapsedArgs& a, int algo, hipStream_t s) {
   const int n = a.n;
   if (algo == AR_ALGO_RHD && n > 1) {
     switch (n) {
-      case 2: return launch_one<DT, OP, 2, slots_per_thread<2>(), true>(a, 1, s);
-      case 4: return launch_one<DT, OP, 4, slots_per_thread<4>(), true>(a, 1, s);
-      case 8: return launch_one<DT, OP, 8, slots_per_thread<8>(), true>(a, 1, s);
-      case 16: return launch_one<DT, OP, 16, 1, true>(a, 1, s);
-      case 32: return launch_one<DT, OP, 32, 1, true>(a, 1, s);
-      case 64: return launch_one<DT, OP, 64, 1, true>(a, 1, s);
+      case 2: return launch_one<DT, OP, 2, slots_per_thread<2>(), kHalving>(a, 1, s);
+      case 4: return launch_one<DT, OP, 4, slots_per_thread<4>(), kHalving>(a, 1, s);
+      case 8: return launch_one<DT, OP, 8, slots_per_thread<8>(), kHalving>(a, 1, s);
+      case 16: return launch_one<DT, OP, 16, 1, kHalving>(a, 1, s);
+      case 32: return launch_one<DT, OP, 32, 1, kHalving>(a, 1, s);
+      case 64: return launch_one<DT, OP, 64, 1, kHalving>(a, 1, s);
       default: return hipErrorInvalidValue;
     }
   }
+  if (algo == AR_ALGO_TREE && n > 1) {
+    switch (n) {
+      case 2: return launch_one<DT, OP, 2, slots_per_thread<2>(), kBinomial>(a, 1, s);
+      case 4: return launch_one<DT, OP, 4, slots_per_thread<4>(), kBinomial>(a, 1, s);
+      case 8: return launch_one<DT, OP, 8, slots_per_thread<8>(), kBinomial>(a, 1, s);
+      case 16: return launch_one<DT, OP, 16, 1, kBinomial>(a, 1, s);
+      default: return launch_one<DT, OP, 0, 1, kBinomial>(a, 1, s);
+    }
+  }
   switch (n) {
-    case 2: return launch_one<DT, OP, 2, slots_per_thread<2>(), false>(a, n, s);
-    case 4: return launch_one<DT, OP, 4, slots_per_thread<4>(), false>(a, n, s);
-    case 8: return launch_one<DT, OP, 8, slots_per_thread<8>(), false>(a, n, s);
-    case 16: return launch_one<DT, OP, 16, 1, false>(a, n, s);
-    default: return launch_one<DT, OP, 0, 1, false>(a, n, s);
+    case 2: return launch_one<DT, OP, 2, slots_per_thread<2>(), kLinear>(a, n, s);
+    case 4: return launch_one<DT, OP, 4, slots_per_thread<4>(), kLinear>(a, n, s);
+    case 8: return launch_one<DT, OP, 8, slots_per_thread<8>(), kLinear>(a, n, s);
+    case 16: return launch_one<DT, OP, 16, 1, kLinear>(a, n, s);
+    default: return launch_one<DT, OP, 0, 1, kLinear>(a, n, s);
   }
 }
 
@@ -288,7 +330,7 @@ struct SegmentArgs {
   int nseg;
 };
 
-template <int DT, int OP, int NR, int U, bool TREE>
+template <int DT, int OP, int NR, int U, int SHAPE>
 __global__ __launch_bounds__(kThreads) void segment_kernel(SegmentArgs a) {
   constexpr int V = Traits<DT>::kVec;
   constexpr int64_t TS = static_cast<int64_t>(kThreads) * U;
@@ -308,10 +350,7 @@ __global__ __launch_bounds__(kThreads) void segment_kernel(SegmentArgs a) {
 #pragma unroll
     for (int u = 0; u < U; ++u) {
       const int64_t vv = v + u * kThreads;
-      if (vv < vend) {
-        if constexpr (TREE) w[u] = tree_slot<DT, OP, NR>(a.f, vv * 16);
-        else w[u] = ring_slot<DT, OP, NR>(a.f, start, vv * 16);
-      }
+      if (vv < vend) w[u] = fold_slot<DT, OP, NR, SHAPE>(a.f, start, vv * 16);
     }
 #pragma unroll
     for (int u = 0; u < U; ++u) {
@@ -322,14 +361,14 @@ __global__ __launch_bounds__(kThreads) void segment_kernel(SegmentArgs a) {
   }
 }
 
-template <int DT, int OP, int NR, int U, bool TREE>
+template <int DT, int OP, int NR, int U, int SHAPE>
 hipError_t launch_segments(SegmentArgs& a, hipStream_t s) {
   constexpr int kBlocksPerCU = blocks_per_cu<NR>();
   const int64_t total = a.tile_pre[a.nseg];
   int64_t g = static_cast<int64_t>(cu_count()) * kBlocksPerCU;
   if (g > total) g = total;
   if (g < 1) g = 1;
-  hipLaunchKernelGGL((segment_kernel<DT, OP, NR, U, TREE>), dim3(static_cast<unsigned>(g)), dim3(kThreads), 0, s, a);
+  hipLaunchKernelGGL((segment_kernel<DT, OP, NR, U, SHAPE>), dim3(static_cast<unsigned>(g)), dim3(kThreads), 0, s, a);
   return hipGetLastError();
 }
 
@@ -338,21 +377,30 @@ hipError_t segments_n(SegmentArgs& a, int algo, hipStream_t s) {
   const int n = a.f.n;
   if (algo == AR_ALGO_RHD && n > 1) {
     switch (n) {
-      case 2: return launch_segments<DT, OP, 2, slots_per_thread<2>(), true>(a, s);
-      case 4: return launch_segments<DT, OP, 4, slots_per_thread<4>(), true>(a, s);
-      case 8: return launch_segments<DT, OP, 8, slots_per_thread<8>(), true>(a, s);
-      case 16: return launch_segments<DT, OP, 16, 1, true>(a, s);
-      case 32: return launch_segments<DT, OP, 32, 1, true>(a, s);
-      case 64: return launch_segments<DT, OP, 64, 1, true>(a, s);
+      case 2: return launch_segments<DT, OP, 2, slots_per_thread<2>(), kHalving>(a, s);
+      case 4: return launch_segments<DT, OP, 4, slots_per_thread<4>(), kHalving>(a, s);
+      case 8: return launch_segments<DT, OP, 8, slots_per_thread<8>(), kHalving>(a, s);
+      case 16: return launch_segments<DT, OP, 16, 1, kHalving>(a, s);
+      case 32: return launch_segments<DT, OP, 32, 1, kHalving>(a, s);
+      case 64: return launch_segments<DT, OP, 64, 1, kHalving>(a, s);
       default: return hipErrorInvalidValue;
     }
   }
+  if (algo == AR_ALGO_TREE && n > 1) {
+    switch (n) {
+      case 2: return launch_segments<DT, OP, 2, slots_per_thread<2>(), kBinomial>(a, s);
+      case 4: return launch_segments<DT, OP, 4, slots_per_thread<4>(), kBinomial>(a, s);
+      case 8: return launch_segments<DT, OP, 8, slots_per_thread<8>(), kBinomial>(a, s);
+      case 16: return launch_segments<DT, OP, 16, 1, kBinomial>(a, s);
+      default: return launch_segments<DT, OP, 0, 1, kBinomial>(a, s);
+    }
+  }
   switch (n) {
-    case 2: return launch_segments<DT, OP, 2, slots_per_thread<2>(), false>(a, s);
-    case 4: return launch_segments<DT, OP, 4, slots_per_thread<4>(), false>(a, s);
-    case 8: return launch_segments<DT, OP, 8, slots_per_thread<8>(), false>(a, s);
-    case 16: return launch_segments<DT, OP, 16, 1, false>(a, s);
-    default: return launch_segments<DT, OP, 0, 1, false>(a, s);
+    case 2: return launch_segments<DT, OP, 2, slots_per_thread<2>(), kLinear>(a, s);
+    case 4: return launch_segments<DT, OP, 4, slots_per_thread<4>(), kLinear>(a, s);
+    case 8: return launch_segments<DT, OP, 8, slots_per_thread<8>(), kLinear>(a, s);
+    case 16: return launch_segments<DT, OP, 16, 1, kLinear>(a, s);
+    default: return launch_segments<DT, OP, 0, 1, kLinear>(a, s);
   }
 }
 
@@ -374,8 +422,8 @@ static_assert(sizeof(SegmentArgs) <= 4096, "kernel arguments must fit in 4 KiB")
 hipError_t launch_segments(const RankPtrs& p, int n, const int64_t* counts, int nseg, int dtype, int op, int algo,
                            hipStream_t s) {
   const int V = (dtype == AR_BF16 || dtype == AR_F16) ? 8 : 4;
-  const int tree = algo == AR_ALGO_RHD && n > 1;
-  const int U = (n > 0 && n < 8 && (tree ? true : (n == 2 || n == 4))) ? 8 / n : 1;
+  // must match the U each template above is instantiated with: 8/N for N = 2 and 4 (every shape), else 1
+  const int U = (n == 2 || n == 4) ? 8 / n : 1;
   const int64_t TS = static_cast<int64_t>(kThreads) * U;
   int64_t start = 0;
   int done = 0;
@@ -422,7 +470,7 @@ hipError_t launch_collapsed(const RankPtrs& p, int n, int64_t count, int dtype, 
   a.count = count;
   a.n = n;
   a.vec = vec ? 1 : 0;
-  const bool tree = algo == AR_ALGO_RHD && n > 1;
+  const bool tree = (algo == AR_ALGO_RHD || algo == AR_ALGO_TREE) && n > 1;
   const int nchunks = tree ? 1 : n;
   a.q = count / nchunks;
   a.r = count % nchunks;

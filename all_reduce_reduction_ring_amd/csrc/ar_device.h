@@ -156,4 +156,144 @@ __device__ __forceinline__ void st16(void* p, const u32x4& v) {
 // Balanced chunk split: chunk c = [c*q + min(c, r), ...) with q = count / N, r = count % N.
 __device__ __forceinline__ int64_t chunk_lo(int64_t q, int64_t r, int64_t c) { return c * q + (c < r ? c : r); }
 
+// ------------------------------------------------------------------------------------------ binomial tree
+// The binomial reduce (rank i takes rank i + 2^j at step j when i % 2^(j+1) == 0) leaves T(0, n) with
+// T(lo, m) = T(lo, h) (+) T(lo + h, m - h), h the largest power of two below m; for m a power of two that is a
+// perfect tree over consecutive ranks. `ip` holds the rank pointers; `off` is a byte offset (slots) or `e` an
+// element index. No epilogue.
+//   NR > 0 (rank count known at compile time): the recursion above, fully unrolled.
+//   NR == 0: a binary counter over the ranks in order. pend[h] holds a finished perfect tree of 2^h ranks;
+//   adding rank j merges it with pend[0], pend[1], ... (earlier ranks on the left) for every trailing one bit
+//   of j. After all n ranks, pend[h] exists exactly for the set bits of n (the largest tree over the lowest
+//   ranks), and those trees are folded from the smallest up, each new one on the left. Every index into pend
+//   is a compile-time constant, so it stays in registers.
+template <int M> constexpr int below_pow2() { int h = 1; while (h * 2 < M) h *= 2; return h; }
+constexpr int kMaxLevels = 7;  // 2^6 = 64 ranks
+
+template <int DT, int OP, int S>
+__device__ __forceinline__ void perfect_fold(const void* const* ip, int base, int64_t off,
+                                             typename Traits<DT>::Acc (&acc)[Traits<DT>::kVec]) {
+  if constexpr (S == 1) {
+    Slot<DT>::unpack(ld16(static_cast<const char*>(ip[base]) + off), acc);
+  } else {
+    typename Traits<DT>::Acc b[Traits<DT>::kVec];
+    perfect_fold<DT, OP, S / 2>(ip, base, off, acc);
+    perfect_fold<DT, OP, S / 2>(ip, base + S / 2, off, b);
+#pragma unroll
+    for (int e = 0; e < Traits<DT>::kVec; ++e) acc[e] = combine<OP>(acc[e], b[e]);
+  }
+}
+
+template <int DT, int OP, int M>
+__device__ __forceinline__ void binomial_fold_ct(const void* const* ip, int base, int64_t off,
+                                                 typename Traits<DT>::Acc (&acc)[Traits<DT>::kVec]) {
+  if constexpr ((M & (M - 1)) == 0) {
+    perfect_fold<DT, OP, M>(ip, base, off, acc);
+  } else {
+    constexpr int H = below_pow2<M>();
+    typename Traits<DT>::Acc b[Traits<DT>::kVec];
+    perfect_fold<DT, OP, H>(ip, base, off, acc);
+    binomial_fold_ct<DT, OP, M - H>(ip, base + H, off, b);
+#pragma unroll
+    for (int e = 0; e < Traits<DT>::kVec; ++e) acc[e] = combine<OP>(acc[e], b[e]);
+  }
+}
+
+template <int DT, int OP, int NR>
+__device__ __forceinline__ void binomial_fold(const void* const* ip, int n, int64_t off,
+                                              typename Traits<DT>::Acc (&acc)[Traits<DT>::kVec]) {
+  using Acc = typename Traits<DT>::Acc;
+  constexpr int V = Traits<DT>::kVec;
+  if constexpr (NR > 0) {
+    binomial_fold_ct<DT, OP, NR>(ip, 0, off, acc);
+  } else {
+    Acc pend[kMaxLevels][V];
+    for (int j = 0; j < n; ++j) {
+      Acc v[V];
+      Slot<DT>::unpack(ld16(static_cast<const char*>(ip[j]) + off), v);
+      bool placed = false;
+#pragma unroll
+      for (int h = 0; h < kMaxLevels; ++h) {
+        if (!placed) {
+          if ((j >> h) & 1) {
+#pragma unroll
+            for (int e = 0; e < V; ++e) v[e] = combine<OP>(pend[h][e], v[e]);
+          } else {
+#pragma unroll
+            for (int e = 0; e < V; ++e) pend[h][e] = v[e];
+            placed = true;
+          }
+        }
+      }
+    }
+    bool have = false;
+#pragma unroll
+    for (int h = 0; h < kMaxLevels; ++h) {
+      if ((n >> h) & 1) {
+#pragma unroll
+        for (int e = 0; e < V; ++e) acc[e] = have ? combine<OP>(pend[h][e], acc[e]) : pend[h][e];
+        have = true;
+      }
+    }
+  }
+}
+
+template <int DT, int OP, int S>
+__device__ __forceinline__ typename Traits<DT>::Acc perfect_fold_elem(const void* const* ip, int base, int64_t e) {
+  if constexpr (S == 1) {
+    return widen<DT>(load_elem<DT>(ip[base], e));
+  } else {
+    const auto lo = perfect_fold_elem<DT, OP, S / 2>(ip, base, e);
+    const auto hi = perfect_fold_elem<DT, OP, S / 2>(ip, base + S / 2, e);
+    return combine<OP>(lo, hi);
+  }
+}
+
+template <int DT, int OP, int M>
+__device__ __forceinline__ typename Traits<DT>::Acc binomial_fold_elem_ct(const void* const* ip, int base, int64_t e) {
+  if constexpr ((M & (M - 1)) == 0) {
+    return perfect_fold_elem<DT, OP, M>(ip, base, e);
+  } else {
+    constexpr int H = below_pow2<M>();
+    const auto lo = perfect_fold_elem<DT, OP, H>(ip, base, e);
+    const auto hi = binomial_fold_elem_ct<DT, OP, M - H>(ip, base + H, e);
+    return combine<OP>(lo, hi);
+  }
+}
+
+template <int DT, int OP, int NR>
+__device__ __forceinline__ typename Traits<DT>::Acc binomial_fold_elem(const void* const* ip, int n, int64_t e) {
+  using Acc = typename Traits<DT>::Acc;
+  if constexpr (NR > 0) {
+    return binomial_fold_elem_ct<DT, OP, NR>(ip, 0, e);
+  } else {
+    Acc pend[kMaxLevels];
+    for (int j = 0; j < n; ++j) {
+      Acc v = widen<DT>(load_elem<DT>(ip[j], e));
+      bool placed = false;
+#pragma unroll
+      for (int h = 0; h < kMaxLevels; ++h) {
+        if (!placed) {
+          if ((j >> h) & 1) {
+            v = combine<OP>(pend[h], v);
+          } else {
+            pend[h] = v;
+            placed = true;
+          }
+        }
+      }
+    }
+    Acc acc = Acc(0);
+    bool have = false;
+#pragma unroll
+    for (int h = 0; h < kMaxLevels; ++h) {
+      if ((n >> h) & 1) {
+        acc = have ? combine<OP>(pend[h], acc) : pend[h];
+        have = true;
+      }
+    }
+    return acc;
+  }
+}
+
 }  // namespace ar

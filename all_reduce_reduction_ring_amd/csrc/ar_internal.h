@@ -40,6 +40,8 @@ hipError_t launch_ring_stepwise(const RankPtrs& p, int n, int64_t count, int dty
                                 hipStream_t s);
 hipError_t launch_rhd_stepwise(const RankPtrs& p, int n, int64_t count, int dtype, int op, float* ws, bool vec,
                                hipStream_t s);
+hipError_t launch_tree_stepwise(const RankPtrs& p, int n, int64_t count, int dtype, int op, float* ws, bool vec,
+                               hipStream_t s);
 
 // Batched copy with zero padding (bucket pack/unpack).
 hipError_t launch_batched_copy(const ar_copy_desc* d_descs, int ndescs, int esize, hipStream_t s);

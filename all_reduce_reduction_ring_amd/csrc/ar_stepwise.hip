@@ -1,4 +1,4 @@
-// ar_stepwise.hip -- the ring and halving-doubling schedules executed one round per kernel launch, with
+// ar_stepwise.hip -- the ring, halving-doubling and binomial-tree schedules executed one round per kernel launch, with
 // every partial passing through HBM as it would cross a link between GPUs.
 //
 // Ring (jisaku.com glossary "AllReduce（オールリデュース）", section Ring-AllReduceの仕組み; astro-wiki
@@ -11,6 +11,11 @@
 // halving step j pairs i with p = i XOR (N >> (j+1)); both hold the same range and split it at its middle;
 // the rank whose partner bit is set keeps the upper half and combines the partner's copy of it into its
 // own. Doubling walks the steps back, each rank copying the partner's finished range. 2 log2 N launches.
+//
+// Binomial tree (wikiprompt "All-reduce", section 算法与实现; glossary algorithm table, Tree-AllReduce): reduce
+// level j has every rank i with i % 2^(j+1) == 0 and i + 2^j < N combine rank i + 2^j's value into its own
+// partial (its own on the left); the last level applies the epilogue at rank 0. Broadcast level j, from the
+// top down, copies rank i's result to rank i + 2^j. 2 ceil(log2 N) launches.
 //
 // Where partials live: for F32/I32 the output buffers themselves (the value in flight is the stored
 // value); for BF16/F16 an fp32 mirror in the caller's workspace, rank r at ws + r * ws_stride, so partial
@@ -104,10 +109,11 @@ template <int DT> struct Partial {
 };
 
 // One combine round: dst rank `d` combines `src`'s value (its input when first, else its partial) with
-// its own input (ring) or own partial (tree, after the first step), over [lo, hi).
+// its own input (ring) or own partial (trees, after the first step), over [lo, hi). The message is the left
+// operand unless own_left.
 template <int DT, int OP>
 __device__ __forceinline__ void combine_range(const StepArgs& a, int src, int d, bool first, bool own_from_input,
-                                              int64_t lo, int64_t hi) {
+                                              int64_t lo, int64_t hi, bool own_left = false) {
   using Acc = typename Traits<DT>::Acc;
   constexpr int V = Traits<DT>::kVec;
   using S = Slot<DT>;
@@ -120,7 +126,7 @@ __device__ __forceinline__ void combine_range(const StepArgs& a, int src, int d,
     if (own_from_input) S::unpack(ld16(static_cast<const char*>(a.p.in[d]) + v * 16), o);
     else P::load(a, d, v, o);
 #pragma unroll
-    for (int k = 0; k < V; ++k) m[k] = combine<OP>(m[k], o[k]);
+    for (int k = 0; k < V; ++k) m[k] = own_left ? combine<OP>(o[k], m[k]) : combine<OP>(m[k], o[k]);
     if (a.last) {
 #pragma unroll
       for (int k = 0; k < V; ++k) m[k] = finalize<OP>(m[k], n);
@@ -132,7 +138,7 @@ __device__ __forceinline__ void combine_range(const StepArgs& a, int src, int d,
   auto elem_fn = [&](int64_t e) {
     Acc m = first ? widen<DT>(load_elem<DT>(a.p.in[src], e)) : P::load_e(a, src, e);
     Acc o = own_from_input ? widen<DT>(load_elem<DT>(a.p.in[d], e)) : P::load_e(a, d, e);
-    m = combine<OP>(m, o);
+    m = own_left ? combine<OP>(o, m) : combine<OP>(m, o);
     if (a.last) store_elem<DT>(a.p.out[d], e, narrow<DT>(finalize<OP>(m, n)));
     else P::store_e(a, d, e, m);
   };
@@ -193,6 +199,21 @@ __global__ __launch_bounds__(kThreads) void rhd_ag_round(StepArgs a) {
   copy_range<DT>(a, p, i, lo, hi);
 }
 
+// ------------------------------------------------------------------------------------------ tree rounds
+// Level j = a.step; pair blockIdx.y has receiver i = blockIdx.y * 2^(j+1) and sender i + 2^j. The sender's value
+// is its input when it never received: at level 0, or when it is the last rank (i + 2^j + 1 == N).
+template <int DT, int OP>
+__global__ __launch_bounds__(kThreads) void tree_reduce_round(StepArgs a) {
+  const int j = a.step, i = static_cast<int>(blockIdx.y) << (j + 1), src = i + (1 << j);
+  combine_range<DT, OP>(a, src, i, j == 0 || src + 1 >= a.n, j == 0, 0, a.count, true);
+}
+
+template <int DT>
+__global__ __launch_bounds__(kThreads) void tree_bcast_round(StepArgs a) {
+  const int j = a.step, i = static_cast<int>(blockIdx.y) << (j + 1);
+  copy_range<DT>(a, i, i + (1 << j), 0, a.count);
+}
+
 // ------------------------------------------------------------------------------------------ launch
 dim3 round_grid(int64_t elems, int n, int V) {
   int64_t slots = (elems + V - 1) / V;
@@ -250,18 +271,55 @@ hipError_t rhd_rounds(StepArgs& a, hipStream_t s) {
   return hipSuccess;
 }
 
-template <int DT>
-hipError_t dispatch(StepArgs& a, int op, bool rhd, hipStream_t s) {
-  switch (op) {
-    case AR_SUM: return rhd ? rhd_rounds<DT, AR_SUM>(a, s) : ring_rounds<DT, AR_SUM>(a, s);
-    case AR_AVG: return rhd ? rhd_rounds<DT, AR_AVG>(a, s) : ring_rounds<DT, AR_AVG>(a, s);
-    case AR_MIN: return rhd ? rhd_rounds<DT, AR_MIN>(a, s) : ring_rounds<DT, AR_MIN>(a, s);
-    case AR_MAX: return rhd ? rhd_rounds<DT, AR_MAX>(a, s) : ring_rounds<DT, AR_MAX>(a, s);
+template <int DT, int OP>
+hipError_t tree_rounds(StepArgs& a, hipStream_t s) {
+  constexpr int V = Traits<DT>::kVec;
+  const int n = a.n;
+  int k = 0;
+  while ((1 << k) < n) ++k;
+  for (int j = 0; j < k; ++j) {
+    const int pairs = (n - (1 << j) + (2 << j) - 1) / (2 << j);  // receivers i = 0, 2^(j+1), ... with i + 2^j < n
+    a.step = j;
+    a.last = j == k - 1;
+    hipLaunchKernelGGL((tree_reduce_round<DT, OP>), round_grid(a.count, pairs, V), dim3(kThreads), 0, s, a);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  a.last = 0;
+  for (int j = k - 1; j >= 0; --j) {
+    const int pairs = (n - (1 << j) + (2 << j) - 1) / (2 << j);
+    a.step = j;
+    hipLaunchKernelGGL((tree_bcast_round<DT>), round_grid(a.count, pairs, V), dim3(kThreads), 0, s, a);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  return hipSuccess;
+}
+
+enum Schedule { kRing = 0, kRhd = 1, kTree = 2 };
+
+template <int DT, int OP>
+hipError_t rounds(StepArgs& a, int sched, hipStream_t s) {
+  switch (sched) {
+    case kRing: return ring_rounds<DT, OP>(a, s);
+    case kRhd: return rhd_rounds<DT, OP>(a, s);
+    case kTree: return tree_rounds<DT, OP>(a, s);
     default: return hipErrorInvalidValue;
   }
 }
 
-hipError_t launch_rounds(const RankPtrs& p, int n, int64_t count, int dtype, int op, float* ws, bool vec, bool rhd,
+template <int DT>
+hipError_t dispatch(StepArgs& a, int op, int sched, hipStream_t s) {
+  switch (op) {
+    case AR_SUM: return rounds<DT, AR_SUM>(a, sched, s);
+    case AR_AVG: return rounds<DT, AR_AVG>(a, sched, s);
+    case AR_MIN: return rounds<DT, AR_MIN>(a, sched, s);
+    case AR_MAX: return rounds<DT, AR_MAX>(a, sched, s);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+hipError_t launch_rounds(const RankPtrs& p, int n, int64_t count, int dtype, int op, float* ws, bool vec, int sched,
                          hipStream_t s) {
   StepArgs a;
   a.p = p;
@@ -275,10 +333,10 @@ hipError_t launch_rounds(const RankPtrs& p, int n, int64_t count, int dtype, int
   a.last = 0;
   a.vec = vec ? 1 : 0;
   switch (dtype) {
-    case AR_F32: return dispatch<AR_F32>(a, op, rhd, s);
-    case AR_BF16: return dispatch<AR_BF16>(a, op, rhd, s);
-    case AR_F16: return dispatch<AR_F16>(a, op, rhd, s);
-    case AR_I32: return dispatch<AR_I32>(a, op, rhd, s);
+    case AR_F32: return dispatch<AR_F32>(a, op, sched, s);
+    case AR_BF16: return dispatch<AR_BF16>(a, op, sched, s);
+    case AR_F16: return dispatch<AR_F16>(a, op, sched, s);
+    case AR_I32: return dispatch<AR_I32>(a, op, sched, s);
     default: return hipErrorInvalidValue;
   }
 }
@@ -289,12 +347,17 @@ int64_t stepwise_ws_stride(int64_t count) { return (count + 63) / 64 * 64; }
 
 hipError_t launch_ring_stepwise(const RankPtrs& p, int n, int64_t count, int dtype, int op, float* ws, bool vec,
                                 hipStream_t s) {
-  return launch_rounds(p, n, count, dtype, op, ws, vec, false, s);
+  return launch_rounds(p, n, count, dtype, op, ws, vec, kRing, s);
 }
 
 hipError_t launch_rhd_stepwise(const RankPtrs& p, int n, int64_t count, int dtype, int op, float* ws, bool vec,
                                hipStream_t s) {
-  return launch_rounds(p, n, count, dtype, op, ws, vec, true, s);
+  return launch_rounds(p, n, count, dtype, op, ws, vec, kRhd, s);
+}
+
+hipError_t launch_tree_stepwise(const RankPtrs& p, int n, int64_t count, int dtype, int op, float* ws, bool vec,
+                                hipStream_t s) {
+  return launch_rounds(p, n, count, dtype, op, ws, vec, kTree, s);
 }
 
 }  // namespace ar

@@ -33,14 +33,20 @@ struct TensorArgs {
 
 template <int NR> constexpr int tensor_blocks_per_cu() { return NR == 8 ? 2 : 4; }
 
+// Fold shapes: rank order from `start` (ring, fused), the halving tree (RHD), the binomial tree.
+enum Shape { kLinear = 0, kHalving = 1, kBinomial = 2 };
+
 // Fold of one 16-byte slot at byte offset `off` over the tensor's rank pointers, starting at rank `start`.
-template <int DT, int OP, int NR, bool TREE>
+template <int DT, int OP, int NR, int SHAPE>
 __device__ __forceinline__ u32x4 fold_slot(const void* const* ip, int n, int start, int64_t off) {
   using S = Slot<DT>;
   using Acc = typename S::Acc;
   constexpr int V = S::V;
+  constexpr bool TREE = SHAPE == kHalving;
   Acc acc[V], t[V];
-  if constexpr (NR > 0) {
+  if constexpr (SHAPE == kBinomial) {
+    binomial_fold<DT, OP, NR>(ip, n, off, acc);
+  } else if constexpr (NR > 0) {
     u32x4 x[NR];
 #pragma unroll
     for (int k = 0; k < NR; ++k) {
@@ -86,11 +92,12 @@ __device__ __forceinline__ u32x4 fold_slot(const void* const* ip, int n, int sta
   return S::pack(acc);
 }
 
-// One element (tensor tails and unaligned tensors). The tree order for a runtime n uses the stack form.
-template <int DT, int OP, bool TREE>
+// One element (tensor tails and unaligned tensors). The halving tree for a runtime n uses the stack form.
+template <int DT, int OP, int SHAPE>
 __device__ __forceinline__ uint32_t fold_elem(const void* const* ip, int n, int start, int64_t e) {
   using Acc = typename Traits<DT>::Acc;
-  if (TREE) {
+  if constexpr (SHAPE == kBinomial) return narrow<DT>(finalize<OP>(binomial_fold_elem<DT, OP, 0>(ip, n, e), n));
+  if constexpr (SHAPE == kHalving) {
     int k = 0;
     while ((1 << k) < n) ++k;
     Acc stack[7];
@@ -121,7 +128,7 @@ __device__ __forceinline__ uint32_t fold_elem(const void* const* ip, int n, int 
   return narrow<DT>(finalize<OP>(acc, n));
 }
 
-template <int DT, int OP, int NR, bool TREE>
+template <int DT, int OP, int NR, int SHAPE>
 __global__ __launch_bounds__(kThreads) void tensor_kernel(TensorArgs a) {
   constexpr int V = Traits<DT>::kVec;
   constexpr int64_t TE = static_cast<int64_t>(kThreads) * V;  // elements per tile
@@ -165,14 +172,14 @@ __global__ __launch_bounds__(kThreads) void tensor_kernel(TensorArgs a) {
       void* const* op = a.out + static_cast<int64_t>(ti) * n;
       uintptr_t anyp = 0;
       for (int r = 0; r < n; ++r) anyp |= reinterpret_cast<uintptr_t>(ip[r]) | reinterpret_cast<uintptr_t>(op[r]);
-      // the tree order for a runtime rank count is evaluated per element
-      const bool vec = (anyp & 15u) == 0 && !(TREE && NR == 0);
+      // the halving tree for a runtime rank count is evaluated per element
+      const bool vec = (anyp & 15u) == 0 && !(SHAPE == kHalving && NR == 0);
       // uniform sub-ranges [s0, s1) of the tile that lie in one bucket chunk
       int64_t s0 = e0;
       while (s0 < e1) {
         int start = 0;
         int64_t s1 = e1;
-        if (!TREE && a.rot && clen > 0) {
+        if (SHAPE == kLinear && a.rot && clen > 0) {
           int64_t c = (boff + s0) / clen;
           c = c < 0 ? 0 : (c < n ? c : n - 1);
           start = static_cast<int>(c);
@@ -186,12 +193,12 @@ __global__ __launch_bounds__(kThreads) void tensor_kernel(TensorArgs a) {
         const int64_t v0 = s0 / V, v1 = vsub ? s1 / V : v0;
         const int64_t v = v0 + t;
         if (v < v1) {
-          const u32x4 w = fold_slot<DT, OP, NR, TREE>(ip, n, start, v * 16);
+          const u32x4 w = fold_slot<DT, OP, NR, SHAPE>(ip, n, start, v * 16);
           for (int r = 0; r < n; ++r) st16(static_cast<char*>(op[r]) + v * 16, w);
         }
         const int64_t tail0 = vsub ? v1 * V : s0;
         for (int64_t e = tail0 + t; e < s1; e += kThreads) {
-          const uint32_t bits = fold_elem<DT, OP, TREE>(ip, n, start, e);
+          const uint32_t bits = fold_elem<DT, OP, SHAPE>(ip, n, start, e);
           for (int r = 0; r < n; ++r) store_elem<DT>(op[r], e, bits);
         }
         s0 = s1;
@@ -202,32 +209,29 @@ __global__ __launch_bounds__(kThreads) void tensor_kernel(TensorArgs a) {
   }
 }
 
-template <int DT, int OP, int NR, bool TREE>
+template <int DT, int OP, int NR, int SHAPE>
 hipError_t launch_t(const TensorArgs& a, hipStream_t s) {
   const int g = cu_count() * tensor_blocks_per_cu<NR>();
-  hipLaunchKernelGGL((tensor_kernel<DT, OP, NR, TREE>), dim3(g), dim3(kThreads), 0, s, a);
+  hipLaunchKernelGGL((tensor_kernel<DT, OP, NR, SHAPE>), dim3(g), dim3(kThreads), 0, s, a);
   return hipGetLastError();
+}
+
+template <int DT, int OP, int SHAPE>
+hipError_t tensors_shape(const TensorArgs& a, hipStream_t s) {
+  switch (a.n) {
+    case 2: return launch_t<DT, OP, 2, SHAPE>(a, s);
+    case 4: return launch_t<DT, OP, 4, SHAPE>(a, s);
+    case 8: return launch_t<DT, OP, 8, SHAPE>(a, s);
+    case 16: return launch_t<DT, OP, 16, SHAPE>(a, s);
+    default: return launch_t<DT, OP, 0, SHAPE>(a, s);
+  }
 }
 
 template <int DT, int OP>
 hipError_t tensors_n(const TensorArgs& a, int algo, hipStream_t s) {
-  const bool tree = algo == AR_ALGO_RHD && a.n > 1;
-  if (tree) {
-    switch (a.n) {
-      case 2: return launch_t<DT, OP, 2, true>(a, s);
-      case 4: return launch_t<DT, OP, 4, true>(a, s);
-      case 8: return launch_t<DT, OP, 8, true>(a, s);
-      case 16: return launch_t<DT, OP, 16, true>(a, s);
-      default: return launch_t<DT, OP, 0, true>(a, s);
-    }
-  }
-  switch (a.n) {
-    case 2: return launch_t<DT, OP, 2, false>(a, s);
-    case 4: return launch_t<DT, OP, 4, false>(a, s);
-    case 8: return launch_t<DT, OP, 8, false>(a, s);
-    case 16: return launch_t<DT, OP, 16, false>(a, s);
-    default: return launch_t<DT, OP, 0, false>(a, s);
-  }
+  if (a.n > 1 && algo == AR_ALGO_RHD) return tensors_shape<DT, OP, kHalving>(a, s);
+  if (a.n > 1 && algo == AR_ALGO_TREE) return tensors_shape<DT, OP, kBinomial>(a, s);
+  return tensors_shape<DT, OP, kLinear>(a, s);
 }
 
 template <int DT>

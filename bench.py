@@ -183,6 +183,25 @@ def stepwise_rhd_bytes(n, count, es, acc):
     return total
 
 
+def stepwise_tree_bytes(n, count, es, acc):
+    """Binomial levels: each receiving pair reads the sender's value and its own and writes a partial (inputs
+    where nothing has been received yet, the output at the last level); broadcast: read + write per pair."""
+    k = int(np.ceil(np.log2(n)))
+    total = 0.0
+    for j in range(k):
+        for i in range(0, n, 2 << j):
+            src = i + (1 << j)
+            if src >= n:
+                continue
+            msg = es if (j == 0 or src + 1 >= n) else acc
+            own = es if j == 0 else acc
+            wr = es if j == k - 1 else acc
+            total += count * (msg + own + wr)
+    for j in range(k):
+        total += sum(1 for i in range(0, n, 2 << j) if i + (1 << j) < n) * count * 2 * es
+    return total
+
+
 def row_entry(name, ms, alg_bytes, S, n, extra=None, factor=None):
     """factor: busbw / algbw; 2(N-1)/N for an all-reduce (default), (N-1)/N for reduce-scatter and all-gather."""
     t = float(np.mean(ms)) * 1e-3
@@ -217,7 +236,8 @@ def other_rows(torch, ar, inputs, ins, outs, dev, reps, host):
     timer = Timer(torch)
     log("timing the other rows")
     for name, algo, ofn in (("fused_reduce_broadcast", ar.AR_ALGO_FUSED, _o.fused_allreduce),
-                            ("rhd_tree", ar.AR_ALGO_RHD, _o.rhd_allreduce)):
+                            ("rhd_tree", ar.AR_ALGO_RHD, _o.rhd_allreduce),
+                            ("binomial_tree", ar.AR_ALGO_TREE, _o.tree_allreduce)):
         fn = lambda: ar.ar_allreduce(ins, outs, ar.AR_AVG, algo)
         fn()
         rows[name] = row_entry(name, timer.run(fn, reps), ring_bytes(N_RANKS, COUNT, 2), S, N_RANKS)
@@ -239,14 +259,18 @@ def other_rows(torch, ar, inputs, ins, outs, dev, reps, host):
     del parts
     ws = torch.empty(ar.ar_allreduce_workspace_size(N_RANKS, COUNT, ar.AR_BF16, ar.AR_AVG, ar.AR_ALGO_RING_STEPWISE),
                      dtype=torch.uint8, device=dev)
-    for name, algo, fb in (("ring_stepwise", ar.AR_ALGO_RING_STEPWISE, stepwise_ring_bytes),
-                           ("rhd_stepwise", ar.AR_ALGO_RHD_STEPWISE, stepwise_rhd_bytes)):
+    levels = int(np.ceil(np.log2(N_RANKS)))
+    for name, algo, fb, launches in (
+            ("ring_stepwise", ar.AR_ALGO_RING_STEPWISE, stepwise_ring_bytes, 2 * (N_RANKS - 1)),
+            ("rhd_stepwise", ar.AR_ALGO_RHD_STEPWISE, stepwise_rhd_bytes, 2 * levels),
+            ("tree_stepwise", ar.AR_ALGO_TREE_STEPWISE, stepwise_tree_bytes, 2 * levels)):
         fn = lambda: ar.ar_allreduce_ws(ins, outs, ar.AR_AVG, algo, ws)
         fn()
         rows[name] = row_entry(name, timer.run(fn, max(3, reps // 2)), fb(N_RANKS, COUNT, 2, 4), S, N_RANKS,
-                               {"launches": 2 * (N_RANKS - 1) if algo == ar.AR_ALGO_RING_STEPWISE else 6,
-                                "cpu_oracle": "same computation as the ring (cpu_baseline) and rhd_tree oracle "
-                                              "timings: the oracle executes the rounds literally"})
+                               {"launches": launches,
+                                "cpu_oracle": "same computation as the ring (cpu_baseline), rhd_tree and "
+                                              "binomial_tree oracle timings: the oracle executes the rounds "
+                                              "literally"})
     del ws
     torch.cuda.empty_cache()
 
@@ -335,12 +359,67 @@ def graph_time_us(torch, call, calls, replays=5):
     return float(np.median(ms)) * 1e3 / calls
 
 
+def overlap_rows(torch, ar, ins, outs, dev, reps=5):
+    """The headline all-reduce on a stream of its own beside another kernel on a second stream ([V]
+    "communicationとcomputeを重ねる条件": overlap hides waiting only if the two do not compete for the same memory
+    bandwidth or compute units; measure it end to end). Partners: an HBM-bound 2 GiB device copy (the same
+    bytes as the all-reduce) and an MFMA-bound 8192^3 bf16 GEMM. All streams keep the default priority."""
+    s_ar, s_p = torch.cuda.Stream(), torch.cuda.Stream()
+    src = torch.empty(1 << 30, dtype=torch.bfloat16, device=dev).normal_()
+    dst = torch.empty_like(src)
+    a = torch.randn(8192, 8192, dtype=torch.bfloat16, device=dev)
+    b = torch.randn(8192, 8192, dtype=torch.bfloat16, device=dev)
+    c = torch.empty(8192, 8192, dtype=torch.bfloat16, device=dev)
+    partners = {"hbm_copy_2GiB": lambda: dst.copy_(src), "gemm_bf16_8192": lambda: torch.mm(a, b, out=c)}
+    run_ar = lambda: ar.ar_allreduce(ins, outs, ar.AR_AVG, ar.AR_ALGO_RING, stream=s_ar)
+
+    def on(stream, fn):
+        with torch.cuda.stream(stream):
+            fn()
+
+    def timed(work):
+        """work: list of (stream, fn) started together; returns (wall us, per-stream us)."""
+        cur = torch.cuda.current_stream()
+        res_wall, res_each = [], []
+        for _ in range(reps + 1):
+            start = torch.cuda.Event(enable_timing=True)
+            start.record(cur)
+            ends = []
+            for st, fn in work:
+                st.wait_event(start)
+                on(st, fn)
+                e = torch.cuda.Event(enable_timing=True)
+                e.record(st)
+                ends.append(e)
+            for e in ends:
+                cur.wait_event(e)
+            end = torch.cuda.Event(enable_timing=True)
+            end.record(cur)
+            torch.cuda.synchronize()
+            res_wall.append(start.elapsed_time(end) * 1e3)
+            res_each.append([start.elapsed_time(e) * 1e3 for e in ends])
+        return float(np.median(res_wall[1:])), [float(np.median([r[k] for r in res_each[1:]])) for k in range(len(work))]
+
+    out = {}
+    ar_alone, _ = timed([(s_ar, run_ar)])
+    for name, fn in partners.items():
+        p_alone, _ = timed([(s_p, fn)])
+        both, each = timed([(s_ar, run_ar), (s_p, fn)])
+        out[name] = {"allreduce_alone_us": ar_alone, "partner_alone_us": p_alone, "together_us": both,
+                     "allreduce_in_overlap_us": each[0], "partner_in_overlap_us": each[1],
+                     "serial_us": ar_alone + p_alone, "gain_vs_serial": (ar_alone + p_alone) / both}
+    del src, dst, a, b, c
+    torch.cuda.empty_cache()
+    return out
+
+
 def sweep(torch, ar, dev, out_path, reps=20, max_log2=30):
     """Message-size sweep: N = 8 fp32 ranks, sum, 8 B ... 1 GiB per rank, ring vs halving-doubling vs rank order
     vs the round-per-launch schedules. Below 1 GiB of total traffic, ceil(1 GiB / (2 N S)) buffer sets (at most
     64) are rotated so that no call finds its data in the 256 MB last-level cache. One JSON line per point."""
     algos = [("ring", ar.AR_ALGO_RING), ("rhd", ar.AR_ALGO_RHD), ("fused", ar.AR_ALGO_FUSED),
-             ("ring_stepwise", ar.AR_ALGO_RING_STEPWISE), ("rhd_stepwise", ar.AR_ALGO_RHD_STEPWISE)]
+             ("tree", ar.AR_ALGO_TREE), ("ring_stepwise", ar.AR_ALGO_RING_STEPWISE),
+             ("rhd_stepwise", ar.AR_ALGO_RHD_STEPWISE), ("tree_stepwise", ar.AR_ALGO_TREE_STEPWISE)]
     n = N_RANKS
     g = torch.Generator(device=dev)
     lines = []
@@ -368,8 +447,9 @@ def sweep(torch, ar, dev, out_path, reps=20, max_log2=30):
                 if S <= (16 << 20):
                     # device time per call: 100 calls captured in one HIP graph, replayed
                     graph_us = graph_time_us(torch, call, 100)
-                alg = ring_bytes(n, count, 4) if "stepwise" not in name else (
-                    stepwise_ring_bytes(n, count, 4, 4) if name == "ring_stepwise" else stepwise_rhd_bytes(n, count, 4, 4))
+                alg = {"ring_stepwise": stepwise_ring_bytes, "rhd_stepwise": stepwise_rhd_bytes,
+                       "tree_stepwise": stepwise_tree_bytes}.get(name, lambda n_, c_, e_, a_: ring_bytes(n_, c_, e_))(
+                    n, count, 4, 4)
                 rec = {"bytes_per_rank": S, "algo": name, "us_p50": t * 1e6, "us": stats_us(ms),
                        "algbw_GBps": S / t / GB, "busbw_GBps": S / t / GB * bus_factor(n),
                        "hbm_GBps": alg / t / GB, "frac_of_peak": alg / t / GB / PEAK_HBM_GBPS, "buffer_sets": sets,
@@ -458,6 +538,8 @@ def main():
     }
     if not args.headline_only:
         result["copy_ceiling_GBps"] = copy_ceiling(torch, ins, outs)
+        log("overlap row")
+        result["overlap"] = overlap_rows(torch, ar, ins, outs, dev)
         result["rows"] = other_rows(torch, ar, inputs, ins, outs, dev, reps=max(5, args.steps // 2), host=host)
         del ins, outs
         torch.cuda.empty_cache()

@@ -87,6 +87,21 @@ enum ar_op { AR_SUM = 0, AR_AVG = 1, AR_MIN = 2, AR_MAX = 3 };
  *   ignored); inv = 448/amax and scale = amax/448 (fp32 divisions); amax == 0, or an infinite inv, gives
  *   inv = scale = 1; code = E4M3(v*inv) rounded to nearest even and saturated to +-448; NaN -> 0x7F;
  *   dequant = value(code) * scale. dtype AR_F32 or AR_BF16, op AR_SUM or AR_AVG. Codes never reach HBM.
+ * AR_ALGO_TREE ([P] "算法与实现", tree-based all-reduce over a binomial tree; [G] algorithm table,
+ *   Tree-AllReduce; [W] "其他 AllReduce 算法"): binomial reduce to rank 0, then binomial broadcast. Reduce
+ *   step j (j = 0, 1, ...): every rank i with i % 2^(j+1) == 0 receives the partial of rank i + 2^j, when
+ *   that rank exists, and combines it into its own (receiver's partial on the left). Rank 0 applies the
+ *   epilogue; the broadcast walks the same tree back down. Every element is therefore the binomial fold
+ *   T(0, N), T(lo, n) = T(lo, h) (+) T(lo + h, n - h) with h the largest power of two below n, e.g.
+ *   N=8: ((x0+x1)+(x2+x3))+((x4+x5)+(x6+x7)); N=5: ((x0+x1)+(x2+x3))+x4. Any N. Collapsed into one pass.
+ * AR_ALGO_TREE_STEPWISE: the binomial schedule one level per kernel launch (2 ceil(log2 N) launches),
+ *   partials through HBM; bit-identical to AR_ALGO_TREE. bf16/f16 need ar_allreduce_ws.
+ * AR_ALGO_AUTO ([G] "NCCLにおけるAllReduce": ring for large tensors, tree for small ones; [W] "NCCL 的拓扑感知
+ *   选择"): AR_ALGO_TREE or AR_ALGO_RING, whichever the cost table of [G] (time = steps * alpha + bytes moved
+ *   per rank / link bandwidth; ring 2(N-1) steps and 2(N-1)/N * M bytes, tree 2 ceil(log2 N) steps and 2 M
+ *   bytes) prices lower for M = count * element size bytes on an xGMI link: tree iff
+ *   M < N * (N - 1 - ceil(log2 N)) * AR_AUTO_STEP_NS * AR_AUTO_LINK_GBPS. ar_auto_algo() returns the choice,
+ *   and ar_last_call records the algorithm that ran.
  */
 enum ar_algo {
     AR_ALGO_RING = 0,
@@ -94,8 +109,20 @@ enum ar_algo {
     AR_ALGO_RHD = 2,
     AR_ALGO_RING_STEPWISE = 3,
     AR_ALGO_RHD_STEPWISE = 4,
-    AR_ALGO_RING_FP8 = 5
+    AR_ALGO_RING_FP8 = 5,
+    AR_ALGO_TREE = 6,
+    AR_ALGO_TREE_STEPWISE = 7,
+    AR_ALGO_AUTO = 8
 };
+
+/* Cost-model constants of AR_ALGO_AUTO: per-step latency (ns) and per-link bandwidth (GB/s) of one xGMI hop
+ * between MI355X GPUs. N=8 switches from tree to ring at 4,896,000 bytes; N <= 3 always takes the ring. */
+#define AR_AUTO_STEP_NS 1000
+#define AR_AUTO_LINK_GBPS 153
+
+/* The algorithm AR_ALGO_AUTO runs for this call shape (AR_ALGO_TREE or AR_ALGO_RING), or -AR_ERR_INVALID for
+ * a bad nranks or dtype. Pure host function. */
+int ar_auto_algo(int nranks, size_t count, int dtype);
 
 /* All-reduce of N rank buffers ([P] opening definition: every process contributes a buffer, buffers are
  * combined element-wise and the result is copied back to all; [V] "All-Reduceは全rankの値を集約して全rankへ返す").
@@ -105,7 +132,8 @@ enum ar_algo {
  *   Alignment: any. A 16-byte vector path is used where every pointer is 16-byte aligned.
  * Errors: AR_ERR_INVALID (enum, nranks, NULL), AR_ERR_UNSUPPORTED (RHD with N not a power of two; FP8
  *   with a dtype other than F32/BF16 or an op other than SUM/AVG), AR_ERR_ALIAS, AR_ERR_WORKSPACE (the
- *   stepwise algorithms on bf16/f16 need ar_allreduce_ws), AR_ERR_HIP. */
+ *   stepwise algorithms on bf16/f16 need ar_allreduce_ws), AR_ERR_HIP. AR_ALGO_AUTO is resolved first, so
+ *   its errors are those of the algorithm it picks. */
 int ar_allreduce(const void* const* in_bufs, void* const* out_bufs, int nranks, size_t count, int dtype, int op,
                  int algo, void* stream);
 
@@ -170,7 +198,7 @@ int ar_bucket_plan(const int64_t* numels, int ntensors, int dtype, int nranks, s
  *     bucket counts; flat_out[r] may equal flat_in[r]; no other overlap.
  *   bucket_count: host array [nbuckets]; every count must be a multiple of nranks * (16 / element size), as
  *     ar_bucket_plan produces, so every chunk starts on a 16-byte boundary.
- *   algo: AR_ALGO_RING, AR_ALGO_FUSED or AR_ALGO_RHD.
+ *   algo: AR_ALGO_RING, AR_ALGO_FUSED, AR_ALGO_RHD or AR_ALGO_TREE.
  * Errors: AR_ERR_INVALID (enums, NULLs, misaligned pointers, a count that is negative or not such a
  * multiple), AR_ERR_UNSUPPORTED (another algorithm; RHD with N not a power of two), AR_ERR_ALIAS, AR_ERR_HIP. */
 int ar_allreduce_buckets(const void* const* flat_in, void* const* flat_out, int nranks, const int64_t* bucket_count,
@@ -190,7 +218,8 @@ typedef struct ar_tensor_desc {
 } ar_tensor_desc;
 /*   d_in, d_out: DEVICE arrays of ntensors * nranks device pointers, entry [t * nranks + r] is rank r's copy of
  *     tensor t; d_out entries may equal the d_in ones (in place), no other overlap.
- *   algo: AR_ALGO_RING (the bucket ring's order), AR_ALGO_FUSED or AR_ALGO_RHD (chunk-agnostic orders).
+ *   algo: AR_ALGO_RING (the bucket ring's order), AR_ALGO_FUSED, AR_ALGO_RHD or AR_ALGO_TREE (chunk-agnostic
+ *     orders).
  * The descriptors are read on the device only: the call checks its scalar arguments, and a descriptor that
  * breaks the rules above gives wrong values for that tensor (the kernel never loops forever on it).
  * Errors: AR_ERR_INVALID (enums, NULLs, ntensors < 0), AR_ERR_UNSUPPORTED (other algorithms; RHD with N not a

@@ -60,6 +60,8 @@ ORACLE_FOR = {
     ar.AR_ALGO_RHD: oracle.rhd_allreduce,
     ar.AR_ALGO_RHD_STEPWISE: oracle.rhd_allreduce,
     ar.AR_ALGO_RING_FP8: oracle.fp8_ring_allreduce,
+    ar.AR_ALGO_TREE: oracle.tree_allreduce,
+    ar.AR_ALGO_TREE_STEPWISE: oracle.tree_allreduce,
 }
 
 

@@ -1,6 +1,7 @@
 """CPU-only checks of the C ABI: the library loads, exports every declared symbol, its enums agree with the
 binding, and argument validation returns before anything is launched (no GPU needed)."""
 import ctypes
+import math
 import os
 import re
 
@@ -42,6 +43,8 @@ def test_binding_constants_match_header():
     assert ar.AR_MAX_RANKS == int(re.search(r"#define AR_MAX_RANKS (\d+)", text).group(1))
     assert ar.AR_FP8_BLOCK == int(re.search(r"#define AR_FP8_BLOCK (\d+)", text).group(1))
     assert ar.ar_version() == int(re.search(r"#define AR_VERSION (\d+)", text).group(1))
+    assert ar.AR_AUTO_STEP_NS == int(re.search(r"#define AR_AUTO_STEP_NS (\d+)", text).group(1))
+    assert ar.AR_AUTO_LINK_GBPS == int(re.search(r"#define AR_AUTO_LINK_GBPS (\d+)", text).group(1))
 
 
 def test_status_strings():
@@ -66,7 +69,8 @@ def _call(n, count, dtype=ar.AR_F32, op=ar.AR_SUM, algo=ar.AR_ALGO_RING, ins=Non
 def test_invalid_arguments():
     assert _call(2, 10, dtype=7) == ar.AR_ERR_INVALID
     assert _call(2, 10, op=9) == ar.AR_ERR_INVALID
-    assert _call(2, 10, algo=6) == ar.AR_ERR_INVALID
+    assert _call(2, 10, algo=9) == ar.AR_ERR_INVALID
+    assert _call(2, 10, algo=-1) == ar.AR_ERR_INVALID
     assert _call(0, 10) == ar.AR_ERR_INVALID
     assert _call(65, 10) == ar.AR_ERR_INVALID
     assert _call(2, 10, ins=[0x1000, 0]) == ar.AR_ERR_INVALID
@@ -79,6 +83,8 @@ def test_invalid_arguments():
 def test_unsupported_combinations():
     assert _call(3, 10, algo=ar.AR_ALGO_RHD) == ar.AR_ERR_UNSUPPORTED
     assert _call(6, 10, algo=ar.AR_ALGO_RHD_STEPWISE) == ar.AR_ERR_UNSUPPORTED
+    # AUTO picks the ring for a large message; the ring's own rules then apply
+    assert _call(4, 1 << 20, dtype=ar.AR_I32, algo=ar.AR_ALGO_AUTO, ins=[0x10000000, 0, 0, 0]) == ar.AR_ERR_INVALID
     assert _call(4, 10, dtype=ar.AR_I32, algo=ar.AR_ALGO_RING_FP8) == ar.AR_ERR_UNSUPPORTED
     assert _call(4, 10, dtype=ar.AR_F16, algo=ar.AR_ALGO_RING_FP8) == ar.AR_ERR_UNSUPPORTED
     assert _call(4, 10, op=ar.AR_MAX, algo=ar.AR_ALGO_RING_FP8) == ar.AR_ERR_UNSUPPORTED
@@ -98,7 +104,12 @@ def test_workspace_rules():
     assert need == 8 * 1024 * 4
     assert ar.ar_allreduce_workspace_size(8, 1000, ar.AR_F32, ar.AR_SUM, ar.AR_ALGO_RING_STEPWISE) == 0
     assert ar.ar_allreduce_workspace_size(8, 1000, ar.AR_BF16, ar.AR_SUM, ar.AR_ALGO_RING) == 0
+    assert ar.ar_allreduce_workspace_size(5, 1000, ar.AR_F16, ar.AR_MAX, ar.AR_ALGO_TREE_STEPWISE) == 5 * 1024 * 4
+    assert ar.ar_allreduce_workspace_size(5, 1000, ar.AR_I32, ar.AR_MAX, ar.AR_ALGO_TREE_STEPWISE) == 0
+    assert ar.ar_allreduce_workspace_size(8, 1000, ar.AR_BF16, ar.AR_SUM, ar.AR_ALGO_TREE) == 0
+    assert ar.ar_allreduce_workspace_size(8, 1000, ar.AR_BF16, ar.AR_SUM, ar.AR_ALGO_AUTO) == 0
     assert _call(8, 1000, dtype=ar.AR_BF16, algo=ar.AR_ALGO_RING_STEPWISE) == ar.AR_ERR_WORKSPACE
+    assert _call(3, 1000, dtype=ar.AR_F16, algo=ar.AR_ALGO_TREE_STEPWISE) == ar.AR_ERR_WORKSPACE
     assert _call(8, 1000, dtype=ar.AR_BF16, algo=ar.AR_ALGO_RHD_STEPWISE, ws=0x7000000000, wsb=need - 1) \
         == ar.AR_ERR_WORKSPACE
     assert _call(8, 1000, dtype=ar.AR_BF16, algo=ar.AR_ALGO_RING_STEPWISE, ws=0x7000000010, wsb=need) \
@@ -116,6 +127,48 @@ def test_last_call_record():
     assert r2["seq"] == r1["seq"] + 1
     assert r2["entry"] == "ar_allreduce_ws" and r2["nranks"] == 3 and r2["status"] == ar.AR_ERR_UNSUPPORTED
     assert r2["algo"] == ar.AR_ALGO_RHD and r2["count"] == 10
+    # AR_ALGO_AUTO is recorded as the algorithm it resolved to (here a validation error after resolving)
+    _call(8, 100, dtype=ar.AR_BF16, algo=ar.AR_ALGO_AUTO, ins=[0x10000000] + [0] * 7)
+    r3 = ar.ar_last_call()
+    assert r3["algo"] == ar.AR_ALGO_TREE and r3["status"] == ar.AR_ERR_INVALID
+
+
+def _auto_by_cost_table(n, nbytes):
+    """Tree or ring from the cost table (time = steps * alpha + bytes per rank / bandwidth), exact rationals."""
+    from fractions import Fraction
+    alpha = Fraction(ar.AR_AUTO_STEP_NS, 10 ** 9)
+    bw = Fraction(ar.AR_AUTO_LINK_GBPS * 10 ** 9)
+    levels = math.ceil(math.log2(n)) if n > 1 else 0
+    t_ring = 2 * (n - 1) * alpha + Fraction(2 * (n - 1), n) * nbytes / bw
+    t_tree = 2 * levels * alpha + 2 * Fraction(nbytes) / bw
+    return ar.AR_ALGO_TREE if t_tree < t_ring else ar.AR_ALGO_RING
+
+
+@pytest.mark.parametrize("n", [1, 2, 3, 4, 5, 7, 8, 9, 16, 33, 64])
+@pytest.mark.parametrize("dtype,es", [(ar.AR_F32, 4), (ar.AR_BF16, 2)])
+def test_auto_algo_follows_cost_table(n, dtype, es):
+    counts = [0, 1, 1000, 100_000, 10 ** 6, 10 ** 8]
+    # the crossover itself, from both sides, where there is one
+    levels = math.ceil(math.log2(n)) if n > 1 else 0
+    spare = n - 1 - levels
+    if spare > 0:
+        cross = n * spare * ar.AR_AUTO_STEP_NS * ar.AR_AUTO_LINK_GBPS  # bytes
+        c = -(-cross // es)
+        counts += [c - 1, c, c + 1]
+    for count in counts:
+        assert ar.ar_auto_algo(n, count, dtype) == _auto_by_cost_table(n, count * es), (n, count)
+    if n <= 3:
+        assert all(ar.ar_auto_algo(n, c, dtype) == ar.AR_ALGO_RING for c in counts)
+
+
+def test_auto_algo_examples_and_errors():
+    assert ar.ar_auto_algo(8, 2_447_999, ar.AR_BF16) == ar.AR_ALGO_TREE   # 4,895,998 bytes
+    assert ar.ar_auto_algo(8, 2_448_000, ar.AR_BF16) == ar.AR_ALGO_RING   # 4,896,000 bytes
+    assert ar.ar_auto_algo(8, 134_217_728, ar.AR_BF16) == ar.AR_ALGO_RING
+    with pytest.raises(ar.ArError):
+        ar.ar_auto_algo(0, 10, ar.AR_F32)
+    with pytest.raises(ar.ArError):
+        ar.ar_auto_algo(4, 10, 9)
 
 
 def test_codec_and_copy_validation():
@@ -166,6 +219,8 @@ def test_allreduce_buckets_validation():
         L.ar_allreduce_buckets(i, o, n, np.ascontiguousarray(c, np.int64).ctypes.data, len(c), dt, op, algo, None)
     assert call(np.array([], np.int64)) == ar.AR_OK
     assert call(counts, algo=ar.AR_ALGO_RING_STEPWISE) == ar.AR_ERR_UNSUPPORTED
+    assert call(counts, algo=ar.AR_ALGO_TREE_STEPWISE) == ar.AR_ERR_UNSUPPORTED
+    assert call(counts, algo=ar.AR_ALGO_AUTO) == ar.AR_ERR_UNSUPPORTED
     assert call(counts, algo=ar.AR_ALGO_RING_FP8) == ar.AR_ERR_UNSUPPORTED
     assert call(counts, n=3, algo=ar.AR_ALGO_RHD,
                 i=(ctypes.c_void_p * 3)(base, base + (1 << 20), base + (4 << 20)),
@@ -189,6 +244,7 @@ def test_allreduce_tensors_validation():
     assert call(dt=5) == ar.AR_ERR_INVALID
     assert call(d=None) == ar.AR_ERR_INVALID
     assert call(algo=ar.AR_ALGO_RING_STEPWISE) == ar.AR_ERR_UNSUPPORTED
+    assert call(algo=ar.AR_ALGO_TREE_STEPWISE) == ar.AR_ERR_UNSUPPORTED
     assert call(algo=ar.AR_ALGO_RING_FP8) == ar.AR_ERR_UNSUPPORTED
     assert call(n=6, algo=ar.AR_ALGO_RHD) == ar.AR_ERR_UNSUPPORTED
 

@@ -99,7 +99,8 @@ def test_sweep_largest_point_one_GiB_per_rank():
     idx = np.unique(np.concatenate([rng.integers(0, count, 1 << 20), np.arange(1000), np.arange(count - 1000, count)]))
     sub = [h[idx] for h in host]
     for algo, fn in ((ar.AR_ALGO_FUSED, oracle.fused_allreduce), (ar.AR_ALGO_RHD, oracle.rhd_allreduce),
-                     (ar.AR_ALGO_RHD_STEPWISE, oracle.rhd_allreduce)):
+                     (ar.AR_ALGO_RHD_STEPWISE, oracle.rhd_allreduce), (ar.AR_ALGO_TREE, oracle.tree_allreduce),
+                     (ar.AR_ALGO_TREE_STEPWISE, oracle.tree_allreduce)):
         ar.ar_allreduce(ins, outs, ar.AR_SUM, algo)
         torch.cuda.synchronize()
         _same_on_all_ranks(outs)

@@ -29,7 +29,7 @@ def _inputs(dt, n, count, seed):
 
 
 @pytest.mark.parametrize("algo", [ar.AR_ALGO_RING, ar.AR_ALGO_FUSED, ar.AR_ALGO_RHD, ar.AR_ALGO_RING_STEPWISE,
-                                  ar.AR_ALGO_RHD_STEPWISE])
+                                  ar.AR_ALGO_RHD_STEPWISE, ar.AR_ALGO_TREE, ar.AR_ALGO_TREE_STEPWISE])
 @pytest.mark.parametrize("dt", [ar.AR_I32, ar.AR_F32])
 def test_worked_example(algo, dt):
     rows = {}
@@ -93,12 +93,42 @@ def test_rhd_stepwise(n, dt):
         assert_bitwise(got, expect(xs, dt, op, ar.AR_ALGO_RHD), f"rhd stepwise n={n} op={op}")
 
 
+@pytest.mark.parametrize("n", [1, 2, 3, 4, 5, 6, 7, 8, 9, 12, 16, 33, 64])
+@pytest.mark.parametrize("dt", DTYPES)
+def test_tree_all_ops(n, dt):
+    """Binomial tree, one pass: compile-time rank counts (2, 4, 8, 16) and the run-time fold (all others)."""
+    count = 2053 if n <= 16 else 517
+    xs = _inputs(dt, n, count, 18)
+    for op in OPS:
+        assert_bitwise(run(xs, dt, op, ar.AR_ALGO_TREE), expect(xs, dt, op, ar.AR_ALGO_TREE), f"tree n={n} op={op}")
+
+
+@pytest.mark.parametrize("n", [2, 3, 5, 6, 8, 13])
+@pytest.mark.parametrize("dt", DTYPES)
+def test_tree_stepwise(n, dt):
+    xs = _inputs(dt, n, 2500 + n, 19)
+    for op in OPS:
+        got = run(xs, dt, op, ar.AR_ALGO_TREE_STEPWISE)
+        assert_bitwise(got, expect(xs, dt, op, ar.AR_ALGO_TREE), f"tree stepwise n={n} op={op}")
+
+
+@pytest.mark.parametrize("n,count", [(8, 1000), (8, 2_447_999), (8, 2_448_000), (4, 306_000), (3, 5000), (16, 70_001)])
+def test_auto_runs_the_algorithm_it_reports(n, count):
+    dt = ar.AR_BF16
+    xs = inputs.rank_inputs("uniform_bf16", n, count, cfg=20, extra=(n, count))
+    picked = ar.ar_auto_algo(n, count, dt)
+    got = run(xs, dt, ar.AR_AVG, ar.AR_ALGO_AUTO)
+    rec = ar.ar_last_call()
+    assert rec["algo"] == picked and rec["status"] == ar.AR_OK
+    assert_bitwise(got, expect(xs, dt, ar.AR_AVG, picked), f"auto n={n} count={count} -> {picked}")
+
+
 # ---------------------------------------------------------------- edges: tiny, ragged, unaligned, in place
 
 
 @pytest.mark.parametrize("count", [1, 2, 3, 7, 8, 9, 31, 33, 63, 65, 127, 1023])
 @pytest.mark.parametrize("algo", [ar.AR_ALGO_RING, ar.AR_ALGO_FUSED, ar.AR_ALGO_RHD, ar.AR_ALGO_RING_STEPWISE,
-                                  ar.AR_ALGO_RHD_STEPWISE])
+                                  ar.AR_ALGO_RHD_STEPWISE, ar.AR_ALGO_TREE, ar.AR_ALGO_TREE_STEPWISE])
 def test_small_and_ragged_counts(count, algo):
     for dt in (ar.AR_F32, ar.AR_BF16):
         xs = _inputs(dt, 8, count, 15)
@@ -106,7 +136,7 @@ def test_small_and_ragged_counts(count, algo):
 
 
 @pytest.mark.parametrize("algo", [ar.AR_ALGO_RING, ar.AR_ALGO_FUSED, ar.AR_ALGO_RHD, ar.AR_ALGO_RING_STEPWISE,
-                                  ar.AR_ALGO_RHD_STEPWISE])
+                                  ar.AR_ALGO_RHD_STEPWISE, ar.AR_ALGO_TREE, ar.AR_ALGO_TREE_STEPWISE])
 @pytest.mark.parametrize("dt", [ar.AR_F32, ar.AR_BF16, ar.AR_I32])
 def test_unaligned_buffers_take_the_element_path(algo, dt):
     xs = _inputs(dt, 4, 1000, 16)
@@ -115,7 +145,8 @@ def test_unaligned_buffers_take_the_element_path(algo, dt):
 
 
 @pytest.mark.parametrize("algo", [ar.AR_ALGO_RING, ar.AR_ALGO_FUSED, ar.AR_ALGO_RHD, ar.AR_ALGO_RING_STEPWISE,
-                                  ar.AR_ALGO_RHD_STEPWISE, ar.AR_ALGO_RING_FP8])
+                                  ar.AR_ALGO_RHD_STEPWISE, ar.AR_ALGO_RING_FP8, ar.AR_ALGO_TREE,
+                                  ar.AR_ALGO_TREE_STEPWISE])
 def test_in_place_equals_out_of_place(algo):
     for dt in (ar.AR_F32, ar.AR_BF16):
         xs = _inputs(dt, 8, 70000, 17)
@@ -125,7 +156,8 @@ def test_in_place_equals_out_of_place(algo):
 
 
 @pytest.mark.parametrize("algo", [ar.AR_ALGO_RING, ar.AR_ALGO_FUSED, ar.AR_ALGO_RHD, ar.AR_ALGO_RING_STEPWISE,
-                                  ar.AR_ALGO_RHD_STEPWISE, ar.AR_ALGO_RING_FP8])
+                                  ar.AR_ALGO_RHD_STEPWISE, ar.AR_ALGO_RING_FP8, ar.AR_ALGO_TREE,
+                                  ar.AR_ALGO_TREE_STEPWISE])
 def test_guard_bands_untouched_and_every_output_written(algo):
     dt, n, count, guard = ar.AR_BF16, 8, 50001, 64
     xs = _inputs(dt, n, count, 18)
@@ -169,7 +201,7 @@ def test_fused_and_rhd_within_tolerance_of_ring(n):
     xs = _inputs(ar.AR_F32, n, count, 19)
     ring = run(xs, ar.AR_F32, ar.AR_SUM, ar.AR_ALGO_RING)[0].view(np.float32).astype(np.float64)
     abss = np.sum(np.abs(np.array(xs, np.float64)), axis=0)
-    for algo in (ar.AR_ALGO_FUSED, ar.AR_ALGO_RHD):
+    for algo in (ar.AR_ALGO_FUSED, ar.AR_ALGO_RHD, ar.AR_ALGO_TREE):
         y = run(xs, ar.AR_F32, ar.AR_SUM, algo)[0].view(np.float32).astype(np.float64)
         assert np.all(np.abs(y - ring) <= 1e-6 * n * abss)
     xb = inputs.rank_inputs("normal_bf16", n, count, cfg=19)
@@ -179,7 +211,7 @@ def test_fused_and_rhd_within_tolerance_of_ring(n):
     ulp = np.abs(rf) * 2.0 ** -7
     ulp = np.maximum(ulp, 2.0 ** -133)
     reorder = 2 * (n - 1) * 2.0 ** -24 * absb
-    for algo in (ar.AR_ALGO_FUSED, ar.AR_ALGO_RHD):
+    for algo in (ar.AR_ALGO_FUSED, ar.AR_ALGO_RHD, ar.AR_ALGO_TREE):
         yb = oracle.bf16_to_f32(run(xb, ar.AR_BF16, ar.AR_SUM, algo)[0]).astype(np.float64)
         d = np.abs(yb - rf)
         tol = np.where(reorder > ulp / 2, ulp + reorder, ulp)
@@ -352,7 +384,7 @@ def test_allreduce_buckets_equals_one_call_per_bucket(n, dt):
     total = int(counts.sum())
     xs = _inputs(dt, n, total, 20)
     starts = np.concatenate([[0], np.cumsum(counts)])
-    algos = [ar.AR_ALGO_RING, ar.AR_ALGO_FUSED] + ([ar.AR_ALGO_RHD] if n & (n - 1) == 0 else [])
+    algos = [ar.AR_ALGO_RING, ar.AR_ALGO_FUSED, ar.AR_ALGO_TREE] + ([ar.AR_ALGO_RHD] if n & (n - 1) == 0 else [])
     for algo in algos:
         for op in OPS:
             want_flat = [np.empty(total, dtype=NP_BITS[dt]) for _ in range(n)]
@@ -373,7 +405,8 @@ def test_allreduce_buckets_equals_one_call_per_bucket(n, dt):
             assert_bitwise([from_dev(o, dt) for o in ins], want_flat, f"buckets in place n={n} op={op}")
 
 
-@pytest.mark.parametrize("algo", [ar.AR_ALGO_RING, ar.AR_ALGO_RHD, ar.AR_ALGO_RING_STEPWISE, ar.AR_ALGO_RING_FP8])
+@pytest.mark.parametrize("algo", [ar.AR_ALGO_RING, ar.AR_ALGO_RHD, ar.AR_ALGO_RING_STEPWISE, ar.AR_ALGO_RING_FP8,
+                                  ar.AR_ALGO_TREE_STEPWISE])
 def test_hip_graph_capture_replays_match_eager(algo):
     """Calls captured in a HIP graph replay to the eager result, every replay, with eager work in between."""
     n, count = 8, 50_003
@@ -414,7 +447,7 @@ def test_fused_tensor_path_equals_pack_reduce_unpack(n, dt):
     rng = np.random.default_rng(40 + n + 10 * dt)
     sizes = [int(s) for s in rng.integers(1, 3000, 23)] + [1, 2, 9, 70001, 4096, 40000]
     tdt = {ar.AR_F32: torch.float32, ar.AR_BF16: torch.bfloat16, ar.AR_I32: torch.int32}[dt]
-    algos = [ar.AR_ALGO_RING, ar.AR_ALGO_FUSED] + ([ar.AR_ALGO_RHD] if n & (n - 1) == 0 else [])
+    algos = [ar.AR_ALGO_RING, ar.AR_ALGO_FUSED, ar.AR_ALGO_TREE] + ([ar.AR_ALGO_RHD] if n & (n - 1) == 0 else [])
     for cap in (4096, 200 << 10):
         host = [[inputs.rank_inputs(KIND[dt], 1, s, cfg=41, extra=(r, t, n))[0] for t, s in enumerate(sizes)]
                 for r in range(n)]
@@ -500,3 +533,25 @@ def test_reduce_scatter_all_gather_page_examples_and_in_place():
     torch.cuda.synchronize()
     assert_bitwise([from_dev(b, ar.AR_F32) for b in bufs], expect(xs, ar.AR_F32, ar.AR_SUM, ar.AR_ALGO_RING),
                    "in-place RS + AG")
+
+
+def test_allreduce_on_a_side_stream_beside_other_kernels_is_bit_exact():
+    """The all-reduce on its own stream, running concurrently with a copy and a GEMM on another stream."""
+    n, count = 8, 3_000_007
+    xs = inputs.rank_inputs("normal_bf16", n, count, cfg=60)
+    ins = [to_dev(x, ar.AR_BF16)[1] for x in xs]
+    outs = [empty_like_dev(count, ar.AR_BF16)[1] for _ in range(n)]
+    s_ar, s_p = torch.cuda.Stream(), torch.cuda.Stream()
+    a = torch.randn(2048, 2048, device=DEV)
+    src = torch.randn(1 << 24, device=DEV)
+    dst = torch.empty_like(src)
+    torch.cuda.synchronize()
+    with torch.cuda.stream(s_p):
+        for _ in range(4):
+            torch.mm(a, a)
+            dst.copy_(src)
+    ar.ar_allreduce(ins, outs, ar.AR_AVG, ar.AR_ALGO_RING, stream=s_ar)
+    torch.cuda.synchronize()
+    assert_bitwise([from_dev(o, ar.AR_BF16) for o in outs], expect(xs, ar.AR_BF16, ar.AR_AVG, ar.AR_ALGO_RING),
+                   "side stream")
+    assert torch.equal(dst, src)
