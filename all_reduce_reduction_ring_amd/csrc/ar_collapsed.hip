@@ -22,8 +22,11 @@
 // power of two below n. The blocks of N's binary expansion are perfect trees over consecutive ranks, largest
 // first, folded right to left; the pass evaluates that in registers for any N.
 //
-// Layout: grid.y = chunk c (ring/fused) or 1 (trees); grid.x strides over the chunk's 16-byte slots. A chunk
-// whose start or end is not slot-aligned has its few edge elements done element-wise by block x = 0.
+// Layout: the ring on 16-byte aligned buffers runs the one-front kernel below (tiles of the whole buffer, each
+// folded from the rank of the chunk it lies in). Otherwise grid.y = chunk c (the unaligned ring, element-wise) or
+// 1 (rank order and the trees, whose order does not depend on the chunk), and grid.x strides over the chunk's
+// 16-byte slots; a chunk whose start or end is not slot-aligned has its few edge elements done element-wise by
+// block x = 0.
 #include "ar_device.h"
 #include "ar_internal.h"
 
@@ -55,6 +58,26 @@ struct CollapsedArgs {
 };
 
 // ------------------------------------------------------------------------------------------ fold orders
+// Ring-order fold of one slot over rank pointers already in fold order; epilogue applied.
+template <int DT, int OP, int NR>
+__device__ __forceinline__ u32x4 fold_ptrs(const char* const (&rot)[NR], int64_t off) {
+  using S = Slot<DT>;
+  typename S::Acc acc[S::V], t[S::V];
+  u32x4 x[NR];
+#pragma unroll
+  for (int k = 0; k < NR; ++k) x[k] = ld16(rot[k] + off);
+  S::unpack(x[0], acc);
+#pragma unroll
+  for (int k = 1; k < NR; ++k) {
+    S::unpack(x[k], t);
+#pragma unroll
+    for (int e = 0; e < S::V; ++e) acc[e] = combine<OP>(acc[e], t[e]);
+  }
+#pragma unroll
+  for (int e = 0; e < S::V; ++e) acc[e] = finalize<OP>(acc[e], NR);
+  return S::pack(acc);
+}
+
 // Ring / rank order for one slot at byte offset `off`: x[start], x[start+1], ... (mod n).
 template <int DT, int OP, int NR>
 __device__ __forceinline__ u32x4 ring_slot(const CollapsedArgs& a, int start, int64_t off) {
@@ -254,6 +277,94 @@ __global__ __launch_bounds__(kThreads) void collapsed_kernel(CollapsedArgs a) {
   }
 }
 
+// ------------------------------------------------------------------------------------------ ring, one front
+// The ring order with every workgroup on one moving front. With a grid per chunk, the N chunks advance as N
+// separate fronts through every rank buffer (N x 2N streams into HBM); a single front keeps 2N streams, as the
+// tree orders have, and measured faster on MI355X. Tile t = slots [t*TS, (t+1)*TS) of the whole buffer goes to
+// block t mod G; inside a tile, the slots wholly in chunk c fold from rank c (one uniform sub-range per chunk
+// the tile touches, nearly always one). Slots that straddle a chunk boundary, and the elements after the last
+// whole slot, go element by element (block 0). Needs 16-byte aligned buffers.
+template <int DT, int OP, int NR, int U>
+__device__ __forceinline__ void ring_front_elem(const CollapsedArgs& a, int64_t e) {
+  const int n = NR > 0 ? NR : a.n;
+  int c = 0;
+  while (c + 1 < n && chunk_lo(a.q, a.r, c + 1) <= e) ++c;  // largest c with chunk start <= e
+  edge_elem<DT, OP, NR, kLinear>(a, c, e);
+}
+
+template <int DT, int OP, int NR, int U>
+__global__ __launch_bounds__(kThreads) void ring_front_kernel(CollapsedArgs a) {
+  constexpr int V = Traits<DT>::kVec;
+  constexpr int64_t TS = static_cast<int64_t>(kThreads) * U;
+  constexpr int NT = NR > 0 ? NR : 1;
+  const int n = NR > 0 ? NR : a.n;
+  const int64_t nslots = a.count / V;
+  const int64_t ntiles = (nslots + TS - 1) / TS;
+  // The block's tiles t = blockIdx.x + k G come in increasing order, so they meet the chunks in order: the outer
+  // loop walks the chunks (the rotated rank pointers are fixed inside it), the inner one the tiles. A tile that
+  // reaches past the chunk's last whole slot is kept for the next chunk.
+  int64_t t = blockIdx.x;
+  for (int cc = 0; cc < n && t < ntiles; ++cc) {
+    const int64_t lo = chunk_lo(a.q, a.r, cc), hi = chunk_lo(a.q, a.r, cc + 1);
+    const int64_t w0 = (lo + V - 1) / V, w1 = hi / V;  // whole slots of chunk cc
+    if (w0 >= w1) continue;
+    const char* rot[NT];
+#pragma unroll
+    for (int k = 0; k < NT; ++k) {
+      int r = cc + k;
+      r = r >= n ? r - n : r;
+      rot[k] = static_cast<const char*>(a.p.in[r]);
+    }
+    while (t < ntiles) {
+      const int64_t s0 = t * TS, s1 = s0 + TS < nslots ? s0 + TS : nslots;
+      if (s0 >= w1) break;
+      const int64_t v0 = w0 > s0 ? w0 : s0, v1 = w1 < s1 ? w1 : s1;
+      if (v0 < v1) {
+        u32x4 w[U];
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+          const int64_t v = s0 + threadIdx.x + u * kThreads;
+          if (v >= v0 && v < v1) {
+            if constexpr (NR > 0) w[u] = fold_ptrs<DT, OP, NR>(rot, v * 16);
+            else w[u] = ring_slot<DT, OP, NR>(a, cc, v * 16);
+          }
+        }
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+          const int64_t v = s0 + threadIdx.x + u * kThreads;
+          if (v >= v0 && v < v1)
+            for (int r = 0; r < n; ++r) st16(static_cast<char*>(a.p.out[r]) + v * 16, w[u]);
+        }
+      }
+      if (s1 > w1) break;
+      t += gridDim.x;
+    }
+  }
+  if (blockIdx.x == 0) {
+    // a slot with a chunk boundary strictly inside it is done by the first such boundary only
+    for (int cb = 1; cb < n; ++cb) {
+      const int64_t b = chunk_lo(a.q, a.r, cb);
+      const int64_t sl = b / V;
+      if (b % V == 0 || sl >= nslots) continue;
+      if (cb > 1 && chunk_lo(a.q, a.r, cb - 1) > sl * V) continue;
+      if (threadIdx.x < V) ring_front_elem<DT, OP, NR, U>(a, sl * V + threadIdx.x);
+    }
+    for (int64_t e = nslots * V + threadIdx.x; e < a.count; e += kThreads) ring_front_elem<DT, OP, NR, U>(a, e);
+  }
+}
+
+template <int DT, int OP, int NR, int U>
+hipError_t launch_front(CollapsedArgs& a, hipStream_t s) {
+  constexpr int V = Traits<DT>::kVec;
+  constexpr int64_t TS = static_cast<int64_t>(kThreads) * U;
+  const int64_t ntiles = (a.count / V + TS - 1) / TS;
+  int64_t g = static_cast<int64_t>(cu_count()) * blocks_per_cu<NR>();
+  if (g > ntiles) g = ntiles;
+  if (g < 1) g = 1;
+  hipLaunchKernelGGL((ring_front_kernel<DT, OP, NR, U>), dim3(static_cast<unsigned>(g)), dim3(kThreads), 0, s, a);
+  return hipGetLastError();
+}
+
 // ------------------------------------------------------------------------------------------ launch
 template <int DT, int OP, int NR, int U, int SHAPE>
 hipError_t launch_one(CollapsedArgs& a, int nchunks, hipStream_t s) {
@@ -294,12 +405,23 @@ hipError_t dispatch_n(CollapsedArgs& a, int algo, hipStream_t s) {
       default: return launch_one<DT, OP, 0, 1, kBinomial>(a, 1, s);
     }
   }
+  if (algo == AR_ALGO_RING && a.vec && n > 1) {
+    switch (n) {
+      case 2: return launch_front<DT, OP, 2, slots_per_thread<2>()>(a, s);
+      case 4: return launch_front<DT, OP, 4, slots_per_thread<4>()>(a, s);
+      case 8: return launch_front<DT, OP, 8, slots_per_thread<8>()>(a, s);
+      case 16: return launch_front<DT, OP, 16, 1>(a, s);
+      default: return launch_front<DT, OP, 0, 1>(a, s);
+    }
+  }
+  // rank order (one chunk, so one front) and the unaligned ring (element-wise, one grid row per chunk)
+  const int nchunks = algo == AR_ALGO_RING ? n : 1;
   switch (n) {
-    case 2: return launch_one<DT, OP, 2, slots_per_thread<2>(), kLinear>(a, n, s);
-    case 4: return launch_one<DT, OP, 4, slots_per_thread<4>(), kLinear>(a, n, s);
-    case 8: return launch_one<DT, OP, 8, slots_per_thread<8>(), kLinear>(a, n, s);
-    case 16: return launch_one<DT, OP, 16, 1, kLinear>(a, n, s);
-    default: return launch_one<DT, OP, 0, 1, kLinear>(a, n, s);
+    case 2: return launch_one<DT, OP, 2, slots_per_thread<2>(), kLinear>(a, nchunks, s);
+    case 4: return launch_one<DT, OP, 4, slots_per_thread<4>(), kLinear>(a, nchunks, s);
+    case 8: return launch_one<DT, OP, 8, slots_per_thread<8>(), kLinear>(a, nchunks, s);
+    case 16: return launch_one<DT, OP, 16, 1, kLinear>(a, nchunks, s);
+    default: return launch_one<DT, OP, 0, 1, kLinear>(a, nchunks, s);
   }
 }
 
@@ -470,8 +592,8 @@ hipError_t launch_collapsed(const RankPtrs& p, int n, int64_t count, int dtype, 
   a.count = count;
   a.n = n;
   a.vec = vec ? 1 : 0;
-  const bool tree = (algo == AR_ALGO_RHD || algo == AR_ALGO_TREE) && n > 1;
-  const int nchunks = tree ? 1 : n;
+  // the ring splits into n chunks (each folds from its own rank); every other order is one chunk
+  const int nchunks = algo == AR_ALGO_RING ? n : 1;
   a.q = count / nchunks;
   a.r = count % nchunks;
   a.rot = algo == AR_ALGO_RING ? 1 : 0;
