@@ -12,7 +12,11 @@
 //
 // Chunks are the balanced split used everywhere in the library (count/N + 1 elements for c < count%N). The 16-byte
 // vector path needs every chunk start on a slot boundary (count a multiple of N slots) and aligned buffers;
-// otherwise elements go one by one.
+// otherwise elements go one by one, with one grid row per chunk.
+//
+// The vector path runs on one front: tiles of kThreads slots of the whole buffer go round-robin to the blocks,
+// and each block walks the chunks in order, so all workgroups move through the rank buffers together (one
+// front per buffer instead of one per chunk, which MI355X's HBM serves faster).
 #include "ar_device.h"
 #include "ar_internal.h"
 
@@ -28,20 +32,39 @@ struct RsAgArgs {
   int vec;
 };
 
+// Visit, on one front, every whole slot of the balanced chunks (all chunk starts slot-aligned): calls
+// fn(c, v) for the slots v of chunk c that this thread owns. Tile t = slots [t * kThreads, (t + 1) * kThreads)
+// goes to block t mod G; a block's tiles come in increasing order, so the chunk loop is outside the tile loop
+// and c is constant (and wave-uniform) inside it.
+template <int V, typename F>
+__device__ __forceinline__ void one_front(const RsAgArgs& a, int n, int64_t count, F fn) {
+  const int64_t nslots = count / V;
+  const int64_t ntiles = (nslots + kThreads - 1) / kThreads;
+  int64_t t = blockIdx.x;
+  for (int c = 0; c < n && t < ntiles; ++c) {
+    const int64_t w0 = chunk_lo(a.q, a.r, c) / V, w1 = chunk_lo(a.q, a.r, c + 1) / V;
+    if (w0 >= w1) continue;
+    while (t < ntiles) {
+      const int64_t s0 = t * kThreads, s1 = s0 + kThreads < nslots ? s0 + kThreads : nslots;
+      if (s0 >= w1) break;
+      const int64_t v = s0 + threadIdx.x;
+      if (v >= w0 && v < w1) fn(c, v);
+      if (s1 > w1) break;
+      t += gridDim.x;
+    }
+  }
+}
+
 template <int DT, int OP, int NR>
 __global__ __launch_bounds__(kThreads) void reduce_scatter_kernel(RsAgArgs a) {
   using S = Slot<DT>;
   using Acc = typename S::Acc;
   constexpr int V = S::V;
   const int n = NR > 0 ? NR : a.n;
-  const int c = blockIdx.y;
-  const int64_t lo = chunk_lo(a.q, a.r, c), hi = chunk_lo(a.q, a.r, c + 1);
-  const int64_t stride = static_cast<int64_t>(gridDim.x) * kThreads;
-  const int64_t tid = static_cast<int64_t>(blockIdx.x) * kThreads + threadIdx.x;
-  char* out = static_cast<char*>(a.p.out[c]);
   if (a.vec) {
-    const int64_t v0 = lo / V, v1 = hi / V;
-    for (int64_t v = v0 + tid; v < v1; v += stride) {
+    one_front<V>(a, n, a.q * n + a.r, [&](int c, int64_t v) {
+      const int64_t v0 = chunk_lo(a.q, a.r, c) / V;
+      char* out = static_cast<char*>(a.p.out[c]);
       Acc acc[V], t[V];
       if constexpr (NR > 0) {
         u32x4 x[NR];
@@ -71,8 +94,13 @@ __global__ __launch_bounds__(kThreads) void reduce_scatter_kernel(RsAgArgs a) {
 #pragma unroll
       for (int e = 0; e < V; ++e) acc[e] = finalize<OP>(acc[e], n);
       st16(out + (v - v0) * 16, S::pack(acc));
-    }
+    });
   } else {
+    const int c = blockIdx.y;
+    const int64_t lo = chunk_lo(a.q, a.r, c), hi = chunk_lo(a.q, a.r, c + 1);
+    const int64_t stride = static_cast<int64_t>(gridDim.x) * kThreads;
+    const int64_t tid = static_cast<int64_t>(blockIdx.x) * kThreads + threadIdx.x;
+    char* out = static_cast<char*>(a.p.out[c]);
     for (int64_t e = lo + tid; e < hi; e += stride) {
       auto acc = widen<DT>(load_elem<DT>(a.p.in[c], e));
       for (int k = 1; k < n; ++k) {
@@ -88,19 +116,18 @@ __global__ __launch_bounds__(kThreads) void reduce_scatter_kernel(RsAgArgs a) {
 template <int ES>
 __global__ __launch_bounds__(kThreads) void all_gather_kernel(RsAgArgs a) {
   const int n = a.n;
-  const int c = blockIdx.y;
-  const int64_t lo = chunk_lo(a.q, a.r, c), hi = chunk_lo(a.q, a.r, c + 1);
-  const int64_t stride = static_cast<int64_t>(gridDim.x) * kThreads;
-  const int64_t tid = static_cast<int64_t>(blockIdx.x) * kThreads + threadIdx.x;
-  const char* in = static_cast<const char*>(a.p.in[c]);
   if (a.vec) {
     constexpr int V = 16 / ES;
-    const int64_t v0 = lo / V, v1 = hi / V;
-    for (int64_t v = v0 + tid; v < v1; v += stride) {
-      const u32x4 w = ld16(in + (v - v0) * 16);
+    one_front<V>(a, n, a.q * n + a.r, [&](int c, int64_t v) {
+      const u32x4 w = ld16(static_cast<const char*>(a.p.in[c]) + (v - chunk_lo(a.q, a.r, c) / V) * 16);
       for (int r = 0; r < n; ++r) st16(static_cast<char*>(a.p.out[r]) + v * 16, w);
-    }
+    });
   } else {
+    const int c = blockIdx.y;
+    const int64_t lo = chunk_lo(a.q, a.r, c), hi = chunk_lo(a.q, a.r, c + 1);
+    const int64_t stride = static_cast<int64_t>(gridDim.x) * kThreads;
+    const int64_t tid = static_cast<int64_t>(blockIdx.x) * kThreads + threadIdx.x;
+    const char* in = static_cast<const char*>(a.p.in[c]);
     for (int64_t e = lo + tid; e < hi; e += stride) {
       if constexpr (ES == 4) {
         const uint32_t w = reinterpret_cast<const uint32_t*>(in)[e - lo];
@@ -113,18 +140,25 @@ __global__ __launch_bounds__(kThreads) void all_gather_kernel(RsAgArgs a) {
   }
 }
 
-dim3 grid_for(int64_t per_chunk_slots, int n) {
-  int64_t want = (per_chunk_slots + kThreads - 1) / kThreads;
-  int64_t cap = (static_cast<int64_t>(cu_count()) * 4 + n - 1) / n;
+// Vector path: one row of min(tiles, 4 per CU) blocks over the whole buffer. Element path: one row per chunk.
+dim3 grid_for(const RsAgArgs& a, int V) {
+  if (a.vec) {
+    const int64_t tiles = ((a.q * a.n + a.r) / V + kThreads - 1) / kThreads;
+    int64_t g = static_cast<int64_t>(cu_count()) * 4;
+    if (g > tiles) g = tiles;
+    if (g < 1) g = 1;
+    return dim3(static_cast<unsigned>(g), 1);
+  }
+  int64_t want = (a.q + 1 + kThreads - 1) / kThreads;
+  int64_t cap = (static_cast<int64_t>(cu_count()) * 4 + a.n - 1) / a.n;
   int64_t bx = want < cap ? want : cap;
   if (bx < 1) bx = 1;
-  return dim3(static_cast<unsigned>(bx), static_cast<unsigned>(n));
+  return dim3(static_cast<unsigned>(bx), static_cast<unsigned>(a.n));
 }
 
 template <int DT, int OP>
 hipError_t rs_n(const RsAgArgs& a, hipStream_t s) {
-  constexpr int V = Traits<DT>::kVec;
-  const dim3 g = grid_for(a.vec ? (a.q + V) / V : a.q + 1, a.n);
+  const dim3 g = grid_for(a, Traits<DT>::kVec);
   switch (a.n) {
     case 2: hipLaunchKernelGGL((reduce_scatter_kernel<DT, OP, 2>), g, dim3(kThreads), 0, s, a); break;
     case 4: hipLaunchKernelGGL((reduce_scatter_kernel<DT, OP, 4>), g, dim3(kThreads), 0, s, a); break;
@@ -173,7 +207,7 @@ hipError_t launch_reduce_scatter(const RankPtrs& p, int n, int64_t count, int dt
 hipError_t launch_all_gather(const RankPtrs& p, int n, int64_t count, int esize, bool vec, hipStream_t s) {
   const int V = 16 / esize;
   const RsAgArgs a = make_args(p, n, count, vec, V);
-  const dim3 g = grid_for(a.vec ? (a.q + V) / V : a.q + 1, n);
+  const dim3 g = grid_for(a, V);
   if (esize == 4) hipLaunchKernelGGL((all_gather_kernel<4>), g, dim3(kThreads), 0, s, a);
   else hipLaunchKernelGGL((all_gather_kernel<2>), g, dim3(kThreads), 0, s, a);
   return hipGetLastError();
