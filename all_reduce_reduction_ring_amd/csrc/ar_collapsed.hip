@@ -22,8 +22,9 @@
 // power of two below n. The blocks of N's binary expansion are perfect trees over consecutive ranks, largest
 // first, folded right to left; the pass evaluates that in registers for any N.
 //
-// Layout: the ring on 16-byte aligned buffers runs the one-front kernel below (tiles of the whole buffer, each
-// folded from the rank of the chunk it lies in). Otherwise grid.y = chunk c (the unaligned ring, element-wise) or
+// Layout: the ring on 16-byte aligned buffers of at least a grid of tiles runs the one-front kernel below (tiles
+// of the whole buffer, each folded from the rank of the chunk it lies in). Otherwise grid.y = chunk c (the ring:
+// small or unaligned buffers) or
 // 1 (rank order and the trees, whose order does not depend on the chunk), and grid.x strides over the chunk's
 // 16-byte slots; a chunk whose start or end is not slot-aligned has its few edge elements done element-wise by
 // block x = 0.
@@ -304,7 +305,9 @@ __global__ __launch_bounds__(kThreads) void ring_front_kernel(CollapsedArgs a) {
   // loop walks the chunks (the rotated rank pointers are fixed inside it), the inner one the tiles. A tile that
   // reaches past the chunk's last whole slot is kept for the next chunk.
   int64_t t = blockIdx.x;
-  for (int cc = 0; cc < n && t < ntiles; ++cc) {
+  int c0 = 0;  // chunks that end before the block's first tile have no work for it
+  while (c0 + 1 < n && chunk_lo(a.q, a.r, c0 + 1) <= t * TS * V) ++c0;
+  for (int cc = c0; cc < n && t < ntiles; ++cc) {
     const int64_t lo = chunk_lo(a.q, a.r, cc), hi = chunk_lo(a.q, a.r, cc + 1);
     const int64_t w0 = (lo + V - 1) / V, w1 = hi / V;  // whole slots of chunk cc
     if (w0 >= w1) continue;
@@ -382,6 +385,18 @@ hipError_t launch_one(CollapsedArgs& a, int nchunks, hipStream_t s) {
   return hipGetLastError();
 }
 
+// The aligned ring: one front when the buffer has at least a full grid of tiles; below that the grid cannot be
+// filled anyway, and one grid row per chunk runs the chunks side by side (a single block walking N chunks in
+// turn would add N dependent memory latencies to a small message).
+template <int DT, int OP, int NR, int U>
+hipError_t front_or_chunks(CollapsedArgs& a, hipStream_t s) {
+  constexpr int V = Traits<DT>::kVec;
+  constexpr int64_t TS = static_cast<int64_t>(kThreads) * U;
+  const int64_t tiles = (a.count / V + TS - 1) / TS;
+  if (tiles >= static_cast<int64_t>(cu_count()) * blocks_per_cu<NR>()) return launch_front<DT, OP, NR, U>(a, s);
+  return launch_one<DT, OP, NR, U, kLinear>(a, a.n, s);
+}
+
 template <int DT, int OP>
 hipError_t dispatch_n(CollapsedArgs& a, int algo, hipStream_t s) {
   const int n = a.n;
@@ -407,11 +422,11 @@ hipError_t dispatch_n(CollapsedArgs& a, int algo, hipStream_t s) {
   }
   if (algo == AR_ALGO_RING && a.vec && n > 1) {
     switch (n) {
-      case 2: return launch_front<DT, OP, 2, slots_per_thread<2>()>(a, s);
-      case 4: return launch_front<DT, OP, 4, slots_per_thread<4>()>(a, s);
-      case 8: return launch_front<DT, OP, 8, slots_per_thread<8>()>(a, s);
-      case 16: return launch_front<DT, OP, 16, 1>(a, s);
-      default: return launch_front<DT, OP, 0, 1>(a, s);
+      case 2: return front_or_chunks<DT, OP, 2, slots_per_thread<2>()>(a, s);
+      case 4: return front_or_chunks<DT, OP, 4, slots_per_thread<4>()>(a, s);
+      case 8: return front_or_chunks<DT, OP, 8, slots_per_thread<8>()>(a, s);
+      case 16: return front_or_chunks<DT, OP, 16, 1>(a, s);
+      default: return front_or_chunks<DT, OP, 0, 1>(a, s);
     }
   }
   // rank order (one chunk, so one front) and the unaligned ring (element-wise, one grid row per chunk)

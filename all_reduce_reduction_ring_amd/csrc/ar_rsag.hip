@@ -41,7 +41,9 @@ __device__ __forceinline__ void one_front(const RsAgArgs& a, int n, int64_t coun
   const int64_t nslots = count / V;
   const int64_t ntiles = (nslots + kThreads - 1) / kThreads;
   int64_t t = blockIdx.x;
-  for (int c = 0; c < n && t < ntiles; ++c) {
+  int c0 = 0;  // chunks that end before the block's first tile have no work for it
+  while (c0 + 1 < n && chunk_lo(a.q, a.r, c0 + 1) <= t * kThreads * V) ++c0;
+  for (int c = c0; c < n && t < ntiles; ++c) {
     const int64_t w0 = chunk_lo(a.q, a.r, c) / V, w1 = chunk_lo(a.q, a.r, c + 1) / V;
     if (w0 >= w1) continue;
     while (t < ntiles) {

@@ -511,7 +511,7 @@ def main():
     alg_bytes = ring_bytes(N_RANKS, COUNT, 2)
     achieved = alg_bytes / t_kernel / GB
     sources = ["ar_collapsed.hip", "ar_device.h"]
-    traffic = _load_traffic("collapsed_kernel<bf16,avg,8>", sources)
+    traffic = _load_traffic("ring_front_kernel<bf16,avg,8>", sources)
     result = {
         "metric": METRIC,
         "value": algbw * bus_factor(N_RANKS),

@@ -123,6 +123,19 @@ def test_auto_runs_the_algorithm_it_reports(n, count):
     assert_bitwise(got, expect(xs, dt, ar.AR_AVG, picked), f"auto n={n} count={count} -> {picked}")
 
 
+@pytest.mark.parametrize("n", [2, 3, 4, 5, 8, 16])
+@pytest.mark.parametrize("dt", [ar.AR_F32, ar.AR_BF16])
+def test_ring_one_front_kernel_ragged(n, dt):
+    """Aligned buffers of more than a grid of tiles take the one-front ring kernel: chunk boundaries inside
+    tiles and inside 16-byte slots, and a ragged tail, every op, against the literal ring."""
+    # at least a grid of tiles for every rank count on 256 CUs (the largest need: 4,194,304 bf16 elements)
+    count = 4_500_007 + 3 * n
+    xs = _inputs(dt, n, count, 21)
+    for op in OPS:
+        got = run(xs, dt, op, ar.AR_ALGO_RING)
+        assert_bitwise(got, expect(xs, dt, op, ar.AR_ALGO_RING), f"one-front ring n={n} dt={dt} op={op}")
+
+
 # ---------------------------------------------------------------- edges: tiny, ragged, unaligned, in place
 
 
@@ -483,9 +496,12 @@ def _chunks(x_np, lo):
 
 
 @pytest.mark.parametrize("n", [1, 2, 3, 4, 5, 8])
-@pytest.mark.parametrize("count", [1, 7, 64, 4099, 65536])
+@pytest.mark.parametrize("count", [1, 7, 64, 4099, 65536, "many_tiles"])
 @pytest.mark.parametrize("dt", [ar.AR_F32, ar.AR_BF16, ar.AR_I32])
 def test_reduce_scatter_and_all_gather_match_oracle(n, count, dt):
+    if count == "many_tiles":
+        # slot-aligned chunks (the vector path) spanning several tiles per block on the one-front grid
+        count = n * (16 // (2 if dt == ar.AR_BF16 else 4)) * 150_001
     xs = _inputs(dt, n, count, 50)
     lo = ar.chunk_bounds(count, n)
     tdt = {ar.AR_F32: torch.float32, ar.AR_BF16: torch.bfloat16, ar.AR_I32: torch.int32}[dt]
