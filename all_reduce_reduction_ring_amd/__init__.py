@@ -34,7 +34,7 @@ AR_F32, AR_BF16, AR_F16, AR_I32 = 0, 1, 2, 3
 AR_SUM, AR_AVG, AR_MIN, AR_MAX = 0, 1, 2, 3
 AR_ALGO_RING, AR_ALGO_FUSED, AR_ALGO_RHD, AR_ALGO_RING_STEPWISE, AR_ALGO_RHD_STEPWISE, AR_ALGO_RING_FP8 = range(6)
 AR_ALGO_TREE, AR_ALGO_TREE_STEPWISE, AR_ALGO_AUTO = 6, 7, 8
-AR_AUTO_STEP_NS, AR_AUTO_LINK_GBPS = 1000, 153
+AR_AUTO_STEP_NS, AR_AUTO_LINK_GBPS = 1900, 153
 AR_MAX_RANKS = 64
 AR_FP8_BLOCK = 128
 

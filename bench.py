@@ -413,6 +413,28 @@ def overlap_rows(torch, ar, ins, outs, dev, reps=5):
     return out
 
 
+def alpha_beta_fit(lines, n):
+    """Least-squares fit of time = rounds * alpha + bytes / beta to the one-level-per-launch schedules' HIP-graph
+    device times (the pages' cost tables), and the tree/ring switch point of the same table with that alpha and
+    one xGMI link's bandwidth (the AR_ALGO_AUTO rule)."""
+    levels = int(np.ceil(np.log2(n)))
+    rounds = {"ring_stepwise": 2 * (n - 1), "rhd_stepwise": 2 * levels, "tree_stepwise": 2 * levels}
+    fb = {"ring_stepwise": stepwise_ring_bytes, "rhd_stepwise": stepwise_rhd_bytes,
+          "tree_stepwise": stepwise_tree_bytes}
+    a, y = [], []
+    for r in lines:
+        if r["algo"] in rounds and r.get("graph_us_per_call"):
+            a.append([rounds[r["algo"]], fb[r["algo"]](n, r["bytes_per_rank"] // 4, 4, 4)])
+            y.append(r["graph_us_per_call"] * 1e-6)
+    if len(y) < 2:
+        return None
+    (alpha, inv_beta), *_ = np.linalg.lstsq(np.array(a), np.array(y), rcond=None)
+    link = 153e9
+    return {"fit": "steps * alpha + bytes / beta, stepwise schedules, HIP-graph device time", "points": len(y),
+            "alpha_us": float(alpha) * 1e6, "beta_GBps": float(1.0 / inv_beta) / GB,
+            "tree_below_bytes_at_153GBps_link": float(n * max(0, n - 1 - levels) * alpha * link)}
+
+
 def sweep(torch, ar, dev, out_path, reps=20, max_log2=30):
     """Message-size sweep: N = 8 fp32 ranks, sum, 8 B ... 1 GiB per rank, ring vs halving-doubling vs rank order
     vs the round-per-launch schedules. Below 1 GiB of total traffic, ceil(1 GiB / (2 N S)) buffer sets (at most
@@ -460,6 +482,9 @@ def sweep(torch, ar, dev, out_path, reps=20, max_log2=30):
             log(f"sweep {S} B done")
             del bufs
             torch.cuda.empty_cache()
+        fit = alpha_beta_fit(lines, n)
+        if fit:
+            f.write(json.dumps(fit) + "\n")
     return lines
 
 

@@ -115,9 +115,11 @@ enum ar_algo {
     AR_ALGO_AUTO = 8
 };
 
-/* Cost-model constants of AR_ALGO_AUTO: per-step latency (ns) and per-link bandwidth (GB/s) of one xGMI hop
- * between MI355X GPUs. N=8 switches from tree to ring at 4,896,000 bytes; N <= 3 always takes the ring. */
-#define AR_AUTO_STEP_NS 1000
+/* Cost-model constants of AR_ALGO_AUTO. AR_AUTO_STEP_NS: latency of one schedule step, fitted (least squares,
+ * time = steps * alpha + bytes / beta) to the one-level-per-launch ring, halving-doubling and tree schedules of
+ * an N=8 fp32 size sweep on MI355X under HIP-graph replay (1.89 us). AR_AUTO_LINK_GBPS: bandwidth of one xGMI
+ * link between MI355X GPUs. N=8 switches from tree to ring at 9,302,400 bytes; N <= 3 always takes the ring. */
+#define AR_AUTO_STEP_NS 1900
 #define AR_AUTO_LINK_GBPS 153
 
 /* The algorithm AR_ALGO_AUTO runs for this call shape (AR_ALGO_TREE or AR_ALGO_RING), or -AR_ERR_INVALID for

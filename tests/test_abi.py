@@ -162,8 +162,8 @@ def test_auto_algo_follows_cost_table(n, dtype, es):
 
 
 def test_auto_algo_examples_and_errors():
-    assert ar.ar_auto_algo(8, 2_447_999, ar.AR_BF16) == ar.AR_ALGO_TREE   # 4,895,998 bytes
-    assert ar.ar_auto_algo(8, 2_448_000, ar.AR_BF16) == ar.AR_ALGO_RING   # 4,896,000 bytes
+    assert ar.ar_auto_algo(8, 4_651_199, ar.AR_BF16) == ar.AR_ALGO_TREE   # 9,302,398 bytes
+    assert ar.ar_auto_algo(8, 4_651_200, ar.AR_BF16) == ar.AR_ALGO_RING   # 9,302,400 bytes
     assert ar.ar_auto_algo(8, 134_217_728, ar.AR_BF16) == ar.AR_ALGO_RING
     with pytest.raises(ar.ArError):
         ar.ar_auto_algo(0, 10, ar.AR_F32)
