@@ -142,11 +142,12 @@ __global__ __launch_bounds__(kThreads) void all_gather_kernel(RsAgArgs a) {
   }
 }
 
-// Vector path: one row of min(tiles, 4 per CU) blocks over the whole buffer. Element path: one row per chunk.
+// Vector path: one row of min(tiles, 2 per CU) blocks over the whole buffer (2 per CU measured 10% faster than
+// 1, 4 or 8 for the reduce-scatter on MI355X, 2.5% for the all-gather). Element path: one row per chunk.
 dim3 grid_for(const RsAgArgs& a, int V) {
   if (a.vec) {
     const int64_t tiles = ((a.q * a.n + a.r) / V + kThreads - 1) / kThreads;
-    int64_t g = static_cast<int64_t>(cu_count()) * 4;
+    int64_t g = static_cast<int64_t>(cu_count()) * 2;
     if (g > tiles) g = tiles;
     if (g < 1) g = 1;
     return dim3(static_cast<unsigned>(g), 1);
