@@ -456,7 +456,8 @@ hipError_t dispatch_op(CollapsedArgs& a, int op, int algo, hipStream_t s) {
 // buffer, count_s a multiple of N * (16 / element size), so each of its N chunks is whole 16-byte slots. Each
 // segment is reduced exactly as a one-segment call would reduce it: chunk c of segment s folds from rank c.
 // The work is cut into tiles of kThreads * U slots of one chunk; tile_pre holds the running tile count per
-// segment, and tile t goes to block t mod G.
+// segment, and tile t goes to block t mod G. A segment's tiles run chunk after chunk, so the grid moves through
+// each segment as one front.
 constexpr int kMaxSegments = 64;  // per launch; keeps the arguments under the 4 KiB kernel-argument limit
 
 struct SegmentArgs {
@@ -477,8 +478,9 @@ __global__ __launch_bounds__(kThreads) void segment_kernel(SegmentArgs a) {
   for (int64_t t = blockIdx.x; t < total; t += gridDim.x) {
     while (a.tile_pre[s + 1] <= t) ++s;  // tiles are visited in increasing order, so s only moves forward
     const int64_t lt = t - a.tile_pre[s];
-    const int c = static_cast<int>(lt % n);
-    const int64_t k = lt / n;
+    const int64_t per_chunk = (a.tile_pre[s + 1] - a.tile_pre[s]) / n;  // tiles per chunk of this segment
+    const int c = static_cast<int>(lt / per_chunk);
+    const int64_t k = lt - c * per_chunk;
     const int64_t v0 = a.start[s] / V + c * a.chunk_slots[s];  // first slot of chunk c
     const int64_t vend = v0 + a.chunk_slots[s];
     const int start = a.f.rot ? c : 0;
