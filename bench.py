@@ -500,8 +500,8 @@ def main():
     p.add_argument("--sweep-max-log2", type=int, default=30)
     args = p.parse_args()
     if args.gpus != 1:
-        print(f"bench.py: this build runs on one GPU; --gpus {args.gpus} is not supported (the N ranks are "
-              "simulated as separate buffers on one MI355X)", file=sys.stderr)
+        print(f"bench.py: --gpus {args.gpus} is not supported: the library runs all N ranks as separate buffers "
+              "on one MI355X, so only --gpus 1 is measured", file=sys.stderr)
         sys.exit(2)
 
     import torch
