@@ -21,6 +21,10 @@ LIB = os.path.join(HERE, "libar.so")
 ARCH = "gfx950"
 
 SOURCES = ["ar_api.hip", "ar_collapsed.hip", "ar_stepwise.hip", "ar_bucket.hip", "ar_fp8.hip", "ar_tensors.hip", "ar_rsag.hip"]
+# ar_collapsed.hip holds several hundred kernel instances; it is compiled once per element type (AR_F32 = 0 ..
+# AR_I32 = 3), so the four parts build in parallel.
+UNITS = [(src, []) for src in SOURCES if src != "ar_collapsed.hip"] + [
+    ("ar_collapsed.hip", [f"-DAR_COLLAPSED_DTYPE={dt}"]) for dt in range(4)]
 
 CFLAGS = [
     f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC", "-ffp-contract=off",
@@ -37,9 +41,11 @@ def hipcc() -> str:
     raise RuntimeError("hipcc not found: the HIP toolchain is required to build libar")
 
 
-def _compile(src: str) -> str:
-    obj = os.path.join(BUILD, os.path.splitext(src)[0] + ".o")
-    cmd = [hipcc(), "-c", *CFLAGS, "-o", obj, os.path.join(CSRC, src)]
+def _compile(unit) -> str:
+    src, defs = unit
+    tag = "".join("_" + d.split("=")[-1] for d in defs)
+    obj = os.path.join(BUILD, os.path.splitext(src)[0] + tag + ".o")
+    cmd = [hipcc(), "-c", *CFLAGS, *defs, "-o", obj, os.path.join(CSRC, src)]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"hipcc failed for {src}:\n{r.stdout}\n{r.stderr}")
@@ -52,11 +58,14 @@ def _compile(src: str) -> str:
 def build(jobs: int | None = None) -> str:
     """Compile every source and link libar.so; returns the library path."""
     os.makedirs(BUILD, exist_ok=True)
-    jobs = jobs or min(len(SOURCES), max(1, (os.cpu_count() or 4)))
+    jobs = jobs or min(len(UNITS), max(1, (os.cpu_count() or 4)))
+    # the slowest units first, so they are not left running alone at the end
+    order = sorted(UNITS, key=lambda u: u[0] not in ("ar_collapsed.hip", "ar_tensors.hip"))
     with concurrent.futures.ThreadPoolExecutor(max_workers=jobs) as ex:
-        objs = list(ex.map(_compile, SOURCES))
+        objs = list(ex.map(_compile, order))
     tmp = LIB + ".tmp"
-    cmd = [hipcc(), "-shared", f"--offload-arch={ARCH}", "-fPIC", "-o", tmp, *objs]
+    # -z defs: an unresolved symbol (say a missing per-type part) fails the link instead of the first call
+    cmd = [hipcc(), "-shared", f"--offload-arch={ARCH}", "-fPIC", "-Wl,-z,defs", "-o", tmp, *objs]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"link failed:\n{r.stdout}\n{r.stderr}")

@@ -28,6 +28,32 @@ int cu_count() {
 
 }  // namespace ar
 
+namespace ar {
+
+hipError_t launch_collapsed(const RankPtrs& p, int n, int64_t count, int dtype, int op, int algo, bool vec,
+                            hipStream_t s) {
+  switch (dtype) {
+    case AR_F32: return launch_collapsed_dt<AR_F32>(p, n, count, op, algo, vec, s);
+    case AR_BF16: return launch_collapsed_dt<AR_BF16>(p, n, count, op, algo, vec, s);
+    case AR_F16: return launch_collapsed_dt<AR_F16>(p, n, count, op, algo, vec, s);
+    case AR_I32: return launch_collapsed_dt<AR_I32>(p, n, count, op, algo, vec, s);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+hipError_t launch_segments(const RankPtrs& p, int n, const int64_t* counts, int nseg, int dtype, int op, int algo,
+                           hipStream_t s) {
+  switch (dtype) {
+    case AR_F32: return launch_segments_dt<AR_F32>(p, n, counts, nseg, op, algo, s);
+    case AR_BF16: return launch_segments_dt<AR_BF16>(p, n, counts, nseg, op, algo, s);
+    case AR_F16: return launch_segments_dt<AR_F16>(p, n, counts, nseg, op, algo, s);
+    case AR_I32: return launch_segments_dt<AR_I32>(p, n, counts, nseg, op, algo, s);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+}  // namespace ar
+
 namespace {
 
 thread_local ar_call_record g_last;

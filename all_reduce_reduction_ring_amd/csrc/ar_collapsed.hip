@@ -558,9 +558,15 @@ static_assert(sizeof(SegmentArgs) <= 4096, "kernel arguments must fit in 4 KiB")
 
 }  // namespace
 
-hipError_t launch_segments(const RankPtrs& p, int n, const int64_t* counts, int nseg, int dtype, int op, int algo,
-                           hipStream_t s) {
-  const int V = (dtype == AR_BF16 || dtype == AR_F16) ? 8 : 4;
+#ifndef AR_COLLAPSED_DTYPE
+#error "ar_collapsed.hip is compiled once per element type: -DAR_COLLAPSED_DTYPE=<ar_dtype value>"
+#endif
+constexpr int kDT = AR_COLLAPSED_DTYPE;
+
+template <>
+hipError_t launch_segments_dt<kDT>(const RankPtrs& p, int n, const int64_t* counts, int nseg, int op, int algo,
+                                   hipStream_t s) {
+  constexpr int V = Traits<kDT>::kVec;
   // must match the U each template above is instantiated with: 8/N for N = 2 and 4 (every shape), else 1
   const int U = (n == 2 || n == 4) ? 8 / n : 1;
   const int64_t TS = static_cast<int64_t>(kThreads) * U;
@@ -587,23 +593,16 @@ hipError_t launch_segments(const RankPtrs& p, int n, const int64_t* counts, int 
     }
     a.nseg = m;
     hipError_t e = hipSuccess;
-    if (a.tile_pre[m] > 0) {
-      switch (dtype) {
-        case AR_F32: e = segments_op<AR_F32>(a, op, algo, s); break;
-        case AR_BF16: e = segments_op<AR_BF16>(a, op, algo, s); break;
-        case AR_F16: e = segments_op<AR_F16>(a, op, algo, s); break;
-        case AR_I32: e = segments_op<AR_I32>(a, op, algo, s); break;
-        default: e = hipErrorInvalidValue;
-      }
-    }
+    if (a.tile_pre[m] > 0) e = segments_op<kDT>(a, op, algo, s);
     if (e != hipSuccess) return e;
     done += m;
   }
   return hipSuccess;
 }
 
-hipError_t launch_collapsed(const RankPtrs& p, int n, int64_t count, int dtype, int op, int algo, bool vec,
-                            hipStream_t s) {
+template <>
+hipError_t launch_collapsed_dt<kDT>(const RankPtrs& p, int n, int64_t count, int op, int algo, bool vec,
+                                    hipStream_t s) {
   CollapsedArgs a;
   a.p = p;
   a.count = count;
@@ -614,13 +613,7 @@ hipError_t launch_collapsed(const RankPtrs& p, int n, int64_t count, int dtype, 
   a.q = count / nchunks;
   a.r = count % nchunks;
   a.rot = algo == AR_ALGO_RING ? 1 : 0;
-  switch (dtype) {
-    case AR_F32: return dispatch_op<AR_F32>(a, op, algo, s);
-    case AR_BF16: return dispatch_op<AR_BF16>(a, op, algo, s);
-    case AR_F16: return dispatch_op<AR_F16>(a, op, algo, s);
-    case AR_I32: return dispatch_op<AR_I32>(a, op, algo, s);
-    default: return hipErrorInvalidValue;
-  }
+  return dispatch_op<kDT>(a, op, algo, s);
 }
 
 }  // namespace ar

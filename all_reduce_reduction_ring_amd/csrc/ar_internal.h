@@ -26,6 +26,14 @@ hipError_t launch_collapsed(const RankPtrs& p, int n, int64_t count, int dtype, 
 hipError_t launch_segments(const RankPtrs& p, int n, const int64_t* counts, int nseg, int dtype, int op, int algo,
                            hipStream_t s);
 
+// The same two for one element type: ar_collapsed.hip is compiled once per type (its many kernel instances then
+// build in parallel) and defines the specialisation for its type; the two functions above pick one.
+template <int DT>
+hipError_t launch_collapsed_dt(const RankPtrs& p, int n, int64_t count, int op, int algo, bool vec, hipStream_t s);
+template <int DT>
+hipError_t launch_segments_dt(const RankPtrs& p, int n, const int64_t* counts, int nseg, int op, int algo,
+                              hipStream_t s);
+
 // Bucketed all-reduce from and to per-tensor buffers (device descriptor and pointer tables).
 hipError_t launch_tensors(const ar_tensor_desc* d_descs, const void* const* d_in, void* const* d_out, int ntensors,
                           int n, int dtype, int op, int algo, hipStream_t s);
