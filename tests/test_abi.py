@@ -267,3 +267,22 @@ def test_reduce_scatter_all_gather_validation():
     nfull = (ctypes.c_void_p * 2)(base, 0)
     assert L.ar_reduce_scatter(nfull, nul, 2, 1, ar.AR_F32, ar.AR_SUM, None) == ar.AR_ERR_INVALID
     assert L.ar_all_gather((ctypes.c_void_p * 2)(0, 0), full, 2, 1, ar.AR_F32, None) == ar.AR_ERR_INVALID
+
+
+def test_last_call_record_is_per_thread():
+    """Each host thread sees only its own last call (the record is thread-local)."""
+    import threading
+    seen = {}
+
+    def worker(k):
+        for _ in range(50):
+            _call(2 + k, 10, dtype=7)  # invalid dtype: validated and recorded, nothing launched
+        seen[k] = ar.ar_last_call()
+
+    threads = [threading.Thread(target=worker, args=(k,)) for k in range(4)]
+    for t in threads:
+        t.start()
+    for t in threads:
+        t.join()
+    for k in range(4):
+        assert seen[k]["nranks"] == 2 + k and seen[k]["status"] == ar.AR_ERR_INVALID
