@@ -472,30 +472,49 @@ template <int DT, int OP, int NR, int U, int SHAPE>
 __global__ __launch_bounds__(kThreads) void segment_kernel(SegmentArgs a) {
   constexpr int V = Traits<DT>::kVec;
   constexpr int64_t TS = static_cast<int64_t>(kThreads) * U;
+  constexpr int NT = NR > 0 ? NR : 1;
   const int n = NR > 0 ? NR : a.f.n;
   const int64_t total = a.tile_pre[a.nseg];
-  int s = 0;
-  for (int64_t t = blockIdx.x; t < total; t += gridDim.x) {
-    while (a.tile_pre[s + 1] <= t) ++s;  // tiles are visited in increasing order, so s only moves forward
-    const int64_t lt = t - a.tile_pre[s];
-    const int64_t per_chunk = (a.tile_pre[s + 1] - a.tile_pre[s]) / n;  // tiles per chunk of this segment
-    const int c = static_cast<int>(lt / per_chunk);
-    const int64_t k = lt - c * per_chunk;
-    const int64_t v0 = a.start[s] / V + c * a.chunk_slots[s];  // first slot of chunk c
-    const int64_t vend = v0 + a.chunk_slots[s];
-    const int start = a.f.rot ? c : 0;
-    int64_t v = v0 + k * TS + threadIdx.x;
-    u32x4 w[U];
+  // The block's tiles t = blockIdx.x + k G in increasing order: segment by segment, and inside a segment chunk
+  // by chunk, so everything per segment and per chunk (tile counts, chunk index, the rotated rank pointers) is
+  // worked out once, outside the tile loop.
+  int64_t t = blockIdx.x;
+  for (int sg = 0; sg < a.nseg && t < total; ++sg) {
+    const int64_t seg0 = a.tile_pre[sg], seg1 = a.tile_pre[sg + 1];
+    if (t >= seg1) continue;
+    const int64_t per_chunk = (seg1 - seg0) / n;  // tiles per chunk (>= 1 here: the segment has tiles)
+    const int64_t cslots = a.chunk_slots[sg];
+    for (int c = static_cast<int>((t - seg0) / per_chunk); c < n && t < seg1; ++c) {
+      const int64_t c1 = seg0 + (c + 1) * per_chunk;  // first tile of the next chunk
+      if (t >= c1) continue;                          // the stride stepped over this chunk
+      const int64_t v0 = a.start[sg] / V + c * cslots;  // first slot of chunk c
+      const int64_t vend = v0 + cslots;
+      const int start = a.f.rot ? c : 0;
+      const char* rot[NT];
 #pragma unroll
-    for (int u = 0; u < U; ++u) {
-      const int64_t vv = v + u * kThreads;
-      if (vv < vend) w[u] = fold_slot<DT, OP, NR, SHAPE>(a.f, start, vv * 16);
-    }
+      for (int k = 0; k < NT; ++k) {
+        int r = start + k;
+        r = r >= n ? r - n : r;
+        rot[k] = static_cast<const char*>(a.f.p.in[r]);
+      }
+      for (; t < c1; t += gridDim.x) {
+        const int64_t v = v0 + (t - seg0 - c * per_chunk) * TS + threadIdx.x;
+        u32x4 w[U];
 #pragma unroll
-    for (int u = 0; u < U; ++u) {
-      const int64_t vv = v + u * kThreads;
-      if (vv < vend)
-        for (int r = 0; r < n; ++r) st16(static_cast<char*>(a.f.p.out[r]) + vv * 16, w[u]);
+        for (int u = 0; u < U; ++u) {
+          const int64_t vv = v + u * kThreads;
+          if (vv < vend) {
+            if constexpr (SHAPE == kLinear && NR > 0) w[u] = fold_ptrs<DT, OP, NR>(rot, vv * 16);
+            else w[u] = fold_slot<DT, OP, NR, SHAPE>(a.f, start, vv * 16);
+          }
+        }
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+          const int64_t vv = v + u * kThreads;
+          if (vv < vend)
+            for (int r = 0; r < n; ++r) st16(static_cast<char*>(a.f.p.out[r]) + vv * 16, w[u]);
+        }
+      }
     }
   }
 }

@@ -192,8 +192,9 @@ typedef struct ar_copy_desc {
 int ar_bucket_plan(const int64_t* numels, int ntensors, int dtype, int nranks, size_t cap_bytes,
                    int32_t* bucket_of, int64_t* offset_of, int64_t* bucket_count, int* nbuckets);
 
-/* All-reduce every bucket of N flat per-rank buffers in one launch (per-bucket rings without a launch per
- * bucket). Bucket b occupies elements [sum_{b'<b} bucket_count[b'], ... + bucket_count[b]) of every rank's
+/* All-reduce every bucket of N flat per-rank buffers in one call: a bucket of 16 MiB or more per rank gets an
+ * all-reduce launch of its own, and runs of smaller buckets share launches (up to 64 buckets each) instead of paying a launch
+ * per bucket. Bucket b occupies elements [sum_{b'<b} bucket_count[b'], ... + bucket_count[b]) of every rank's
  * buffer, and is reduced exactly as ar_allreduce would reduce it alone: same balanced chunks, same fold
  * order, same epilogue, so the results are bit-identical to one ar_allreduce call per bucket.
  *   flat_in, flat_out: host arrays of nranks device pointers, 16-byte aligned, each to the sum of the

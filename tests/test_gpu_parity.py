@@ -418,6 +418,34 @@ def test_allreduce_buckets_equals_one_call_per_bucket(n, dt):
             assert_bitwise([from_dev(o, dt) for o in ins], want_flat, f"buckets in place n={n} op={op}")
 
 
+@pytest.mark.parametrize("n,dt", [(3, ar.AR_F32), (4, ar.AR_BF16)])
+def test_allreduce_buckets_mixing_own_launch_and_shared_launch_buckets(n, dt):
+    """Buckets of 16 MiB or more per rank get a launch of their own and the runs of smaller buckets between them
+    share segment launches; the result must still be one ring per bucket, in place and out of place."""
+    es = 2 if dt == ar.AR_BF16 else 4
+    unit = n * (16 // es)
+    big = ((16 << 20) // es + unit - 1) // unit * unit  # exactly 16 MiB per rank, rounded up to the unit
+    counts = np.array([unit * 5, big, unit * 7, 0, unit * 3, big + unit * 11, unit], dtype=np.int64)
+    total = int(counts.sum())
+    xs = _inputs(dt, n, total, 22)
+    starts = np.concatenate([[0], np.cumsum(counts)])
+    for op in (ar.AR_SUM, ar.AR_AVG):
+        want = [np.empty(total, dtype=NP_BITS[dt]) for _ in range(n)]
+        for b in range(len(counts)):
+            if counts[b]:
+                seg = [x.view(NP_BITS[dt])[starts[b]:starts[b + 1]].view(xs[0].dtype) for x in xs]
+                for r, w in enumerate(expect(seg, dt, op, ar.AR_ALGO_RING)):
+                    want[r][starts[b]:starts[b + 1]] = w
+        ins = [to_dev(x, dt)[1] for x in xs]
+        outs = [empty_like_dev(total, dt)[1] for _ in range(n)]
+        ar.ar_allreduce_buckets(ins, outs, counts, op, ar.AR_ALGO_RING)
+        torch.cuda.synchronize()
+        assert_bitwise([from_dev(o, dt) for o in outs], want, f"mixed buckets n={n} op={op}")
+        ar.ar_allreduce_buckets(ins, ins, counts, op, ar.AR_ALGO_RING)
+        torch.cuda.synchronize()
+        assert_bitwise([from_dev(o, dt) for o in ins], want, f"mixed buckets in place n={n} op={op}")
+
+
 @pytest.mark.parametrize("algo", [ar.AR_ALGO_RING, ar.AR_ALGO_RHD, ar.AR_ALGO_RING_STEPWISE, ar.AR_ALGO_RING_FP8,
                                   ar.AR_ALGO_TREE_STEPWISE])
 def test_hip_graph_capture_replays_match_eager(algo):
