@@ -1,7 +1,7 @@
 """GPU parity at the workloads' full sizes, in the launch configuration the benchmark times, against the oracle.
 
 - headline: 8 ranks x 134,217,728 bf16 (256 MiB each), fp32 ring-order sum, /8, bf16 out: every element of
-  every rank, bit for bit.
+  every rank, bit for bit; the same inputs through reduce-scatter + all-gather and through the binomial tree.
 - compressed ring: 8 ranks x 67,108,864 bf16 with 0.1% outliers x100, E4M3 blocks of 128: every element.
 - largest sweep point: 8 ranks x 268,435,456 fp32 (1 GiB each): ring and ring-stepwise, every element; the
   rank-order and halving-doubling variants (which do not depend on chunk positions) on 2^20 sampled elements,
@@ -56,6 +56,32 @@ def test_headline_eight_ranks_256MiB_bf16_avg():
     _same_on_all_ranks(outs)
     for r in range(n):
         np.testing.assert_array_equal(_down_bits(outs[r]), want[r])
+
+
+@pytest.mark.timeout(600)
+def test_headline_size_reduce_scatter_all_gather_and_tree():
+    """The headline inputs through reduce-scatter then all-gather (must equal the ring all-reduce, every element)
+    and through the binomial tree (against its own oracle, every element)."""
+    n, count = 8, 134_217_728
+    host = _par(lambda r: inputs.normal_bf16((2, r), count), range(n))
+    ins = _up(host, torch.bfloat16)
+    lo = ar.chunk_bounds(count, n)
+    parts = [torch.empty(int(lo[c + 1] - lo[c]), dtype=torch.bfloat16, device=DEV) for c in range(n)]
+    outs = [torch.empty_like(t) for t in ins]
+    ar.ar_reduce_scatter(ins, parts, ar.AR_AVG)
+    ar.ar_all_gather(parts, outs)
+    torch.cuda.synchronize()
+    want = oracle.ring_allreduce(host, oracle.BF16, oracle.AVG)[0]
+    for c in range(n):
+        np.testing.assert_array_equal(_down_bits(parts[c]), want[lo[c]:lo[c + 1]])
+    _same_on_all_ranks(outs)
+    np.testing.assert_array_equal(_down_bits(outs[3]), want)
+    del parts, want
+    ar.ar_allreduce(ins, outs, ar.AR_AVG, ar.AR_ALGO_TREE)
+    torch.cuda.synchronize()
+    del ins
+    _same_on_all_ranks(outs)
+    np.testing.assert_array_equal(_down_bits(outs[6]), oracle.tree_allreduce(host, oracle.BF16, oracle.AVG)[0])
 
 
 @pytest.mark.timeout(600)
