@@ -28,11 +28,11 @@ constexpr int kSlotsPerThread = kTileBytes / 16 / kThreads;
 __device__ __forceinline__ void copy_elems(const ar_copy_desc& d, int64_t e0, int64_t e1, int es) {
   for (int64_t e = e0 + threadIdx.x; e < e1; e += kThreads) {
     if (e < d.numel) {
-      if (es == 4) static_cast<uint32_t*>(d.dst)[e] = static_cast<const uint32_t*>(d.src)[e];
-      else static_cast<uint16_t*>(d.dst)[e] = static_cast<const uint16_t*>(d.src)[e];
+      if (es == 4) gptr<uint32_t>(d.dst)[e] = gptr<uint32_t>(d.src)[e];
+      else gptr<uint16_t>(d.dst)[e] = gptr<uint16_t>(d.src)[e];
     } else {
-      if (es == 4) static_cast<uint32_t*>(d.dst)[e] = 0u;
-      else static_cast<uint16_t*>(d.dst)[e] = 0u;
+      if (es == 4) gptr<uint32_t>(d.dst)[e] = 0u;
+      else gptr<uint16_t>(d.dst)[e] = 0u;
     }
   }
 }

@@ -134,24 +134,29 @@ template <int DT> struct Slot {
   }
 };
 
+// Every buffer the library reads or writes is device (global) memory. Saying so lets the compiler emit global
+// loads and stores also through pointers it read from device memory (descriptor and pointer tables), where it
+// cannot infer the address space and would otherwise fall back to flat accesses.
+#define AR_GLOBAL __attribute__((address_space(1)))
+template <typename T> __device__ __forceinline__ const AR_GLOBAL T* gptr(const void* p) {
+  return (const AR_GLOBAL T*)(p);
+}
+template <typename T> __device__ __forceinline__ AR_GLOBAL T* gptr(void* p) { return (AR_GLOBAL T*)(p); }
+
 // Scalar element access by element index on raw storage.
 template <int DT> __device__ __forceinline__ uint32_t load_elem(const void* base, int64_t e) {
-  if constexpr (Traits<DT>::kSize == 4) return static_cast<const uint32_t*>(base)[e];
-  else return static_cast<const uint16_t*>(base)[e];
+  if constexpr (Traits<DT>::kSize == 4) return gptr<uint32_t>(base)[e];
+  else return gptr<uint16_t>(base)[e];
 }
 template <int DT> __device__ __forceinline__ void store_elem(void* base, int64_t e, uint32_t bits) {
-  if constexpr (Traits<DT>::kSize == 4) static_cast<uint32_t*>(base)[e] = bits;
-  else static_cast<uint16_t*>(base)[e] = static_cast<uint16_t>(bits);
+  if constexpr (Traits<DT>::kSize == 4) gptr<uint32_t>(base)[e] = bits;
+  else gptr<uint16_t>(base)[e] = static_cast<uint16_t>(bits);
 }
 
 // Streaming 16-byte loads and stores. Each element is read once and written once per call, so the data
 // is marked non-temporal to keep it from displacing anything useful in the caches.
-__device__ __forceinline__ u32x4 ld16(const void* p) {
-  return __builtin_nontemporal_load(static_cast<const u32x4*>(p));
-}
-__device__ __forceinline__ void st16(void* p, const u32x4& v) {
-  __builtin_nontemporal_store(v, static_cast<u32x4*>(p));
-}
+__device__ __forceinline__ u32x4 ld16(const void* p) { return __builtin_nontemporal_load(gptr<u32x4>(p)); }
+__device__ __forceinline__ void st16(void* p, const u32x4& v) { __builtin_nontemporal_store(v, gptr<u32x4>(p)); }
 
 // Balanced chunk split: chunk c = [c*q + min(c, r), ...) with q = count / N, r = count % N.
 __device__ __forceinline__ int64_t chunk_lo(int64_t q, int64_t r, int64_t c) { return c * q + (c < r ? c : r); }
