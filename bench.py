@@ -137,6 +137,21 @@ def copy_ceiling(torch, ins, outs, reps=10):
     return nbytes / (np.mean(ms) * 1e-3) / GB
 
 
+def write_ceiling(torch, ins, reps=10):
+    """Context for the roofline on this machine: a plain write (torch fill_) of the headline's N*S bytes, median of
+    10 after warm-up calls. Beside the copy above it brackets the all-reduce, which mixes reads and writes half
+    and half."""
+    dst = torch.empty(sum(t.numel() for t in ins) * ins[0].element_size() // 4, dtype=torch.float32,
+                      device=ins[0].device)
+    write = lambda: dst.fill_(0.5)
+    for _ in range(3):  # first calls load the kernel
+        write()
+    ms = Timer(torch).run(write, reps)
+    nbytes = dst.numel() * dst.element_size()
+    del dst
+    return nbytes / (np.median(ms) * 1e-3) / GB
+
+
 def cpu_baseline(host, budget_s=10.0, max_reps=5):
     """The oracle's literal ring on the headline inputs, repeated until ~budget_s of CPU time."""
     import oracle as _o
@@ -563,6 +578,7 @@ def main():
     }
     if not args.headline_only:
         result["copy_ceiling_GBps"] = copy_ceiling(torch, ins, outs)
+        result["write_ceiling_GBps"] = write_ceiling(torch, ins)
         log("overlap row")
         result["overlap"] = overlap_rows(torch, ar, ins, outs, dev)
         result["rows"] = other_rows(torch, ar, inputs, ins, outs, dev, reps=max(5, args.steps // 2), host=host)
