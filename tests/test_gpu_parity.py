@@ -136,6 +136,15 @@ def test_ring_one_front_kernel_ragged(n, dt):
         assert_bitwise(got, expect(xs, dt, op, ar.AR_ALGO_RING), f"one-front ring n={n} dt={dt} op={op}")
 
 
+def test_ring_one_front_kernel_sixty_four_ranks():
+    """The largest rank count on the one-front kernel (rank count known only at run time), ragged count."""
+    n, count = 64, 2_200_007  # above a grid of tiles for a run-time rank count (2,097,152 fp32 elements)
+    xs = _inputs(ar.AR_F32, n, count, 23)
+    for op in (ar.AR_SUM, ar.AR_MAX):
+        got = run(xs, ar.AR_F32, op, ar.AR_ALGO_RING)
+        assert_bitwise(got, expect(xs, ar.AR_F32, op, ar.AR_ALGO_RING), f"one-front ring n=64 op={op}")
+
+
 # ---------------------------------------------------------------- edges: tiny, ragged, unaligned, in place
 
 
