@@ -533,12 +533,13 @@ def _chunks(x_np, lo):
 
 
 @pytest.mark.parametrize("n", [1, 2, 3, 4, 5, 8])
-@pytest.mark.parametrize("count", [1, 7, 64, 4099, 65536, "many_tiles"])
+@pytest.mark.parametrize("count", [1, 7, 64, 4099, 65536, "many_tiles", "many_tiles_ragged"])
 @pytest.mark.parametrize("dt", [ar.AR_F32, ar.AR_BF16, ar.AR_I32])
 def test_reduce_scatter_and_all_gather_match_oracle(n, count, dt):
-    if count == "many_tiles":
-        # slot-aligned chunks (the vector path) spanning several tiles per block on the one-front grid
-        count = n * (16 // (2 if dt == ar.AR_BF16 else 4)) * 150_001
+    if count in ("many_tiles", "many_tiles_ragged"):
+        # several tiles per block on the one-front grid; slot-aligned chunk starts, or starts inside slots (the
+        # shifted vector path, plus each chunk's edge elements)
+        count = n * (16 // (2 if dt == ar.AR_BF16 else 4)) * 150_001 + (13 if count == "many_tiles_ragged" else 0)
     xs = _inputs(dt, n, count, 50)
     lo = ar.chunk_bounds(count, n)
     tdt = {ar.AR_F32: torch.float32, ar.AR_BF16: torch.bfloat16, ar.AR_I32: torch.int32}[dt]
@@ -586,6 +587,16 @@ def test_reduce_scatter_all_gather_page_examples_and_in_place():
     torch.cuda.synchronize()
     assert_bitwise([from_dev(b, ar.AR_F32) for b in bufs], expect(xs, ar.AR_F32, ar.AR_SUM, ar.AR_ALGO_RING),
                    "in-place RS + AG")
+    # in place with chunk starts inside 16-byte slots (the chunk views are then not 16-byte aligned)
+    n, count = 5, 80_003
+    xs = _inputs(ar.AR_BF16, n, count, 52)
+    lo = ar.chunk_bounds(count, n)
+    bufs = [to_dev(x, ar.AR_BF16)[1] for x in xs]
+    ar.ar_reduce_scatter(bufs, [bufs[c][lo[c]:lo[c + 1]] for c in range(n)], ar.AR_AVG)
+    ar.ar_all_gather([bufs[c][lo[c]:lo[c + 1]] for c in range(n)], bufs)
+    torch.cuda.synchronize()
+    assert_bitwise([from_dev(b, ar.AR_BF16) for b in bufs], expect(xs, ar.AR_BF16, ar.AR_AVG, ar.AR_ALGO_RING),
+                   "in-place RS + AG, ragged")
 
 
 def test_allreduce_on_a_side_stream_beside_other_kernels_is_bit_exact():
