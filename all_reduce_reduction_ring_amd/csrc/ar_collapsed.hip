@@ -1,5 +1,6 @@
-// ar_collapsed.hip -- one-pass all-reduce kernels: ring order, rank order (reduce + broadcast) and the
-// recursive halving-doubling tree.
+// ar_collapsed.hip -- one-pass all-reduce kernels: ring order, rank order (reduce + broadcast), the recursive
+// halving-doubling tree and the binomial tree, and the many-bucket segment kernel. Compiled once per element
+// type (AR_COLLAPSED_DTYPE).
 //
 // Ring order (jisaku.com glossary "AllReduce（オールリデュース）", section Ring-AllReduceの仕組み; astro-wiki
 // "AllReduce", section Ring AllReduce, phases 阶段一 and 阶段二): with reduce-scatter round s sending chunk
@@ -23,11 +24,10 @@
 // first, folded right to left; the pass evaluates that in registers for any N.
 //
 // Layout: the ring on 16-byte aligned buffers of at least a grid of tiles runs the one-front kernel below (tiles
-// of the whole buffer, each folded from the rank of the chunk it lies in). Otherwise grid.y = chunk c (the ring:
-// small or unaligned buffers) or
-// 1 (rank order and the trees, whose order does not depend on the chunk), and grid.x strides over the chunk's
-// 16-byte slots; a chunk whose start or end is not slot-aligned has its few edge elements done element-wise by
-// block x = 0.
+// of the whole buffer, each folded from the rank of the chunk it lies in). Otherwise grid.y = chunk c (the ring on
+// small or unaligned buffers) or 1 (rank order and the trees, whose order does not depend on the chunk), and
+// grid.x strides over the chunk's 16-byte slots; a chunk whose start or end is not slot-aligned has its few edge
+// elements done element-wise by block x = 0.
 #include "ar_device.h"
 #include "ar_internal.h"
 
@@ -452,7 +452,8 @@ hipError_t dispatch_op(CollapsedArgs& a, int op, int algo, hipStream_t s) {
 }
 
 // ------------------------------------------------------------------------------------------ segments
-// Many buckets in one launch. Segment s occupies elements [start_s, start_s + count_s) of every rank's flat
+// Many buckets in one launch (the host layer sends the small ones here; a large bucket gets a launch of its
+// own). Segment s occupies elements [start_s, start_s + count_s) of every rank's flat
 // buffer, count_s a multiple of N * (16 / element size), so each of its N chunks is whole 16-byte slots. Each
 // segment is reduced exactly as a one-segment call would reduce it: chunk c of segment s folds from rank c.
 // The work is cut into tiles of kThreads * U slots of one chunk; tile_pre holds the running tile count per
