@@ -12,7 +12,7 @@ CPU oracle timed on this host on the same inputs; and, beside the headline, ever
 (rank-order and halving-doubling one-pass kernels, the round-per-launch schedules, bucketing with 25 MiB
 buckets over 300 tensors, the fp8 codec and compressed ring) with its own algorithmic-bytes roofline.
 
-Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--headline-only] [--copy-calibration]
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--headline-only] [--fp8-only] [--copy-calibration]
 """
 from __future__ import annotations
 
@@ -511,6 +511,9 @@ def main():
     p.add_argument("--headline-only", action="store_true", help="time the headline only (for profiler runs)")
     p.add_argument("--copy-calibration", action="store_true",
                    help="run only a plain 2 GiB device copy, the reference for HBM counter scaling")
+    p.add_argument("--fp8-only", action="store_true",
+                   help="time only the compressed ring on its workload (8 x 67,108,864 bf16, 0.1%% outliers; for "
+                        "profiler runs)")
     p.add_argument("--sweep", metavar="OUT.jsonl", help="run only the message-size sweep, one JSON line per point")
     p.add_argument("--sweep-max-log2", type=int, default=30)
     args = p.parse_args()
@@ -532,6 +535,23 @@ def main():
 
     if args.sweep:
         sweep(torch, ar, dev, args.sweep, max_log2=args.sweep_max_log2)
+        return
+
+    if args.fp8_only:
+        n8 = 67_108_864
+        log("generating the compressed-ring inputs")
+        h8 = _gen_parallel(lambda r: inputs.outlier_bf16((5, r), n8), range(N_RANKS))
+        i8 = _upload(torch, h8, torch.bfloat16, dev)
+        o8 = [torch.empty_like(t) for t in i8]
+        step = lambda: ar.ar_allreduce(i8, o8, ar.AR_SUM, ar.AR_ALGO_RING_FP8)
+        for _ in range(args.warmup):
+            step()
+        torch.cuda.synchronize()
+        ms = Timer(torch).run(step, args.steps)
+        t = float(np.mean(ms)) * 1e-3
+        print(json.dumps({"fp8_ring": {"kernel_us": stats_us(ms), "hbm_GBps": ring_bytes(N_RANKS, n8, 2) / t / GB,
+                                       "busbw_GBps": n8 * 2 / t / GB * bus_factor(N_RANKS),
+                                       "steps": args.steps, "warmup": args.warmup}}))
         return
 
     if args.copy_calibration:
