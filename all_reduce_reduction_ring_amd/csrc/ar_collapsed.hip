@@ -23,11 +23,15 @@
 // power of two below n. The blocks of N's binary expansion are perfect trees over consecutive ranks, largest
 // first, folded right to left; the pass evaluates that in registers for any N.
 //
-// Layout: the ring on 16-byte aligned buffers of at least a grid of tiles runs the one-front kernel below (tiles
+// Layout: every buffer is cut the same way into a head of `head` elements and then 16-byte slots (slot v holds
+// elements head + [vV, vV + V)). When all buffer addresses agree modulo 16, the host picks the head so that the
+// slots start at an aligned address in every buffer (at a 256-byte boundary for large buffers: HBM writes that
+// share a 128-byte line between two workgroups cost measurably more); otherwise there are no slots and every
+// element goes one by one. The ring on buffers of at least a grid of tiles runs the one-front kernel below (tiles
 // of the whole buffer, each folded from the rank of the chunk it lies in). Otherwise grid.y = chunk c (the ring on
-// small or unaligned buffers) or 1 (rank order and the trees, whose order does not depend on the chunk), and
-// grid.x strides over the chunk's 16-byte slots; a chunk whose start or end is not slot-aligned has its few edge
-// elements done element-wise by block x = 0.
+// small buffers) or 1 (rank order and the trees, whose order does not depend on the chunk), and grid.x strides
+// over the chunk's slots; the elements of a chunk that are not in a whole slot (head, edges) are done
+// element-wise by block x = 0.
 #include "ar_device.h"
 #include "ar_internal.h"
 
@@ -54,9 +58,23 @@ struct CollapsedArgs {
   int64_t q;  // count / nchunks
   int64_t r;  // count % nchunks
   int n;      // ranks
-  int rot;    // 1: chunk c folds from rank c (ring); 0: from rank 0
-  int vec;    // 1: all buffers 16-byte aligned
+  int64_t head;  // elements before the first 16-byte slot (when vec)
+  int64_t hb;    // head in bytes: slot v starts hb + 16 v bytes into every buffer
+  int rot;       // 1: chunk c folds from rank c (ring); 0: from rank 0
+  int vec;       // 1: the slots exist (every buffer address + hb is a multiple of 16)
 };
+
+// Whole slots and element ranges: slots [slot_ceil(lo), slot_floor(hi)) lie inside elements [lo, hi).
+template <int V>
+__device__ __forceinline__ int64_t slot_ceil(int64_t e, int64_t head) {
+  e -= head;
+  return e > 0 ? (e + V - 1) / V : 0;
+}
+template <int V>
+__device__ __forceinline__ int64_t slot_floor(int64_t e, int64_t head) {
+  e -= head;
+  return e > 0 ? e / V : 0;
+}
 
 // ------------------------------------------------------------------------------------------ fold orders
 // Ring-order fold of one slot over rank pointers already in fold order; epilogue applied.
@@ -252,24 +270,24 @@ __global__ __launch_bounds__(kThreads) void collapsed_kernel(CollapsedArgs a) {
     return;
   }
 
-  const int64_t vlo = (lo + V - 1) / V, vhi = hi / V;
+  const int64_t vlo = slot_ceil<V>(lo, a.head), vhi = slot_floor<V>(hi, a.head);
   int64_t v = vlo + static_cast<int64_t>(blockIdx.x) * kThreads + threadIdx.x;
   for (; v + (U - 1) * stride < vhi; v += U * stride) {
     u32x4 w[U];
 #pragma unroll
-    for (int u = 0; u < U; ++u) w[u] = fold_slot<DT, OP, NR, SHAPE>(a, start, (v + u * stride) * 16);
+    for (int u = 0; u < U; ++u) w[u] = fold_slot<DT, OP, NR, SHAPE>(a, start, a.hb + (v + u * stride) * 16);
 #pragma unroll
     for (int u = 0; u < U; ++u)
-      for (int r = 0; r < n; ++r) st16(static_cast<char*>(a.p.out[r]) + (v + u * stride) * 16, w[u]);
+      for (int r = 0; r < n; ++r) st16(static_cast<char*>(a.p.out[r]) + a.hb + (v + u * stride) * 16, w[u]);
   }
   for (; v < vhi; v += stride) {
-    u32x4 w = fold_slot<DT, OP, NR, SHAPE>(a, start, v * 16);
-    for (int r = 0; r < n; ++r) st16(static_cast<char*>(a.p.out[r]) + v * 16, w);
+    u32x4 w = fold_slot<DT, OP, NR, SHAPE>(a, start, a.hb + v * 16);
+    for (int r = 0; r < n; ++r) st16(static_cast<char*>(a.p.out[r]) + a.hb + v * 16, w);
   }
 
   if (blockIdx.x == 0) {
-    int64_t h1 = vlo * V, t0 = vhi * V;
-    if (vlo >= vhi) {  // no whole aligned slot inside the chunk
+    int64_t h1 = a.head + vlo * V, t0 = a.head + vhi * V;
+    if (vlo >= vhi) {  // no whole slot inside the chunk
       h1 = hi;
       t0 = hi;
     }
@@ -283,8 +301,8 @@ __global__ __launch_bounds__(kThreads) void collapsed_kernel(CollapsedArgs a) {
 // separate fronts through every rank buffer (N x 2N streams into HBM); a single front keeps 2N streams, as the
 // tree orders have, and measured faster on MI355X. Tile t = slots [t*TS, (t+1)*TS) of the whole buffer goes to
 // block t mod G; inside a tile, the slots wholly in chunk c fold from rank c (one uniform sub-range per chunk
-// the tile touches, nearly always one). Slots that straddle a chunk boundary, and the elements after the last
-// whole slot, go element by element (block 0). Needs 16-byte aligned buffers.
+// the tile touches, nearly always one). The head, slots that straddle a chunk boundary, and the elements after the
+// last whole slot go element by element (block 0). Needs the slots (vec).
 template <int DT, int OP, int NR, int U>
 __device__ __forceinline__ void ring_front_elem(const CollapsedArgs& a, int64_t e) {
   const int n = NR > 0 ? NR : a.n;
@@ -299,24 +317,24 @@ __global__ __launch_bounds__(kThreads) void ring_front_kernel(CollapsedArgs a) {
   constexpr int64_t TS = static_cast<int64_t>(kThreads) * U;
   constexpr int NT = NR > 0 ? NR : 1;
   const int n = NR > 0 ? NR : a.n;
-  const int64_t nslots = a.count / V;
+  const int64_t nslots = slot_floor<V>(a.count, a.head);
   const int64_t ntiles = (nslots + TS - 1) / TS;
   // The block's tiles t = blockIdx.x + k G come in increasing order, so they meet the chunks in order: the outer
   // loop walks the chunks (the rotated rank pointers are fixed inside it), the inner one the tiles. A tile that
   // reaches past the chunk's last whole slot is kept for the next chunk.
   int64_t t = blockIdx.x;
   int c0 = 0;  // chunks that end before the block's first tile have no work for it
-  while (c0 + 1 < n && chunk_lo(a.q, a.r, c0 + 1) <= t * TS * V) ++c0;
+  while (c0 + 1 < n && chunk_lo(a.q, a.r, c0 + 1) <= a.head + t * TS * V) ++c0;
   for (int cc = c0; cc < n && t < ntiles; ++cc) {
     const int64_t lo = chunk_lo(a.q, a.r, cc), hi = chunk_lo(a.q, a.r, cc + 1);
-    const int64_t w0 = (lo + V - 1) / V, w1 = hi / V;  // whole slots of chunk cc
+    const int64_t w0 = slot_ceil<V>(lo, a.head), w1 = slot_floor<V>(hi, a.head);  // whole slots of chunk cc
     if (w0 >= w1) continue;
     const char* rot[NT];
 #pragma unroll
     for (int k = 0; k < NT; ++k) {
       int r = cc + k;
       r = r >= n ? r - n : r;
-      rot[k] = static_cast<const char*>(a.p.in[r]);
+      rot[k] = static_cast<const char*>(a.p.in[r]) + a.hb;
     }
     while (t < ntiles) {
       const int64_t s0 = t * TS, s1 = s0 + TS < nslots ? s0 + TS : nslots;
@@ -329,14 +347,14 @@ __global__ __launch_bounds__(kThreads) void ring_front_kernel(CollapsedArgs a) {
           const int64_t v = s0 + threadIdx.x + u * kThreads;
           if (v >= v0 && v < v1) {
             if constexpr (NR > 0) w[u] = fold_ptrs<DT, OP, NR>(rot, v * 16);
-            else w[u] = ring_slot<DT, OP, NR>(a, cc, v * 16);
+            else w[u] = ring_slot<DT, OP, NR>(a, cc, a.hb + v * 16);
           }
         }
 #pragma unroll
         for (int u = 0; u < U; ++u) {
           const int64_t v = s0 + threadIdx.x + u * kThreads;
           if (v >= v0 && v < v1)
-            for (int r = 0; r < n; ++r) st16(static_cast<char*>(a.p.out[r]) + v * 16, w[u]);
+            for (int r = 0; r < n; ++r) st16(static_cast<char*>(a.p.out[r]) + a.hb + v * 16, w[u]);
         }
       }
       if (s1 > w1) break;
@@ -346,13 +364,16 @@ __global__ __launch_bounds__(kThreads) void ring_front_kernel(CollapsedArgs a) {
   if (blockIdx.x == 0) {
     // a slot with a chunk boundary strictly inside it is done by the first such boundary only
     for (int cb = 1; cb < n; ++cb) {
-      const int64_t b = chunk_lo(a.q, a.r, cb);
+      const int64_t b = chunk_lo(a.q, a.r, cb) - a.head;  // boundary relative to the first slot
+      if (b <= 0) continue;                                // inside the head
       const int64_t sl = b / V;
       if (b % V == 0 || sl >= nslots) continue;
-      if (cb > 1 && chunk_lo(a.q, a.r, cb - 1) > sl * V) continue;
-      if (threadIdx.x < V) ring_front_elem<DT, OP, NR, U>(a, sl * V + threadIdx.x);
+      if (cb > 1 && chunk_lo(a.q, a.r, cb - 1) > a.head + sl * V) continue;
+      if (threadIdx.x < V) ring_front_elem<DT, OP, NR, U>(a, a.head + sl * V + threadIdx.x);
     }
-    for (int64_t e = nslots * V + threadIdx.x; e < a.count; e += kThreads) ring_front_elem<DT, OP, NR, U>(a, e);
+    const int64_t head_end = a.head < a.count ? a.head : a.count;
+    for (int64_t e = threadIdx.x; e < head_end; e += kThreads) ring_front_elem<DT, OP, NR, U>(a, e);
+    for (int64_t e = a.head + nslots * V + threadIdx.x; e < a.count; e += kThreads) ring_front_elem<DT, OP, NR, U>(a, e);
   }
 }
 
@@ -360,7 +381,8 @@ template <int DT, int OP, int NR, int U>
 hipError_t launch_front(CollapsedArgs& a, hipStream_t s) {
   constexpr int V = Traits<DT>::kVec;
   constexpr int64_t TS = static_cast<int64_t>(kThreads) * U;
-  const int64_t ntiles = (a.count / V + TS - 1) / TS;
+  const int64_t nslots = a.count > a.head ? (a.count - a.head) / V : 0;
+  const int64_t ntiles = (nslots + TS - 1) / TS;
   int64_t g = static_cast<int64_t>(cu_count()) * blocks_per_cu<NR>();
   if (g > ntiles) g = ntiles;
   if (g < 1) g = 1;
@@ -392,7 +414,8 @@ template <int DT, int OP, int NR, int U>
 hipError_t front_or_chunks(CollapsedArgs& a, hipStream_t s) {
   constexpr int V = Traits<DT>::kVec;
   constexpr int64_t TS = static_cast<int64_t>(kThreads) * U;
-  const int64_t tiles = (a.count / V + TS - 1) / TS;
+  const int64_t nslots = a.count > a.head ? (a.count - a.head) / V : 0;
+  const int64_t tiles = (nslots + TS - 1) / TS;
   if (tiles >= static_cast<int64_t>(cu_count()) * blocks_per_cu<NR>()) return launch_front<DT, OP, NR, U>(a, s);
   return launch_one<DT, OP, NR, U, kLinear>(a, a.n, s);
 }
@@ -601,6 +624,8 @@ hipError_t launch_segments_dt<kDT>(const RankPtrs& p, int n, const int64_t* coun
     a.f.n = n;
     a.f.rot = algo == AR_ALGO_RING ? 1 : 0;
     a.f.vec = 1;
+    a.f.head = 0;
+    a.f.hb = 0;
     int m = 0;
     a.tile_pre[0] = 0;
     while (done + m < nseg && m < kMaxSegments) {
@@ -621,13 +646,15 @@ hipError_t launch_segments_dt<kDT>(const RankPtrs& p, int n, const int64_t* coun
 }
 
 template <>
-hipError_t launch_collapsed_dt<kDT>(const RankPtrs& p, int n, int64_t count, int op, int algo, bool vec,
+hipError_t launch_collapsed_dt<kDT>(const RankPtrs& p, int n, int64_t count, int op, int algo, int64_t head,
                                     hipStream_t s) {
   CollapsedArgs a;
   a.p = p;
   a.count = count;
   a.n = n;
-  a.vec = vec ? 1 : 0;
+  a.vec = head >= 0 ? 1 : 0;
+  a.head = head > 0 ? head : 0;
+  a.hb = a.head * Traits<kDT>::kSize;
   // the ring splits into n chunks (each folds from its own rank); every other order is one chunk
   const int nchunks = algo == AR_ALGO_RING ? n : 1;
   a.q = count / nchunks;

@@ -17,10 +17,17 @@ struct RankPtrs {
 // Number of compute units of the current device (cached per device id).
 int cu_count();
 
-// One-pass kernels. algo: AR_ALGO_RING (chunk c folds from rank c), AR_ALGO_FUSED (folds from rank 0) or
-// AR_ALGO_RHD (pairwise XOR tree, n a power of two). vec: every buffer is 16-byte aligned.
-hipError_t launch_collapsed(const RankPtrs& p, int n, int64_t count, int dtype, int op, int algo, bool vec,
+// One-pass kernels. algo: AR_ALGO_RING (chunk c folds from rank c), AR_ALGO_FUSED (folds from rank 0),
+// AR_ALGO_RHD (pairwise XOR tree, n a power of two) or AR_ALGO_TREE (binomial tree). head: elements before the
+// first 16-byte slot, so that every buffer address plus head elements is a multiple of 16 (see vector_head), or
+// -1 for element-by-element work throughout.
+hipError_t launch_collapsed(const RankPtrs& p, int n, int64_t count, int dtype, int op, int algo, int64_t head,
                             hipStream_t s);
+
+// The head for launch_collapsed: the fewest elements to skip in every buffer so that the rest starts at a multiple
+// of 256 bytes (buffers of 1 MiB and more) or of 16 bytes in all of them; -1 if the addresses of the buffers
+// (in and out) differ modulo 16 or are not multiples of the element size. Never more than count.
+int64_t vector_head(const RankPtrs& p, int n, int64_t count, int esize);
 
 // Many buckets of flat per-rank buffers in as few launches as possible (each count a multiple of N slots).
 hipError_t launch_segments(const RankPtrs& p, int n, const int64_t* counts, int nseg, int dtype, int op, int algo,
@@ -29,7 +36,7 @@ hipError_t launch_segments(const RankPtrs& p, int n, const int64_t* counts, int 
 // The same two for one element type: ar_collapsed.hip is compiled once per type (its many kernel instances then
 // build in parallel) and defines the specialisation for its type; the two functions above pick one.
 template <int DT>
-hipError_t launch_collapsed_dt(const RankPtrs& p, int n, int64_t count, int op, int algo, bool vec, hipStream_t s);
+hipError_t launch_collapsed_dt(const RankPtrs& p, int n, int64_t count, int op, int algo, int64_t head, hipStream_t s);
 template <int DT>
 hipError_t launch_segments_dt(const RankPtrs& p, int n, const int64_t* counts, int nseg, int op, int algo,
                               hipStream_t s);

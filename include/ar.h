@@ -127,11 +127,14 @@ enum ar_algo {
 int ar_auto_algo(int nranks, size_t count, int dtype);
 
 /* All-reduce of N rank buffers ([P] opening definition: every process contributes a buffer, buffers are
- * combined element-wise and the result is copied back to all; [V] "All-Reduceは全rankの値を集約して全rankへ返す").
+ * combined element-wise and the result is copied back to all; [V] section "All-Reduceは全rankの値を集約して全rankへ返す").
  *   in_bufs, out_bufs: host arrays of nranks device pointers, each to `count` elements of `dtype`.
  *     out_bufs[r] may equal in_bufs[r] (in place); any other overlap among the 2N ranges -> AR_ERR_ALIAS.
  *   count == 0 returns AR_OK and enqueues nothing. nranks == 1 copies (avg divides by 1).
- *   Alignment: any. A 16-byte vector path is used where every pointer is 16-byte aligned.
+ *   Alignment: any. RING, FUSED, RHD and TREE work in 16-byte vectors whenever all 2N pointers share one address
+ *   modulo 16 (a multiple of the element size): the first few elements of every buffer go one by one, up to a
+ *   multiple of 256 bytes (buffers of 1 MiB or more) or of 16 bytes, the rest in vectors. The other algorithms
+ *   use vectors only when every pointer is 16-byte aligned. Otherwise the work goes element by element.
  * Errors: AR_ERR_INVALID (enum, nranks, NULL), AR_ERR_UNSUPPORTED (RHD with N not a power of two; FP8
  *   with a dtype other than F32/BF16 or an op other than SUM/AVG), AR_ERR_ALIAS, AR_ERR_WORKSPACE (the
  *   stepwise algorithms on bf16/f16 need ar_allreduce_ws), AR_ERR_HIP. AR_ALGO_AUTO is resolved first, so
@@ -139,7 +142,7 @@ int ar_auto_algo(int nranks, size_t count, int dtype);
 int ar_allreduce(const void* const* in_bufs, void* const* out_bufs, int nranks, size_t count, int dtype, int op,
                  int algo, void* stream);
 
-/* Reduce-scatter ([V] "Reduce-Scatterは集約後の結果をrankへ分ける"; [W] primitives table; [P] "变体与相关操作"): rank c
+/* Reduce-scatter ([V] section "Reduce-Scatterは集約後の結果をrankへ分ける"; [W] primitives table; [P] "变体与相关操作"): rank c
  * receives chunk c (the balanced split) of the element-wise reduction. Chunk c is folded starting at rank c,
  * the ring's own order, with the same epilogue as ar_allreduce, so ar_reduce_scatter followed by
  * ar_all_gather equals AR_ALGO_RING bit for bit.
@@ -152,7 +155,7 @@ int ar_allreduce(const void* const* in_bufs, void* const* out_bufs, int nranks, 
 int ar_reduce_scatter(const void* const* in_bufs, void* const* out_bufs, int nranks, size_t count, int dtype, int op,
                       void* stream);
 
-/* All-gather ([V] "All-Gatherは分割dataを連結して全rankへ配る"; [W] primitives table): rank r contributes chunk r of
+/* All-gather ([V] section "All-Gatherは分割dataを連結して全rankへ配る"; [W] primitives table): rank r contributes chunk r of
  * the balanced split of `count`; every rank receives all chunks in rank order.
  *   in_bufs: host array; in_bufs[r] points to chunk r's elements (NULL allowed when it is empty).
  *   out_bufs: host array of nranks device pointers to `count` elements each. In place:

@@ -160,10 +160,52 @@ def test_small_and_ragged_counts(count, algo):
 @pytest.mark.parametrize("algo", [ar.AR_ALGO_RING, ar.AR_ALGO_FUSED, ar.AR_ALGO_RHD, ar.AR_ALGO_RING_STEPWISE,
                                   ar.AR_ALGO_RHD_STEPWISE, ar.AR_ALGO_TREE, ar.AR_ALGO_TREE_STEPWISE])
 @pytest.mark.parametrize("dt", [ar.AR_F32, ar.AR_BF16, ar.AR_I32])
-def test_unaligned_buffers_take_the_element_path(algo, dt):
+def test_unaligned_buffers(algo, dt):
     xs = _inputs(dt, 4, 1000, 16)
     want = expect(xs, dt, ar.AR_AVG, algo)
     assert_bitwise(run(xs, dt, ar.AR_AVG, algo, offset=1), want, f"offset 1 algo={algo}")
+
+
+ONE_PASS = [ar.AR_ALGO_RING, ar.AR_ALGO_FUSED, ar.AR_ALGO_RHD, ar.AR_ALGO_TREE]
+
+
+@pytest.mark.parametrize("offset", [1, 3, 8, 64, 127])
+@pytest.mark.parametrize("algo", ONE_PASS)
+@pytest.mark.parametrize("dt", [ar.AR_F32, ar.AR_BF16, ar.AR_I32])
+def test_same_offset_in_every_buffer_vector_path_after_a_head(offset, algo, dt):
+    """Every buffer the same number of elements past an aligned address: a head of elements one by one, then
+    16-byte slots (from a 256-byte boundary on 1 MiB and more). Small (per-chunk grid) and large (one-front
+    ring) calls, in place and out of place, against the oracle."""
+    for n, count in ((4, 1000), (8, 600_003)):
+        xs = _inputs(dt, n, count, 24)
+        want = expect(xs, dt, ar.AR_SUM, algo)
+        for inplace in (False, True):
+            got = run(xs, dt, ar.AR_SUM, algo, offset=offset, inplace=inplace)
+            assert_bitwise(got, want, f"offset {offset} n={n} count={count} algo={algo} in place={inplace}")
+
+
+@pytest.mark.parametrize("algo", ONE_PASS)
+@pytest.mark.parametrize("in_off,out_off", [(3, 11), (0, 1), (5, 5 + 128)])
+def test_inputs_and_outputs_at_different_offsets(algo, in_off, out_off):
+    """Inputs and outputs at different residues: (3, 11) bf16 agree modulo 16 bytes but not 256 (16-byte head),
+    (0, 1) share no residue (element path), (5, 133) agree modulo 256 bytes."""
+    dt, n, count = ar.AR_BF16, 8, 600_003
+    xs = _inputs(dt, n, count, 25)
+    ins = [to_dev(x, dt, offset=in_off)[1] for x in xs]
+    outs = [empty_like_dev(count, dt, offset=out_off)[1] for _ in xs]
+    ar.ar_allreduce(ins, outs, ar.AR_MAX, algo)
+    torch.cuda.synchronize()
+    assert_bitwise([from_dev(o, dt) for o in outs], expect(xs, dt, ar.AR_MAX, algo), f"{in_off}/{out_off} {algo}")
+
+
+@pytest.mark.parametrize("algo", ONE_PASS)
+def test_rank_buffers_at_different_offsets_take_the_element_path(algo):
+    dt, n, count = ar.AR_F32, 8, 300_001
+    xs = _inputs(dt, n, count, 26)
+    ins = [to_dev(x, dt, offset=r)[1] for r, x in enumerate(xs)]
+    ar.ar_allreduce(ins, ins, ar.AR_AVG, algo)
+    torch.cuda.synchronize()
+    assert_bitwise([from_dev(t, dt) for t in ins], expect(xs, dt, ar.AR_AVG, algo), f"per-rank offsets {algo}")
 
 
 @pytest.mark.parametrize("algo", [ar.AR_ALGO_RING, ar.AR_ALGO_FUSED, ar.AR_ALGO_RHD, ar.AR_ALGO_RING_STEPWISE,
