@@ -45,6 +45,9 @@ constexpr int kThreads = 256;
 // U = 8/N for small N), and the grid is a small number of 256-thread workgroups per CU in total (split over
 // the chunks): one for N = 8, more where a thread has fewer loads in flight or writes fewer streams.
 template <int NR> constexpr int slots_per_thread() { return (NR > 0 && NR < 8) ? 8 / NR : 1; }
+// Element by element (buffers whose addresses differ modulo 16 between ranks): UE elements per thread and tile,
+// about 64 independent loads in flight per thread (UE x N); one at a time for a run-time rank count.
+template <int NR> constexpr int elems_per_thread() { return NR == 0 ? 1 : NR >= 64 ? 1 : 64 / NR > 16 ? 16 : 64 / NR; }
 template <int NR> constexpr int blocks_per_cu() {
   return NR == 8 ? 1 : NR == 2 ? 2 : (NR == 4 || NR == 16) ? 4 : 8;
 }
@@ -196,17 +199,44 @@ __device__ __forceinline__ uint32_t binomial_elem(const CollapsedArgs& a, int64_
   return narrow<DT>(finalize<OP>(binomial_fold_elem<DT, OP, NR>(a.p.in, n, e), n));
 }
 
-// Element-wise versions for slot edges and unaligned buffers.
-template <int DT, int OP>
+// Element-wise versions for slot edges and buffers without slots. With the rank count known at compile time every
+// load is issued before the first combine.
+template <int DT, int OP, int NR>
 __device__ __forceinline__ uint32_t ring_elem(const CollapsedArgs& a, int start, int64_t e) {
-  const int n = a.n;
-  auto acc = widen<DT>(load_elem<DT>(a.p.in[start], e));
-  for (int k = 1; k < n; ++k) {
-    int r = start + k;
-    r = r >= n ? r - n : r;
-    acc = combine<OP>(acc, widen<DT>(load_elem<DT>(a.p.in[r], e)));
+  if constexpr (NR > 0) {
+    uint32_t x[NR];
+#pragma unroll
+    for (int k = 0; k < NR; ++k) {
+      int r = start + k;
+      r = r >= NR ? r - NR : r;
+      x[k] = load_elem<DT>(a.p.in[r], e);
+    }
+    auto acc = widen<DT>(x[0]);
+#pragma unroll
+    for (int k = 1; k < NR; ++k) acc = combine<OP>(acc, widen<DT>(x[k]));
+    return narrow<DT>(finalize<OP>(acc, NR));
+  } else {
+    const int n = a.n;
+    auto acc = widen<DT>(load_elem<DT>(a.p.in[start], e));
+    for (int k = 1; k < n; ++k) {
+      int r = start + k;
+      r = r >= n ? r - n : r;
+      acc = combine<OP>(acc, widen<DT>(load_elem<DT>(a.p.in[r], e)));
+    }
+    return narrow<DT>(finalize<OP>(acc, n));
   }
-  return narrow<DT>(finalize<OP>(acc, n));
+}
+
+// The halving tree of one element, NR ranks OFF, OFF+STRIDE, ... (as tree_fold).
+template <int DT, int OP, int NR, int STRIDE, int OFF>
+__device__ __forceinline__ typename Traits<DT>::Acc tree_fold_elem(const CollapsedArgs& a, int64_t e) {
+  if constexpr (NR == 1) {
+    return widen<DT>(load_elem<DT>(a.p.in[OFF], e));
+  } else {
+    const auto lo = tree_fold_elem<DT, OP, NR / 2, STRIDE * 2, OFF>(a, e);
+    const auto hi = tree_fold_elem<DT, OP, NR / 2, STRIDE * 2, OFF + STRIDE>(a, e);
+    return combine<OP>(lo, hi);
+  }
 }
 
 // Tree for runtime n (power of two): the halving tree evaluated as a binary counter over the leaves in
@@ -238,11 +268,18 @@ __device__ __forceinline__ uint32_t tree_elem(const CollapsedArgs& a, int64_t e)
 }
 
 template <int DT, int OP, int NR, int SHAPE>
+__device__ __forceinline__ uint32_t elem_bits(const CollapsedArgs& a, int start, int64_t e) {
+  // (for 64 ranks the unrolled tree would spill next to the slot tree)
+  if constexpr (SHAPE == kHalving && NR > 0 && NR <= 32)
+    return narrow<DT>(finalize<OP>(tree_fold_elem<DT, OP, NR, 1, 0>(a, e), NR));
+  else if constexpr (SHAPE == kHalving) return tree_elem<DT, OP>(a, e);
+  else if constexpr (SHAPE == kBinomial) return binomial_elem<DT, OP, NR>(a, e);
+  else return ring_elem<DT, OP, NR>(a, start, e);
+}
+
+template <int DT, int OP, int NR, int SHAPE>
 __device__ __forceinline__ void edge_elem(const CollapsedArgs& a, int start, int64_t e) {
-  uint32_t b;
-  if constexpr (SHAPE == kHalving) b = tree_elem<DT, OP>(a, e);
-  else if constexpr (SHAPE == kBinomial) b = binomial_elem<DT, OP, NR>(a, e);
-  else b = ring_elem<DT, OP>(a, start, e);
+  const uint32_t b = elem_bits<DT, OP, NR, SHAPE>(a, start, e);
   const int n = NR > 0 ? NR : a.n;
   for (int r = 0; r < n; ++r) store_elem<DT>(a.p.out[r], e, b);
 }
@@ -265,8 +302,24 @@ __global__ __launch_bounds__(kThreads) void collapsed_kernel(CollapsedArgs a) {
   const int n = NR > 0 ? NR : a.n;
 
   if (!a.vec) {
-    for (int64_t e = lo + static_cast<int64_t>(blockIdx.x) * kThreads + threadIdx.x; e < hi; e += stride)
-      edge_elem<DT, OP, NR, SHAPE>(a, start, e);
+    // tiles of kThreads x UE elements; lane-consecutive elements, so each load and store instruction of a wave
+    // covers 64 consecutive elements
+    constexpr int UE = elems_per_thread<NR>();
+    constexpr int64_t TE = static_cast<int64_t>(kThreads) * UE;
+    for (int64_t t0 = lo + static_cast<int64_t>(blockIdx.x) * TE; t0 < hi; t0 += static_cast<int64_t>(gridDim.x) * TE) {
+      uint32_t b[UE];
+#pragma unroll
+      for (int u = 0; u < UE; ++u) {
+        const int64_t e = t0 + u * kThreads + threadIdx.x;
+        if (e < hi) b[u] = elem_bits<DT, OP, NR, SHAPE>(a, start, e);
+      }
+#pragma unroll
+      for (int u = 0; u < UE; ++u) {
+        const int64_t e = t0 + u * kThreads + threadIdx.x;
+        if (e < hi)
+          for (int r = 0; r < n; ++r) store_elem<DT>(a.p.out[r], e, b[u]);
+      }
+    }
     return;
   }
 
@@ -396,8 +449,8 @@ hipError_t launch_one(CollapsedArgs& a, int nchunks, hipStream_t s) {
   constexpr int V = Traits<DT>::kVec;
   constexpr int kBlocksPerCU = blocks_per_cu<NR>();
   const int64_t per_chunk = a.q + 1;
-  const int64_t slots = a.vec ? (per_chunk + V - 1) / V : per_chunk;
-  int64_t want = (slots + static_cast<int64_t>(kThreads) * U - 1) / (static_cast<int64_t>(kThreads) * U);
+  const int64_t per_block = a.vec ? static_cast<int64_t>(kThreads) * U * V : static_cast<int64_t>(kThreads) * elems_per_thread<NR>();
+  int64_t want = (per_chunk + per_block - 1) / per_block;
   int64_t cap = (static_cast<int64_t>(cu_count()) * kBlocksPerCU + nchunks - 1) / nchunks;
   if (cap < 1) cap = 1;
   int64_t bx = want < cap ? want : cap;
