@@ -320,9 +320,11 @@ __global__ __launch_bounds__(kThreads) void fp8_ring_kernel(Fp8RingArgs a) {
   }
 }
 
-int grid_for_waves(int64_t waves) {
+// Workgroups for `waves` wave tasks, at most blocks_per_cu per CU. Measured on MI355X (N = 8, 64 Mi bf16): the
+// compressed ring ran within noise from 2 to 16 per CU; the codec kernels gained 7% from 8 to 16 per CU.
+int grid_for_waves(int64_t waves, int blocks_per_cu) {
   int64_t blocks = (waves + 3) / 4;
-  const int64_t cap = static_cast<int64_t>(cu_count()) * 8;
+  const int64_t cap = static_cast<int64_t>(cu_count()) * blocks_per_cu;
   if (blocks > cap) blocks = cap;
   if (blocks < 1) blocks = 1;
   return static_cast<int>(blocks);
@@ -330,7 +332,7 @@ int grid_for_waves(int64_t waves) {
 
 template <int DT, int OP>
 hipError_t ring_n(Fp8RingArgs& a, hipStream_t s) {
-  const int g = grid_for_waves(a.tasks);
+  const int g = grid_for_waves(a.tasks, 8);
   switch (a.n) {
     case 8: hipLaunchKernelGGL((fp8_ring_kernel<DT, OP, 8>), dim3(g), dim3(kThreads), 0, s, a); break;
     case 4: hipLaunchKernelGGL((fp8_ring_kernel<DT, OP, 4>), dim3(g), dim3(kThreads), 0, s, a); break;
@@ -344,7 +346,7 @@ hipError_t ring_n(Fp8RingArgs& a, hipStream_t s) {
 
 hipError_t launch_fp8_quant(const void* in, int dtype, int64_t count, uint8_t* codes, float* scales, hipStream_t s) {
   const int64_t nblocks = (count + kBlock - 1) / kBlock;
-  const int g = grid_for_waves((nblocks + 3) / 4);
+  const int g = grid_for_waves((nblocks + 3) / 4, 16);
   const int vec = (((reinterpret_cast<uintptr_t>(in) | reinterpret_cast<uintptr_t>(codes)) & 15u) == 0) ? 1 : 0;
   if (dtype == AR_BF16) hipLaunchKernelGGL((quant_kernel<AR_BF16>), dim3(g), dim3(kThreads), 0, s, in, count, codes, scales, vec);
   else hipLaunchKernelGGL((quant_kernel<AR_F32>), dim3(g), dim3(kThreads), 0, s, in, count, codes, scales, vec);
@@ -355,7 +357,7 @@ hipError_t launch_fp8_dequant(const uint8_t* codes, const float* scales, int64_t
                               hipStream_t s) {
   const int64_t groups = (count + kPerLane - 1) / kPerLane;
   int64_t blocks = (groups + kThreads - 1) / kThreads;
-  const int64_t cap = static_cast<int64_t>(cu_count()) * 8;
+  const int64_t cap = static_cast<int64_t>(cu_count()) * 16;
   if (blocks > cap) blocks = cap;
   if (blocks < 1) blocks = 1;
   const int vec = ((reinterpret_cast<uintptr_t>(out) & 15u) == 0) ? 1 : 0;

@@ -258,6 +258,19 @@ def other_rows(torch, ar, inputs, ins, outs, dev, reps, host):
         rows[name] = row_entry(name, timer.run(fn, reps), ring_bytes(N_RANKS, COUNT, 2), S, N_RANKS)
         rows[name]["cpu_oracle"] = cpu_row(oracle_time(ofn, host, _o.BF16, _o.AVG), S, N_RANKS,
                                            "the full headline workload, one call")
+    # the ring on views that do not start on a 16-byte boundary: the same offset in every buffer (a head of
+    # elements, then 256-byte aligned slots), and rank r at an offset of r elements (element by element)
+    for name, offs in (("ring_common_offset", [1] * N_RANKS), ("ring_per_rank_offsets", list(range(N_RANKS)))):
+        vin = [torch.empty(COUNT + 8, dtype=torch.bfloat16, device=dev)[o:o + COUNT] for o in offs]
+        vout = [torch.empty(COUNT + 8, dtype=torch.bfloat16, device=dev)[o:o + COUNT] for o in offs]
+        for v, t in zip(vin, ins):
+            v.copy_(t)
+        fn = lambda: ar.ar_allreduce(vin, vout, ar.AR_AVG, ar.AR_ALGO_RING)
+        fn()
+        rows[name] = row_entry(name, timer.run(fn, reps), ring_bytes(N_RANKS, COUNT, 2), S, N_RANKS,
+                               {"offsets_elements": offs})
+        del vin, vout, fn
+    torch.cuda.empty_cache()
     # the two halves on their own: reduce-scatter (N reads + 1 write per element) and all-gather (1 read + N writes)
     lo = ar.chunk_bounds(COUNT, N_RANKS)
     parts = [torch.empty(lo[c + 1] - lo[c], dtype=torch.bfloat16, device=dev) for c in range(N_RANKS)]
