@@ -102,13 +102,36 @@ def dtype_code(t) -> int:
     return codes[t]
 
 
-def _stream(stream):
+def _stream(stream, device=None):
+    """The HIP stream handle: `stream` (a torch stream or a raw handle), else the current stream of `device`."""
     import torch
     if stream is None:
-        return ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+        return ctypes.c_void_p(torch.cuda.current_stream(device).cuda_stream)
     if isinstance(stream, int):
         return ctypes.c_void_p(stream)
     return ctypes.c_void_p(stream.cuda_stream)
+
+
+def _on(device):
+    """Make `device` current for a call (the library launches on the current device)."""
+    import torch
+    return torch.cuda.device(device)
+
+
+def _gpu_tensor(t, what, dtype=None, device=None, min_numel=0):
+    """Every tensor handed to the library: a contiguous GPU tensor (of `dtype`, on `device`, at least
+    `min_numel` elements). A host tensor would give the kernels a host address."""
+    if t.device.type != "cuda":
+        raise ValueError(f"{what} must be a GPU tensor")
+    if device is not None and t.device != device:
+        raise ValueError(f"{what} must be on {device}")
+    if not t.is_contiguous():
+        raise ValueError(f"{what} must be contiguous")
+    if dtype is not None and t.dtype != dtype:
+        raise ValueError(f"{what} must be {dtype}, not {t.dtype}")
+    if t.numel() < min_numel:
+        raise ValueError(f"{what} must hold at least {min_numel} elements")
+    return t
 
 
 def _check(rc: int, entry: str):
@@ -124,10 +147,7 @@ def _rank_arrays(ins, outs):
         # every rank must call with the same count and dtype; one call enforces it
         if t.dtype != t0.dtype or t.numel() != t0.numel() or t.device != t0.device:
             raise ValueError("all rank tensors must share dtype, element count and device")
-        if not t.is_contiguous():
-            raise ValueError("rank tensors must be contiguous")
-        if t.device.type != "cuda":
-            raise ValueError("rank tensors must be GPU tensors")
+        _gpu_tensor(t, "rank tensors")
     n = len(ins)
     arr_in = (ctypes.c_void_p * n)(*[t.data_ptr() for t in ins])
     arr_out = (ctypes.c_void_p * n)(*[t.data_ptr() for t in outs])
@@ -137,7 +157,9 @@ def _rank_arrays(ins, outs):
 def ar_allreduce(ins, outs, op=AR_SUM, algo=AR_ALGO_RING, stream=None):
     """All-reduce ins[r] -> outs[r] for every rank r (outs[r] may be ins[r])."""
     arr_in, arr_out, n, count, dt = _rank_arrays(ins, outs)
-    _check(lib().ar_allreduce(arr_in, arr_out, n, count, dt, op, algo, _stream(stream)), "ar_allreduce")
+    dev = ins[0].device
+    with _on(dev):
+        _check(lib().ar_allreduce(arr_in, arr_out, n, count, dt, op, algo, _stream(stream, dev)), "ar_allreduce")
 
 
 def ar_allreduce_workspace_size(nranks, count, dtype, op, algo) -> int:
@@ -149,11 +171,15 @@ def ar_allreduce_workspace_size(nranks, count, dtype, op, algo) -> int:
 
 def ar_allreduce_ws(ins, outs, op=AR_SUM, algo=AR_ALGO_RING, workspace=None, stream=None):
     """ar_allreduce with a caller workspace tensor (any dtype, contiguous, on the same GPU)."""
+    if workspace is not None and ins:
+        _gpu_tensor(workspace, "workspace", device=ins[0].device)
     arr_in, arr_out, n, count, dt = _rank_arrays(ins, outs)
+    dev = ins[0].device
     wp = ctypes.c_void_p(workspace.data_ptr()) if workspace is not None else ctypes.c_void_p(0)
     wb = workspace.numel() * workspace.element_size() if workspace is not None else 0
-    _check(lib().ar_allreduce_ws(arr_in, arr_out, n, count, dt, op, algo, wp, wb, _stream(stream)),
-           "ar_allreduce_ws")
+    with _on(dev):
+        _check(lib().ar_allreduce_ws(arr_in, arr_out, n, count, dt, op, algo, wp, wb, _stream(stream, dev)),
+               "ar_allreduce_ws")
 
 
 def ar_allreduce_buckets(flat_ins, flat_outs, bucket_count, op=AR_SUM, algo=AR_ALGO_RING, stream=None):
@@ -162,17 +188,25 @@ def ar_allreduce_buckets(flat_ins, flat_outs, bucket_count, op=AR_SUM, algo=AR_A
     counts = np.ascontiguousarray(bucket_count, dtype=np.int64)
     if int(counts.sum()) > total:
         raise ValueError("the buckets do not fit in the flat tensors")
-    _check(lib().ar_allreduce_buckets(arr_in, arr_out, n, counts.ctypes.data, counts.size, dt, op, algo,
-                                      _stream(stream)), "ar_allreduce_buckets")
+    dev = flat_ins[0].device
+    with _on(dev):
+        _check(lib().ar_allreduce_buckets(arr_in, arr_out, n, counts.ctypes.data, counts.size, dt, op, algo,
+                                          _stream(stream, dev)), "ar_allreduce_buckets")
 
 
 def ar_allreduce_tensors(descs, in_ptrs, out_ptrs, ntensors, nranks, dtype, op=AR_AVG, algo=AR_ALGO_RING,
                          stream=None):
     """descs: device int64 tensor [ntensors, 4] laid out as ar_tensor_desc; in_ptrs/out_ptrs: device int64
     tensors [ntensors * nranks] of device addresses (entry t * nranks + r)."""
-    _check(lib().ar_allreduce_tensors(ctypes.c_void_p(descs.data_ptr()), ctypes.c_void_p(in_ptrs.data_ptr()),
-                                      ctypes.c_void_p(out_ptrs.data_ptr()), ntensors, nranks, dtype, op, algo,
-                                      _stream(stream)), "ar_allreduce_tensors")
+    import torch
+    dev = descs.device
+    _gpu_tensor(descs, "descs", torch.int64, dev, 4 * ntensors)
+    _gpu_tensor(in_ptrs, "in_ptrs", torch.int64, dev, ntensors * nranks)
+    _gpu_tensor(out_ptrs, "out_ptrs", torch.int64, dev, ntensors * nranks)
+    with _on(dev):
+        _check(lib().ar_allreduce_tensors(ctypes.c_void_p(descs.data_ptr()), ctypes.c_void_p(in_ptrs.data_ptr()),
+                                          ctypes.c_void_p(out_ptrs.data_ptr()), ntensors, nranks, dtype, op, algo,
+                                          _stream(stream, dev)), "ar_allreduce_tensors")
 
 
 def chunk_bounds(count, nranks):
@@ -185,28 +219,48 @@ def _ptr(t):
     return t.data_ptr() if t is not None and t.numel() > 0 else 0
 
 
+def _chunk_tensors(full, parts, what):
+    """Check N full tensors and N chunk tensors (None allowed for an empty chunk) of one dtype and device."""
+    n = len(full)
+    if n == 0 or len(parts) != n:
+        raise ValueError("one full tensor and one chunk tensor per rank")
+    t0 = full[0]
+    for t in full:
+        if t.numel() != t0.numel():
+            raise ValueError("all full tensors must have the same element count")
+        _gpu_tensor(t, "full tensors", t0.dtype, t0.device)
+    lo = chunk_bounds(t0.numel(), n)
+    for c, p in enumerate(parts):
+        want = lo[c + 1] - lo[c]
+        if p is None:
+            if want:
+                raise ValueError(f"{what}[{c}] is None but chunk {c} has {want} elements")
+            continue
+        if p.numel() != want:
+            raise ValueError(f"{what}[{c}] must hold exactly chunk {c} of the balanced split ({want} elements)")
+        if want:
+            _gpu_tensor(p, f"{what}[{c}]", t0.dtype, t0.device)
+    return n, t0.numel(), t0.device
+
+
 def ar_reduce_scatter(ins, outs, op=AR_SUM, stream=None):
     """ins: N full tensors; outs[c]: a tensor of chunk c's length (the balanced split) receiving chunk c."""
-    n, count = len(ins), ins[0].numel()
-    lo = chunk_bounds(count, n)
-    if len(outs) != n or any(o is not None and o.numel() != lo[c + 1] - lo[c] for c, o in enumerate(outs)):
-        raise ValueError("outs[c] must hold exactly chunk c of the balanced split")
+    n, count, dev = _chunk_tensors(ins, outs, "outs")
     arr_in = (ctypes.c_void_p * n)(*[t.data_ptr() for t in ins])
     arr_out = (ctypes.c_void_p * n)(*[_ptr(o) for o in outs])
-    _check(lib().ar_reduce_scatter(arr_in, arr_out, n, count, dtype_code(ins[0].dtype), op, _stream(stream)),
-           "ar_reduce_scatter")
+    with _on(dev):
+        _check(lib().ar_reduce_scatter(arr_in, arr_out, n, count, dtype_code(ins[0].dtype), op,
+                                       _stream(stream, dev)), "ar_reduce_scatter")
 
 
 def ar_all_gather(ins, outs, stream=None):
     """ins[r]: rank r's chunk (the balanced split of the outputs' length); outs: N full tensors."""
-    n, count = len(outs), outs[0].numel()
-    lo = chunk_bounds(count, n)
-    if len(ins) != n or any(i is not None and i.numel() != lo[c + 1] - lo[c] for c, i in enumerate(ins)):
-        raise ValueError("ins[r] must hold exactly chunk r of the balanced split")
+    n, count, dev = _chunk_tensors(outs, ins, "ins")
     arr_in = (ctypes.c_void_p * n)(*[_ptr(i) for i in ins])
     arr_out = (ctypes.c_void_p * n)(*[t.data_ptr() for t in outs])
-    _check(lib().ar_all_gather(arr_in, arr_out, n, count, dtype_code(outs[0].dtype), _stream(stream)),
-           "ar_all_gather")
+    with _on(dev):
+        _check(lib().ar_all_gather(arr_in, arr_out, n, count, dtype_code(outs[0].dtype), _stream(stream, dev)),
+               "ar_all_gather")
 
 
 def ar_bucket_plan(numels, dtype, nranks, cap_bytes=25 << 20):
@@ -230,31 +284,50 @@ def make_copy_descs(tasks, device):
     return torch.from_numpy(host).to(device)
 
 
+def _copy_descs(descs):
+    import torch
+    _gpu_tensor(descs, "descs", torch.int64)
+    if descs.dim() != 2 or descs.shape[1] != 4:
+        raise ValueError("descs must be an int64 tensor [ndescs, 4] (ar_copy_desc rows)")
+    return descs.device
+
+
 def ar_bucket_pack(descs, dtype, stream=None):
-    _check(lib().ar_bucket_pack(ctypes.c_void_p(descs.data_ptr()), descs.shape[0], dtype, _stream(stream)),
-           "ar_bucket_pack")
+    dev = _copy_descs(descs)
+    with _on(dev):
+        _check(lib().ar_bucket_pack(ctypes.c_void_p(descs.data_ptr()), descs.shape[0], dtype, _stream(stream, dev)),
+               "ar_bucket_pack")
 
 
 def ar_bucket_unpack(descs, dtype, stream=None):
-    _check(lib().ar_bucket_unpack(ctypes.c_void_p(descs.data_ptr()), descs.shape[0], dtype, _stream(stream)),
-           "ar_bucket_unpack")
+    dev = _copy_descs(descs)
+    with _on(dev):
+        _check(lib().ar_bucket_unpack(ctypes.c_void_p(descs.data_ptr()), descs.shape[0], dtype,
+                                      _stream(stream, dev)), "ar_bucket_unpack")
 
 
 def ar_fp8_quant(x, codes, scales, stream=None):
     """x: float32/bfloat16 GPU tensor; codes: uint8[numel]; scales: float32[ceil(numel/128)]."""
-    if codes.numel() < x.numel() or scales.numel() < (x.numel() + AR_FP8_BLOCK - 1) // AR_FP8_BLOCK:
-        raise ValueError("codes/scales too small")
-    _check(lib().ar_fp8_quant(ctypes.c_void_p(x.data_ptr()), dtype_code(x.dtype), x.numel(),
-                              ctypes.c_void_p(codes.data_ptr()), ctypes.c_void_p(scales.data_ptr()),
-                              _stream(stream)), "ar_fp8_quant")
+    import torch
+    dev = _gpu_tensor(x, "x").device
+    _gpu_tensor(codes, "codes", torch.uint8, dev, x.numel())
+    _gpu_tensor(scales, "scales", torch.float32, dev, (x.numel() + AR_FP8_BLOCK - 1) // AR_FP8_BLOCK)
+    with _on(dev):
+        _check(lib().ar_fp8_quant(ctypes.c_void_p(x.data_ptr()), dtype_code(x.dtype), x.numel(),
+                                  ctypes.c_void_p(codes.data_ptr()), ctypes.c_void_p(scales.data_ptr()),
+                                  _stream(stream, dev)), "ar_fp8_quant")
 
 
 def ar_fp8_dequant(codes, scales, out, stream=None):
-    if codes.numel() < out.numel() or scales.numel() < (out.numel() + AR_FP8_BLOCK - 1) // AR_FP8_BLOCK:
-        raise ValueError("codes/scales too small")
-    _check(lib().ar_fp8_dequant(ctypes.c_void_p(codes.data_ptr()), ctypes.c_void_p(scales.data_ptr()), out.numel(),
-                                ctypes.c_void_p(out.data_ptr()), dtype_code(out.dtype), _stream(stream)),
-           "ar_fp8_dequant")
+    """codes: uint8[numel]; scales: float32[ceil(numel/128)]; out: float32/bfloat16 GPU tensor of numel."""
+    import torch
+    dev = _gpu_tensor(out, "out").device
+    _gpu_tensor(codes, "codes", torch.uint8, dev, out.numel())
+    _gpu_tensor(scales, "scales", torch.float32, dev, (out.numel() + AR_FP8_BLOCK - 1) // AR_FP8_BLOCK)
+    with _on(dev):
+        _check(lib().ar_fp8_dequant(ctypes.c_void_p(codes.data_ptr()), ctypes.c_void_p(scales.data_ptr()),
+                                    out.numel(), ctypes.c_void_p(out.data_ptr()), dtype_code(out.dtype),
+                                    _stream(stream, dev)), "ar_fp8_dequant")
 
 
 def ar_auto_algo(nranks, count, dtype) -> int:

@@ -286,3 +286,79 @@ def test_last_call_record_is_per_thread():
         t.join()
     for k in range(4):
         assert seen[k]["nranks"] == 2 + k and seen[k]["status"] == ar.AR_ERR_INVALID
+
+
+# ---------------------------------------------------------------- binding: tensors are checked before any call
+class _StubTensor:
+    """Stands in for a GPU tensor in these host-only checks. data_ptr() raises, so an argument that slipped
+    through the binding's checks can never reach the library as an address."""
+
+    def __init__(self, numel, dtype, device="cuda:0", contiguous=True, shape=None):
+        import torch
+        self._n, self.dtype, self._c = numel, dtype, contiguous
+        self.device = torch.device(device)
+        self.shape = shape if shape is not None else (numel,)
+
+    def numel(self):
+        return self._n
+
+    def dim(self):
+        return len(self.shape)
+
+    def is_contiguous(self):
+        return self._c
+
+    def data_ptr(self):
+        raise AssertionError("an unchecked tensor reached the library call")
+
+
+def test_binding_rejects_host_noncontiguous_and_mismatched_rank_tensors():
+    import torch
+    cpu = [torch.zeros(16) for _ in range(2)]
+    with pytest.raises(ValueError, match="GPU tensor"):
+        ar.ar_allreduce(cpu, cpu)
+    nc = [_StubTensor(16, torch.float32, contiguous=False) for _ in range(2)]
+    with pytest.raises(ValueError, match="contiguous"):
+        ar.ar_allreduce(nc, nc)
+    mixed = [_StubTensor(16, torch.float32), _StubTensor(16, torch.bfloat16)]
+    with pytest.raises(ValueError, match="share dtype"):
+        ar.ar_allreduce(mixed, mixed)
+    ok = [_StubTensor(16, torch.float32) for _ in range(2)]
+    with pytest.raises(ValueError, match="workspace"):
+        ar.ar_allreduce_ws(ok, ok, workspace=torch.zeros(64, dtype=torch.uint8))
+
+
+def test_binding_checks_reduce_scatter_and_all_gather_chunks():
+    import torch
+    n, count = 4, 10  # chunks of 3, 3, 2, 2
+    full = [_StubTensor(count, torch.float32) for _ in range(n)]
+    with pytest.raises(ValueError, match="must be torch.float32"):
+        ar.ar_reduce_scatter(full, [_StubTensor(k, torch.bfloat16) for k in (3, 3, 2, 2)])
+    with pytest.raises(ValueError, match="exactly chunk 2"):
+        ar.ar_reduce_scatter(full, [_StubTensor(k, torch.float32) for k in (3, 3, 3, 2)])
+    with pytest.raises(ValueError, match="is None"):
+        ar.ar_all_gather([_StubTensor(3, torch.float32), None, _StubTensor(2, torch.float32),
+                          _StubTensor(2, torch.float32)], full)
+    with pytest.raises(ValueError, match="GPU tensor"):
+        ar.ar_all_gather([torch.zeros(k) for k in (3, 3, 2, 2)], full)
+    with pytest.raises(ValueError, match="cuda:0"):
+        ar.ar_reduce_scatter(full, [_StubTensor(k, torch.float32, device="cuda:1") for k in (3, 3, 2, 2)])
+
+
+def test_binding_checks_codec_and_descriptor_tensors():
+    import torch
+    x = _StubTensor(1000, torch.bfloat16)
+    with pytest.raises(ValueError, match="codes must be torch.uint8"):
+        ar.ar_fp8_quant(x, _StubTensor(1000, torch.float16), _StubTensor(8, torch.float32))
+    with pytest.raises(ValueError, match="scales must hold at least 8"):
+        ar.ar_fp8_quant(x, _StubTensor(1000, torch.uint8), _StubTensor(7, torch.float32))
+    with pytest.raises(ValueError, match="scales must be torch.float32"):
+        ar.ar_fp8_dequant(_StubTensor(1000, torch.uint8), _StubTensor(8, torch.float16), x)
+    with pytest.raises(ValueError, match="descs must be torch.int64"):
+        ar.ar_allreduce_tensors(_StubTensor(8, torch.int32), _StubTensor(4, torch.int64), _StubTensor(4, torch.int64),
+                                2, 2, ar.AR_F32)
+    with pytest.raises(ValueError, match="in_ptrs must hold at least 4"):
+        ar.ar_allreduce_tensors(_StubTensor(8, torch.int64), _StubTensor(3, torch.int64), _StubTensor(4, torch.int64),
+                                2, 2, ar.AR_F32)
+    with pytest.raises(ValueError, match=r"\[ndescs, 4\]"):
+        ar.ar_bucket_pack(_StubTensor(12, torch.int64, shape=(3, 4, 1)), ar.AR_F32)
