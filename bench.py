@@ -168,6 +168,35 @@ def cpu_baseline(host, budget_s=10.0, max_reps=5):
                       f"{reps} repetition(s), {t:.2f} s each"}
 
 
+def host_info(host, frac=8):
+    """The host the oracle ran on, and the oracle on one thread over a 1/frac prefix of every headline rank."""
+    import oracle as _o
+    model = "unknown"
+    try:
+        with open("/proc/cpuinfo") as f:
+            for ln in f:
+                if ln.startswith("model name"):
+                    model = ln.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    m = COUNT // frac
+    sample = [np.ascontiguousarray(h[:m]) for h in host]
+    default_threads = _o.num_threads()
+    _o.set_num_threads(1)
+    try:
+        t0 = time.perf_counter()
+        _o.ring_allreduce(sample, _o.BF16, _o.AVG)
+        t = time.perf_counter() - t0
+    finally:
+        _o.set_num_threads(0)
+    S = m * 2
+    return {"cpu_model": model, "logical_cpus": os.cpu_count(), "usable_cpus": len(os.sched_getaffinity(0)),
+            "oracle_threads": default_threads,
+            "oracle_one_thread": {"s": t, "busbw_GBps": S / t / GB * bus_factor(N_RANKS),
+                                  "sample": f"first {m} elements of each of the {N_RANKS} headline ranks"}}
+
+
 def ring_bytes(n, count, es):
     return 2 * n * count * es
 
@@ -608,6 +637,8 @@ def main():
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": PEAK_HBM_GBPS, "unit": "GB/s",
                      "frac": achieved / PEAK_HBM_GBPS,
                      "traffic": traffic},
+        # the counted HBM bytes of one launch over the same measured time (null while the counters are stale)
+        "hbm_counter_GBps": traffic / (float(np.mean(ms)) * 1e-3) / GB if traffic else None,
     }
     if not args.headline_only:
         result["copy_ceiling_GBps"] = copy_ceiling(torch, ins, outs)
@@ -619,6 +650,7 @@ def main():
         torch.cuda.empty_cache()
         log("timing the CPU oracle")
         result["cpu_baseline"] = cpu_baseline(host)
+        result["host"] = host_info(host)
     print(json.dumps(result))
 
 

@@ -66,6 +66,8 @@ def lib():
         L.oracle_bucketed_allreduce.argtypes = [pp, pp, i32, i32, vp, i32, i32, i64]
         L.oracle_bucketed_allreduce.restype = i32
         L.oracle_num_threads.restype = i32
+        L.oracle_set_num_threads.argtypes = [i32]
+        L.oracle_set_num_threads.restype = None
         L.oracle_version.restype = i32
         _lib = L
     return _lib
@@ -238,3 +240,8 @@ def bucketed_allreduce(tensors, dtype=F32, op=AVG, cap_bytes=25 << 20):
 
 def num_threads():
     return lib().oracle_num_threads()
+
+
+def set_num_threads(n):
+    """Threads for the following calls (n < 1: the default); results do not depend on it."""
+    lib().oracle_set_num_threads(int(n))

@@ -71,6 +71,18 @@ int oracle_num_threads(void) {
 #endif
 }
 
+/* Threads for the following calls (timing only: every routine gives the same bits for any thread count, since
+ * the threads split independent elements). n < 1 restores the default. */
+void oracle_set_num_threads(int n) {
+#ifdef _OPENMP
+    static int dflt = 0;
+    if (dflt == 0) dflt = omp_get_max_threads();
+    omp_set_num_threads(n >= 1 ? n : dflt);
+#else
+    (void)n;
+#endif
+}
+
 /* ------------------------------------------------------------------------------------------------ */
 /* Number formats, from their definitions.                                                           */
 /* ------------------------------------------------------------------------------------------------ */

@@ -602,3 +602,20 @@ def test_tree_worked_example_and_integer_ops():
         np.testing.assert_array_equal(oracle.tree_allreduce(xs, oracle.I32, op)[0],
                                       oracle.ring_allreduce(xs, oracle.I32, op)[0])
     assert ring.dtype == np.int32
+
+
+def test_oracle_results_do_not_depend_on_its_thread_count():
+    """The oracle's threads split independent elements, so one thread gives the same bits (timing uses both)."""
+    n, count = 5, 10_007
+    xs = inputs.rank_inputs("uniform_bf16", n, count, cfg=61, extra=(n, count))
+    want = [oracle.ring_allreduce(xs, oracle.BF16, oracle.AVG), oracle.fp8_ring_allreduce(xs, oracle.BF16, oracle.SUM),
+            oracle.tree_allreduce(xs, oracle.BF16, oracle.SUM)]
+    oracle.set_num_threads(1)
+    try:
+        got = [oracle.ring_allreduce(xs, oracle.BF16, oracle.AVG), oracle.fp8_ring_allreduce(xs, oracle.BF16, oracle.SUM),
+               oracle.tree_allreduce(xs, oracle.BF16, oracle.SUM)]
+    finally:
+        oracle.set_num_threads(0)
+    for w, g in zip(want, got):
+        for a, b in zip(w, g):
+            np.testing.assert_array_equal(np.asarray(a), np.asarray(b))
