@@ -3,7 +3,8 @@
 - headline: 8 ranks x 134,217,728 bf16 (256 MiB each), fp32 ring-order sum, /8, bf16 out: every element of
   every rank, bit for bit; the same inputs through reduce-scatter + all-gather and through the binomial tree.
 - compressed ring: 8 ranks x 67,108,864 bf16 with 0.1% outliers x100, E4M3 blocks of 128: every element.
-- beyond 2^31 elements: 3 ranks x (2^31 + 1001) bf16 in place, sampled against the oracle.
+- beyond 2^31 elements: 3 ranks x (2^31 + 1001) bf16 in place (ring, tree, rank order, a common offset and
+  per-rank offsets), sampled against the oracle.
 - largest sweep point: 8 ranks x 268,435,456 fp32 (1 GiB each): ring and ring-stepwise, every element; the
   rank-order and halving-doubling variants (which do not depend on chunk positions) on 2^20 sampled elements,
   for which the oracle is evaluated on exactly those elements.
@@ -85,18 +86,26 @@ def test_headline_size_reduce_scatter_all_gather_and_tree():
     np.testing.assert_array_equal(_down_bits(outs[6]), oracle.tree_allreduce(host, oracle.BF16, oracle.AVG)[0])
 
 
+BEYOND_2_31 = [("ring", ar.AR_ALGO_RING, (0, 0, 0)), ("tree", ar.AR_ALGO_TREE, (0, 0, 0)),
+               ("fused", ar.AR_ALGO_FUSED, (0, 0, 0)), ("ring_common_offset", ar.AR_ALGO_RING, (3, 3, 3)),
+               ("ring_per_rank_offsets", ar.AR_ALGO_RING, (0, 1, 2))]
+
+
 @pytest.mark.timeout(900)
-def test_ring_beyond_two_to_the_31_elements_sampled():
-    """Maximum size: 3 ranks x (2^31 + 1001) bf16 (4 GiB each), in place, avg, through the one-front kernel with
-    64-bit element and byte offsets. Sampled positions (random, both ends, around every chunk boundary) against the
-    oracle: each chunk's samples go into the same chunk of a small array, so the oracle folds them from the same
-    rank as the ring does at full size."""
+@pytest.mark.parametrize("name,algo,offs", BEYOND_2_31, ids=[c[0] for c in BEYOND_2_31])
+def test_beyond_two_to_the_31_elements_sampled(name, algo, offs):
+    """Maximum size: 3 ranks x (2^31 + 1001) bf16 (4 GiB each), in place, avg, with 64-bit element and byte
+    offsets: the one-front ring kernel, the one-pass tree and rank-order kernels, a common offset (head, then
+    slots) and per-rank offsets (element by element). Sampled positions (random, both ends, around every chunk
+    boundary) against the oracle. For the ring each chunk's samples go into the same chunk of a small array, so
+    the oracle folds them from the same rank as the ring does at full size; the other orders do not depend on
+    the position."""
     n, count = 3, (1 << 31) + 1001
     g = torch.Generator(device=DEV)
     g.manual_seed(2031)
     bufs = []
-    for _ in range(n):
-        t = torch.empty(count, dtype=torch.bfloat16, device=DEV)
+    for r in range(n):
+        t = torch.empty(count + 8, dtype=torch.bfloat16, device=DEV)[offs[r]:offs[r] + count]
         for s0 in range(0, count, 1 << 28):
             m = min(1 << 28, count - s0)
             t[s0:s0 + m] = (torch.randn(m, generator=g, device=DEV) * 1e-3).to(torch.bfloat16)
@@ -107,21 +116,26 @@ def test_ring_beyond_two_to_the_31_elements_sampled():
                                    + [np.arange(b - 40, b + 40) for b in lo[1:-1]]))
     idx = torch.from_numpy(pos).to(DEV)
     samples = [_down_bits(b[idx]) for b in bufs]
-    ar.ar_allreduce(bufs, bufs, ar.AR_AVG, ar.AR_ALGO_RING)
+    ar.ar_allreduce(bufs, bufs, ar.AR_AVG, algo)
     torch.cuda.synchronize()
     got = [_down_bits(b[idx]) for b in bufs]
     del bufs
-    chunk_of = np.searchsorted(lo, pos, side="right") - 1
-    want = np.empty(len(pos), np.uint16)
-    for c in range(n):
-        sel = np.nonzero(chunk_of == c)[0]
-        k = len(sel)
-        small = [np.zeros(n * k, np.uint16) for _ in range(n)]
-        for r in range(n):
-            small[r][c * k:(c + 1) * k] = samples[r][sel]
-        want[sel] = oracle.ring_allreduce(small, oracle.BF16, oracle.AVG)[0][c * k:(c + 1) * k]
+    torch.cuda.empty_cache()
+    if algo == ar.AR_ALGO_RING:
+        chunk_of = np.searchsorted(lo, pos, side="right") - 1
+        want = np.empty(len(pos), np.uint16)
+        for c in range(n):
+            sel = np.nonzero(chunk_of == c)[0]
+            k = len(sel)
+            small = [np.zeros(n * k, np.uint16) for _ in range(n)]
+            for r in range(n):
+                small[r][c * k:(c + 1) * k] = samples[r][sel]
+            want[sel] = oracle.ring_allreduce(small, oracle.BF16, oracle.AVG)[0][c * k:(c + 1) * k]
+    else:
+        fn = oracle.tree_allreduce if algo == ar.AR_ALGO_TREE else oracle.fused_allreduce
+        want = np.asarray(fn(samples, oracle.BF16, oracle.AVG)[0])
     for r in range(n):
-        np.testing.assert_array_equal(got[r], want)
+        np.testing.assert_array_equal(got[r], want, err_msg=f"{name} rank {r}")
 
 
 @pytest.mark.timeout(600)
