@@ -218,7 +218,6 @@ int rsag_impl(const char* entry, const void* const* full, const void* const* par
   const size_t q = count / nranks, rr = count % nranks;
   Range ranges[2 * AR_MAX_RANKS];
   int m = 0;
-  bool vec = true;
   for (int r = 0; r < nranks; ++r) {
     const size_t lo = r * q + (static_cast<size_t>(r) < rr ? r : rr), len = q + (static_cast<size_t>(r) < rr ? 1 : 0);
     const uintptr_t f = reinterpret_cast<uintptr_t>(full[r]), c = reinterpret_cast<uintptr_t>(part[r]);
@@ -227,7 +226,6 @@ int rsag_impl(const char* entry, const void* const* full, const void* const* par
     if (f > UINTPTR_MAX - bytes || (c && c > UINTPTR_MAX - len * es)) return done(AR_ERR_INVALID);
     ranges[m++] = Range{f, f + bytes};
     if (len > 0 && c != f + lo * es) ranges[m++] = Range{c, c + len * es};
-    if ((f | c) & 15u) vec = false;
   }
   if (any_overlap(ranges, m)) return done(AR_ERR_ALIAS);
   ar::RankPtrs p;
@@ -237,8 +235,8 @@ int rsag_impl(const char* entry, const void* const* full, const void* const* par
     p.out[r] = is_rs ? writable_part[r] : writable_full[r];
   }
   hipStream_t s = static_cast<hipStream_t>(stream);
-  hipError_t e = is_rs ? ar::launch_reduce_scatter(p, nranks, static_cast<int64_t>(count), dtype, op, vec, s)
-                       : ar::launch_all_gather(p, nranks, static_cast<int64_t>(count), static_cast<int>(es), vec, s);
+  hipError_t e = is_rs ? ar::launch_reduce_scatter(p, nranks, static_cast<int64_t>(count), dtype, op, s)
+                       : ar::launch_all_gather(p, nranks, static_cast<int64_t>(count), static_cast<int>(es), s);
   return done(e == hipSuccess ? AR_OK : AR_ERR_HIP);
 }
 

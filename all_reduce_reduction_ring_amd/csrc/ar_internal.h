@@ -46,8 +46,9 @@ hipError_t launch_tensors(const ar_tensor_desc* d_descs, const void* const* d_in
                           int n, int dtype, int op, int algo, hipStream_t s);
 
 // Standalone reduce-scatter (chunk c folded from rank c into out[c]) and all-gather (in[c] -> chunk c of all).
-hipError_t launch_reduce_scatter(const RankPtrs& p, int n, int64_t count, int dtype, int op, bool vec, hipStream_t s);
-hipError_t launch_all_gather(const RankPtrs& p, int n, int64_t count, int esize, bool vec, hipStream_t s);
+// The vector path is planned from the pointers themselves (any alignment; see ar_rsag.hip).
+hipError_t launch_reduce_scatter(const RankPtrs& p, int n, int64_t count, int dtype, int op, hipStream_t s);
+hipError_t launch_all_gather(const RankPtrs& p, int n, int64_t count, int esize, hipStream_t s);
 
 // Round-per-launch schedules. ws: fp32 partial mirror (n * ws_stride floats) for 16-bit types, else null.
 int64_t stepwise_ws_stride(int64_t count);

@@ -11,13 +11,19 @@
 // to every rank.
 //
 // Chunks are the balanced split used everywhere in the library (count/N + 1 elements for c < count%N). The 16-byte
-// vector path needs every buffer 16-byte aligned. A chunk start that falls inside a slot is handled by loading the
-// two aligned slots around each vector and shifting them together in registers; a chunk's few elements outside
-// its vector slots go one by one. Unaligned buffers go element by element, with one grid row per chunk.
+// vector path works on aligned slots on both sides: the full buffers (N ranks at one address modulo 16) are cut
+// into a head of elements and 16-byte slots, each chunk buffer likewise. Where a chunk's data sits at a different
+// position within a slot on the two sides, each vector is assembled from the two aligned slots around it, shifted
+// together in registers; in place (chunk buffer c inside full buffer c at its own chunk) both grids coincide and
+// nothing is shifted. The host works out, per chunk, the slot range, the shift and the offset of the chunk
+// buffer's first vector; a chunk's few elements outside its vectors go one by one. Full buffers at different
+// addresses modulo 16 go element by element, with one grid row per chunk.
 //
 // The vector path runs on one front: tiles of kThreads slots of the whole buffer go round-robin to the blocks,
 // and each block walks the chunks in order, so all workgroups move through the rank buffers together (one
 // front per buffer instead of one per chunk, which MI355X's HBM serves faster).
+#include <cstring>
+
 #include "ar_device.h"
 #include "ar_internal.h"
 
@@ -26,48 +32,28 @@ namespace {
 
 constexpr int kThreads = 256;
 
+// Vector work of chunk c: full slots [w0[c], w1[c]) (full slot v = elements hf + vV .. hf + vV + V - 1 of every
+// full buffer, at byte hb + 16 v). The chunk buffer's vector that goes with full slot v starts cb[c] + 16 (v -
+// w0[c]) bytes into it.
+//   reduce-scatter: that output vector holds elements m.. of full slot v and ..m-1 of slot v + 1;
+//   all-gather: full slot v holds elements m.. of that chunk-buffer slot and ..m-1 of the next one.
+// The spans increase with c (a chunk without vector work sits at the slot of its end), as one_front needs.
 struct RsAgArgs {
-  RankPtrs p;
-  int64_t q, r;  // balanced split of count over n
+  RankPtrs p;  // reduce-scatter: in = full buffers, out = chunk buffers; all-gather: in = chunk buffers, out = full
+  int64_t q, r;      // balanced split of count over n
+  int64_t hf, hb;    // full-buffer head: elements, bytes
+  int64_t nslots;    // full slots after the head
+  int64_t w0[AR_MAX_RANKS], w1[AR_MAX_RANKS], cb[AR_MAX_RANKS];
+  int8_t m[AR_MAX_RANKS];
   int n;
-  int vec;  // every pointer 16-byte aligned (chunk starts need not be)
+  int vec;  // 1: the vector plan above holds; 0: element by element
 };
+static_assert(sizeof(RsAgArgs) <= 4096, "kernel arguments must fit in 4 KiB");
 
-// Work of one chunk on the vector path, in 16-byte slots of the full (N-chunk) buffers: slots [w0, w1) are done
-// as whole vectors; m is how many elements the chunk's start sits past a slot boundary (0 when aligned).
 struct Span {
   int64_t w0, w1;
   int m;
 };
-
-// Reduce-scatter, chunk c = [lo, hi): output slot k of the chunk buffer holds full-buffer elements lo + kV ..
-// lo + kV + V - 1, that is elements m.. of full slot lo/V + k and ..m-1 of the next one. Slots run [lo/V, lo/V + K)
-// with K the whole output slots, fewer when m > 0 and the next full slot would run past the end of the buffer.
-template <int V>
-__device__ __forceinline__ Span rs_span(const RsAgArgs& a, int64_t count, int c) {
-  const int64_t lo = chunk_lo(a.q, a.r, c), hi = chunk_lo(a.q, a.r, c + 1);
-  const int m = static_cast<int>(lo % V);
-  const int64_t b = lo / V;
-  int64_t k = (hi - lo) / V;
-  if (m != 0 && k > count / V - b - 1) k = count / V - b - 1;
-  if (k < 0) k = 0;
-  return Span{b, b + k, m};
-}
-
-// All-gather, chunk c = [lo, hi): the full-buffer slots wholly inside the chunk, [ceil(lo/V), ...). Slot v holds
-// chunk-buffer elements vV - lo ..: elements m.. of chunk slot v - w0 and ..m-1 of the next one, m = w0*V - lo;
-// the range stops where that next chunk slot would run past the chunk buffer's end.
-template <int V>
-__device__ __forceinline__ Span ag_span(const RsAgArgs& a, int c) {
-  const int64_t lo = chunk_lo(a.q, a.r, c), hi = chunk_lo(a.q, a.r, c + 1);
-  const int64_t w0 = (lo + V - 1) / V;
-  const int m = static_cast<int>(w0 * V - lo);
-  int64_t w1 = hi / V;
-  const int64_t lim = w0 + (hi - lo) / V - (m != 0 ? 1 : 0);
-  if (w1 > lim) w1 = lim;
-  if (w1 < w0) w1 = w0;
-  return Span{w0, w1, m};
-}
 
 // The 16 bytes that start M elements (of ES bytes) into x0 and run on into x1. M is a compile-time constant, so
 // every index below is one too and the result is assembled in registers.
@@ -93,9 +79,8 @@ __device__ __forceinline__ u32x4 shift_concat(const u32x4& x0, const u32x4& x1) 
 // thread owns. Tile t = slots [t * kThreads, (t + 1) * kThreads) goes to block t mod G; a block's tiles come in
 // increasing order and the chunks' slot ranges are disjoint and increasing, so the chunk loop is outside the tile
 // loop and c (and the span) is constant, and wave-uniform, inside it.
-template <int V, typename SP, typename F>
-__device__ __forceinline__ void one_front(int n, int64_t count, SP span_of, F fn) {
-  const int64_t nslots = count / V;
+template <typename SP, typename F>
+__device__ __forceinline__ void one_front(int n, int64_t nslots, SP span_of, F fn) {
   const int64_t ntiles = (nslots + kThreads - 1) / kThreads;
   int64_t t = blockIdx.x;
   int c0 = 0;  // the spans increase with c: a chunk whose successor starts at or before this tile has no work left
@@ -122,7 +107,7 @@ __device__ __forceinline__ u32x4 rs_slot(const RsAgArgs& a, int n, int c, int64_
   constexpr int V = S::V;
   typename S::Acc acc[V], t[V];
   auto load = [&](int rr) -> u32x4 {
-    const char* base = static_cast<const char*>(a.p.in[rr]) + v * 16;
+    const char* base = static_cast<const char*>(a.p.in[rr]) + a.hb + v * 16;
     if constexpr (M == 0) return ld16(base);
     else return shift_concat<Traits<DT>::kSize, M>(ld16(base), ld16(base + 16));
   };
@@ -194,17 +179,19 @@ template <int DT, int OP, int NR>
 __global__ __launch_bounds__(kThreads) void reduce_scatter_kernel(RsAgArgs a) {
   constexpr int V = Traits<DT>::kVec;
   const int n = NR > 0 ? NR : a.n;
-  const int64_t count = a.q * n + a.r;
   if (a.vec) {
-    one_front<V>(n, count, [&](int c) { return rs_span<V>(a, count, c); }, [&](int c, int64_t v, const Span& sp) {
+    one_front(n, a.nslots, [&](int c) { return Span{a.w0[c], a.w1[c], a.m[c]}; },
+              [&](int c, int64_t v, const Span& sp) {
       const u32x4 w = sp.m == 0 ? rs_slot<DT, OP, NR, 0>(a, n, c, v) : rs_slot_m<DT, OP, NR>(a, n, c, v, sp.m);
-      st16(static_cast<char*>(a.p.out[c]) + (v - sp.w0) * 16, w);
+      st16(static_cast<char*>(a.p.out[c]) + a.cb[c] + (v - sp.w0) * 16, w);
     });
-    if (blockIdx.x == 0) {  // each chunk's elements after its vector slots
+    if (blockIdx.x == 0) {  // each chunk's output elements before and after its vectors
       for (int c = 0; c < n; ++c) {
-        const int64_t lo = chunk_lo(a.q, a.r, c), hi = chunk_lo(a.q, a.r, c + 1);
-        const Span sp = rs_span<V>(a, count, c);
-        for (int64_t e = lo + (sp.w1 - sp.w0) * V + threadIdx.x; e < hi; e += kThreads) rs_elem<DT, OP>(a, n, c, lo, e);
+        const int64_t lo = chunk_lo(a.q, a.r, c), len = chunk_lo(a.q, a.r, c + 1) - lo;
+        const int64_t h = a.cb[c] / static_cast<int64_t>(Traits<DT>::kSize), h1 = h < len ? h : len;
+        for (int64_t i = threadIdx.x; i < h1; i += kThreads) rs_elem<DT, OP>(a, n, c, lo, lo + i);
+        for (int64_t i = h + (a.w1[c] - a.w0[c]) * V + threadIdx.x; i < len; i += kThreads)
+          rs_elem<DT, OP>(a, n, c, lo, lo + i);
       }
     }
   } else {
@@ -260,18 +247,18 @@ template <int ES>
 __global__ __launch_bounds__(kThreads) void all_gather_kernel(RsAgArgs a) {
   constexpr int V = 16 / ES;
   const int n = a.n;
-  const int64_t count = a.q * n + a.r;
   if (a.vec) {
-    one_front<V>(n, count, [&](int c) { return ag_span<V>(a, c); }, [&](int c, int64_t v, const Span& sp) {
-      const char* in = static_cast<const char*>(a.p.in[c]);
+    one_front(n, a.nslots, [&](int c) { return Span{a.w0[c], a.w1[c], a.m[c]}; },
+              [&](int c, int64_t v, const Span& sp) {
+      const char* in = static_cast<const char*>(a.p.in[c]) + a.cb[c];
       const u32x4 w = sp.m == 0 ? ag_load<ES, 0>(in, v - sp.w0) : ag_load_m<ES>(in, v - sp.w0, sp.m);
-      for (int r = 0; r < n; ++r) st16(static_cast<char*>(a.p.out[r]) + v * 16, w);
+      for (int r = 0; r < n; ++r) st16(static_cast<char*>(a.p.out[r]) + a.hb + v * 16, w);
     });
     if (blockIdx.x == 0) {  // each chunk's elements outside its vector slots
       for (int c = 0; c < n; ++c) {
         const int64_t lo = chunk_lo(a.q, a.r, c), hi = chunk_lo(a.q, a.r, c + 1);
-        const Span sp = ag_span<V>(a, c);
-        const int64_t h1 = sp.w0 < sp.w1 ? sp.w0 * V : hi, t0 = sp.w0 < sp.w1 ? sp.w1 * V : hi;
+        const bool any = a.w0[c] < a.w1[c];
+        const int64_t h1 = any ? a.hf + a.w0[c] * V : hi, t0 = any ? a.hf + a.w1[c] * V : hi;
         for (int64_t e = lo + threadIdx.x; e < h1; e += kThreads) ag_elem<ES>(a, n, c, lo, e);
         for (int64_t e = t0 + threadIdx.x; e < hi; e += kThreads) ag_elem<ES>(a, n, c, lo, e);
       }
@@ -289,7 +276,8 @@ __global__ __launch_bounds__(kThreads) void all_gather_kernel(RsAgArgs a) {
 // 1, 4 or 8 for the reduce-scatter on MI355X, 2.5% for the all-gather). Element path: one row per chunk.
 dim3 grid_for(const RsAgArgs& a, int V) {
   if (a.vec) {
-    const int64_t tiles = ((a.q * a.n + a.r) / V + kThreads - 1) / kThreads;
+    (void)V;
+    const int64_t tiles = (a.nslots + kThreads - 1) / kThreads;
     int64_t g = static_cast<int64_t>(cu_count()) * 2;
     if (g > tiles) g = tiles;
     if (g < 1) g = 1;
@@ -325,23 +313,95 @@ hipError_t rs_op(const RsAgArgs& a, int op, hipStream_t s) {
   }
 }
 
-RsAgArgs make_args(const RankPtrs& p, int n, int64_t count, bool vec, int V) {
+int64_t host_chunk_lo(int64_t q, int64_t r, int64_t c) { return c * q + (c < r ? c : r); }
+
+// The vector plan (see RsAgArgs). full[r]: the N full buffers; part[c]: the chunk buffers. Returns false, leaving
+// the element path, when the full buffers sit at different addresses modulo 16 or a pointer is not a multiple of
+// the element size.
+bool plan_vectors(RsAgArgs& a, const void* const* full, const void* const* part, int64_t count, int es, bool is_rs) {
+  const int64_t V = 16 / es;
+  const uintptr_t rf = reinterpret_cast<uintptr_t>(full[0]) % 16;
+  if (rf % es) return false;
+  for (int r = 0; r < a.n; ++r)
+    if (reinterpret_cast<uintptr_t>(full[r]) % 16 != rf) return false;
+  const int64_t hf = static_cast<int64_t>((16 - rf) % 16) / es;
+  a.hf = hf;
+  a.hb = hf * es;
+  a.nslots = count > hf ? (count - hf) / V : 0;
+  for (int c = 0; c < a.n; ++c) {
+    const int64_t lo = host_chunk_lo(a.q, a.r, c), hi = host_chunk_lo(a.q, a.r, c + 1), len = hi - lo;
+    const int64_t end_slot = hi > hf ? (hi - hf) / V : 0;  // where a chunk without vector work sits
+    int64_t w0 = end_slot, w1 = end_slot, cb = 0, m = 0;
+    if (len > 0) {
+      const uintptr_t rp = reinterpret_cast<uintptr_t>(part[c]) % 16;
+      if (rp % es) return false;
+      int64_t g = static_cast<int64_t>((16 - rp) % 16) / es;  // chunk-buffer elements before its first slot
+      if (is_rs) {
+        // output vector j = chunk elements g + jV ..: full elements lo + g + jV .., at full-grid position rel + jV
+        int64_t rel = lo + g - hf;
+        if (rel < 0) {  // the first chunk-buffer slots start before the full grid: leave them to the elements
+          g += (-rel + V - 1) / V * V;
+          rel = lo + g - hf;
+        }
+        int64_t k = len > g ? (len - g) / V : 0;
+        const int64_t b = rel / V;
+        m = rel % V;
+        const int64_t lim = a.nslots - b - (m ? 1 : 0);  // the shifted read takes slot b + j + 1 too
+        if (k > lim) k = lim;
+        if (k > 0) {
+          w0 = b;
+          w1 = b + k;
+        }
+        cb = g * es;
+      } else {
+        // full slots wholly inside the chunk; full slot v = chunk elements hf + vV - lo .., at d + (v - vs)V past
+        // the chunk buffer's first slot
+        int64_t vs = lo > hf ? (lo - hf + V - 1) / V : 0;
+        const int64_t ve0 = end_slot;
+        int64_t d = hf + vs * V - lo - g;
+        if (d < 0) {
+          const int64_t skip = (-d + V - 1) / V;
+          vs += skip;
+          d += skip * V;
+        }
+        const int64_t k0 = d / V;
+        m = d % V;
+        const int64_t nps = len > g ? (len - g) / V : 0;  // whole chunk-buffer slots
+        int64_t ve = vs + nps - k0 - (m ? 1 : 0);         // the shifted read takes chunk slot k + 1 too
+        if (ve > ve0) ve = ve0;
+        if (ve > vs) {
+          w0 = vs;
+          w1 = ve;
+          cb = (g + k0 * V) * es;
+        }
+      }
+    }
+    a.w0[c] = w0;
+    a.w1[c] = w1;
+    a.cb[c] = cb;
+    a.m[c] = static_cast<int8_t>(m);
+  }
+  return true;
+}
+
+RsAgArgs make_args(const RankPtrs& p, int n, int64_t count, int es, bool is_rs) {
   RsAgArgs a;
+  std::memset(&a, 0, sizeof(a));
   a.p = p;
   a.n = n;
   a.q = count / n;
   a.r = count % n;
-  (void)count;
-  (void)V;
-  a.vec = vec ? 1 : 0;  // chunk starts off slot boundaries take the shifted vector path
+  const void* const* full = is_rs ? p.in : const_cast<const void* const*>(p.out);
+  const void* const* part = is_rs ? const_cast<const void* const*>(p.out) : p.in;
+  a.vec = plan_vectors(a, full, part, count, es, is_rs) ? 1 : 0;
   return a;
 }
 
 }  // namespace
 
-hipError_t launch_reduce_scatter(const RankPtrs& p, int n, int64_t count, int dtype, int op, bool vec, hipStream_t s) {
-  const int V = (dtype == AR_BF16 || dtype == AR_F16) ? 8 : 4;
-  const RsAgArgs a = make_args(p, n, count, vec, V);
+hipError_t launch_reduce_scatter(const RankPtrs& p, int n, int64_t count, int dtype, int op, hipStream_t s) {
+  const int es = (dtype == AR_BF16 || dtype == AR_F16) ? 2 : 4;
+  const RsAgArgs a = make_args(p, n, count, es, true);
   switch (dtype) {
     case AR_F32: return rs_op<AR_F32>(a, op, s);
     case AR_BF16: return rs_op<AR_BF16>(a, op, s);
@@ -351,9 +411,9 @@ hipError_t launch_reduce_scatter(const RankPtrs& p, int n, int64_t count, int dt
   }
 }
 
-hipError_t launch_all_gather(const RankPtrs& p, int n, int64_t count, int esize, bool vec, hipStream_t s) {
+hipError_t launch_all_gather(const RankPtrs& p, int n, int64_t count, int esize, hipStream_t s) {
   const int V = 16 / esize;
-  const RsAgArgs a = make_args(p, n, count, vec, V);
+  const RsAgArgs a = make_args(p, n, count, esize, false);
   const dim3 g = grid_for(a, V);
   if (esize == 4) hipLaunchKernelGGL((all_gather_kernel<4>), g, dim3(kThreads), 0, s, a);
   else hipLaunchKernelGGL((all_gather_kernel<2>), g, dim3(kThreads), 0, s, a);

@@ -150,8 +150,10 @@ int ar_allreduce(const void* const* in_bufs, void* const* out_bufs, int nranks, 
  *   out_bufs: host array; out_bufs[c] points to the count/N (+1 when c < count%N) elements of chunk c; it may
  *     be NULL when that chunk is empty. In place: out_bufs[c] == in_bufs[c] + (start of chunk c); any other
  *     overlap -> AR_ERR_ALIAS. Errors as ar_allreduce.
- * Alignment (both calls): any. When every pointer is 16-byte aligned the work goes in 16-byte vectors, also for
- * chunks whose start falls inside a 16-byte slot; otherwise element by element. */
+ * Alignment (both calls): any. When the N full buffers share one address modulo 16 (and every pointer is a
+ * multiple of the element size) the work goes in 16-byte vectors, whatever the chunk buffers' offsets and chunk
+ * starts: in place at full speed, otherwise with each vector assembled from two aligned loads. Full buffers at
+ * different addresses modulo 16 go element by element. */
 int ar_reduce_scatter(const void* const* in_bufs, void* const* out_bufs, int nranks, size_t count, int dtype, int op,
                       void* stream);
 

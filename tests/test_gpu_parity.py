@@ -609,6 +609,39 @@ def test_reduce_scatter_and_all_gather_match_oracle(n, count, dt):
     assert_bitwise([from_dev(f, dt) for f in full], [np.asarray(w).view(NP_BITS[dt]) for w in want], "all-gather")
 
 
+@pytest.mark.parametrize("layout", ["full_at_common_offset", "chunks_at_offsets", "both_offset",
+                                    "full_at_different_offsets", "in_place_full_offset"])
+@pytest.mark.parametrize("n,count", [(3, 5003), (8, 1_200_013), (5, 80_003)])
+@pytest.mark.parametrize("dt", [ar.AR_F32, ar.AR_BF16])
+def test_reduce_scatter_and_all_gather_at_any_alignment(layout, n, count, dt):
+    """Full buffers and chunk buffers at any element offset: a common offset of the full buffers (a head, then
+    slots), chunk buffers at assorted offsets (each vector assembled from two aligned slots), in place inside
+    offset full buffers (no shift), and full buffers at different residues (element by element). Every result
+    bit-exact against the oracle; RS then AG equals the ring all-reduce."""
+    xs = _inputs(dt, n, count, 53)
+    lo = ar.chunk_bounds(count, n)
+    full_off = {"full_at_common_offset": [3] * n, "chunks_at_offsets": [0] * n, "both_offset": [1] * n,
+                "full_at_different_offsets": list(range(n)), "in_place_full_offset": [5] * n}[layout]
+    part_off = [(c * 3 + 1) % 8 for c in range(n)] if layout in ("chunks_at_offsets", "both_offset") else [0] * n
+    full = [to_dev(x, dt, offset=full_off[r])[1] for r, x in enumerate(xs)]
+    if layout == "in_place_full_offset":
+        parts = [full[c][lo[c]:lo[c + 1]] for c in range(n)]
+    else:
+        parts = [empty_like_dev(lo[c + 1] - lo[c], dt, offset=part_off[c])[1] for c in range(n)]
+    ar.ar_reduce_scatter(full, parts, ar.AR_SUM)
+    torch.cuda.synchronize()
+    want = oracle.reduce_scatter(xs, ORACLE_DT[dt], ORACLE_OP[ar.AR_SUM])
+    for c in range(n):
+        np.testing.assert_array_equal(from_dev(parts[c], dt), np.asarray(want[c]).view(NP_BITS[dt]),
+                                      err_msg=f"reduce-scatter {layout} chunk {c}")
+    outs = full if layout == "in_place_full_offset" else [empty_like_dev(count, dt, offset=full_off[r])[1]
+                                                          for r in range(n)]
+    ar.ar_all_gather(parts, outs)
+    torch.cuda.synchronize()
+    assert_bitwise([from_dev(o, dt) for o in outs], expect(xs, dt, ar.AR_SUM, ar.AR_ALGO_RING),
+                   f"RS then AG {layout} n={n} count={count}")
+
+
 def test_reduce_scatter_all_gather_page_examples_and_in_place():
     # two-rank reduce-scatter halves and the four-rank all-gather placement (tests/golden fixtures)
     ins = [torch.tensor(v, dtype=torch.int32, device=DEV) for v in ([1, 2, 3, 4], [10, 20, 30, 40])]
