@@ -694,3 +694,45 @@ def test_allreduce_on_a_side_stream_beside_other_kernels_is_bit_exact():
     assert_bitwise([from_dev(o, ar.AR_BF16) for o in outs], expect(xs, ar.AR_BF16, ar.AR_AVG, ar.AR_ALGO_RING),
                    "side stream")
     assert torch.equal(dst, src)
+
+
+def test_concurrent_calls_from_host_threads_on_their_own_streams():
+    """The library keeps no shared state across calls (the last-call record is per thread): four host threads,
+    each with its own stream, algorithm and inputs, call at once; every result matches the oracle and every
+    thread sees its own last call."""
+    import threading
+    cases = [(ar.AR_ALGO_RING, ar.AR_BF16, 8, 2_000_003), (ar.AR_ALGO_TREE, ar.AR_F32, 5, 700_001),
+             (ar.AR_ALGO_FUSED, ar.AR_BF16, 3, 900_007), (ar.AR_ALGO_RHD, ar.AR_I32, 4, 1_000_003)]
+    data = []
+    for k, (algo, dt, n, count) in enumerate(cases):
+        xs = _inputs(dt, n, count, 70 + k)
+        ins = [to_dev(x, dt)[1] for x in xs]
+        outs = [empty_like_dev(count, dt)[1] for _ in range(n)]
+        data.append((xs, ins, outs, torch.cuda.Stream()))
+    torch.cuda.synchronize()
+    barrier = threading.Barrier(len(cases))
+    records, errors = [None] * len(cases), []
+
+    def work(k):
+        try:
+            algo, dt, n, count = cases[k]
+            _, ins, outs, s = data[k]
+            barrier.wait()
+            for _ in range(3):
+                ar.ar_allreduce(ins, outs, ar.AR_SUM, algo, stream=s)
+            records[k] = ar.ar_last_call()
+            s.synchronize()
+        except Exception as e:  # reported by the main thread
+            errors.append(e)
+
+    threads = [threading.Thread(target=work, args=(k,)) for k in range(len(cases))]
+    for t in threads:
+        t.start()
+    for t in threads:
+        t.join(timeout=60)
+    assert not errors, errors
+    torch.cuda.synchronize()
+    for k, (algo, dt, n, count) in enumerate(cases):
+        xs, _, outs, _ = data[k]
+        assert records[k]["algo"] == algo and records[k]["count"] == count and records[k]["nranks"] == n
+        assert_bitwise([from_dev(o, dt) for o in outs], expect(xs, dt, ar.AR_SUM, algo), f"thread {k} algo {algo}")
