@@ -348,12 +348,17 @@ def other_rows(torch, ar, inputs, ins, outs, dev, reps, host):
     fn = lambda: ar.ar_fp8_quant(i8[0], codes, scales)
     fn()
     qb = n8 * 2 + n8 + n8 // 128 * 4
-    rows["fp8_quant"] = row_entry("fp8_quant", timer.run(fn, reps), qb, n8 * 2, 1, {"count": n8})
+    # the codec kernels run shorter than a host call: timed as 20 calls in one HIP graph, per-call events beside
+    rows["fp8_quant"] = row_entry("fp8_quant", graph_ms(torch, fn), qb, n8 * 2, 1,
+                                  {"count": n8, "timing": "HIP graph of 20 calls",
+                                   "us_per_call_events": stats_us(timer.run(fn, reps))})
     rows["fp8_quant"]["cpu_oracle"] = cpu_row(oracle_time(_o.fp8_quant, h8[0], _o.BF16), n8 * 2, 1,
                                               "one rank's 67,108,864 bf16, one call")
     fn = lambda: ar.ar_fp8_dequant(codes, scales, o8[0])
     fn()
-    rows["fp8_dequant"] = row_entry("fp8_dequant", timer.run(fn, reps), qb, n8 * 2, 1, {"count": n8})
+    rows["fp8_dequant"] = row_entry("fp8_dequant", graph_ms(torch, fn), qb, n8 * 2, 1,
+                                    {"count": n8, "timing": "HIP graph of 20 calls",
+                                     "us_per_call_events": stats_us(timer.run(fn, reps))})
     del i8, o8, codes, scales, h8
     torch.cuda.empty_cache()
 
@@ -396,6 +401,24 @@ def other_rows(torch, ar, inputs, ins, outs, dev, reps, host):
                                             N_RANKS, f"the first {k} of the 300 tensors ({s_k} bytes per rank): "
                                                      "plan, pack, per-bucket literal rings, unpack")
     return rows
+
+
+def graph_ms(torch, call, calls=20, replays=5):
+    """Per-call device times (ms, one per replay) of `calls` back-to-back calls captured in one HIP graph: for
+    kernels shorter than the host's cost of a call, whose per-call events would time the launch gaps."""
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        call()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        for _ in range(calls):
+            call()
+    g.replay()
+    torch.cuda.synchronize()
+    return [m / calls for m in Timer(torch).run(g.replay, replays)]
 
 
 def graph_time_us(torch, call, calls, replays=5):
