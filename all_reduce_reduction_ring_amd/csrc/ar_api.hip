@@ -43,6 +43,7 @@ hipError_t launch_collapsed(const RankPtrs& p, int n, int64_t count, int dtype, 
 
 // Measured on MI355X (N = 8, 256 MiB bf16 per rank, in place): slots starting 16 bytes past a 256-byte boundary
 // ran 24% slower than aligned ones, 64 bytes past 10%, 128 bytes past 2.5%; a multiple of 256 bytes matched.
+// Buffers whose addresses differ modulo 16 but are all multiples of 4 take slots from element 0.
 int64_t vector_head(const RankPtrs& p, int n, int64_t count, int esize) {
   constexpr uintptr_t kWide = 256, kNarrow = 16;
   constexpr int64_t kWideMinBytes = 1 << 20;
@@ -57,7 +58,11 @@ int64_t vector_head(const RankPtrs& p, int n, int64_t count, int esize) {
     const int64_t head = static_cast<int64_t>(((al - res) % al) / static_cast<uintptr_t>(esize));
     return head < count ? head : count;
   }
-  return -1;
+  // Addresses that differ modulo 16: the 16-byte accesses need only 4-byte alignment, so slots from element 0
+  // still work when every address is a multiple of 4 (some vectors then straddle two cache lines).
+  for (int r = 0; r < n; ++r)
+    if ((reinterpret_cast<uintptr_t>(p.in[r]) | reinterpret_cast<uintptr_t>(p.out[r])) % 4 != 0) return -1;
+  return 0;
 }
 
 hipError_t launch_segments(const RankPtrs& p, int n, const int64_t* counts, int nseg, int dtype, int op, int algo,

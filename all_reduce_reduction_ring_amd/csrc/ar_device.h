@@ -154,9 +154,14 @@ template <int DT> __device__ __forceinline__ void store_elem(void* base, int64_t
 }
 
 // Streaming 16-byte loads and stores. Each element is read once and written once per call, so the data
-// is marked non-temporal to keep it from displacing anything useful in the caches.
-__device__ __forceinline__ u32x4 ld16(const void* p) { return __builtin_nontemporal_load(gptr<u32x4>(p)); }
-__device__ __forceinline__ void st16(void* p, const u32x4& v) { __builtin_nontemporal_store(v, gptr<u32x4>(p)); }
+// is marked non-temporal to keep it from displacing anything useful in the caches. The address needs 4-byte
+// alignment only: a dword-aligned global_load_dwordx4 / global_store_dwordx4 is a legal access on gfx950, and the
+// type below tells the compiler so without changing the instruction (the same single dwordx4 as for 16-byte
+// aligned data). Callers still start slots on 16-byte (or 256-byte) boundaries wherever the buffers allow:
+// a vector that straddles two cache lines costs more.
+typedef u32x4 u32x4_a4 __attribute__((aligned(4)));
+__device__ __forceinline__ u32x4 ld16(const void* p) { return __builtin_nontemporal_load(gptr<u32x4_a4>(p)); }
+__device__ __forceinline__ void st16(void* p, const u32x4& v) { __builtin_nontemporal_store(v, gptr<u32x4_a4>(p)); }
 
 // Balanced chunk split: chunk c = [c*q + min(c, r), ...) with q = count / N, r = count % N.
 __device__ __forceinline__ int64_t chunk_lo(int64_t q, int64_t r, int64_t c) { return c * q + (c < r ? c : r); }

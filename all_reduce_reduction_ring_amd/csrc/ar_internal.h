@@ -25,8 +25,9 @@ hipError_t launch_collapsed(const RankPtrs& p, int n, int64_t count, int dtype, 
                             hipStream_t s);
 
 // The head for launch_collapsed: the fewest elements to skip in every buffer so that the rest starts at a multiple
-// of 256 bytes (buffers of 1 MiB and more) or of 16 bytes in all of them; -1 if the addresses of the buffers
-// (in and out) differ modulo 16 or are not multiples of the element size. Never more than count.
+// of 256 bytes (buffers of 1 MiB and more) or of 16 bytes in all of them. When the addresses (in and out) differ
+// modulo 16 but are all multiples of 4, 0 (16-byte accesses at 4-byte alignment); otherwise -1. Never more than
+// count.
 int64_t vector_head(const RankPtrs& p, int n, int64_t count, int esize);
 
 // Many buckets of flat per-rank buffers in as few launches as possible (each count a multiple of N slots).

@@ -17,7 +17,8 @@
 // together in registers; in place (chunk buffer c inside full buffer c at its own chunk) both grids coincide and
 // nothing is shifted. The host works out, per chunk, the slot range, the shift and the offset of the chunk
 // buffer's first vector; a chunk's few elements outside its vectors go one by one. Full buffers at different
-// addresses modulo 16 go element by element, with one grid row per chunk.
+// addresses modulo 16 take their slots from element 0 when all are 4-byte aligned, else go element by element
+// with one grid row per chunk.
 //
 // The vector path runs on one front: tiles of kThreads slots of the whole buffer go round-robin to the blocks,
 // and each block walks the chunks in order, so all workgroups move through the rank buffers together (one
@@ -315,15 +316,23 @@ hipError_t rs_op(const RsAgArgs& a, int op, hipStream_t s) {
 
 int64_t host_chunk_lo(int64_t q, int64_t r, int64_t c) { return c * q + (c < r ? c : r); }
 
-// The vector plan (see RsAgArgs). full[r]: the N full buffers; part[c]: the chunk buffers. Returns false, leaving
-// the element path, when the full buffers sit at different addresses modulo 16 or a pointer is not a multiple of
-// the element size.
+// The vector plan (see RsAgArgs). full[r]: the N full buffers; part[c]: the chunk buffers. The full-buffer
+// accesses need 4-byte alignment only (16-byte accesses at a dword boundary are legal), so full buffers at
+// different addresses modulo 16 take slots from element 0 when every address is a multiple of 4. Returns false,
+// leaving the element path, when that fails too or a pointer is not a multiple of the element size.
 bool plan_vectors(RsAgArgs& a, const void* const* full, const void* const* part, int64_t count, int es, bool is_rs) {
   const int64_t V = 16 / es;
-  const uintptr_t rf = reinterpret_cast<uintptr_t>(full[0]) % 16;
+  uintptr_t rf = reinterpret_cast<uintptr_t>(full[0]) % 16;
+  bool same = true, words = true;
+  for (int r = 0; r < a.n; ++r) {
+    same = same && reinterpret_cast<uintptr_t>(full[r]) % 16 == rf;
+    words = words && reinterpret_cast<uintptr_t>(full[r]) % 4 == 0;
+  }
+  if (!same) {
+    if (!words) return false;
+    rf = 0;  // full buffers at different residues, all multiples of 4: slots from element 0 (4-byte aligned)
+  }
   if (rf % es) return false;
-  for (int r = 0; r < a.n; ++r)
-    if (reinterpret_cast<uintptr_t>(full[r]) % 16 != rf) return false;
   const int64_t hf = static_cast<int64_t>((16 - rf) % 16) / es;
   a.hf = hf;
   a.hb = hf * es;

@@ -175,7 +175,8 @@ __global__ __launch_bounds__(kThreads) void tensor_kernel(TensorArgs a) {
       uintptr_t anyp = 0;
       for (int r = 0; r < n; ++r) anyp |= reinterpret_cast<uintptr_t>(ip[r]) | reinterpret_cast<uintptr_t>(op[r]);
       // the halving tree for a runtime rank count is evaluated per element
-      const bool vec = (anyp & 15u) == 0 && !(SHAPE == kHalving && NR == 0);
+      // 16-byte accesses need 4-byte alignment only (a tensor at another offset straddles cache lines)
+      const bool vec = (anyp & 3u) == 0 && !(SHAPE == kHalving && NR == 0);
       // uniform sub-ranges [s0, s1) of the tile that lie in one bucket chunk
       int64_t s0 = e0;
       while (s0 < e1) {

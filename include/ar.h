@@ -133,8 +133,9 @@ int ar_auto_algo(int nranks, size_t count, int dtype);
  *   count == 0 returns AR_OK and enqueues nothing. nranks == 1 copies (avg divides by 1).
  *   Alignment: any. RING, FUSED, RHD and TREE work in 16-byte vectors whenever all 2N pointers share one address
  *   modulo 16 (a multiple of the element size): the first few elements of every buffer go one by one, up to a
- *   multiple of 256 bytes (buffers of 1 MiB or more) or of 16 bytes, the rest in vectors. The other algorithms
- *   use vectors only when every pointer is 16-byte aligned. Otherwise the work goes element by element.
+ *   multiple of 256 bytes (buffers of 1 MiB or more) or of 16 bytes, the rest in vectors. Pointers that differ
+ *   modulo 16 but are all multiples of 4 use vectors from element 0 (slower: they straddle cache lines). The
+ *   other algorithms use vectors only when every pointer is 16-byte aligned. Otherwise element by element.
  * Errors: AR_ERR_INVALID (enum, nranks, NULL), AR_ERR_UNSUPPORTED (RHD with N not a power of two; FP8
  *   with a dtype other than F32/BF16 or an op other than SUM/AVG), AR_ERR_ALIAS, AR_ERR_WORKSPACE (the
  *   stepwise algorithms on bf16/f16 need ar_allreduce_ws), AR_ERR_HIP. AR_ALGO_AUTO is resolved first, so
@@ -150,10 +151,10 @@ int ar_allreduce(const void* const* in_bufs, void* const* out_bufs, int nranks, 
  *   out_bufs: host array; out_bufs[c] points to the count/N (+1 when c < count%N) elements of chunk c; it may
  *     be NULL when that chunk is empty. In place: out_bufs[c] == in_bufs[c] + (start of chunk c); any other
  *     overlap -> AR_ERR_ALIAS. Errors as ar_allreduce.
- * Alignment (both calls): any. When the N full buffers share one address modulo 16 (and every pointer is a
- * multiple of the element size) the work goes in 16-byte vectors, whatever the chunk buffers' offsets and chunk
- * starts: in place at full speed, otherwise with each vector assembled from two aligned loads. Full buffers at
- * different addresses modulo 16 go element by element. */
+ * Alignment (both calls): any. When the N full buffers share one address modulo 16, or are all multiples of 4,
+ * (and every pointer is a multiple of the element size) the work goes in 16-byte vectors, whatever the chunk
+ * buffers' offsets and chunk starts: in place at full speed, otherwise with each vector assembled from two
+ * aligned loads. Other full buffers go element by element. */
 int ar_reduce_scatter(const void* const* in_bufs, void* const* out_bufs, int nranks, size_t count, int dtype, int op,
                       void* stream);
 

@@ -88,7 +88,8 @@ def test_headline_size_reduce_scatter_all_gather_and_tree():
 
 BEYOND_2_31 = [("ring", ar.AR_ALGO_RING, (0, 0, 0)), ("tree", ar.AR_ALGO_TREE, (0, 0, 0)),
                ("fused", ar.AR_ALGO_FUSED, (0, 0, 0)), ("ring_common_offset", ar.AR_ALGO_RING, (3, 3, 3)),
-               ("ring_per_rank_offsets", ar.AR_ALGO_RING, (0, 1, 2))]
+               ("ring_per_rank_offsets", ar.AR_ALGO_RING, (0, 1, 2)),
+               ("ring_per_rank_even_offsets", ar.AR_ALGO_RING, (0, 2, 6))]
 
 
 @pytest.mark.timeout(900)
@@ -96,7 +97,7 @@ BEYOND_2_31 = [("ring", ar.AR_ALGO_RING, (0, 0, 0)), ("tree", ar.AR_ALGO_TREE, (
 def test_beyond_two_to_the_31_elements_sampled(name, algo, offs):
     """Maximum size: 3 ranks x (2^31 + 1001) bf16 (4 GiB each), in place, avg, with 64-bit element and byte
     offsets: the one-front ring kernel, the one-pass tree and rank-order kernels, a common offset (head, then
-    slots) and per-rank offsets (element by element). Sampled positions (random, both ends, around every chunk
+    slots), per-rank odd offsets (element by element) and per-rank even offsets (slots at 4-byte alignment). Sampled positions (random, both ends, around every chunk
     boundary) against the oracle. For the ring each chunk's samples go into the same chunk of a small array, so
     the oracle folds them from the same rank as the ring does at full size; the other orders do not depend on
     the position."""

@@ -199,13 +199,19 @@ def test_inputs_and_outputs_at_different_offsets(algo, in_off, out_off):
 
 
 @pytest.mark.parametrize("algo", ONE_PASS)
-def test_rank_buffers_at_different_offsets_take_the_element_path(algo):
-    dt, n, count = ar.AR_F32, 8, 300_001
+@pytest.mark.parametrize("dt,step", [(ar.AR_F32, 1), (ar.AR_BF16, 2), (ar.AR_BF16, 1), (ar.AR_I32, 3)])
+@pytest.mark.parametrize("count", [300_001, 5_000_011])
+def test_rank_buffers_at_different_offsets(algo, dt, step, count):
+    """Rank r at r*step elements past an aligned address: addresses that differ modulo 16 but are multiples of 4
+    (fp32 and int32 at any offset, bf16 at even ones) take 16-byte slots at 4-byte alignment; bf16 at odd offsets
+    goes element by element. Small calls and one-front-sized ones, in place."""
+    n = 8
     xs = _inputs(dt, n, count, 26)
-    ins = [to_dev(x, dt, offset=r)[1] for r, x in enumerate(xs)]
+    ins = [to_dev(x, dt, offset=r * step)[1] for r, x in enumerate(xs)]
     ar.ar_allreduce(ins, ins, ar.AR_AVG, algo)
     torch.cuda.synchronize()
-    assert_bitwise([from_dev(t, dt) for t in ins], expect(xs, dt, ar.AR_AVG, algo), f"per-rank offsets {algo}")
+    assert_bitwise([from_dev(t, dt) for t in ins], expect(xs, dt, ar.AR_AVG, algo),
+                   f"per-rank offsets x{step} dt={dt} count={count} algo={algo}")
 
 
 @pytest.mark.parametrize("algo", [ar.AR_ALGO_RING, ar.AR_ALGO_FUSED, ar.AR_ALGO_RHD, ar.AR_ALGO_RING_STEPWISE,
@@ -610,18 +616,21 @@ def test_reduce_scatter_and_all_gather_match_oracle(n, count, dt):
 
 
 @pytest.mark.parametrize("layout", ["full_at_common_offset", "chunks_at_offsets", "both_offset",
-                                    "full_at_different_offsets", "in_place_full_offset"])
+                                    "full_at_different_offsets", "full_at_different_even_offsets",
+                                    "in_place_full_offset"])
 @pytest.mark.parametrize("n,count", [(3, 5003), (8, 1_200_013), (5, 80_003)])
 @pytest.mark.parametrize("dt", [ar.AR_F32, ar.AR_BF16])
 def test_reduce_scatter_and_all_gather_at_any_alignment(layout, n, count, dt):
     """Full buffers and chunk buffers at any element offset: a common offset of the full buffers (a head, then
     slots), chunk buffers at assorted offsets (each vector assembled from two aligned slots), in place inside
-    offset full buffers (no shift), and full buffers at different residues (element by element). Every result
-    bit-exact against the oracle; RS then AG equals the ring all-reduce."""
+    offset full buffers (no shift), and full buffers at different residues (slots at 4-byte alignment from
+    element 0 where every address is a multiple of 4, else element by element). Every result bit-exact against
+    the oracle; RS then AG equals the ring all-reduce."""
     xs = _inputs(dt, n, count, 53)
     lo = ar.chunk_bounds(count, n)
     full_off = {"full_at_common_offset": [3] * n, "chunks_at_offsets": [0] * n, "both_offset": [1] * n,
-                "full_at_different_offsets": list(range(n)), "in_place_full_offset": [5] * n}[layout]
+                "full_at_different_offsets": list(range(n)), "full_at_different_even_offsets": [2 * r for r in range(n)],
+                "in_place_full_offset": [5] * n}[layout]
     part_off = [(c * 3 + 1) % 8 for c in range(n)] if layout in ("chunks_at_offsets", "both_offset") else [0] * n
     full = [to_dev(x, dt, offset=full_off[r])[1] for r, x in enumerate(xs)]
     if layout == "in_place_full_offset":
