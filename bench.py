@@ -292,8 +292,9 @@ def other_rows(torch, ar, inputs, ins, outs, dev, reps, host):
     # (bf16 at even per-rank offsets: 4-byte aligned, so 16-byte slots from element 0 that straddle cache lines)
     for name, offs in (("ring_common_offset", [1] * N_RANKS), ("ring_per_rank_offsets", list(range(N_RANKS))),
                        ("ring_per_rank_even_offsets", [2 * r for r in range(N_RANKS)])):
-        vin = [torch.empty(COUNT + 8, dtype=torch.bfloat16, device=dev)[o:o + COUNT] for o in offs]
-        vout = [torch.empty(COUNT + 8, dtype=torch.bfloat16, device=dev)[o:o + COUNT] for o in offs]
+        pad = max(offs)
+        vin = [torch.empty(COUNT + pad, dtype=torch.bfloat16, device=dev)[o:o + COUNT] for o in offs]
+        vout = [torch.empty(COUNT + pad, dtype=torch.bfloat16, device=dev)[o:o + COUNT] for o in offs]
         for v, t in zip(vin, ins):
             v.copy_(t)
         fn = lambda: ar.ar_allreduce(vin, vout, ar.AR_AVG, ar.AR_ALGO_RING)
