@@ -38,18 +38,21 @@
 namespace ar {
 namespace {
 
-constexpr int kThreads = 256;
+constexpr int kThreads = 128;
 
 // Launch shape, measured on MI355X: HBM3E streams writes best with few concurrent writers, while reads need
 // bytes in flight. Each thread keeps about eight independent 16-byte loads in flight (U slots x N ranks,
-// U = 8/N for small N), and the grid is a small number of 256-thread workgroups per CU in total (split over
-// the chunks): one for N = 8, more where a thread has fewer loads in flight or writes fewer streams.
+// U = 8/N for small N), and the grid is a small number of waves per CU in total (split over the chunks): four
+// for N = 8 (two 128-thread workgroups), more where a thread has fewer loads in flight or writes fewer
+// streams. More bytes in flight (longer tiles, a second tile's loads issued before the first tile's stores,
+// more workgroups) measured slower. 128-thread workgroups ran level with 256-thread ones of the same wave
+// count on most boxes and up to 11% faster on a box where the 256-thread shape was slow.
 template <int NR> constexpr int slots_per_thread() { return (NR > 0 && NR < 8) ? 8 / NR : 1; }
 // Element by element (buffers whose addresses differ modulo 16 between ranks): UE elements per thread and tile,
 // about 64 independent loads in flight per thread (UE x N); one at a time for a run-time rank count.
 template <int NR> constexpr int elems_per_thread() { return NR == 0 ? 1 : NR >= 64 ? 1 : 64 / NR > 16 ? 16 : 64 / NR; }
 template <int NR> constexpr int blocks_per_cu() {
-  return NR == 8 ? 1 : NR == 2 ? 2 : (NR == 4 || NR == 16) ? 4 : 8;
+  return NR == 8 ? 2 : NR == 2 ? 4 : (NR == 4 || NR == 16) ? 8 : 16;
 }
 
 // Fold shapes: rank order (ring and fused, from rank `start`), the halving tree, the binomial tree.

@@ -179,7 +179,7 @@ __global__ __launch_bounds__(kThreads) void dequant_kernel(const uint8_t* codes,
     uint32_t w[2] = {0, 0};
     if (vec && nvalid == kPerLane) {
       typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
-      const u32x2 p = __builtin_nontemporal_load(reinterpret_cast<const u32x2*>(codes + e0));
+      const u32x2 p = *reinterpret_cast<const u32x2*>(codes + e0);  // default-policy load, as ld16
       w[0] = p[0];
       w[1] = p[1];
     } else {
