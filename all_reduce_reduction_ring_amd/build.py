@@ -22,9 +22,10 @@ ARCH = "gfx950"
 
 SOURCES = ["ar_api.hip", "ar_collapsed.hip", "ar_stepwise.hip", "ar_bucket.hip", "ar_fp8.hip", "ar_tensors.hip", "ar_rsag.hip"]
 # ar_collapsed.hip holds several hundred kernel instances; it is compiled once per element type (AR_F32 = 0 ..
-# AR_I32 = 3), so the four parts build in parallel.
+# AR_I32 = 3) and per build of its launch shape and load policy (AR_COLLAPSED_LARGE = 0, 1), so the eight parts
+# build in parallel.
 UNITS = [(src, []) for src in SOURCES if src != "ar_collapsed.hip"] + [
-    ("ar_collapsed.hip", [f"-DAR_COLLAPSED_DTYPE={dt}"]) for dt in range(4)]
+    ("ar_collapsed.hip", [f"-DAR_COLLAPSED_DTYPE={dt}", f"-DAR_COLLAPSED_LARGE={lg}"]) for dt in range(4) for lg in (0, 1)]
 
 CFLAGS = [
     f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC", "-ffp-contract=off",

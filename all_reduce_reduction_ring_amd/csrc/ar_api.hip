@@ -30,13 +30,19 @@ int cu_count() {
 
 namespace ar {
 
+template <int DT>
+hipError_t collapsed_for(const RankPtrs& p, int n, int64_t count, int op, int algo, int64_t head, hipStream_t s) {
+  if (large_launch(n, count, kElemSize<DT>)) return launch_collapsed_dt<DT, 1>(p, n, count, op, algo, head, s);
+  return launch_collapsed_dt<DT, 0>(p, n, count, op, algo, head, s);
+}
+
 hipError_t launch_collapsed(const RankPtrs& p, int n, int64_t count, int dtype, int op, int algo, int64_t head,
                             hipStream_t s) {
   switch (dtype) {
-    case AR_F32: return launch_collapsed_dt<AR_F32>(p, n, count, op, algo, head, s);
-    case AR_BF16: return launch_collapsed_dt<AR_BF16>(p, n, count, op, algo, head, s);
-    case AR_F16: return launch_collapsed_dt<AR_F16>(p, n, count, op, algo, head, s);
-    case AR_I32: return launch_collapsed_dt<AR_I32>(p, n, count, op, algo, head, s);
+    case AR_F32: return collapsed_for<AR_F32>(p, n, count, op, algo, head, s);
+    case AR_BF16: return collapsed_for<AR_BF16>(p, n, count, op, algo, head, s);
+    case AR_F16: return collapsed_for<AR_F16>(p, n, count, op, algo, head, s);
+    case AR_I32: return collapsed_for<AR_I32>(p, n, count, op, algo, head, s);
     default: return hipErrorInvalidValue;
   }
 }
@@ -65,13 +71,21 @@ int64_t vector_head(const RankPtrs& p, int n, int64_t count, int esize) {
   return 0;
 }
 
+template <int DT>
+hipError_t segments_for(const RankPtrs& p, int n, const int64_t* counts, int nseg, int op, int algo, hipStream_t s) {
+  int64_t total = 0;
+  for (int i = 0; i < nseg; ++i) total += counts[i];
+  if (large_launch(n, total, kElemSize<DT>)) return launch_segments_dt<DT, 1>(p, n, counts, nseg, op, algo, s);
+  return launch_segments_dt<DT, 0>(p, n, counts, nseg, op, algo, s);
+}
+
 hipError_t launch_segments(const RankPtrs& p, int n, const int64_t* counts, int nseg, int dtype, int op, int algo,
                            hipStream_t s) {
   switch (dtype) {
-    case AR_F32: return launch_segments_dt<AR_F32>(p, n, counts, nseg, op, algo, s);
-    case AR_BF16: return launch_segments_dt<AR_BF16>(p, n, counts, nseg, op, algo, s);
-    case AR_F16: return launch_segments_dt<AR_F16>(p, n, counts, nseg, op, algo, s);
-    case AR_I32: return launch_segments_dt<AR_I32>(p, n, counts, nseg, op, algo, s);
+    case AR_F32: return segments_for<AR_F32>(p, n, counts, nseg, op, algo, s);
+    case AR_BF16: return segments_for<AR_BF16>(p, n, counts, nseg, op, algo, s);
+    case AR_F16: return segments_for<AR_F16>(p, n, counts, nseg, op, algo, s);
+    case AR_I32: return segments_for<AR_I32>(p, n, counts, nseg, op, algo, s);
     default: return hipErrorInvalidValue;
   }
 }

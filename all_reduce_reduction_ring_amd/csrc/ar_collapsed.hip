@@ -1,6 +1,6 @@
 // ar_collapsed.hip -- one-pass all-reduce kernels: ring order, rank order (reduce + broadcast), the recursive
 // halving-doubling tree and the binomial tree, and the many-bucket segment kernel. Compiled once per element
-// type (AR_COLLAPSED_DTYPE).
+// type (AR_COLLAPSED_DTYPE) and build (AR_COLLAPSED_LARGE, below).
 //
 // Ring order (jisaku.com glossary "AllReduce（オールリデュース）", section Ring-AllReduceの仕組み; astro-wiki
 // "AllReduce", section Ring AllReduce, phases 阶段一 and 阶段二): with reduce-scatter round s sending chunk
@@ -32,27 +32,41 @@
 // small buffers) or 1 (rank order and the trees, whose order does not depend on the chunk), and grid.x strides
 // over the chunk's slots; the elements of a chunk that are not in a whole slot (head, edges) are done
 // element-wise by block x = 0.
+//
+// Two builds (AR_COLLAPSED_LARGE, with AR_COLLAPSED_DTYPE): 0 for launches of up to 1 GiB of HBM traffic
+// (non-temporal 16-byte loads, 256-thread workgroups), 1 above that (default-policy loads, 128-thread
+// workgroups at twice the count per CU); the host picks one per launch (large_launch).
+#ifndef AR_COLLAPSED_LARGE
+#error "ar_collapsed.hip is compiled once per build: -DAR_COLLAPSED_LARGE=0 or 1"
+#endif
+#if AR_COLLAPSED_LARGE
+#define AR_LOADS_NONTEMPORAL 0
+#else
+#define AR_LOADS_NONTEMPORAL 1
+#endif
 #include "ar_device.h"
 #include "ar_internal.h"
 
 namespace ar {
 namespace {
 
-constexpr int kThreads = 128;
+constexpr int kLarge = AR_COLLAPSED_LARGE;
+constexpr int kThreads = kLarge ? 128 : 256;
 
 // Launch shape, measured on MI355X: HBM3E streams writes best with few concurrent writers, while reads need
 // bytes in flight. Each thread keeps about eight independent 16-byte loads in flight (U slots x N ranks,
 // U = 8/N for small N), and the grid is a small number of waves per CU in total (split over the chunks): four
-// for N = 8 (two 128-thread workgroups), more where a thread has fewer loads in flight or writes fewer
-// streams. More bytes in flight (longer tiles, a second tile's loads issued before the first tile's stores,
-// more workgroups) measured slower. 128-thread workgroups ran level with 256-thread ones of the same wave
-// count on most boxes and up to 11% faster on a box where the 256-thread shape was slow.
+// for N = 8 (one 256-thread workgroup, or two 128-thread ones in the large build), more where a thread has
+// fewer loads in flight or writes fewer streams. More bytes in flight (longer tiles, a second tile's loads
+// issued before the first tile's stores, more workgroups) measured slower. On large launches 128-thread
+// workgroups ran level with 256-thread ones of the same wave count on most boxes and up to 11% faster on a box
+// where the 256-thread shape was slow; on launches of 2-4 MiB per rank they ran 8% slower.
 template <int NR> constexpr int slots_per_thread() { return (NR > 0 && NR < 8) ? 8 / NR : 1; }
 // Element by element (buffers whose addresses differ modulo 16 between ranks): UE elements per thread and tile,
 // about 64 independent loads in flight per thread (UE x N); one at a time for a run-time rank count.
 template <int NR> constexpr int elems_per_thread() { return NR == 0 ? 1 : NR >= 64 ? 1 : 64 / NR > 16 ? 16 : 64 / NR; }
 template <int NR> constexpr int blocks_per_cu() {
-  return NR == 8 ? 2 : NR == 2 ? 4 : (NR == 4 || NR == 16) ? 8 : 16;
+  return (kLarge ? 2 : 1) * (NR == 8 ? 1 : NR == 2 ? 2 : (NR == 4 || NR == 16) ? 4 : 8);
 }
 
 // Fold shapes: rank order (ring and fused, from rank `start`), the halving tree, the binomial tree.
@@ -663,7 +677,7 @@ static_assert(sizeof(SegmentArgs) <= 4096, "kernel arguments must fit in 4 KiB")
 constexpr int kDT = AR_COLLAPSED_DTYPE;
 
 template <>
-hipError_t launch_segments_dt<kDT>(const RankPtrs& p, int n, const int64_t* counts, int nseg, int op, int algo,
+hipError_t launch_segments_dt<kDT, kLarge>(const RankPtrs& p, int n, const int64_t* counts, int nseg, int op, int algo,
                                    hipStream_t s) {
   constexpr int V = Traits<kDT>::kVec;
   // must match the U each template above is instantiated with: 8/N for N = 2 and 4 (every shape), else 1
@@ -702,7 +716,7 @@ hipError_t launch_segments_dt<kDT>(const RankPtrs& p, int n, const int64_t* coun
 }
 
 template <>
-hipError_t launch_collapsed_dt<kDT>(const RankPtrs& p, int n, int64_t count, int op, int algo, int64_t head,
+hipError_t launch_collapsed_dt<kDT, kLarge>(const RankPtrs& p, int n, int64_t count, int op, int algo, int64_t head,
                                     hipStream_t s) {
   CollapsedArgs a;
   a.p = p;

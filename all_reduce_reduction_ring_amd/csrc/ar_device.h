@@ -154,16 +154,34 @@ template <int DT> __device__ __forceinline__ void store_elem(void* base, int64_t
 }
 
 // Streaming 16-byte loads and stores. Each element is read once and written once per call. The stores are
-// marked non-temporal; the loads are plain loads: on MI355X the N-read, N-write fold ran about 4% faster with
-// default-policy loads beside non-temporal stores than with both non-temporal (N = 8, 256 MiB of bf16 per
-// rank, measured twice on one box: 771-775 us against 800-806 us), and the two policies together beat every
-// other pairing tried (write-through and system-scope bits on either side). The address needs 4-byte
-// alignment only: a dword-aligned global_load_dwordx4 / global_store_dwordx4 is a legal access on gfx950, and the
-// type below tells the compiler so without changing the instruction (the same single dwordx4 as for 16-byte
-// aligned data). Callers still start slots on 16-byte (or 256-byte) boundaries wherever the buffers allow:
-// a vector that straddles two cache lines costs more.
+// non-temporal. Loads come in two cache policies, and which one is faster depends on the kernel's mix of
+// reads and writes and on the launch's size. Measured on MI355X, cache-cold calls, one box per comparison:
+//   - N-read, N-write fold, N = 8: default-policy loads 2-12% faster from 128 MiB per rank up (771-775 us
+//     against 800-806 us at 256 MiB of bf16 on one box, level or 1% slower on another), but 5-8% slower from
+//     2 to 64 MiB per rank;
+//   - all-gather (1 read, N writes) and the E4M3 quantizer (2 bytes read, ~1 written): default policy 13% and
+//     10% faster; reduce-scatter (N reads, 1 write) and the compressed ring: non-temporal 7% and 3% faster.
+// Write-through and system-scope bits on the stores gained nothing on top, and plain stores beside
+// non-temporal loads lost 12%. ld16 is the non-temporal load unless a file defines AR_LOADS_NONTEMPORAL as 0
+// before including this header; ld16_nt and ld16_cached name a policy explicitly. Every device code object is
+// compiled on its own (no relocatable device code), so files may differ in this choice.
+// The address needs 4-byte alignment only: a dword-aligned global_load_dwordx4 / global_store_dwordx4 is a
+// legal access on gfx950, and the type below tells the compiler so without changing the instruction (the same
+// single dwordx4 as for 16-byte aligned data). Callers still start slots on 16-byte (or 256-byte) boundaries
+// wherever the buffers allow: a vector that straddles two cache lines costs more.
+#ifndef AR_LOADS_NONTEMPORAL
+#define AR_LOADS_NONTEMPORAL 1
+#endif
 typedef u32x4 u32x4_a4 __attribute__((aligned(4)));
-__device__ __forceinline__ u32x4 ld16(const void* p) { return *gptr<u32x4_a4>(p); }
+__device__ __forceinline__ u32x4 ld16_nt(const void* p) { return __builtin_nontemporal_load(gptr<u32x4_a4>(p)); }
+__device__ __forceinline__ u32x4 ld16_cached(const void* p) { return *gptr<u32x4_a4>(p); }
+__device__ __forceinline__ u32x4 ld16(const void* p) {
+#if AR_LOADS_NONTEMPORAL
+  return ld16_nt(p);
+#else
+  return ld16_cached(p);
+#endif
+}
 __device__ __forceinline__ void st16(void* p, const u32x4& v) { __builtin_nontemporal_store(v, gptr<u32x4_a4>(p)); }
 
 // Balanced chunk split: chunk c = [c*q + min(c, r), ...) with q = count / N, r = count % N.

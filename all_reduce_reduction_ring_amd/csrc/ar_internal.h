@@ -34,13 +34,23 @@ int64_t vector_head(const RankPtrs& p, int n, int64_t count, int esize);
 hipError_t launch_segments(const RankPtrs& p, int n, const int64_t* counts, int nseg, int dtype, int op, int algo,
                            hipStream_t s);
 
-// The same two for one element type: ar_collapsed.hip is compiled once per type (its many kernel instances then
-// build in parallel) and defines the specialisation for its type; the two functions above pick one.
-template <int DT>
+// The same two for one element type and one of two builds of the one-pass kernels. ar_collapsed.hip is compiled
+// once per (type, build) pair (its many kernel instances then build in parallel) and defines the specialisation
+// for its pair; the two functions above pick one. LARGE = 0: non-temporal 16-byte loads, 256-thread workgroups;
+// LARGE = 1: default-policy loads, 128-thread workgroups at twice the count per CU. Measured on MI355X (N = 8,
+// fp32 and bf16, cache-cold calls): the first is 5-8% faster up to 64 MiB per rank, the second 2-12% faster
+// from 128 MiB per rank (the headline's 256 MiB of bf16 among them), depending on the box.
+template <int DT, int LARGE>
 hipError_t launch_collapsed_dt(const RankPtrs& p, int n, int64_t count, int op, int algo, int64_t head, hipStream_t s);
-template <int DT>
+template <int DT, int LARGE>
 hipError_t launch_segments_dt(const RankPtrs& p, int n, const int64_t* counts, int nseg, int op, int algo,
                               hipStream_t s);
+
+// Which build a one-pass launch uses: the large one once the launch moves more than 1 GiB of HBM traffic (N reads
+// plus N writes of `elems` elements of `esize` bytes per rank).
+constexpr int64_t kLargeTrafficBytes = int64_t(1) << 30;
+template <int DT> constexpr int kElemSize = (DT == AR_BF16 || DT == AR_F16) ? 2 : 4;
+inline bool large_launch(int n, int64_t elems, int esize) { return 2 * int64_t(n) * elems * esize > kLargeTrafficBytes; }
 
 // Bucketed all-reduce from and to per-tensor buffers (device descriptor and pointer tables).
 hipError_t launch_tensors(const ar_tensor_desc* d_descs, const void* const* d_in, void* const* d_out, int ntensors,

@@ -248,3 +248,63 @@ def test_fp8_encoder_exhaustive_every_fp32_up_to_448():
                 bad = np.nonzero(got != wc)[0][:5]
                 raise AssertionError(f"codes differ at inputs {x[bad].view(np.uint32)}: got {got[bad]} want {wc[bad]}")
             del xd, codes, scales
+
+
+# One-pass launches switch builds at 1 GiB of HBM traffic (2 * N * count * element size): non-temporal loads and
+# 256-thread workgroups up to it, default-policy loads and 128-thread workgroups above. Both sides of the switch,
+# with ragged counts, every element against the oracle.
+THRESHOLD_CASES = [
+    # (n, dt, count): N=8 fp32 at exactly 1 GiB (small build) and just above it (large build); N=3 bf16 on
+    # both sides of 1 GiB with chunk starts inside 16-byte slots
+    (8, ar.AR_F32, 1 << 25),
+    (8, ar.AR_F32, (1 << 25) + 1003),
+    (3, ar.AR_BF16, (1 << 30) // 12 - 5),
+    (3, ar.AR_BF16, (1 << 30) // 12 + 7),
+]
+
+
+@pytest.mark.timeout(900)
+@pytest.mark.parametrize("n,dt,count", THRESHOLD_CASES, ids=[f"n{c[0]}_dt{c[1]}_{c[2]}" for c in THRESHOLD_CASES])
+def test_one_pass_builds_on_both_sides_of_the_switch(n, dt, count):
+    from gpu_util import KIND, ORACLE_DT, ORACLE_OP, from_dev
+    print(f"case n={n} dt={dt} count={count}", flush=True)
+    xs = inputs.rank_inputs(KIND[dt], n, count, cfg=41, extra=(n, count))
+    tdt = torch.float32 if dt == ar.AR_F32 else torch.bfloat16
+    ins = _up(xs, tdt)
+    outs = [torch.empty_like(t) for t in ins]
+    algos = [(ar.AR_ALGO_RING, oracle.ring_allreduce), (ar.AR_ALGO_FUSED, oracle.fused_allreduce),
+             (ar.AR_ALGO_TREE, oracle.tree_allreduce)] + ([(ar.AR_ALGO_RHD, oracle.rhd_allreduce)] if n == 8 else [])
+    for algo, ofn in algos:
+        for op in (ar.AR_AVG, ar.AR_MAX):
+            ar.ar_allreduce(ins, outs, op, algo)
+            torch.cuda.synchronize()
+            _same_on_all_ranks(outs)
+            want = ofn(xs, ORACLE_DT[dt], ORACLE_OP[op])[0]
+            got = from_dev(outs[0], dt)
+            assert np.array_equal(got, np.asarray(want).view(got.dtype)), f"algo={algo} op={op}"
+    del ins, outs
+    torch.cuda.empty_cache()
+
+
+@pytest.mark.timeout(900)
+def test_shared_segment_launch_above_the_switch():
+    """Twelve buckets of just under 16 MiB per rank (8 ranks, fp32) share one segment launch of 1.5 GiB of
+    traffic (the large build); every bucket must equal its own ring, every element."""
+    from gpu_util import from_dev
+    n, dt = 8, ar.AR_F32
+    unit = n * 4
+    counts = np.array([((16 << 20) // 4 // unit - 1 - 7 * b) * unit for b in range(12)], dtype=np.int64)
+    assert counts.max() * 4 < (16 << 20) and 2 * n * 4 * int(counts.sum()) > (1 << 30)
+    total = int(counts.sum())
+    xs = inputs.rank_inputs("uniform_f32", n, total, cfg=42)
+    ins = _up(xs, torch.float32)
+    outs = [torch.empty_like(t) for t in ins]
+    ar.ar_allreduce_buckets(ins, outs, counts, ar.AR_AVG, ar.AR_ALGO_RING)
+    torch.cuda.synchronize()
+    _same_on_all_ranks(outs)
+    got = from_dev(outs[0], dt)
+    starts = np.concatenate([[0], np.cumsum(counts)])
+    for b in range(len(counts)):
+        seg = [x[starts[b]:starts[b + 1]] for x in xs]
+        want = np.asarray(oracle.ring_allreduce(seg, oracle.F32, oracle.AVG)[0]).view(np.uint32)
+        assert np.array_equal(got[starts[b]:starts[b + 1]], want), f"bucket {b}"
