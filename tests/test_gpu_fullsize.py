@@ -10,6 +10,9 @@
   for which the oracle is evaluated on exactly those elements.
 - buckets: 300 fp32 tensors per rank (log-uniform 1K..16M elements, 2.07 GB per rank), 25 MiB buckets, avg:
   every tensor of every rank, through pack + per-bucket rings + unpack and through the fused tensor path.
+- the switch between the two builds of the one-pass kernels at 1 GiB of traffic: ring, rank order and trees on
+  both sides of it (fp32, bf16, f16, int32; N = 2, 3, 4, 8, 16; ragged counts), and one shared segment launch of
+  small buckets above it: every element.
 """
 import concurrent.futures
 
@@ -260,6 +263,10 @@ THRESHOLD_CASES = [
     (8, ar.AR_F32, (1 << 25) + 1003),
     (3, ar.AR_BF16, (1 << 30) // 12 - 5),
     (3, ar.AR_BF16, (1 << 30) // 12 + 7),
+    # the large build for the other element types and compile-time rank counts
+    (2, ar.AR_I32, (1 << 26) + 5),
+    (4, ar.AR_F16, (1 << 26) + 3),
+    (16, ar.AR_F16, (1 << 24) + 9),
 ]
 
 
@@ -269,11 +276,12 @@ def test_one_pass_builds_on_both_sides_of_the_switch(n, dt, count):
     from gpu_util import KIND, ORACLE_DT, ORACLE_OP, from_dev
     print(f"case n={n} dt={dt} count={count}", flush=True)
     xs = inputs.rank_inputs(KIND[dt], n, count, cfg=41, extra=(n, count))
-    tdt = torch.float32 if dt == ar.AR_F32 else torch.bfloat16
-    ins = _up(xs, tdt)
+    tdt = {ar.AR_F32: torch.float32, ar.AR_BF16: torch.bfloat16, ar.AR_F16: torch.float16, ar.AR_I32: torch.int32}[dt]
+    ins = [torch.from_numpy(x.view(np.int16) if x.dtype == np.uint16 else x).to(DEV).view(tdt) for x in xs]
     outs = [torch.empty_like(t) for t in ins]
     algos = [(ar.AR_ALGO_RING, oracle.ring_allreduce), (ar.AR_ALGO_FUSED, oracle.fused_allreduce),
-             (ar.AR_ALGO_TREE, oracle.tree_allreduce)] + ([(ar.AR_ALGO_RHD, oracle.rhd_allreduce)] if n == 8 else [])
+             (ar.AR_ALGO_TREE, oracle.tree_allreduce)] + ([(ar.AR_ALGO_RHD, oracle.rhd_allreduce)]
+                                                          if n & (n - 1) == 0 else [])
     for algo, ofn in algos:
         for op in (ar.AR_AVG, ar.AR_MAX):
             ar.ar_allreduce(ins, outs, op, algo)
