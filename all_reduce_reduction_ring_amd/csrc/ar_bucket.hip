@@ -16,6 +16,8 @@ namespace {
 
 constexpr int kThreads = 256;
 constexpr int kBatch = 256;
+// each thread stages one descriptor and one entry of the tile-count prefix sum
+static_assert(kBatch == kThreads, "the descriptor batch is one per thread");
 #ifndef AR_COPY_TILE_BYTES
 #define AR_COPY_TILE_BYTES 16384
 #endif

@@ -21,6 +21,8 @@ namespace {
 
 constexpr int kThreads = 256;
 constexpr int kBatch = 256;
+// each thread stages one descriptor and one entry of the tile-count prefix sum
+static_assert(kBatch == kThreads, "the descriptor batch is one per thread");
 
 struct TensorArgs {
   const ar_tensor_desc* descs;
