@@ -184,6 +184,26 @@ __device__ __forceinline__ u32x4 ld16(const void* p) {
 }
 __device__ __forceinline__ void st16(void* p, const u32x4& v) { __builtin_nontemporal_store(v, gptr<u32x4_a4>(p)); }
 
+// The 16 bytes that start M elements (of ES bytes) into x0 and run on into x1. M is a compile-time constant, so
+// every index below is one too and the result is assembled in registers.
+template <int ES, int M>
+__device__ __forceinline__ u32x4 shift_concat(const u32x4& x0, const u32x4& x1) {
+  u32x4 o;
+  if constexpr (ES == 4) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) o[i] = i + M < 4 ? x0[i + M] : x1[i + M - 4];
+  } else {
+    auto half = [&](int k) -> uint32_t {
+      const int w = k >> 1;
+      const uint32_t word = w < 4 ? x0[w] : x1[w - 4];
+      return (k & 1) ? word >> 16 : word & 0xFFFFu;
+    };
+#pragma unroll
+    for (int j = 0; j < 4; ++j) o[j] = half(2 * j + M) | (half(2 * j + 1 + M) << 16);
+  }
+  return o;
+}
+
 // Balanced chunk split: chunk c = [c*q + min(c, r), ...) with q = count / N, r = count % N.
 __device__ __forceinline__ int64_t chunk_lo(int64_t q, int64_t r, int64_t c) { return c * q + (c < r ? c : r); }
 

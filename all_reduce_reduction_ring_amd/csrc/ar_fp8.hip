@@ -209,7 +209,7 @@ struct Fp8RingArgs {
   int64_t wt_a, wt_b;  // wave tasks (4 blocks each, never spanning two chunks) per such chunk
   int64_t tasks;       // total wave tasks
   int n;
-  int vec;
+  int vec;  // 1: every rank buffer starts on a 16-byte boundary
 };
 
 // One hop: the sender's partial p goes out as E4M3 codes + block scale and comes back as d * scale; the
@@ -263,6 +263,29 @@ template <> struct Raw8<AR_F32> {
   }
 };
 
+// bf16 chunks that start m elements past the 16-byte grid (0 < m < 8: counts that are not a multiple of 8 N).
+// Every lane's 8 elements then sit m elements into the aligned slot at A = e0 - m, with the same m across the
+// wave task (it never spans two chunks). The lane loads the aligned slots at A and A + 8 and shifts; after the
+// fold, the aligned output slot [A + 8, A + 16) holds the lane's last m elements and the next lane's first 8 - m
+// (a lane shuffle), so every store is one aligned 16-byte store except at the wave task's two edges.
+template <int M, int NR>
+__device__ __forceinline__ void shift_ranks(const u32x4 (&x0)[NR], const u32x4 (&x1)[NR], u32x4 (&w)[NR]) {
+#pragma unroll
+  for (int k = 0; k < NR; ++k) w[k] = shift_concat<2, M>(x0[k], x1[k]);
+}
+template <int NR>
+__device__ __forceinline__ void shift_ranks_by(int m, const u32x4 (&x0)[NR], const u32x4 (&x1)[NR], u32x4 (&w)[NR]) {
+  switch (m) {  // wave-uniform
+    case 1: shift_ranks<1, NR>(x0, x1, w); break;
+    case 2: shift_ranks<2, NR>(x0, x1, w); break;
+    case 3: shift_ranks<3, NR>(x0, x1, w); break;
+    case 4: shift_ranks<4, NR>(x0, x1, w); break;
+    case 5: shift_ranks<5, NR>(x0, x1, w); break;
+    case 6: shift_ranks<6, NR>(x0, x1, w); break;
+    default: shift_ranks<7, NR>(x0, x1, w); break;
+  }
+}
+
 template <int DT, int OP, int NR>
 __global__ __launch_bounds__(kThreads) void fp8_ring_kernel(Fp8RingArgs a) {
   const int lane = threadIdx.x & 63, row = lane >> 4, l16 = lane & 15;
@@ -287,8 +310,12 @@ __global__ __launch_bounds__(kThreads) void fp8_ring_kernel(Fp8RingArgs a) {
     const int64_t nv = bend - e0;
     const int nvalid = nv <= 0 ? 0 : (nv >= kPerLane ? kPerLane : static_cast<int>(nv));
     const int start = static_cast<int>(c);
+    // elements between the chunk start and the 16-byte grid below it (the same for every lane of the wave task)
+    const int mis = static_cast<int>(lo & (DT == AR_BF16 ? 7 : 3));
+    const bool lane_vec = a.vec != 0 && mis == 0;
+    const bool full = __all(nvalid == kPerLane);
     float p[kPerLane];
-    if (NR > 0 && a.vec && __all(nvalid == kPerLane)) {
+    if (NR > 0 && lane_vec && full) {
       // every lane holds 8 in-range, aligned elements: issue all N loads before any arithmetic
       Raw8<DT> raw[NR > 0 ? NR : 1];
 #pragma unroll
@@ -307,17 +334,52 @@ __global__ __launch_bounds__(kThreads) void fp8_ring_kernel(Fp8RingArgs a) {
       finish<OP>(p, NR);
 #pragma unroll
       for (int r = 0; r < NR; ++r) store8<DT>(a.p.out[r], e0, kPerLane, true, p);
+    } else if (NR > 0 && DT == AR_BF16 && a.vec && full && __all(e0 - mis + 16 <= a.count)) {
+      constexpr int NT = NR > 0 ? NR : 1;
+      const int64_t A = e0 - mis;  // a multiple of 8 elements; A + 16 <= count, so both slots are in the buffer
+      u32x4 x0[NT], x1[NT], w[NT];
+#pragma unroll
+      for (int k = 0; k < NT; ++k) {
+        int rr = start + k;
+        rr = rr >= NT ? rr - NT : rr;
+        x0[k] = ld16(static_cast<const uint16_t*>(a.p.in[rr]) + A);
+        x1[k] = ld16(static_cast<const uint16_t*>(a.p.in[rr]) + A + 8);
+      }
+      shift_ranks_by<NT>(mis, x0, x1, w);
+      Slot<AR_BF16>::unpack(w[0], p);
+#pragma unroll
+      for (int k = 1; k < NT; ++k) {
+        float own[kPerLane];
+        Slot<AR_BF16>::unpack(w[k], own);
+        hop(p, own);
+      }
+      finish<OP>(p, NT);
+      const u32x4 o = Slot<AR_BF16>::pack(p);
+      u32x4 nx;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) nx[i] = static_cast<uint32_t>(__shfl_down(static_cast<int>(o[i]), 1));
+      u32x4 one[1] = {o}, two[1] = {nx}, slot[1];
+      shift_ranks_by<1>(8 - mis, one, two, slot);
+#pragma unroll
+      for (int r = 0; r < NT; ++r) {
+        uint16_t* out = static_cast<uint16_t*>(a.p.out[r]);
+        if (lane < 63) st16(out + A + 8, slot[0]);
+        if (lane == 0)  // [A + m, A + 8): the slot below also holds the previous wave task's elements
+          for (int k = 0; k < 8 - mis; ++k) store_elem<AR_BF16>(out, e0 + k, narrow<AR_BF16>(p[k]));
+        if (lane == 63)  // [A + 8, A + 8 + m): the slot above is the next wave task's
+          for (int k = 8 - mis; k < kPerLane; ++k) store_elem<AR_BF16>(out, e0 + k, narrow<AR_BF16>(p[k]));
+      }
     } else {
-      load8<DT>(a.p.in[start], e0, nvalid, a.vec != 0, p);
+      load8<DT>(a.p.in[start], e0, nvalid, lane_vec, p);
       for (int k = 1; k < n; ++k) {
         int rr = start + k;
         rr = rr >= n ? rr - n : rr;
         float own[kPerLane];
-        load8<DT>(a.p.in[rr], e0, nvalid, a.vec != 0, own);
+        load8<DT>(a.p.in[rr], e0, nvalid, lane_vec, own);
         hop(p, own);
       }
       finish<OP>(p, n);
-      for (int r = 0; r < n; ++r) store8<DT>(a.p.out[r], e0, nvalid, a.vec != 0, p);
+      for (int r = 0; r < n; ++r) store8<DT>(a.p.out[r], e0, nvalid, lane_vec, p);
     }
   }
 }
@@ -382,8 +444,8 @@ hipError_t launch_fp8_ring(const RankPtrs& p, int n, int64_t count, int dtype, i
   a.wt_a = (a.nb_a + 3) / 4;
   a.wt_b = (a.nb_b + 3) / 4;
   a.tasks = a.r * a.wt_a + (n - a.r) * a.wt_b;
-  // 16-byte slots of 8 elements need every chunk start on an 8-element boundary
-  a.vec = (vec && a.r == 0 && a.q % kPerLane == 0) ? 1 : 0;
+  // chunk starts off the 16-byte grid are handled per wave task in the kernel
+  a.vec = vec ? 1 : 0;
   if (dtype == AR_BF16) return op == AR_AVG ? ring_n<AR_BF16, AR_AVG>(a, s) : ring_n<AR_BF16, AR_SUM>(a, s);
   return op == AR_AVG ? ring_n<AR_F32, AR_AVG>(a, s) : ring_n<AR_F32, AR_SUM>(a, s);
 }

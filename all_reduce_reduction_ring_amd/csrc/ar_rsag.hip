@@ -56,26 +56,6 @@ struct Span {
   int m;
 };
 
-// The 16 bytes that start M elements (of ES bytes) into x0 and run on into x1. M is a compile-time constant, so
-// every index below is one too and the result is assembled in registers.
-template <int ES, int M>
-__device__ __forceinline__ u32x4 shift_concat(const u32x4& x0, const u32x4& x1) {
-  u32x4 o;
-  if constexpr (ES == 4) {
-#pragma unroll
-    for (int i = 0; i < 4; ++i) o[i] = i + M < 4 ? x0[i + M] : x1[i + M - 4];
-  } else {
-    auto half = [&](int k) -> uint32_t {
-      const int w = k >> 1;
-      const uint32_t word = w < 4 ? x0[w] : x1[w - 4];
-      return (k & 1) ? word >> 16 : word & 0xFFFFu;
-    };
-#pragma unroll
-    for (int j = 0; j < 4; ++j) o[j] = half(2 * j + M) | (half(2 * j + 1 + M) << 16);
-  }
-  return o;
-}
-
 // Visit, on one front, the vector slots of every chunk: calls fn(c, v, span) for the slots v of chunk c that this
 // thread owns. Tile t = slots [t * kThreads, (t + 1) * kThreads) goes to block t mod G; a block's tiles come in
 // increasing order and the chunks' slot ranges are disjoint and increasing, so the chunk loop is outside the tile
