@@ -460,6 +460,210 @@ hipError_t launch_front(CollapsedArgs& a, hipStream_t s) {
   return hipGetLastError();
 }
 
+// ------------------------------------------------------------------------------------------ skewed buffers
+// 2-byte rank buffers whose addresses differ modulo 16 and are not all multiples of 4 bytes (views at different,
+// some odd, element offsets), ring or rank order. Work runs on the
+// element grid: slot j = elements [jV, jV + V) of every rank, and a wave tile is 64 consecutive slots. Rank r's
+// input sits im[r] elements past the 16-byte grid, so a lane loads the two aligned 16-byte slots around its V
+// elements and shifts them into place; output rank r sits om[r] elements past the grid, so the aligned output
+// slot above a lane holds its last om[r] elements and the next lane's first V - om[r] (a lane shuffle). Tiles
+// that straddle a chunk boundary, the first tile (whose lower aligned slots start before the buffers) and the last
+// ones (whose upper slots end after them) go element by element. Same bits as the aligned kernels: every element still folds from its chunk's rank.
+struct SkewArgs {
+  CollapsedArgs f;
+  int8_t im[AR_MAX_RANKS], om[AR_MAX_RANKS];  // elements past the 16-byte grid: each rank's input and output
+};
+static_assert(sizeof(SkewArgs) <= 4096, "kernel arguments must fit in 4 KiB");
+
+// x0 from 2-byte element m on, continued into x1 (m is wave-uniform; each case is a compile-time shift)
+template <int ES>
+__device__ __forceinline__ u32x4 shift_by(int m, const u32x4& x0, const u32x4& x1) {
+  static_assert(ES == 2, "2-byte elements");
+  switch (m) {
+    case 0: return x0;
+    case 1: return shift_concat<2, 1>(x0, x1);
+    case 2: return shift_concat<2, 2>(x0, x1);
+    case 3: return shift_concat<2, 3>(x0, x1);
+    case 4: return shift_concat<2, 4>(x0, x1);
+    case 5: return shift_concat<2, 5>(x0, x1);
+    case 6: return shift_concat<2, 6>(x0, x1);
+    default: return shift_concat<2, 7>(x0, x1);
+  }
+}
+
+// storage bits of element k of a packed slot
+template <int DT>
+__device__ __forceinline__ uint32_t slot_elem(const u32x4& v, int k) {
+  if constexpr (Traits<DT>::kSize == 4) return v[k];
+  else return (v[k >> 1] >> (16 * (k & 1))) & 0xFFFFu;
+}
+
+// A wave tile takes the vector path when it lies in one chunk and both aligned slots of every lane lie inside the
+// buffers: tile 0's lower slots would start before them, and the upper slots of a tile need V more elements.
+template <int V, int NR>
+__device__ __forceinline__ bool skew_vec_tile(const CollapsedArgs& a, int64_t w, int* chunk) {
+  const int64_t t0 = w * 64 * V, t1 = t0 + 64 * V;
+  if (w <= 0 || t1 + V > a.count) return false;
+  int c = 0, cl = 0;
+  while (c + 1 < NR && chunk_lo(a.q, a.r, c + 1) <= t0) ++c;
+  while (cl + 1 < NR && chunk_lo(a.q, a.r, cl + 1) <= t1 - 1) ++cl;
+  *chunk = c;
+  return c == cl;
+}
+
+// A wave walks a strip of kSkewStrip consecutive tiles and carries the previous tile's results into the next, so
+// the output slot shared by two tiles of a strip is stored whole by the later one; only slots at the ends of a
+// strip (or next to an element-path tile) are stored element by element.
+constexpr int kSkewStrip = 8;
+
+template <int DT, int OP, int NR>
+__global__ __launch_bounds__(kThreads) void skew_kernel(SkewArgs s) {
+  using S = Slot<DT>;
+  constexpr int V = S::V, ES = Traits<DT>::kSize;
+  static_assert(ES == 2, "2-byte element types only: 4-byte ones are always 4-byte aligned");
+  const CollapsedArgs& a = s.f;
+  const int lane = threadIdx.x & 63;
+  const int64_t nwt = (a.count + 64 * V - 1) / (64 * V);
+  const int64_t nstrips = (nwt + kSkewStrip - 1) / kSkewStrip;
+  const int64_t nw = static_cast<int64_t>(gridDim.x) * (kThreads / 64);
+  const int64_t wv = static_cast<int64_t>(blockIdx.x) * (kThreads / 64) + (threadIdx.x >> 6);
+  for (int64_t sp = wv; sp < nstrips; sp += nw) {
+    u32x4 prev = {0u, 0u, 0u, 0u};  // this lane's result in the previous tile of the strip
+    bool prev_vec = false;           // the previous tile of the strip took the vector path
+    int c = 0;
+    bool cur_vec = skew_vec_tile<V, NR>(a, sp * kSkewStrip, &c);
+    for (int k = 0; k < kSkewStrip; ++k) {
+      const int64_t w = sp * kSkewStrip + k;
+      if (w >= nwt) break;
+      int cn = 0;
+      const bool next_vec = k + 1 < kSkewStrip && skew_vec_tile<V, NR>(a, w + 1, &cn);
+      const int64_t j = w * 64 + lane, e = j * V;
+      if (cur_vec) {
+        const int start = a.rot ? c : 0;
+        u32x4 x0[NR], x1[NR];
+#pragma unroll
+        for (int q = 0; q < NR; ++q) {
+          int rr = start + q;
+          rr = rr >= NR ? rr - NR : rr;
+          const char* base = static_cast<const char*>(a.p.in[rr]) - s.im[rr] * ES + j * 16;
+          x0[q] = ld16(base);
+          x1[q] = ld16(base + 16);
+        }
+        typename S::Acc acc[V], t[V];
+        S::unpack(shift_by<ES>(s.im[start], x0[0], x1[0]), acc);
+#pragma unroll
+        for (int q = 1; q < NR; ++q) {
+          int rr = start + q;
+          rr = rr >= NR ? rr - NR : rr;
+          S::unpack(shift_by<ES>(s.im[rr], x0[q], x1[q]), t);
+#pragma unroll
+          for (int i = 0; i < V; ++i) acc[i] = combine<OP>(acc[i], t[i]);
+        }
+#pragma unroll
+        for (int i = 0; i < V; ++i) acc[i] = finalize<OP>(acc[i], NR);
+        const u32x4 o = S::pack(acc);
+        u32x4 nx, last;  // the next lane's result; the previous tile's last lane
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          nx[i] = static_cast<uint32_t>(__shfl_down(static_cast<int>(o[i]), 1));
+          last[i] = static_cast<uint32_t>(__shfl(static_cast<int>(prev[i]), 63));
+        }
+#pragma unroll
+        for (int r = 0; r < NR; ++r) {
+          const int m = s.om[r];
+          char* ob = static_cast<char*>(a.p.out[r]) - m * ES;  // the output's 16-byte grid
+          if (m == 0) {
+            st16(ob + j * 16, o);
+          } else {
+            const u32x4 up = shift_by<ES>(V - m, o, nx);  // aligned slot j + 1: last m of this lane, first V - m of next
+            if (lane < 63) st16(ob + (j + 1) * 16, up);
+            if (lane == 0) {
+              if (prev_vec) {
+                st16(ob + j * 16, shift_by<ES>(V - m, last, o));  // slot j: the previous tile's last m, then ours
+              } else {
+                for (int q = 0; q < V - m; ++q) store_elem<DT>(a.p.out[r], e + q, slot_elem<DT>(o, q));
+              }
+            }
+            if (lane == 63 && !next_vec)
+              for (int q = V - m; q < V; ++q) store_elem<DT>(a.p.out[r], e + q, slot_elem<DT>(o, q));
+          }
+        }
+        prev = o;
+      } else {
+        for (int q = 0; q < V; ++q) {
+          const int64_t eq = e + q;
+          if (eq >= a.count) break;
+          int ce = 0;
+          if (a.rot)
+            while (ce + 1 < NR && chunk_lo(a.q, a.r, ce + 1) <= eq) ++ce;
+          edge_elem<DT, OP, NR, kLinear>(a, ce, eq);
+        }
+      }
+      prev_vec = cur_vec;
+      cur_vec = next_vec;
+      c = cn;
+    }
+  }
+}
+
+template <int DT, int OP, int NR>
+hipError_t launch_skew(SkewArgs& s, hipStream_t st) {
+  constexpr int V = Traits<DT>::kVec;
+  const int64_t tiles = (s.f.count + 64 * V - 1) / (64 * V);
+  const int64_t strips = (tiles + kSkewStrip - 1) / kSkewStrip;
+  int64_t g = static_cast<int64_t>(cu_count()) * blocks_per_cu<NR>();
+  const int64_t need = (strips + kThreads / 64 - 1) / (kThreads / 64);
+  if (g > need) g = need;
+  if (g < 1) g = 1;
+  hipLaunchKernelGGL((skew_kernel<DT, OP, NR>), dim3(static_cast<unsigned>(g)), dim3(kThreads), 0, st, s);
+  return hipGetLastError();
+}
+
+template <int DT, int OP>
+hipError_t skew_n(SkewArgs& s, hipStream_t st) {
+  switch (s.f.n) {
+    case 2: return launch_skew<DT, OP, 2>(s, st);
+    case 4: return launch_skew<DT, OP, 4>(s, st);
+    case 8: return launch_skew<DT, OP, 8>(s, st);
+    case 16: return launch_skew<DT, OP, 16>(s, st);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+template <int DT>
+hipError_t skew_op(SkewArgs& s, int op, hipStream_t st) {
+  switch (op) {
+    case AR_SUM: return skew_n<DT, AR_SUM>(s, st);
+    case AR_AVG: return skew_n<DT, AR_AVG>(s, st);
+    case AR_MIN: return skew_n<DT, AR_MIN>(s, st);
+    case AR_MAX: return skew_n<DT, AR_MAX>(s, st);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+// The skewed-buffer kernel takes a call when the 2N addresses are element-aligned, not all equal modulo 16 and
+// not all multiples of 4 bytes (2-byte types at odd offsets), the rank count is 2, 4, 8 or 16, the order is the
+// ring's or rank order, and there are a few wave tiles of work; it fills the per-rank offsets.
+template <int DT>
+bool plan_skew(const RankPtrs& p, int n, int64_t count, int algo, SkewArgs& s) {
+  constexpr int ES = Traits<DT>::kSize, V = Traits<DT>::kVec;
+  if (!(algo == AR_ALGO_RING || algo == AR_ALGO_FUSED) || !(n == 2 || n == 4 || n == 8 || n == 16)) return false;
+  if (count < 4 * 64 * V) return false;
+  bool differ = false, words = true;
+  const uintptr_t r0 = reinterpret_cast<uintptr_t>(p.in[0]) % 16;
+  for (int r = 0; r < n; ++r) {
+    const uintptr_t i = reinterpret_cast<uintptr_t>(p.in[r]), o = reinterpret_cast<uintptr_t>(p.out[r]);
+    if (i % ES || o % ES) return false;
+    differ = differ || i % 16 != r0 || o % 16 != r0;
+    words = words && i % 4 == 0 && o % 4 == 0;
+    s.im[r] = static_cast<int8_t>((i % 16) / ES);
+    s.om[r] = static_cast<int8_t>((o % 16) / ES);
+  }
+  // addresses that are all multiples of 4 bytes keep the one-front kernel with 16-byte accesses at 4-byte
+  // alignment, which measured faster (N = 8, 256 MiB of bf16, rank r at 2r elements: 938 us against 1,354 us)
+  return differ && !words;
+}
+
 // ------------------------------------------------------------------------------------------ launch
 template <int DT, int OP, int NR, int U, int SHAPE>
 hipError_t launch_one(CollapsedArgs& a, int nchunks, hipStream_t s) {
@@ -730,6 +934,13 @@ hipError_t launch_collapsed_dt<kDT, kLarge>(const RankPtrs& p, int n, int64_t co
   a.q = count / nchunks;
   a.r = count % nchunks;
   a.rot = algo == AR_ALGO_RING ? 1 : 0;
+  if constexpr (Traits<kDT>::kSize == 2) {
+    SkewArgs sk;
+    if (plan_skew<kDT>(p, n, count, algo, sk)) {
+      sk.f = a;
+      return skew_op<kDT>(sk, op, s);
+    }
+  }
   return dispatch_op<kDT>(a, op, algo, s);
 }
 

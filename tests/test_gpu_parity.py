@@ -198,6 +198,38 @@ def test_inputs_and_outputs_at_different_offsets(algo, in_off, out_off):
     assert_bitwise([from_dev(o, dt) for o in outs], expect(xs, dt, ar.AR_MAX, algo), f"{in_off}/{out_off} {algo}")
 
 
+@pytest.mark.parametrize("n", [2, 4, 8, 16])
+@pytest.mark.parametrize("dt", [ar.AR_F32, ar.AR_BF16, ar.AR_F16, ar.AR_I32])
+@pytest.mark.parametrize("algo", [ar.AR_ALGO_RING, ar.AR_ALGO_FUSED])
+def test_skewed_rank_buffers_every_residue(n, dt, algo):
+    """Every rank's input and output at an element offset of its own (residues modulo 16 bytes all over, inputs
+    and outputs different). 2-byte types (odd offsets among them): aligned loads shifted per rank, aligned stores
+    assembled across lanes and carried between the tiles of a strip, wave tiles that straddle a chunk boundary
+    and the first and last tiles element by element. 4-byte types: 16-byte accesses at 4-byte alignment. Counts
+    with ragged chunks, and the smallest count the skewed kernel takes and one below it; out of place and in
+    place, sum and min."""
+    v = 16 // (2 if dt in (ar.AR_BF16, ar.AR_F16) else 4)
+    for count in (64 * v * 37 + 5 * n + 3, 4 * 64 * v, 4 * 64 * v - 1):
+        xs = _inputs(dt, n, count, 27)
+        in_off = [(3 * r + 1) % v for r in range(n)]
+        out_off = [(5 * r + 2) % v for r in range(n)]
+        for op in (ar.AR_SUM, ar.AR_MIN):
+            want = expect(xs, dt, op, algo)
+            ins = [to_dev(x, dt, offset=in_off[r], guard=8)[1] for r, x in enumerate(xs)]
+            outs = [empty_like_dev(count, dt, offset=out_off[r], guard=8) for r in range(n)]
+            ar.ar_allreduce(ins, [o[1] for o in outs], op, algo)
+            torch.cuda.synchronize()
+            assert_bitwise([from_dev(o[1], dt) for o in outs], want, f"skewed n={n} dt={dt} count={count} op={op}")
+            for r, (base, _) in enumerate(outs):  # nothing written outside the views (poisoned all-ones)
+                bits = from_dev(base, dt)
+                lo = 8 + out_off[r]
+                full = np.iinfo(bits.dtype).max
+                assert np.all(bits[:lo] == full) and np.all(bits[lo + count:] == full), f"guard band rank {r}"
+            ar.ar_allreduce(ins, ins, op, algo)
+            torch.cuda.synchronize()
+            assert_bitwise([from_dev(t, dt) for t in ins], want, f"skewed in place n={n} dt={dt} count={count}")
+
+
 @pytest.mark.parametrize("algo", ONE_PASS)
 @pytest.mark.parametrize("dt,step", [(ar.AR_F32, 1), (ar.AR_BF16, 2), (ar.AR_BF16, 1), (ar.AR_I32, 3)])
 @pytest.mark.parametrize("count", [300_001, 5_000_011])
