@@ -32,7 +32,7 @@ namespace ar {
 
 template <int DT>
 hipError_t collapsed_for(const RankPtrs& p, int n, int64_t count, int op, int algo, int64_t head, hipStream_t s) {
-  if (large_launch(n, count, kElemSize<DT>)) return launch_collapsed_dt<DT, 1>(p, n, count, op, algo, head, s);
+  if (large_launch(n, count, kElemSize<DT>, algo)) return launch_collapsed_dt<DT, 1>(p, n, count, op, algo, head, s);
   return launch_collapsed_dt<DT, 0>(p, n, count, op, algo, head, s);
 }
 
@@ -75,7 +75,7 @@ template <int DT>
 hipError_t segments_for(const RankPtrs& p, int n, const int64_t* counts, int nseg, int op, int algo, hipStream_t s) {
   int64_t total = 0;
   for (int i = 0; i < nseg; ++i) total += counts[i];
-  if (large_launch(n, total, kElemSize<DT>)) return launch_segments_dt<DT, 1>(p, n, counts, nseg, op, algo, s);
+  if (large_launch(n, total, kElemSize<DT>, algo)) return launch_segments_dt<DT, 1>(p, n, counts, nseg, op, algo, s);
   return launch_segments_dt<DT, 0>(p, n, counts, nseg, op, algo, s);
 }
 

@@ -47,10 +47,15 @@ hipError_t launch_segments_dt(const RankPtrs& p, int n, const int64_t* counts, i
                               hipStream_t s);
 
 // Which build a one-pass launch uses: the large one once the launch moves more than 1 GiB of HBM traffic (N reads
-// plus N writes of `elems` elements of `esize` bytes per rank).
+// plus N writes of `elems` elements of `esize` bytes per rank), except the ring on 2 or 4 ranks, which stays on
+// the small build (bf16 avg, one box, two runs: N = 2 at 512 MiB per rank 439-455 us against 459-465 us, N = 4 at
+// 256 MiB 399-404 against 416-418; the trees there ran 4-12% faster on the large build, N = 16 level or faster).
 constexpr int64_t kLargeTrafficBytes = int64_t(1) << 30;
 template <int DT> constexpr int kElemSize = (DT == AR_BF16 || DT == AR_F16) ? 2 : 4;
-inline bool large_launch(int n, int64_t elems, int esize) { return 2 * int64_t(n) * elems * esize > kLargeTrafficBytes; }
+inline bool large_launch(int n, int64_t elems, int esize, int algo) {
+  if (algo == AR_ALGO_RING && n <= 4) return false;
+  return 2 * int64_t(n) * elems * esize > kLargeTrafficBytes;
+}
 
 // Bucketed all-reduce from and to per-tensor buffers (device descriptor and pointer tables).
 hipError_t launch_tensors(const ar_tensor_desc* d_descs, const void* const* d_in, void* const* d_out, int ntensors,
