@@ -59,7 +59,7 @@ constexpr int kThreads = kLarge ? 128 : 256;
 // for N = 8 (one 256-thread workgroup, or two 128-thread ones in the large build), more where a thread has
 // fewer loads in flight or writes fewer streams. More bytes in flight (longer tiles, a second tile's loads
 // issued before the first tile's stores, more workgroups) measured slower. On large launches 128-thread
-// workgroups ran level with 256-thread ones of the same wave count on most boxes and up to 11% faster on a box
+// workgroups ran level with 256-thread ones of the same wave count on most MI355X parts and up to 11% faster on one
 // where the 256-thread shape was slow; on launches of 2-4 MiB per rank they ran 8% slower.
 template <int NR> constexpr int slots_per_thread() { return (NR > 0 && NR < 8) ? 8 / NR : 1; }
 // Element by element (buffers whose addresses differ modulo 16 between ranks): UE elements per thread and tile,

@@ -155,9 +155,9 @@ template <int DT> __device__ __forceinline__ void store_elem(void* base, int64_t
 
 // Streaming 16-byte loads and stores. Each element is read once and written once per call. The stores are
 // non-temporal. Loads come in two cache policies, and which one is faster depends on the kernel's mix of
-// reads and writes and on the launch's size. Measured on MI355X, cache-cold calls, one box per comparison:
+// reads and writes and on the launch's size. Measured on MI355X, cache-cold calls, one GPU per comparison:
 //   - N-read, N-write fold, N = 8: default-policy loads 2-12% faster from 128 MiB per rank up (771-775 us
-//     against 800-806 us at 256 MiB of bf16 on one box, level or 1% slower on another), but 5-8% slower from
+//     against 800-806 us at 256 MiB of bf16 on one GPU, level or 1% slower on another), but 5-8% slower from
 //     2 to 64 MiB per rank;
 //   - all-gather (1 read, N writes) and the E4M3 quantizer (2 bytes read, ~1 written): default policy 13% and
 //     10% faster; reduce-scatter (N reads, 1 write) and the compressed ring: non-temporal 7% and 3% faster.

@@ -39,7 +39,7 @@ hipError_t launch_segments(const RankPtrs& p, int n, const int64_t* counts, int 
 // for its pair; the two functions above pick one. LARGE = 0: non-temporal 16-byte loads, 256-thread workgroups;
 // LARGE = 1: default-policy loads, 128-thread workgroups at twice the count per CU. Measured on MI355X (N = 8,
 // fp32 and bf16, cache-cold calls): the first is 5-8% faster up to 64 MiB per rank, the second 2-12% faster
-// from 128 MiB per rank (the headline's 256 MiB of bf16 among them), depending on the box.
+// from 128 MiB per rank (8 ranks of 256 MiB of bf16 among them), depending on the part.
 template <int DT, int LARGE>
 hipError_t launch_collapsed_dt(const RankPtrs& p, int n, int64_t count, int op, int algo, int64_t head, hipStream_t s);
 template <int DT, int LARGE>
@@ -48,7 +48,7 @@ hipError_t launch_segments_dt(const RankPtrs& p, int n, const int64_t* counts, i
 
 // Which build a one-pass launch uses: the large one once the launch moves more than 1 GiB of HBM traffic (N reads
 // plus N writes of `elems` elements of `esize` bytes per rank), except the ring on 2 or 4 ranks, which stays on
-// the small build (bf16 avg, one box, two runs: N = 2 at 512 MiB per rank 439-455 us against 459-465 us, N = 4 at
+// the small build (bf16 avg, one MI355X, two runs: N = 2 at 512 MiB per rank 439-455 us against 459-465 us, N = 4 at
 // 256 MiB 399-404 against 416-418; the trees there ran 4-12% faster on the large build, N = 16 level or faster).
 constexpr int64_t kLargeTrafficBytes = int64_t(1) << 30;
 template <int DT> constexpr int kElemSize = (DT == AR_BF16 || DT == AR_F16) ? 2 : 4;

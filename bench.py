@@ -138,7 +138,7 @@ def copy_ceiling(torch, ins, outs, reps=10):
 
 
 def write_ceiling(torch, ins, reps=10):
-    """Context for the roofline on this machine: a plain write (torch fill_) of the headline's N*S bytes, median of
+    """Context for the roofline on this GPU: a plain write (torch fill_) of the headline's N*S bytes, median of
     10 after warm-up calls. Beside the copy above it brackets the all-reduce, which mixes reads and writes half
     and half."""
     dst = torch.empty(sum(t.numel() for t in ins) * ins[0].element_size() // 4, dtype=torch.float32,
