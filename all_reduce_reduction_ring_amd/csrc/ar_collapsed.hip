@@ -575,7 +575,8 @@ __global__ __launch_bounds__(kThreads) void skew_kernel(SkewArgs s) {
           if (m == 0) {
             st16(ob + j * 16, o);
           } else {
-            const u32x4 up = shift_by<ES>(V - m, o, nx);  // aligned slot j + 1: last m of this lane, first V - m of next
+            // aligned slot j + 1: the last m elements of this lane, then the first V - m of the next
+            const u32x4 up = shift_by<ES>(V - m, o, nx);
             if (lane < 63) st16(ob + (j + 1) * 16, up);
             if (lane == 0) {
               if (prev_vec) {

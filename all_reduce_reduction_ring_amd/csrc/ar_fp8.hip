@@ -332,107 +332,107 @@ __global__ __launch_bounds__(kThreads) void fp8_ring_kernel(Fp8RingArgs a) {
   const int64_t wave0 = static_cast<int64_t>(blockIdx.x) * (kThreads >> 6) + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int64_t nstrips = (a.tasks + a.strip - 1) / a.strip;
   for (int64_t sp = wave0; sp < nstrips; sp += nwaves) {
-   u32x4 prev = {0u, 0u, 0u, 0u};  // this lane's packed result in the previous task of the strip
-   bool prev_shifted = false;       // that task took the shifted path (in the same chunk as the next one or not)
-   int64_t prev_c = -1;
-   TaskGeo gn = task_geo(a, sp * a.strip);
-   for (int k = 0; k < a.strip; ++k) {
-    const int64_t w = sp * a.strip + k;
-    if (w >= a.tasks) break;
-    const TaskGeo g = gn;
-    if (k + 1 < a.strip && w + 1 < a.tasks) gn = task_geo(a, w + 1);
-    const bool next_shifted = k + 1 < a.strip && w + 1 < a.tasks && gn.c == g.c && shifted_task<DT, NR>(a, gn);
-    const bool carried = prev_shifted && prev_c == g.c;  // the previous task ends where this one starts
-    const int64_t c = g.c, t = g.t, lo = g.lo, hi = g.hi;
-    const int64_t bic = t * 4 + row;
-    const int64_t e0 = lo + bic * kBlock + l16 * kPerLane;
-    const int64_t bend = lo + (bic + 1) * kBlock < hi ? lo + (bic + 1) * kBlock : hi;
-    const int64_t nv = bend - e0;
-    const int nvalid = nv <= 0 ? 0 : (nv >= kPerLane ? kPerLane : static_cast<int>(nv));
-    const int start = static_cast<int>(c);
-    // elements between the chunk start and the 16-byte grid below it (the same for every lane of the wave task)
-    const int mis = static_cast<int>(lo & (DT == AR_BF16 ? 7 : 3));
-    const bool lane_vec = a.vec != 0 && mis == 0;
-    const bool full = g.full;
-    const bool shifted = shifted_task<DT, NR>(a, g);
-    float p[kPerLane];
-    if (NR > 0 && lane_vec && full) {
-      // every lane holds 8 in-range, aligned elements: issue all N loads before any arithmetic
-      Raw8<DT> raw[NR > 0 ? NR : 1];
+    u32x4 prev = {0u, 0u, 0u, 0u};  // this lane's packed result in the previous task of the strip
+    bool prev_shifted = false;       // that task took the shifted path (in the same chunk as the next one or not)
+    int64_t prev_c = -1;
+    TaskGeo gn = task_geo(a, sp * a.strip);
+    for (int k = 0; k < a.strip; ++k) {
+      const int64_t w = sp * a.strip + k;
+      if (w >= a.tasks) break;
+      const TaskGeo g = gn;
+      if (k + 1 < a.strip && w + 1 < a.tasks) gn = task_geo(a, w + 1);
+      const bool next_shifted = k + 1 < a.strip && w + 1 < a.tasks && gn.c == g.c && shifted_task<DT, NR>(a, gn);
+      const bool carried = prev_shifted && prev_c == g.c;  // the previous task ends where this one starts
+      const int64_t c = g.c, t = g.t, lo = g.lo, hi = g.hi;
+      const int64_t bic = t * 4 + row;
+      const int64_t e0 = lo + bic * kBlock + l16 * kPerLane;
+      const int64_t bend = lo + (bic + 1) * kBlock < hi ? lo + (bic + 1) * kBlock : hi;
+      const int64_t nv = bend - e0;
+      const int nvalid = nv <= 0 ? 0 : (nv >= kPerLane ? kPerLane : static_cast<int>(nv));
+      const int start = static_cast<int>(c);
+      // elements between the chunk start and the 16-byte grid below it (the same for every lane of the wave task)
+      const int mis = static_cast<int>(lo & (DT == AR_BF16 ? 7 : 3));
+      const bool lane_vec = a.vec != 0 && mis == 0;
+      const bool full = g.full;
+      const bool shifted = shifted_task<DT, NR>(a, g);
+      float p[kPerLane];
+      if (NR > 0 && lane_vec && full) {
+        // every lane holds 8 in-range, aligned elements: issue all N loads before any arithmetic
+        Raw8<DT> raw[NR > 0 ? NR : 1];
 #pragma unroll
-      for (int k = 0; k < NR; ++k) {
-        int rr = start + k;
-        rr = rr >= NR ? rr - NR : rr;
-        raw[k].load(a.p.in[rr], e0);
-      }
-      raw[0].widen8(p);
-#pragma unroll
-      for (int k = 1; k < NR; ++k) {
-        float own[kPerLane];
-        raw[k].widen8(own);
-        hop(p, own);
-      }
-      finish<OP>(p, NR);
-#pragma unroll
-      for (int r = 0; r < NR; ++r) store8<DT>(a.p.out[r], e0, kPerLane, true, p);
-    } else if (shifted) {
-      constexpr int NT = NR > 0 ? NR : 1;
-      const int64_t A = e0 - mis;  // a multiple of 8 elements; A + 16 <= count, so both slots are in the buffer
-      u32x4 x0[NT], x1[NT], w[NT];
-#pragma unroll
-      for (int k = 0; k < NT; ++k) {
-        int rr = start + k;
-        rr = rr >= NT ? rr - NT : rr;
-        x0[k] = ld16(static_cast<const uint16_t*>(a.p.in[rr]) + A);
-        x1[k] = ld16(static_cast<const uint16_t*>(a.p.in[rr]) + A + 8);
-      }
-      shift_ranks_by<NT>(mis, x0, x1, w);
-      Slot<AR_BF16>::unpack(w[0], p);
-#pragma unroll
-      for (int k = 1; k < NT; ++k) {
-        float own[kPerLane];
-        Slot<AR_BF16>::unpack(w[k], own);
-        hop(p, own);
-      }
-      finish<OP>(p, NT);
-      const u32x4 o = Slot<AR_BF16>::pack(p);
-      u32x4 nx, last;  // the next lane's result; the previous task's last lane
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        nx[i] = static_cast<uint32_t>(__shfl_down(static_cast<int>(o[i]), 1));
-        last[i] = static_cast<uint32_t>(__shfl(static_cast<int>(prev[i]), 63));
-      }
-      u32x4 one[1] = {o}, two[1] = {nx}, slot[1], lst[1] = {last}, low[1];
-      shift_ranks_by<1>(8 - mis, one, two, slot);  // slot [A + 8, A + 16): our last m, the next lane's first 8 - m
-      shift_ranks_by<1>(8 - mis, lst, one, low);   // slot [A, A + 8): the previous task's last m, then our first
-#pragma unroll
-      for (int r = 0; r < NT; ++r) {
-        uint16_t* out = static_cast<uint16_t*>(a.p.out[r]);
-        if (lane < 63) st16(out + A + 8, slot[0]);
-        if (lane == 0) {
-          if (carried) st16(out + A, low[0]);
-          else  // [A + m, A + 8): the rest of the slot below belongs to the previous task
-            for (int q = 0; q < 8 - mis; ++q) store_elem<AR_BF16>(out, e0 + q, narrow<AR_BF16>(p[q]));
+        for (int k = 0; k < NR; ++k) {
+          int rr = start + k;
+          rr = rr >= NR ? rr - NR : rr;
+          raw[k].load(a.p.in[rr], e0);
         }
-        if (lane == 63 && !next_shifted)  // [A + 8, A + 8 + m): the rest of the slot above is the next task's
-          for (int q = 8 - mis; q < kPerLane; ++q) store_elem<AR_BF16>(out, e0 + q, narrow<AR_BF16>(p[q]));
+        raw[0].widen8(p);
+#pragma unroll
+        for (int k = 1; k < NR; ++k) {
+          float own[kPerLane];
+          raw[k].widen8(own);
+          hop(p, own);
+        }
+        finish<OP>(p, NR);
+#pragma unroll
+        for (int r = 0; r < NR; ++r) store8<DT>(a.p.out[r], e0, kPerLane, true, p);
+      } else if (shifted) {
+        constexpr int NT = NR > 0 ? NR : 1;
+        const int64_t A = e0 - mis;  // a multiple of 8 elements; A + 16 <= count, so both slots are in the buffer
+        u32x4 x0[NT], x1[NT], w[NT];
+#pragma unroll
+        for (int k = 0; k < NT; ++k) {
+          int rr = start + k;
+          rr = rr >= NT ? rr - NT : rr;
+          x0[k] = ld16(static_cast<const uint16_t*>(a.p.in[rr]) + A);
+          x1[k] = ld16(static_cast<const uint16_t*>(a.p.in[rr]) + A + 8);
+        }
+        shift_ranks_by<NT>(mis, x0, x1, w);
+        Slot<AR_BF16>::unpack(w[0], p);
+#pragma unroll
+        for (int k = 1; k < NT; ++k) {
+          float own[kPerLane];
+          Slot<AR_BF16>::unpack(w[k], own);
+          hop(p, own);
+        }
+        finish<OP>(p, NT);
+        const u32x4 o = Slot<AR_BF16>::pack(p);
+        u32x4 nx, last;  // the next lane's result; the previous task's last lane
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          nx[i] = static_cast<uint32_t>(__shfl_down(static_cast<int>(o[i]), 1));
+          last[i] = static_cast<uint32_t>(__shfl(static_cast<int>(prev[i]), 63));
+        }
+        u32x4 one[1] = {o}, two[1] = {nx}, slot[1], lst[1] = {last}, low[1];
+        shift_ranks_by<1>(8 - mis, one, two, slot);  // slot [A + 8, A + 16): our last m, the next lane's first 8 - m
+        shift_ranks_by<1>(8 - mis, lst, one, low);   // slot [A, A + 8): the previous task's last m, then our first
+#pragma unroll
+        for (int r = 0; r < NT; ++r) {
+          uint16_t* out = static_cast<uint16_t*>(a.p.out[r]);
+          if (lane < 63) st16(out + A + 8, slot[0]);
+          if (lane == 0) {
+            if (carried) st16(out + A, low[0]);
+            else  // [A + m, A + 8): the rest of the slot below belongs to the previous task
+              for (int q = 0; q < 8 - mis; ++q) store_elem<AR_BF16>(out, e0 + q, narrow<AR_BF16>(p[q]));
+          }
+          if (lane == 63 && !next_shifted)  // [A + 8, A + 8 + m): the rest of the slot above is the next task's
+            for (int q = 8 - mis; q < kPerLane; ++q) store_elem<AR_BF16>(out, e0 + q, narrow<AR_BF16>(p[q]));
+        }
+        prev = o;
+      } else {
+        load8<DT>(a.p.in[start], e0, nvalid, lane_vec, p);
+        for (int k = 1; k < n; ++k) {
+          int rr = start + k;
+          rr = rr >= n ? rr - n : rr;
+          float own[kPerLane];
+          load8<DT>(a.p.in[rr], e0, nvalid, lane_vec, own);
+          hop(p, own);
+        }
+        finish<OP>(p, n);
+        for (int r = 0; r < n; ++r) store8<DT>(a.p.out[r], e0, nvalid, lane_vec, p);
       }
-      prev = o;
-    } else {
-      load8<DT>(a.p.in[start], e0, nvalid, lane_vec, p);
-      for (int k = 1; k < n; ++k) {
-        int rr = start + k;
-        rr = rr >= n ? rr - n : rr;
-        float own[kPerLane];
-        load8<DT>(a.p.in[rr], e0, nvalid, lane_vec, own);
-        hop(p, own);
-      }
-      finish<OP>(p, n);
-      for (int r = 0; r < n; ++r) store8<DT>(a.p.out[r], e0, nvalid, lane_vec, p);
+      prev_shifted = shifted;
+      prev_c = c;
     }
-    prev_shifted = shifted;
-    prev_c = c;
-   }
   }
 }
 
