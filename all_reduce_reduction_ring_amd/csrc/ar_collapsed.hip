@@ -454,6 +454,9 @@ hipError_t launch_front(CollapsedArgs& a, hipStream_t s) {
   const int64_t nslots = a.count > a.head ? (a.count - a.head) / V : 0;
   const int64_t ntiles = (nslots + TS - 1) / TS;
   int64_t g = static_cast<int64_t>(cu_count()) * blocks_per_cu<NR>();
+  // up to two tiles per workgroup: one workgroup per tile instead, so no workgroup walks two in turn (N = 8,
+  // 2 MiB of fp32 per rank: 7.8 us against 9.7 us of device time; from four tiles per workgroup up it gained nothing)
+  if (ntiles <= 2 * g) g = ntiles;
   if (g > ntiles) g = ntiles;
   if (g < 1) g = 1;
   hipLaunchKernelGGL((ring_front_kernel<DT, OP, NR, U>), dim3(static_cast<unsigned>(g)), dim3(kThreads), 0, s, a);
