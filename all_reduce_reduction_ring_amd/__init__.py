@@ -11,6 +11,7 @@ ar_bucket_unpack, ar_fp8_quant, ar_fp8_dequant, ar_auto_algo, ar_status_string, 
 """
 from __future__ import annotations
 
+import contextlib
 import ctypes
 import os
 
@@ -94,18 +95,26 @@ def lib():
 
 
 # ------------------------------------------------------------------------------------------ marshalling
+_DTYPE_CODES = {}
+
+
 def dtype_code(t) -> int:
-    import torch
-    codes = {torch.float32: AR_F32, torch.bfloat16: AR_BF16, torch.float16: AR_F16, torch.int32: AR_I32}
-    if t not in codes:
+    if not _DTYPE_CODES:
+        import torch
+        _DTYPE_CODES.update({torch.float32: AR_F32, torch.bfloat16: AR_BF16, torch.float16: AR_F16,
+                             torch.int32: AR_I32})
+    if t not in _DTYPE_CODES:
         raise TypeError(f"unsupported dtype {t}; expected float32, bfloat16, float16 or int32")
-    return codes[t]
+    return _DTYPE_CODES[t]
 
 
 def _stream(stream, device=None):
     """The HIP stream handle: `stream` (a torch stream or a raw handle), else the current stream of `device`."""
     import torch
     if stream is None:
+        raw = getattr(torch._C, "_cuda_getCurrentRawStream", None)  # the handle without a Stream object
+        if raw is not None and device is not None and device.index is not None:
+            return ctypes.c_void_p(raw(device.index))
         return ctypes.c_void_p(torch.cuda.current_stream(device).cuda_stream)
     if isinstance(stream, int):
         return ctypes.c_void_p(stream)
@@ -113,8 +122,11 @@ def _stream(stream, device=None):
 
 
 def _on(device):
-    """Make `device` current for a call (the library launches on the current device)."""
+    """Make `device` current for a call (the library launches on the current device); no switch when it already
+    is."""
     import torch
+    if device.index is not None and device.index == torch.cuda.current_device():
+        return contextlib.nullcontext()
     return torch.cuda.device(device)
 
 
@@ -140,18 +152,25 @@ def _check(rc: int, entry: str):
 
 
 def _rank_arrays(ins, outs):
-    if len(ins) != len(outs) or not ins:
+    """Check every rank tensor (all before any address is read), then the host arrays of their addresses. The
+    checks are the per-tensor ones of _gpu_tensor plus equal dtype, element count and device, written with the
+    cheapest accessors: this runs on every call, and for small messages it is most of the call's host time."""
+    n = len(ins)
+    if n != len(outs) or not n:
         raise ValueError("ins and outs must be non-empty lists of the same length (one tensor per rank)")
     t0 = ins[0]
-    for t in list(ins) + list(outs):
+    dt0, ne0, dev0 = t0.dtype, t0.numel(), t0.get_device()
+    for t in (*ins, *outs):
         # every rank must call with the same count and dtype; one call enforces it
-        if t.dtype != t0.dtype or t.numel() != t0.numel() or t.device != t0.device:
+        if t.dtype is not dt0 or t.numel() != ne0 or t.get_device() != dev0:
             raise ValueError("all rank tensors must share dtype, element count and device")
-        _gpu_tensor(t, "rank tensors")
-    n = len(ins)
+        if not t.is_contiguous():
+            raise ValueError("rank tensors must be contiguous")
+    if dev0 < 0:  # get_device() is -1 for host tensors
+        raise ValueError("rank tensors must be GPU tensors")
     arr_in = (ctypes.c_void_p * n)(*[t.data_ptr() for t in ins])
     arr_out = (ctypes.c_void_p * n)(*[t.data_ptr() for t in outs])
-    return arr_in, arr_out, n, t0.numel(), dtype_code(t0.dtype)
+    return arr_in, arr_out, n, ne0, dtype_code(dt0)
 
 
 def ar_allreduce(ins, outs, op=AR_SUM, algo=AR_ALGO_RING, stream=None):

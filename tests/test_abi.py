@@ -302,6 +302,9 @@ class _StubTensor:
     def numel(self):
         return self._n
 
+    def get_device(self):
+        return self.device.index if self.device.type == "cuda" else -1
+
     def dim(self):
         return len(self.shape)
 
