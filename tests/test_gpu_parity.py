@@ -136,6 +136,18 @@ def test_ring_one_front_kernel_ragged(n, dt):
         assert_bitwise(got, expect(xs, dt, op, ar.AR_ALGO_RING), f"one-front ring n={n} dt={dt} op={op}")
 
 
+@pytest.mark.parametrize("n,dt,count", [(8, ar.AR_F32, 400_003), (8, ar.AR_BF16, 1_000_005),
+                                         (16, ar.AR_F32, 1_500_001), (4, ar.AR_F32, 3_000_017),
+                                         (2, ar.AR_BF16, 6_000_011)])
+def test_ring_one_front_kernel_one_tile_per_workgroup(n, dt, count):
+    """Between one and two grids of tiles (on 256 CUs) the one-front ring gives every tile a workgroup of its own:
+    ragged counts, chunk boundaries inside tiles and slots, every op, against the literal ring."""
+    xs = _inputs(dt, n, count, 29)
+    for op in OPS:
+        got = run(xs, dt, op, ar.AR_ALGO_RING)
+        assert_bitwise(got, expect(xs, dt, op, ar.AR_ALGO_RING), f"tile per workgroup n={n} dt={dt} op={op}")
+
+
 def test_ring_one_front_kernel_sixty_four_ranks():
     """The largest rank count on the one-front kernel (rank count known only at run time), ragged count."""
     n, count = 64, 2_200_007  # above a grid of tiles for a run-time rank count (2,097,152 fp32 elements)
