@@ -465,7 +465,7 @@ hipError_t launch_front(CollapsedArgs& a, hipStream_t s) {
 
 // ------------------------------------------------------------------------------------------ skewed buffers
 // 2-byte rank buffers whose addresses differ modulo 16 and are not all multiples of 4 bytes (views at different,
-// some odd, element offsets), ring or rank order. Work runs on the
+// some odd, element offsets): the ring, rank order and the two trees. Work runs on the
 // element grid: slot j = elements [jV, jV + V) of every rank, and a wave tile is 64 consecutive slots. Rank r's
 // input sits im[r] elements past the 16-byte grid, so a lane loads the two aligned 16-byte slots around its V
 // elements and shifts them into place; output rank r sits om[r] elements past the grid, so the aligned output
@@ -501,6 +501,37 @@ __device__ __forceinline__ uint32_t slot_elem(const u32x4& v, int k) {
   else return (v[k >> 1] >> (16 * (k & 1))) & 0xFFFFu;
 }
 
+// The two trees over values already loaded and widened, v[r] for rank r (the same association as tree_fold and
+// binomial_fold): the halving tree tree(evens) (+) tree(odds) over ranks OFF, OFF + STRIDE, ..., and for a
+// power-of-two rank count the binomial tree, T(lo, 2h) = T(lo, h) (+) T(lo + h, h).
+template <int OP, int NR, int STRIDE, int OFF, typename Acc, int V, int NV>
+__device__ __forceinline__ void halving_vals(const Acc (&v)[NV][V], Acc (&acc)[V]) {
+  if constexpr (NR == 1) {
+#pragma unroll
+    for (int e = 0; e < V; ++e) acc[e] = v[OFF][e];
+  } else {
+    Acc b[V];
+    halving_vals<OP, NR / 2, STRIDE * 2, OFF>(v, acc);
+    halving_vals<OP, NR / 2, STRIDE * 2, OFF + STRIDE>(v, b);
+#pragma unroll
+    for (int e = 0; e < V; ++e) acc[e] = combine<OP>(acc[e], b[e]);
+  }
+}
+template <int OP, int NR, int LO, typename Acc, int V, int NV>
+__device__ __forceinline__ void binomial_vals(const Acc (&v)[NV][V], Acc (&acc)[V]) {
+  static_assert((NR & (NR - 1)) == 0, "power-of-two rank counts");
+  if constexpr (NR == 1) {
+#pragma unroll
+    for (int e = 0; e < V; ++e) acc[e] = v[LO][e];
+  } else {
+    Acc b[V];
+    binomial_vals<OP, NR / 2, LO>(v, acc);
+    binomial_vals<OP, NR / 2, LO + NR / 2>(v, b);
+#pragma unroll
+    for (int e = 0; e < V; ++e) acc[e] = combine<OP>(acc[e], b[e]);
+  }
+}
+
 // A wave tile takes the vector path when it lies in one chunk and both aligned slots of every lane lie inside the
 // buffers: tile 0's lower slots would start before them, and the upper slots of a tile need V more elements.
 template <int V, int NR>
@@ -519,7 +550,7 @@ __device__ __forceinline__ bool skew_vec_tile(const CollapsedArgs& a, int64_t w,
 // strip (or next to an element-path tile) are stored element by element.
 constexpr int kSkewStrip = 8;
 
-template <int DT, int OP, int NR>
+template <int DT, int OP, int NR, int SHAPE>
 __global__ __launch_bounds__(kThreads) void skew_kernel(SkewArgs s) {
   using S = Slot<DT>;
   constexpr int V = S::V, ES = Traits<DT>::kSize;
@@ -552,15 +583,24 @@ __global__ __launch_bounds__(kThreads) void skew_kernel(SkewArgs s) {
           x0[q] = ld16(base);
           x1[q] = ld16(base + 16);
         }
-        typename S::Acc acc[V], t[V];
-        S::unpack(shift_by<ES>(s.im[start], x0[0], x1[0]), acc);
+        typename S::Acc acc[V];
+        if constexpr (SHAPE == kLinear) {
+          typename S::Acc t[V];
+          S::unpack(shift_by<ES>(s.im[start], x0[0], x1[0]), acc);
 #pragma unroll
-        for (int q = 1; q < NR; ++q) {
-          int rr = start + q;
-          rr = rr >= NR ? rr - NR : rr;
-          S::unpack(shift_by<ES>(s.im[rr], x0[q], x1[q]), t);
+          for (int q = 1; q < NR; ++q) {
+            int rr = start + q;
+            rr = rr >= NR ? rr - NR : rr;
+            S::unpack(shift_by<ES>(s.im[rr], x0[q], x1[q]), t);
 #pragma unroll
-          for (int i = 0; i < V; ++i) acc[i] = combine<OP>(acc[i], t[i]);
+            for (int i = 0; i < V; ++i) acc[i] = combine<OP>(acc[i], t[i]);
+          }
+        } else {  // the trees start at rank 0, so x0[r], x1[r] hold rank r
+          typename S::Acc v[NR][V];
+#pragma unroll
+          for (int r = 0; r < NR; ++r) S::unpack(shift_by<ES>(s.im[r], x0[r], x1[r]), v[r]);
+          if constexpr (SHAPE == kHalving) halving_vals<OP, NR, 1, 0>(v, acc);
+          else binomial_vals<OP, NR, 0>(v, acc);
         }
 #pragma unroll
         for (int i = 0; i < V; ++i) acc[i] = finalize<OP>(acc[i], NR);
@@ -598,9 +638,9 @@ __global__ __launch_bounds__(kThreads) void skew_kernel(SkewArgs s) {
           const int64_t eq = e + q;
           if (eq >= a.count) break;
           int ce = 0;
-          if (a.rot)
+          if (SHAPE == kLinear && a.rot)
             while (ce + 1 < NR && chunk_lo(a.q, a.r, ce + 1) <= eq) ++ce;
-          edge_elem<DT, OP, NR, kLinear>(a, ce, eq);
+          edge_elem<DT, OP, NR, SHAPE>(a, ce, eq);
         }
       }
       prev_vec = cur_vec;
@@ -610,7 +650,7 @@ __global__ __launch_bounds__(kThreads) void skew_kernel(SkewArgs s) {
   }
 }
 
-template <int DT, int OP, int NR>
+template <int DT, int OP, int NR, int SHAPE>
 hipError_t launch_skew(SkewArgs& s, hipStream_t st) {
   constexpr int V = Traits<DT>::kVec;
   const int64_t tiles = (s.f.count + 64 * V - 1) / (64 * V);
@@ -619,39 +659,50 @@ hipError_t launch_skew(SkewArgs& s, hipStream_t st) {
   const int64_t need = (strips + kThreads / 64 - 1) / (kThreads / 64);
   if (g > need) g = need;
   if (g < 1) g = 1;
-  hipLaunchKernelGGL((skew_kernel<DT, OP, NR>), dim3(static_cast<unsigned>(g)), dim3(kThreads), 0, st, s);
+  hipLaunchKernelGGL((skew_kernel<DT, OP, NR, SHAPE>), dim3(static_cast<unsigned>(g)), dim3(kThreads), 0, st, s);
   return hipGetLastError();
 }
 
-template <int DT, int OP>
+template <int DT, int OP, int SHAPE>
 hipError_t skew_n(SkewArgs& s, hipStream_t st) {
   switch (s.f.n) {
-    case 2: return launch_skew<DT, OP, 2>(s, st);
-    case 4: return launch_skew<DT, OP, 4>(s, st);
-    case 8: return launch_skew<DT, OP, 8>(s, st);
-    case 16: return launch_skew<DT, OP, 16>(s, st);
+    case 2: return launch_skew<DT, OP, 2, SHAPE>(s, st);
+    case 4: return launch_skew<DT, OP, 4, SHAPE>(s, st);
+    case 8: return launch_skew<DT, OP, 8, SHAPE>(s, st);
+    case 16: return launch_skew<DT, OP, 16, SHAPE>(s, st);
     default: return hipErrorInvalidValue;
   }
 }
 
+template <int DT, int OP>
+hipError_t skew_shape(SkewArgs& s, int algo, hipStream_t st) {
+  switch (algo) {
+    case AR_ALGO_RHD: return skew_n<DT, OP, kHalving>(s, st);
+    case AR_ALGO_TREE: return skew_n<DT, OP, kBinomial>(s, st);
+    default: return skew_n<DT, OP, kLinear>(s, st);  // ring (rot = 1) and rank order (rot = 0)
+  }
+}
+
 template <int DT>
-hipError_t skew_op(SkewArgs& s, int op, hipStream_t st) {
+hipError_t skew_op(SkewArgs& s, int op, int algo, hipStream_t st) {
   switch (op) {
-    case AR_SUM: return skew_n<DT, AR_SUM>(s, st);
-    case AR_AVG: return skew_n<DT, AR_AVG>(s, st);
-    case AR_MIN: return skew_n<DT, AR_MIN>(s, st);
-    case AR_MAX: return skew_n<DT, AR_MAX>(s, st);
+    case AR_SUM: return skew_shape<DT, AR_SUM>(s, algo, st);
+    case AR_AVG: return skew_shape<DT, AR_AVG>(s, algo, st);
+    case AR_MIN: return skew_shape<DT, AR_MIN>(s, algo, st);
+    case AR_MAX: return skew_shape<DT, AR_MAX>(s, algo, st);
     default: return hipErrorInvalidValue;
   }
 }
 
 // The skewed-buffer kernel takes a call when the 2N addresses are element-aligned, not all equal modulo 16 and
-// not all multiples of 4 bytes (2-byte types at odd offsets), the rank count is 2, 4, 8 or 16, the order is the
-// ring's or rank order, and there are a few wave tiles of work; it fills the per-rank offsets.
+// not all multiples of 4 bytes (2-byte types at odd offsets), the rank count is 2, 4, 8 or 16, the algorithm is
+// a one-pass one, and there are a few wave tiles of work; it fills the per-rank offsets.
 template <int DT>
 bool plan_skew(const RankPtrs& p, int n, int64_t count, int algo, SkewArgs& s) {
   constexpr int ES = Traits<DT>::kSize, V = Traits<DT>::kVec;
-  if (!(algo == AR_ALGO_RING || algo == AR_ALGO_FUSED) || !(n == 2 || n == 4 || n == 8 || n == 16)) return false;
+  if (!(algo == AR_ALGO_RING || algo == AR_ALGO_FUSED || algo == AR_ALGO_RHD || algo == AR_ALGO_TREE) ||
+      !(n == 2 || n == 4 || n == 8 || n == 16))
+    return false;
   if (count < 4 * 64 * V) return false;
   bool differ = false, words = true;
   const uintptr_t r0 = reinterpret_cast<uintptr_t>(p.in[0]) % 16;
@@ -942,7 +993,7 @@ hipError_t launch_collapsed_dt<kDT, kLarge>(const RankPtrs& p, int n, int64_t co
     SkewArgs sk;
     if (plan_skew<kDT>(p, n, count, algo, sk)) {
       sk.f = a;
-      return skew_op<kDT>(sk, op, s);
+      return skew_op<kDT>(sk, op, algo, s);
     }
   }
   return dispatch_op<kDT>(a, op, algo, s);

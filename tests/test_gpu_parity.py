@@ -212,7 +212,7 @@ def test_inputs_and_outputs_at_different_offsets(algo, in_off, out_off):
 
 @pytest.mark.parametrize("n", [2, 4, 8, 16])
 @pytest.mark.parametrize("dt", [ar.AR_F32, ar.AR_BF16, ar.AR_F16, ar.AR_I32])
-@pytest.mark.parametrize("algo", [ar.AR_ALGO_RING, ar.AR_ALGO_FUSED])
+@pytest.mark.parametrize("algo", [ar.AR_ALGO_RING, ar.AR_ALGO_FUSED, ar.AR_ALGO_RHD, ar.AR_ALGO_TREE])
 def test_skewed_rank_buffers_every_residue(n, dt, algo):
     """Every rank's input and output at an element offset of its own (residues modulo 16 bytes all over, inputs
     and outputs different). 2-byte types (odd offsets among them): aligned loads shifted per rank, aligned stores
