@@ -309,13 +309,25 @@ __device__ __forceinline__ TaskGeo task_geo(const Fp8RingArgs& a, int64_t w) {
   return g;
 }
 
-// The shifted bf16 path below takes task g: full, its chunk start off the 16-byte grid, both aligned slots of
-// every lane inside the buffers (the last lane's upper slot ends 16 - m elements past its 8).
+// The shifted path below takes task g: full, its chunk start off the 16-byte grid (m elements past it), and every
+// lane's aligned slots inside the buffers (bf16: two slots, 16 elements from the lower one's start; fp32: three
+// slots, 12 elements).
 template <int DT, int NR>
 __device__ __forceinline__ bool shifted_task(const Fp8RingArgs& a, const TaskGeo& g) {
-  if (!(NR > 0 && DT == AR_BF16) || a.vec == 0 || !g.full) return false;
-  const int mis = static_cast<int>(g.lo & 7);
-  return mis != 0 && g.lo + g.t * 4 * kBlock + 63 * kPerLane - mis + 16 <= a.count;
+  if (!(NR > 0) || a.vec == 0 || !g.full) return false;
+  const int mis = static_cast<int>(g.lo & (DT == AR_BF16 ? 7 : 3));
+  constexpr int kSpan = DT == AR_BF16 ? 16 : 12;
+  return mis != 0 && g.lo + g.t * 4 * kBlock + 63 * kPerLane - mis + kSpan <= a.count;
+}
+
+// fp32 slots: x0 from element m on, continued into x1 (m wave-uniform, 0..3)
+__device__ __forceinline__ u32x4 shift4_by(int m, const u32x4& x0, const u32x4& x1) {
+  switch (m) {
+    case 0: return x0;
+    case 1: return shift_concat<4, 1>(x0, x1);
+    case 2: return shift_concat<4, 2>(x0, x1);
+    default: return shift_concat<4, 3>(x0, x1);
+  }
 }
 
 // With chunk starts off the grid, a wave walks a strip of kStrip consecutive tasks, so that in the shifted path
@@ -332,7 +344,7 @@ __global__ __launch_bounds__(kThreads) void fp8_ring_kernel(Fp8RingArgs a) {
   const int64_t wave0 = static_cast<int64_t>(blockIdx.x) * (kThreads >> 6) + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int64_t nstrips = (a.tasks + a.strip - 1) / a.strip;
   for (int64_t sp = wave0; sp < nstrips; sp += nwaves) {
-    u32x4 prev = {0u, 0u, 0u, 0u};  // this lane's packed result in the previous task of the strip
+    u32x4 prev = {0u, 0u, 0u, 0u};  // this lane's result in the previous task (bf16: packed; fp32: upper half)
     bool prev_shifted = false;       // that task took the shifted path (in the same chunk as the next one or not)
     int64_t prev_c = -1;
     TaskGeo gn = task_geo(a, sp * a.strip);
@@ -375,7 +387,66 @@ __global__ __launch_bounds__(kThreads) void fp8_ring_kernel(Fp8RingArgs a) {
         finish<OP>(p, NR);
 #pragma unroll
         for (int r = 0; r < NR; ++r) store8<DT>(a.p.out[r], e0, kPerLane, true, p);
-      } else if (shifted) {
+      } else if (shifted && DT == AR_F32) {
+        // fp32: a lane's 8 elements start m (1..3) past the grid and span three aligned slots. The slot wholly
+        // inside the lane ([A + 4, A + 8)) is stored as it is; the one above takes the next lane's first 4 - m.
+        constexpr int NT = NR > 0 ? NR : 1;
+        const int64_t A = e0 - mis;  // a multiple of 4 elements; A + 12 <= count, so all three slots are in the buffer
+        u32x4 x0[NT], x1[NT], x2[NT];
+#pragma unroll
+        for (int k = 0; k < NT; ++k) {
+          int rr = start + k;
+          rr = rr >= NT ? rr - NT : rr;
+          const float* base = static_cast<const float*>(a.p.in[rr]) + A;
+          x0[k] = ld16(base);
+          x1[k] = ld16(base + 4);
+          x2[k] = ld16(base + 8);
+        }
+        auto widen8 = [&](int k, float (&v)[kPerLane]) {
+          const u32x4 lo4 = shift4_by(mis, x0[k], x1[k]), hi4 = shift4_by(mis, x1[k], x2[k]);
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            v[i] = __uint_as_float(lo4[i]);
+            v[i + 4] = __uint_as_float(hi4[i]);
+          }
+        };
+        widen8(0, p);
+#pragma unroll
+        for (int k = 1; k < NT; ++k) {
+          float own[kPerLane];
+          widen8(k, own);
+          hop(p, own);
+        }
+        finish<OP>(p, NT);
+        u32x4 o0, o1, nx0, last;  // our two halves; the next lane's first half; the previous task's last lane
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          o0[i] = __float_as_uint(p[i]);
+          o1[i] = __float_as_uint(p[i + 4]);
+        }
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          nx0[i] = static_cast<uint32_t>(__shfl_down(static_cast<int>(o0[i]), 1));
+          last[i] = static_cast<uint32_t>(__shfl(static_cast<int>(prev[i]), 63));
+        }
+        const u32x4 mid = shift4_by(4 - mis, o0, o1);   // [A + 4, A + 8)
+        const u32x4 up = shift4_by(4 - mis, o1, nx0);   // [A + 8, A + 12): our last m, the next lane's first 4 - m
+        const u32x4 low = shift4_by(4 - mis, last, o0); // [A, A + 4): the previous task's last m, then our first
+#pragma unroll
+        for (int r = 0; r < NT; ++r) {
+          float* out = static_cast<float*>(a.p.out[r]);
+          st16(out + A + 4, mid);
+          if (lane < 63) st16(out + A + 8, up);
+          if (lane == 0) {
+            if (carried) st16(out + A, low);
+            else  // [A + m, A + 4): the rest of the slot below belongs to the previous task
+              for (int q = 0; q < 4 - mis; ++q) store_elem<AR_F32>(out, e0 + q, __float_as_uint(p[q]));
+          }
+          if (lane == 63 && !next_shifted)  // [A + 8, A + 8 + m): the rest of the slot above is the next task's
+            for (int q = 8 - mis; q < kPerLane; ++q) store_elem<AR_F32>(out, e0 + q, __float_as_uint(p[q]));
+        }
+        prev = o1;
+      } else if (shifted && DT == AR_BF16) {
         constexpr int NT = NR > 0 ? NR : 1;
         const int64_t A = e0 - mis;  // a multiple of 8 elements; A + 16 <= count, so both slots are in the buffer
         u32x4 x0[NT], x1[NT], w[NT];
@@ -498,7 +569,8 @@ hipError_t launch_fp8_ring(const RankPtrs& p, int n, int64_t count, int dtype, i
   a.tasks = a.r * a.wt_a + (n - a.r) * a.wt_b;
   // chunk starts off the 16-byte grid are handled per wave task in the kernel
   a.vec = vec ? 1 : 0;
-  a.strip = (dtype == AR_BF16 && vec && !(a.r == 0 && a.q % kPerLane == 0)) ? kStrip : 1;
+  // chunk starts on the 16-byte grid: q a multiple of 8 bf16 or 4 fp32 elements (and no remainder)
+  a.strip = (vec && !(a.r == 0 && a.q % (dtype == AR_BF16 ? 8 : 4) == 0)) ? kStrip : 1;
   if (dtype == AR_BF16) return op == AR_AVG ? ring_n<AR_BF16, AR_AVG>(a, s) : ring_n<AR_BF16, AR_SUM>(a, s);
   return op == AR_AVG ? ring_n<AR_F32, AR_AVG>(a, s) : ring_n<AR_F32, AR_SUM>(a, s);
 }

@@ -487,18 +487,20 @@ def test_fp8_ring_matches_oracle(n, count):
 
 @pytest.mark.parametrize("n", [2, 3, 4, 8])
 @pytest.mark.parametrize("extra", [1, 3, 5, 7, 26, 4096 * 3 + 5])
-def test_fp8_ring_bf16_chunks_off_the_16_byte_grid(n, extra):
-    """bf16 counts that are not a multiple of 8 N put chunk starts 1..7 elements past the 16-byte grid (n = 8,
-    extra = 7 gives every one of them); chunks of several 512-element wave tasks take shifted vector loads and
-    lane-exchanged aligned stores, the chunk ends and the last slots of the buffer element by element. Bitwise
-    against the oracle, out of place and in place."""
+@pytest.mark.parametrize("dt", [ar.AR_BF16, ar.AR_F32])
+def test_fp8_ring_chunks_off_the_16_byte_grid(n, extra, dt):
+    """Counts that are not a multiple of 8 N (bf16) or 4 N (fp32) put chunk starts 1..7 (1..3) elements past the
+    16-byte grid (n = 8, extra = 7 gives every bf16 one); chunks of several 512-element wave tasks take shifted
+    vector loads and lane-exchanged aligned stores carried along strips of tasks, the chunk ends and the last
+    slots of the buffer element by element. Bitwise against the oracle, out of place and in place."""
     count = n * 4096 + extra
-    xs = inputs.rank_inputs("outlier_bf16", n, count, cfg=6, extra=(n, count))
+    kind = "outlier_bf16" if dt == ar.AR_BF16 else "uniform_f32"
+    xs = inputs.rank_inputs(kind, n, count, cfg=6, extra=(n, count))
     for op in (ar.AR_SUM, ar.AR_AVG):
-        want = expect(xs, ar.AR_BF16, op, ar.AR_ALGO_RING_FP8)
-        assert_bitwise(run(xs, ar.AR_BF16, op, ar.AR_ALGO_RING_FP8), want, f"fp8 ring n={n} count={count}")
-        assert_bitwise(run(xs, ar.AR_BF16, op, ar.AR_ALGO_RING_FP8, inplace=True), want,
-                       f"fp8 ring in place n={n} count={count}")
+        want = expect(xs, dt, op, ar.AR_ALGO_RING_FP8)
+        assert_bitwise(run(xs, dt, op, ar.AR_ALGO_RING_FP8), want, f"fp8 ring n={n} count={count} dt={dt}")
+        assert_bitwise(run(xs, dt, op, ar.AR_ALGO_RING_FP8, inplace=True), want,
+                       f"fp8 ring in place n={n} count={count} dt={dt}")
 
 
 @pytest.mark.parametrize("n", [1, 2, 3, 5, 8])
