@@ -136,9 +136,9 @@ int ar_auto_algo(int nranks, size_t count, int dtype);
  *   multiple of 256 bytes (buffers of 1 MiB or more) or of 16 bytes, the rest in vectors. Pointers that differ
  *   modulo 16 but are all multiples of 4 use vectors from element 0 (slower: they straddle cache lines). 2-byte
  *   types at odd per-rank offsets use aligned vectors shifted per rank for RING, FUSED, RHD and TREE with nranks
- *   2, 4, 8 or 16 (slower still). RING_FP8 on bf16 uses vectors when every pointer is 16-byte aligned, for any count (chunk
- *   starts off the 16-byte grid take shifted vectors); the other algorithms use vectors only when every pointer
- *   is 16-byte aligned. Otherwise element by element.
+ *   2, 4, 8 or 16 (slower still). RING_FP8 uses vectors when every pointer is 16-byte aligned, for any count
+ *   (chunk starts off the 16-byte grid take shifted vectors); the other algorithms use vectors only when every
+ *   pointer is 16-byte aligned. Otherwise element by element.
  * Errors: AR_ERR_INVALID (enum, nranks, NULL), AR_ERR_UNSUPPORTED (RHD with N not a power of two; FP8
  *   with a dtype other than F32/BF16 or an op other than SUM/AVG), AR_ERR_ALIAS, AR_ERR_WORKSPACE (the
  *   stepwise algorithms on bf16/f16 need ar_allreduce_ws), AR_ERR_HIP. AR_ALGO_AUTO is resolved first, so
