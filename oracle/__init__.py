@@ -20,25 +20,38 @@ NP_DTYPE = {F32: np.float32, BF16: np.uint16, F16: np.uint16, I32: np.int32}
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _SRC = os.path.join(_HERE, "oracle.c")
-_LIB_PATH = os.path.join(_HERE, "liboracle.so")
+_DEFAULT_LIB = os.path.join(_HERE, "liboracle.so")
+# ORACLE_LIB names another build of oracle.c to load instead (the tests use it to run the pins against a
+# sanitizer build and against builds with planted mistakes); that file is never rebuilt here.
+_LIB_PATH = os.environ.get("ORACLE_LIB") or _DEFAULT_LIB
 _lib = None
+
+# gcc flags of every build: IEEE fp32 (no contraction, no fast-math), OpenMP over element loops.
+CFLAGS = ["-std=c11", "-fPIC", "-shared", "-fopenmp", "-ffp-contract=off", "-fno-fast-math", "-Wall", "-Wextra"]
+
+
+def compile_library(src: str, out: str, extra=()) -> str:
+    """Compile an oracle source file into a shared library at `out` (gcc, CFLAGS plus `extra`)."""
+    tmp = out + ".tmp"
+    cmd = ["gcc", "-O2", *CFLAGS, *extra, "-o", tmp, src, "-lm"]
+    subprocess.run(cmd, check=True)
+    os.replace(tmp, out)
+    return out
 
 
 def build(force: bool = True) -> str:
-    """Compile liboracle.so with gcc (IEEE fp32, no contraction, OpenMP over element loops)."""
-    if force or not os.path.exists(_LIB_PATH):
-        tmp = _LIB_PATH + ".tmp"
-        cmd = ["gcc", "-O2", "-std=c11", "-fPIC", "-shared", "-fopenmp", "-ffp-contract=off", "-fno-fast-math",
-               "-Wall", "-Wextra", "-o", tmp, _SRC, "-lm"]
-        subprocess.run(cmd, check=True)
-        os.replace(tmp, _LIB_PATH)
-    return _LIB_PATH
+    """Compile liboracle.so from oracle.c."""
+    if force or not os.path.exists(_DEFAULT_LIB):
+        compile_library(_SRC, _DEFAULT_LIB)
+    return _DEFAULT_LIB
 
 
 def lib():
     global _lib
     if _lib is None:
         if not os.path.exists(_LIB_PATH):
+            if _LIB_PATH != _DEFAULT_LIB:
+                raise RuntimeError(f"ORACLE_LIB={_LIB_PATH} does not exist")
             build(force=False)
         L = ctypes.CDLL(_LIB_PATH)
         vp, i64, i32 = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int
@@ -222,8 +235,18 @@ def bucket_plan(numels, esize, n, cap_bytes):
     return bucket_of[:nt], offset_of[:nt], bcount[: nb.value]
 
 
-def bucketed_allreduce(tensors, dtype=F32, op=AVG, cap_bytes=25 << 20):
-    """tensors[r][t] -> outs[r][t]: plan, pack, ring all-reduce per bucket, unpack."""
+_ALGOS = {"ring": ring_allreduce, "fused": fused_allreduce, "rhd": rhd_allreduce, "tree": tree_allreduce}
+
+
+def bucketed_allreduce(tensors, dtype=F32, op=AVG, cap_bytes=25 << 20, algo="ring"):
+    """tensors[r][t] -> outs[r][t]: plan, pack, all-reduce every bucket, unpack.
+
+    algo "ring" runs the C routine (plan, pack, literal ring per bucket, unpack, all in oracle.c). The other
+    algorithms ("fused", "rhd", "tree") and "ring_py" pack here: the C plan, each tensor copied to its offset in
+    a zero-filled bucket per rank, the named oracle all-reduce on every bucket, and each tensor's first numel
+    elements copied back."""
+    if algo != "ring":
+        return _bucketed_by_packing(tensors, dtype, op, cap_bytes, _ALGOS[algo.replace("_py", "")])
     n = len(tensors)
     nt = len(tensors[0]) if n else 0
     numels = np.array([np.asarray(t).size for t in tensors[0]], dtype=np.int64)
@@ -236,6 +259,33 @@ def bucketed_allreduce(tensors, dtype=F32, op=AVG, cap_bytes=25 << 20):
     _check(lib().oracle_bucketed_allreduce(_ptrs(flat_in), _ptrs(outs), n, nt, numels.ctypes.data, dtype, op,
                                            cap_bytes), "bucketed_allreduce")
     return [[outs[r * nt + t][: int(numels[t])] for t in range(nt)] for r in range(n)]
+
+
+def _bucketed_by_packing(tensors, dtype, op, cap_bytes, allreduce):
+    n = len(tensors)
+    nt = len(tensors[0]) if n else 0
+    numels = np.array([np.asarray(t).size for t in tensors[0]], dtype=np.int64)
+    es = 2 if dtype in (BF16, F16) else 4
+    bucket_of, offset_of, bcount = bucket_plan(numels, es, n, cap_bytes)
+    start = np.concatenate([[0], np.cumsum(bcount)]).astype(np.int64)
+    flat = [np.zeros(int(start[-1]), dtype=NP_DTYPE[dtype]) for _ in range(n)]
+    for r in range(n):
+        for t in range(nt):
+            at = int(start[bucket_of[t]] + offset_of[t])
+            flat[r][at:at + int(numels[t])] = np.asarray(tensors[r][t], dtype=NP_DTYPE[dtype])
+    for b in range(len(bcount)):
+        lo, hi = int(start[b]), int(start[b + 1])
+        red = allreduce([f[lo:hi] for f in flat], dtype, op)
+        for r in range(n):
+            flat[r][lo:hi] = red[r]
+    outs = []
+    for r in range(n):
+        row = []
+        for t in range(nt):
+            at = int(start[bucket_of[t]] + offset_of[t])
+            row.append(flat[r][at:at + int(numels[t])].copy())
+        outs.append(row)
+    return outs
 
 
 def num_threads():

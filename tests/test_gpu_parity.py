@@ -598,15 +598,20 @@ def test_hip_graph_capture_replays_match_eager(algo):
         assert_bitwise([from_dev(o, dt) for o in outs], eager, f"graph replay {rep} algo={algo}")
 
 
+ORACLE_BUCKET_ALGO = {ar.AR_ALGO_RING: "ring", ar.AR_ALGO_FUSED: "fused", ar.AR_ALGO_RHD: "rhd",
+                      ar.AR_ALGO_TREE: "tree"}
+
+
 @pytest.mark.parametrize("n", [1, 2, 3, 4, 8, 16])
 @pytest.mark.parametrize("dt", [ar.AR_F32, ar.AR_BF16, ar.AR_I32])
-def test_fused_tensor_path_equals_pack_reduce_unpack(n, dt):
-    """ar_allreduce_tensors reads and writes the tensors directly and must give the bits of pack + per-bucket ring
-    + unpack: small caps make buckets whose chunks are shorter than a tile, odd sizes leave element tails, and
-    one tensor starting one element into its allocation takes the element path."""
+def test_bucketed_paths_match_the_oracle_in_every_order(n, dt):
+    """Both bucketed paths, pack + per-bucket all-reduce + unpack (BucketedAllReduce) and the fused path that
+    reads and writes the tensors directly (ar_allreduce_tensors), against the oracle's bucketed all-reduce in the
+    same order (its plan, zero-padded packing on the host, the literal ring / rank-order / halving / binomial
+    oracle per bucket, unpacking), every op. Small caps make buckets whose chunks are shorter than a tile, odd
+    sizes leave element tails, and one tensor starting one element into its allocation takes the element path."""
     rng = np.random.default_rng(40 + n + 10 * dt)
     sizes = [int(s) for s in rng.integers(1, 3000, 23)] + [1, 2, 9, 70001, 4096, 40000]
-    tdt = {ar.AR_F32: torch.float32, ar.AR_BF16: torch.bfloat16, ar.AR_I32: torch.int32}[dt]
     algos = [ar.AR_ALGO_RING, ar.AR_ALGO_FUSED, ar.AR_ALGO_TREE] + ([ar.AR_ALGO_RHD] if n & (n - 1) == 0 else [])
     for cap in (4096, 200 << 10):
         host = [[inputs.rank_inputs(KIND[dt], 1, s, cfg=41, extra=(r, t, n))[0] for t, s in enumerate(sizes)]
@@ -621,21 +626,22 @@ def test_fused_tensor_path_equals_pack_reduce_unpack(n, dt):
             ins.append(row)
         for algo in algos:
             for op in OPS:
-                ref = [[torch.empty_like(x) for x in ins[r]] for r in range(n)]
-                got = [[torch.empty_like(x) for x in ins[r]] for r in range(n)]
-                bar_ref = ar.BucketedAllReduce(ins, ref, op=op, algo=algo, cap_bytes=cap)
-                bar_ref()
-                bar = ar.BucketedAllReduce(ins, got, op=op, algo=algo, cap_bytes=cap)
-                bar.fused()
+                want = oracle.bucketed_allreduce(host, ORACLE_DT[dt], ORACLE_OP[op], cap_bytes=cap,
+                                                 algo=ORACLE_BUCKET_ALGO[algo])
+                packed = [[torch.empty_like(x) for x in ins[r]] for r in range(n)]
+                fused = [[torch.empty_like(x) for x in ins[r]] for r in range(n)]
+                ar.BucketedAllReduce(ins, packed, op=op, algo=algo, cap_bytes=cap)()
+                ar.BucketedAllReduce(ins, fused, op=op, algo=algo, cap_bytes=cap).fused()
                 torch.cuda.synchronize()
-                for r in range(n):
-                    for t in range(len(sizes)):
-                        g = from_dev(got[r][t], dt)
-                        w = from_dev(ref[r][t], dt)
-                        if not np.array_equal(g, w):
-                            bad = np.nonzero(g != w)[0][:5]
-                            raise AssertionError(f"n={n} dt={dt} cap={cap} algo={algo} op={op} rank {r} tensor {t} "
-                                                 f"(numel {sizes[t]}): first differences at {bad}")
+                for path, got in (("pack+reduce+unpack", packed), ("fused tensors", fused)):
+                    for r in range(n):
+                        for t in range(len(sizes)):
+                            g = from_dev(got[r][t], dt)
+                            w = np.asarray(want[r][t]).view(NP_BITS[dt])
+                            if not np.array_equal(g, w):
+                                bad = np.nonzero(g != w)[0][:5]
+                                raise AssertionError(f"{path}: n={n} dt={dt} cap={cap} algo={algo} op={op} rank {r} "
+                                                     f"tensor {t} (numel {sizes[t]}): first differences at {bad}")
 
 
 def _chunks(x_np, lo):

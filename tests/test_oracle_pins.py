@@ -484,6 +484,137 @@ def test_fp8_ring_two_ranks_closed_form():
         np.testing.assert_array_equal(o, want_b)
 
 
+def _q_block_def(v):
+    """Block quantization written out from its definition, every special case included: amax over the block's
+    non-NaN magnitudes; inv = 448/amax and scale = amax/448, each one fp32 division; amax 0, or an inv that
+    overflows to infinity, gives inv = scale = 1; code = E4M3(v * inv) with the product in fp32, a NaN product
+    coded 0x7F. The E4M3 conversion is torch's (valid here: |v * inv| stays below 464 or is NaN)."""
+    v = np.asarray(v, np.float32)
+    mag = np.abs(v[~np.isnan(v)])
+    amax = np.float32(mag.max()) if mag.size else np.float32(0)
+    with np.errstate(over="ignore", divide="ignore", invalid="ignore"):
+        inv, scale = (np.float32(448) / amax, amax / np.float32(448)) if amax > 0 else (np.float32(1), np.float32(1))
+        if np.isinf(inv):
+            inv, scale = np.float32(1), np.float32(1)
+        prod = (v * inv).astype(np.float32)
+    codes = torch.from_numpy(np.where(np.isnan(prod), np.float32(0), prod)).to(torch.float8_e4m3fn)
+    codes = codes.view(torch.uint8).numpy().copy()
+    codes[np.isnan(prod)] = 0x7F
+    return codes, np.float32(scale)
+
+
+def _qdq_def(v):
+    """deq(Q(v)) over blocks of 128 tiling v from its start: value(code) * scale, one fp32 multiply."""
+    v = np.asarray(v, np.float32)
+    out = np.empty_like(v)
+    for s in range(0, v.size, 128):
+        codes, scale = _q_block_def(v[s:s + 128])
+        dec = torch.from_numpy(codes.copy()).view(torch.float8_e4m3fn).float().numpy()
+        with np.errstate(invalid="ignore", over="ignore"):
+            out[s:s + 128] = (dec * scale).astype(np.float32)
+    return out
+
+
+def test_fp8_block_below_the_smallest_invertible_amax_takes_scale_one():
+    """amax < 448 / FLT_MAX makes 448/amax overflow, so inv = scale = 1 and the codes are E4M3 of the raw values
+    (all of them round to a signed zero at this size); fp32 subnormal blocks take the same branch."""
+    flt_max = np.finfo(np.float32).max
+    limit = np.float32(448) / flt_max  # 1.3166e-36
+    rng = np.random.default_rng(90)
+    tiny = (rng.uniform(-1, 1, 128) * np.float64(limit) * 0.9).astype(np.float32)
+    tiny[5] = np.float32(-0.0)
+    sub = (rng.uniform(-1, 1, 128) * 1e-40).astype(np.float32)  # fp32 subnormals
+    for blk in (tiny, sub):
+        assert np.abs(blk).max() < limit
+        codes, scales = oracle.fp8_quant(blk, oracle.F32)
+        assert scales[0] == np.float32(1.0)
+        want = np.where(np.signbit(blk), 0x80, 0x00).astype(np.uint8)  # E4M3 of |v| < 2^-10 is a signed zero
+        np.testing.assert_array_equal(codes, want)
+        np.testing.assert_array_equal(codes, _q_block_def(blk)[0])
+    # just above the limit the division is finite and the scale is a tiny (subnormal) fp32
+    blk = tiny.copy()
+    blk[0] = np.float32(limit) * np.float32(1.5)
+    codes, scales = oracle.fp8_quant(blk, oracle.F32)
+    inv = np.float32(448) / blk[0]
+    assert np.isfinite(inv) and scales[0] == blk[0] / np.float32(448) and 0 < scales[0] < np.finfo(np.float32).tiny
+    assert codes[0] == 0x7E  # v * inv = 448 (or within an ulp): the largest finite code
+    np.testing.assert_array_equal(codes, _q_block_def(blk)[0])
+
+
+def test_fp8_block_with_infinities_and_nan():
+    """A block holding +-inf: amax = inf, so inv = 448/inf = 0 and scale = inf/448 = inf; finite values code to
+    a signed zero (v * 0), the infinities to NaN (inf * 0 = NaN -> 0x7F). NaN values never count towards amax
+    and code to 0x7F."""
+    v = np.linspace(-3, 3, 128).astype(np.float32)
+    v[7], v[100] = np.inf, -np.inf
+    codes, scales = oracle.fp8_quant(v, oracle.F32)
+    assert np.isinf(scales[0]) and scales[0] > 0
+    want = np.where(np.signbit(v), 0x80, 0x00).astype(np.uint8)
+    want[[7, 100]] = 0x7F
+    np.testing.assert_array_equal(codes, want)
+    # NaN: ignored by amax (the block's scale is that of its finite values), coded 0x7F
+    w = np.linspace(-2, 2, 128).astype(np.float32)
+    w[3] = w[127] = np.nan  # one NaN after the block's largest magnitude, where a running max would keep it
+    codes, scales = oracle.fp8_quant(w, oracle.F32)
+    assert scales[0] == np.float32(2) / np.float32(448)
+    assert codes[3] == 0x7F and codes[127] == 0x7F
+    assert codes[0] == 0xFE  # -2 * (448/2) = -448
+    np.testing.assert_array_equal(codes, _q_block_def(w)[0])
+
+
+def _fp8_ring_closed_form(fs, op, lo):
+    """The compressed ring's value for chunk c, written from the readings: the partial starts as rank c's own
+    fp32 value; every hop carries deq(Q(partial)) to the next rank, which adds its own full-precision value; the
+    owner divides by N for avg (one fp32 division) and quantizes the finished chunk once; every rank decodes
+    those codes. Blocks tile the chunk from its start."""
+    n = len(fs)
+    out = np.empty(fs[0].size, np.float32)
+    for c in range(n):
+        sl = slice(int(lo[c]), int(lo[c + 1]))
+        p = fs[c][sl].astype(np.float32)
+        for k in range(1, n):
+            p = (_qdq_def(p) + fs[(c + k) % n][sl]).astype(np.float32)
+        if op == oracle.AVG:
+            p = (p / np.float32(n)).astype(np.float32)
+        out[sl] = _qdq_def(p)
+    return out
+
+
+@pytest.mark.parametrize("n", [1, 2, 3, 5, 8])
+@pytest.mark.parametrize("dtype", [oracle.BF16, oracle.F32])
+@pytest.mark.parametrize("op", [oracle.SUM, oracle.AVG])
+def test_fp8_ring_closed_form(n, dtype, op):
+    """Every element of every rank equals the closed form above, for bf16 and fp32 inputs, sum and avg, with
+    chunks whose last block is partial. N = 2 avg: chunk 0 = deq(Q((deq(Q(x0)) + x1) / 2)); N = 3 avg with fp32 outputs
+    tells the owner's divide-then-quantize order apart from decode-then-divide."""
+    count = 128 * n * 3 + 77
+    xs = inputs.rank_inputs("outlier_bf16", n, count, cfg=5, extra=(79, n))
+    if dtype == oracle.F32:  # fp32 inputs with more mantissa than bf16 carries
+        xs = [inputs.normal_f32((5, r, 80, n), count, 1e-3) for r in range(n)]
+        xs[0][::211] *= np.float32(100)
+        fs = xs
+    else:
+        fs = [torch.from_numpy(x.view(np.int16).copy()).view(torch.bfloat16).float().numpy() for x in xs]
+    got = oracle.fp8_ring_allreduce(xs, dtype, op)
+    want = _fp8_ring_closed_form(fs, op, oracle.chunk_bounds(count, n))
+    want = inputs.f32_to_bf16_bits_lib(want) if dtype == oracle.BF16 else want
+    for o in got:
+        np.testing.assert_array_equal(np.asarray(o).view(np.uint8), np.asarray(want).view(np.uint8))
+    if n == 3 and op == oracle.AVG and dtype == oracle.F32:
+        # The avg order: the owner divides before it quantizes. Block quantization is nearly scale-invariant, so
+        # dividing after decoding instead moves only the last fp32 bits: visible in fp32 outputs at N = 3 (for
+        # N = 2, 4, 8 a power-of-two factor passes exactly through the block scale, and bf16 rounding hides the
+        # difference).
+        lo = oracle.chunk_bounds(count, n)
+        sl = slice(0, int(lo[1]))
+        p = fs[0][sl].astype(np.float32)
+        for k in (1, 2):
+            p = (_qdq_def(p) + fs[k][sl]).astype(np.float32)
+        late = (_qdq_def(p) / np.float32(3)).astype(np.float32)
+        late = inputs.f32_to_bf16_bits_lib(late) if dtype == oracle.BF16 else late
+        assert not np.array_equal(np.asarray(got[0][sl]).view(np.uint8), np.asarray(late).view(np.uint8))
+
+
 def test_fp8_ring_accuracy_vs_exact():
     """Reported bound: each of the N-1 hops and the final quantization adds <= 1/16 relative of the block
     scale's grid; compare the eight-rank result with the exact fp64 sum."""
@@ -510,6 +641,11 @@ def test_bucket_plan_hand_example():
     np.testing.assert_array_equal(b, [0, 0, 1, 2, 2, 2, 3])
     np.testing.assert_array_equal(off, [0, 4, 0, 0, 4, 4, 0])
     np.testing.assert_array_equal(cnt, [16, 40, 8, 16])
+    # a bucket filled to exactly the cap stays open (only going past the cap closes it)
+    b, off, cnt = oracle.bucket_plan([8, 8, 1, 16], 4, 2, 64)
+    np.testing.assert_array_equal(b, [0, 0, 1, 2])
+    np.testing.assert_array_equal(off, [0, 8, 0, 0])
+    np.testing.assert_array_equal(cnt, [16, 8, 16])
 
 
 def test_bucket_plan_properties_full_size():
@@ -552,6 +688,47 @@ def test_bucketed_allreduce_equals_per_tensor_exact():
         red = oracle.ring_allreduce(flat, oracle.F32, oracle.AVG)
         for t in np.where(b == k)[0]:
             np.testing.assert_array_equal(outs[0][t], red[0][off[t]:off[t] + sizes[t]])
+
+
+@pytest.mark.parametrize("dtype", [oracle.F32, oracle.BF16, oracle.I32])
+def test_bucketed_allreduce_packing_here_equals_the_c_routine(dtype):
+    """Packing in the wrapper (C plan, numpy copies, the ring oracle per bucket) gives the bits of the C routine
+    that plans, packs, reduces and unpacks by itself: the two packings cross-check each other."""
+    n = 3
+    sizes = [5, 1, 300, 17, 4096, 2, 999, 0, 33]
+    kind = {oracle.F32: "uniform_f32", oracle.BF16: "uniform_bf16", oracle.I32: "int32"}[dtype]
+    ts = [[inputs.rank_inputs(kind, 1, s, cfg=42, extra=(r, t))[0] for t, s in enumerate(sizes)] for r in range(n)]
+    for op in (oracle.SUM, oracle.AVG, oracle.MAX):
+        a = oracle.bucketed_allreduce(ts, dtype, op, cap_bytes=1024)
+        b = oracle.bucketed_allreduce(ts, dtype, op, cap_bytes=1024, algo="ring_py")
+        for r in range(n):
+            for t in range(len(sizes)):
+                np.testing.assert_array_equal(a[r][t], b[r][t])
+
+
+@pytest.mark.parametrize("algo", ["fused", "rhd", "tree"])
+def test_bucketed_allreduce_other_orders_exact_on_integer_values(algo):
+    """Integer-valued fp32 tensors: every association is exact, so each bucket order gives sum/N per tensor; and
+    each bucket is that order's oracle on the packed bucket (rank order, halving tree, binomial tree)."""
+    n = 4
+    sizes = [5, 1, 300, 17, 4096, 2, 999]
+    rng = np.random.default_rng(4)
+    ts = [[rng.integers(-50, 50, s).astype(np.float32) for s in sizes] for _ in range(n)]
+    outs = oracle.bucketed_allreduce(ts, oracle.F32, oracle.AVG, cap_bytes=2048, algo=algo)
+    for t in range(len(sizes)):
+        exact = np.sum(np.array([ts[r][t] for r in range(n)], np.float64), axis=0) / n
+        for r in range(n):
+            np.testing.assert_array_equal(outs[r][t], exact.astype(np.float32))
+    # scaled inputs make the association visible: bucket results follow each order's own fold
+    xs = [[(np.asarray(ts[r][t]) * np.float32(2.0 ** (9 * r)) + np.float32(0.25)).astype(np.float32)
+           for t in range(len(sizes))] for r in range(n)]
+    got = oracle.bucketed_allreduce(xs, oracle.F32, oracle.SUM, cap_bytes=2048, algo=algo)
+    fold = {"fused": lambda v: np.float32(np.float32(np.float32(v[0] + v[1]) + v[2]) + v[3]),
+            "rhd": lambda v: np.float32(np.float32(v[0] + v[2]) + np.float32(v[1] + v[3])),
+            "tree": lambda v: np.float32(np.float32(v[0] + v[1]) + np.float32(v[2] + v[3]))}[algo]
+    for t in range(len(sizes)):
+        for e in range(sizes[t]):
+            assert got[0][t][e] == fold([xs[r][t][e] for r in range(n)])
 
 
 # ---------------------------------------------------------------- binomial tree
