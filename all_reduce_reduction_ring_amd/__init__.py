@@ -7,7 +7,8 @@ call raises.
 
 Entry points (same names as ``include/ar.h``): ar_allreduce, ar_allreduce_ws, ar_allreduce_workspace_size,
 ar_allreduce_buckets, ar_allreduce_tensors, ar_reduce_scatter, ar_all_gather, ar_bucket_plan, ar_bucket_pack,
-ar_bucket_unpack, ar_fp8_quant, ar_fp8_dequant, ar_auto_algo, ar_status_string, ar_last_call, ar_version. Helpers: make_copy_descs, BucketedAllReduce.
+ar_bucket_unpack, ar_fp8_quant, ar_fp8_dequant, ar_auto_algo, ar_chunk_bounds, ar_status_string, ar_last_call,
+ar_version. Helpers: chunk_bounds, make_copy_descs, BucketedAllReduce.
 """
 from __future__ import annotations
 
@@ -24,7 +25,8 @@ __all__ = [
     "AR_ALGO_RING_FP8", "AR_ALGO_TREE", "AR_ALGO_TREE_STEPWISE", "AR_ALGO_AUTO", "AR_AUTO_STEP_NS",
     "AR_AUTO_LINK_GBPS", "AR_MAX_RANKS", "AR_FP8_BLOCK", "ArError", "lib", "lib_path", "ar_auto_algo",
     "ar_allreduce", "ar_allreduce_ws", "ar_allreduce_workspace_size", "ar_allreduce_buckets",
-    "ar_allreduce_tensors", "ar_reduce_scatter", "ar_all_gather", "chunk_bounds", "ar_bucket_plan",
+    "ar_allreduce_tensors", "ar_reduce_scatter", "ar_all_gather", "ar_chunk_bounds", "chunk_bounds",
+    "ar_bucket_plan",
     "ar_bucket_pack",
     "ar_bucket_unpack", "ar_fp8_quant", "ar_fp8_dequant", "ar_status_string", "ar_last_call", "ar_version",
     "make_copy_descs", "BucketedAllReduce", "dtype_code",
@@ -82,13 +84,14 @@ def lib():
         L.ar_fp8_quant.argtypes = [vp, i32, sz, vp, vp, vp]
         L.ar_fp8_dequant.argtypes = [vp, vp, sz, vp, i32, vp]
         L.ar_auto_algo.argtypes = [i32, sz, i32]
+        L.ar_chunk_bounds.argtypes = [i32, sz, vp]
         L.ar_status_string.argtypes = [i32]
         L.ar_status_string.restype = ctypes.c_char_p
         L.ar_last_call.argtypes = [ctypes.POINTER(_CallRecord)]
         for name in ("ar_allreduce", "ar_allreduce_ws", "ar_allreduce_workspace_size", "ar_allreduce_buckets",
                      "ar_allreduce_tensors", "ar_reduce_scatter", "ar_all_gather", "ar_bucket_plan", "ar_bucket_pack",
                      "ar_bucket_unpack", "ar_fp8_quant", "ar_fp8_dequant", "ar_last_call", "ar_version",
-                     "ar_auto_algo"):
+                     "ar_auto_algo", "ar_chunk_bounds"):
             getattr(L, name).restype = i32
         _lib = L
     return _lib
@@ -228,10 +231,16 @@ def ar_allreduce_tensors(descs, in_ptrs, out_ptrs, ntensors, nranks, dtype, op=A
                                           _stream(stream, dev)), "ar_allreduce_tensors")
 
 
+def ar_chunk_bounds(nranks, count):
+    """The library's balanced split (host only): chunk c = [lo[c], lo[c+1]), a list of nranks + 1 ints."""
+    lo = (ctypes.c_int64 * (nranks + 1))() if 1 <= nranks <= AR_MAX_RANKS else None
+    _check(lib().ar_chunk_bounds(nranks, count, lo), "ar_chunk_bounds")
+    return list(lo)
+
+
 def chunk_bounds(count, nranks):
-    """The balanced split: chunk c = [lo[c], lo[c+1]) with count//N + 1 elements for c < count % N."""
-    q, r = divmod(count, nranks)
-    return [c * q + min(c, r) for c in range(nranks + 1)]
+    """ar_chunk_bounds with the arguments in (count, nranks) order."""
+    return ar_chunk_bounds(nranks, count)
 
 
 def _ptr(t):

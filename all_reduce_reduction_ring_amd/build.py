@@ -18,6 +18,10 @@ ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 BUILD = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "libar.so")
+# measurement kernels for the benchmark's roofline context (the fold's read and write halves on their own); a
+# library of their own, so that nothing in libar exists only to be measured
+CEILING_SRC = "ar_ceiling.hip"
+CEILING_LIB = os.path.join(HERE, "libar_ceiling.so")
 ARCH = "gfx950"
 
 SOURCES = ["ar_api.hip", "ar_collapsed.hip", "ar_stepwise.hip", "ar_bucket.hip", "ar_fp8.hip", "ar_tensors.hip", "ar_rsag.hip"]
@@ -56,21 +60,28 @@ def _compile(unit) -> str:
     return obj
 
 
-def build(jobs: int | None = None) -> str:
-    """Compile every source and link libar.so; returns the library path."""
-    os.makedirs(BUILD, exist_ok=True)
-    jobs = jobs or min(len(UNITS), max(1, (os.cpu_count() or 4)))
-    # the slowest units first, so they are not left running alone at the end
-    order = sorted(UNITS, key=lambda u: u[0] not in ("ar_collapsed.hip", "ar_tensors.hip"))
-    with concurrent.futures.ThreadPoolExecutor(max_workers=jobs) as ex:
-        objs = list(ex.map(_compile, order))
-    tmp = LIB + ".tmp"
+def _link(objs, out):
+    tmp = out + ".tmp"
     # -z defs: an unresolved symbol (say a missing per-type part) fails the link instead of the first call
     cmd = [hipcc(), "-shared", f"--offload-arch={ARCH}", "-fPIC", "-Wl,-z,defs", "-o", tmp, *objs]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"link failed:\n{r.stdout}\n{r.stderr}")
-    os.replace(tmp, LIB)
+    os.replace(tmp, out)
+
+
+def build(jobs: int | None = None) -> str:
+    """Compile every source and link libar.so (and libar_ceiling.so); returns libar's path."""
+    os.makedirs(BUILD, exist_ok=True)
+    units = UNITS + [(CEILING_SRC, [])]
+    jobs = jobs or min(len(units), max(1, (os.cpu_count() or 4)))
+    # the slowest units first, so they are not left running alone at the end
+    order = sorted(units, key=lambda u: u[0] not in ("ar_collapsed.hip", "ar_tensors.hip"))
+    with concurrent.futures.ThreadPoolExecutor(max_workers=jobs) as ex:
+        objs = dict(zip([u[0] + "".join(u[1]) for u in order], ex.map(_compile, order)))
+    ceiling = objs.pop(CEILING_SRC)
+    _link(list(objs.values()), LIB)
+    _link([ceiling], CEILING_LIB)
     return LIB
 
 

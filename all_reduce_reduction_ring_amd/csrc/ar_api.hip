@@ -277,6 +277,13 @@ int ar_all_gather(const void* const* in_bufs, void* const* out_bufs, int nranks,
 
 int ar_version(void) { return AR_VERSION; }
 
+int ar_chunk_bounds(int nranks, size_t count, int64_t* lo) {
+  if (!lo || nranks < 1 || nranks > AR_MAX_RANKS || count > static_cast<size_t>(INT64_MAX)) return AR_ERR_INVALID;
+  const int64_t c64 = static_cast<int64_t>(count), q = c64 / nranks, r = c64 % nranks;
+  for (int c = 0; c <= nranks; ++c) lo[c] = c * q + (c < r ? c : r);
+  return AR_OK;
+}
+
 const char* ar_status_string(int status) {
   switch (status) {
     case AR_OK: return "AR_OK: success";

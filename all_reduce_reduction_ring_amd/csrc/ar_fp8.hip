@@ -210,7 +210,8 @@ struct Fp8RingArgs {
   int64_t tasks;       // total wave tasks
   int n;
   int vec;    // 1: every rank buffer starts on a 16-byte boundary
-  int strip;  // wave tasks per strip: kStrip when some bf16 chunk start is off the 16-byte grid, else 1
+  int strip;  // wave tasks per strip: kStrip when some chunk start is off the 16-byte grid (bf16 q % 8 or fp32
+              // q % 4 non-zero, or r != 0), else 1
 };
 
 // One hop: the sender's partial p goes out as E4M3 codes + block scale and comes back as d * scale; the

@@ -152,6 +152,46 @@ def write_ceiling(torch, ins, reps=10):
     return nbytes / (np.median(ms) * 1e-3) / GB
 
 
+def fold_halves(torch, ins, outs, reps=10):
+    """The headline fold's two halves on their own, with its launch shape and access order (libar_ceiling.so, the
+    benchmark's measurement kernels): reading the N rank buffers with nothing written, and writing N buffers with
+    nothing read, each N*S bytes; median of 10 after warm-up calls. Returns (read GB/s, write GB/s), or None when
+    the measurement library is not built."""
+    path = os.path.join(ROOT, "all_reduce_reduction_ring_amd", "libar_ceiling.so")
+    if not os.path.exists(path):
+        return None
+    L = ctypes.CDLL(path)
+    vp = ctypes.c_void_p
+    L.arc_read.argtypes = [vp, ctypes.c_int, ctypes.c_size_t, ctypes.c_uint32, vp, ctypes.c_int, vp]
+    L.arc_write.argtypes = [vp, ctypes.c_int, ctypes.c_size_t, ctypes.c_int, vp]
+    n = len(ins)
+    nbytes = ins[0].numel() * ins[0].element_size()
+    rin = (ctypes.c_void_p * n)(*[t.data_ptr() for t in ins])
+    rout = (ctypes.c_void_p * n)(*[t.data_ptr() for t in outs])
+    sink = torch.zeros(1, dtype=torch.int32, device=ins[0].device)
+    stream = lambda: ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+
+    def check(rc):
+        if rc != 0:
+            raise RuntimeError(f"libar_ceiling call failed ({rc})")
+
+    read = lambda: check(L.arc_read(rin, n, nbytes, 0x9E3779B9, sink.data_ptr(), 1, stream()))
+    write = lambda: check(L.arc_write(rout, n, nbytes, 1, stream()))
+    rates = []
+    for fn in (read, write):
+        for _ in range(3):
+            fn()
+        ms = Timer(torch).run(fn, reps)
+        rates.append(n * nbytes / (np.median(ms) * 1e-3) / GB)
+    return rates[0], rates[1]
+
+
+def mix_bound(read_gbps, write_gbps, read_bytes, write_bytes):
+    """The rate a kernel moving read_bytes and write_bytes could reach if its reads and writes cost what they cost
+    alone (the plain read and plain write ceilings above) and mixing them cost nothing: bytes / (R/r + W/w)."""
+    return (read_bytes + write_bytes) / (read_bytes / read_gbps + write_bytes / write_gbps)
+
+
 def cpu_baseline(host, budget_s=10.0, max_reps=5):
     """The oracle's literal ring on the headline inputs, repeated until ~budget_s of CPU time."""
     import oracle as _o
@@ -518,57 +558,78 @@ def alpha_beta_fit(lines, n):
             "tree_below_bytes_at_153GBps_link": float(n * max(0, n - 1 - levels) * alpha * link)}
 
 
+SWEEP_ALGOS = ("ring", "rhd", "fused", "tree", "ring_stepwise", "rhd_stepwise", "tree_stepwise")
+
+
+def sweep_points(torch, ar, dev, S, names, reps=20, graph_max=16 << 20):
+    """One message size of the sweep: N = 8 fp32 ranks of S bytes each, uniform [-1, 1), sum. Below 1 GiB of total
+    traffic, ceil(1 GiB / (2 N S)) buffer sets (at most 64) are rotated so that no call finds its data in the
+    256 MB last-level cache. Returns one record per algorithm (median of `reps` event-timed calls; sizes up to
+    graph_max also get the per-call device time of 100 calls in one HIP graph)."""
+    codes = {"ring": ar.AR_ALGO_RING, "rhd": ar.AR_ALGO_RHD, "fused": ar.AR_ALGO_FUSED, "tree": ar.AR_ALGO_TREE,
+             "ring_stepwise": ar.AR_ALGO_RING_STEPWISE, "rhd_stepwise": ar.AR_ALGO_RHD_STEPWISE,
+             "tree_stepwise": ar.AR_ALGO_TREE_STEPWISE}
+    n = N_RANKS
+    count = S // 4
+    sets = int(min(64, max(1, -(-(1 << 30) // (2 * n * S)))))
+    g = torch.Generator(device=dev)
+    g.manual_seed(4000 + int(np.log2(S)))
+    bufs = [([torch.rand(count, generator=g, device=dev).mul_(2).sub_(1) for _ in range(n)],
+             [torch.empty(count, device=dev) for _ in range(n)]) for _ in range(sets)]
+    recs = []
+    for name in names:
+        algo = codes[name]
+        k = [0]
+
+        def call():
+            i, o = bufs[k[0] % sets]
+            k[0] += 1
+            ar.ar_allreduce(i, o, ar.AR_SUM, algo)
+
+        for _ in range(3):
+            call()
+        ms = Timer(torch).run(call, reps)
+        t = float(np.median(ms)) * 1e-3
+        graph_us = graph_time_us(torch, call, 100) if S <= graph_max else None
+        alg = {"ring_stepwise": stepwise_ring_bytes, "rhd_stepwise": stepwise_rhd_bytes,
+               "tree_stepwise": stepwise_tree_bytes}.get(name, lambda n_, c_, e_, a_: ring_bytes(n_, c_, e_))(
+            n, count, 4, 4)
+        recs.append({"bytes_per_rank": S, "algo": name, "us_p50": t * 1e6, "us": stats_us(ms),
+                     "algbw_GBps": S / t / GB, "busbw_GBps": S / t / GB * bus_factor(n),
+                     "hbm_GBps": alg / t / GB, "frac_of_peak": alg / t / GB / PEAK_HBM_GBPS, "buffer_sets": sets,
+                     "graph_us_per_call": graph_us})
+    del bufs
+    torch.cuda.empty_cache()
+    return recs
+
+
 def sweep(torch, ar, dev, out_path, reps=20, max_log2=30):
     """Message-size sweep: N = 8 fp32 ranks, sum, 8 B ... 1 GiB per rank, ring vs halving-doubling vs rank order
-    vs the round-per-launch schedules. Below 1 GiB of total traffic, ceil(1 GiB / (2 N S)) buffer sets (at most
-    64) are rotated so that no call finds its data in the 256 MB last-level cache. One JSON line per point."""
-    algos = [("ring", ar.AR_ALGO_RING), ("rhd", ar.AR_ALGO_RHD), ("fused", ar.AR_ALGO_FUSED),
-             ("tree", ar.AR_ALGO_TREE), ("ring_stepwise", ar.AR_ALGO_RING_STEPWISE),
-             ("rhd_stepwise", ar.AR_ALGO_RHD_STEPWISE), ("tree_stepwise", ar.AR_ALGO_TREE_STEPWISE)]
-    n = N_RANKS
-    g = torch.Generator(device=dev)
+    vs the binomial tree vs the round-per-launch schedules. One JSON line per point, then the alpha-beta fit."""
     lines = []
     with open(out_path, "w") as f:
         for lg in range(3, max_log2 + 1):
-            S = 1 << lg
-            count = S // 4
-            sets = int(min(64, max(1, -(-(1 << 30) // (2 * n * S)))))
-            g.manual_seed(4000 + lg)
-            bufs = [([torch.rand(count, generator=g, device=dev).mul_(2).sub_(1) for _ in range(n)],
-                     [torch.empty(count, device=dev) for _ in range(n)]) for _ in range(sets)]
-            for name, algo in algos:
-                k = [0]
-
-                def call():
-                    i, o = bufs[k[0] % sets]
-                    k[0] += 1
-                    ar.ar_allreduce(i, o, ar.AR_SUM, algo)
-
-                for _ in range(3):
-                    call()
-                ms = Timer(torch).run(call, reps)
-                t = float(np.median(ms)) * 1e-3
-                graph_us = None
-                if S <= (16 << 20):
-                    # device time per call: 100 calls captured in one HIP graph, replayed
-                    graph_us = graph_time_us(torch, call, 100)
-                alg = {"ring_stepwise": stepwise_ring_bytes, "rhd_stepwise": stepwise_rhd_bytes,
-                       "tree_stepwise": stepwise_tree_bytes}.get(name, lambda n_, c_, e_, a_: ring_bytes(n_, c_, e_))(
-                    n, count, 4, 4)
-                rec = {"bytes_per_rank": S, "algo": name, "us_p50": t * 1e6, "us": stats_us(ms),
-                       "algbw_GBps": S / t / GB, "busbw_GBps": S / t / GB * bus_factor(n),
-                       "hbm_GBps": alg / t / GB, "frac_of_peak": alg / t / GB / PEAK_HBM_GBPS, "buffer_sets": sets,
-                       "graph_us_per_call": graph_us}
+            for rec in sweep_points(torch, ar, dev, 1 << lg, SWEEP_ALGOS, reps):
                 f.write(json.dumps(rec) + "\n")
                 f.flush()
                 lines.append(rec)
-            log(f"sweep {S} B done")
-            del bufs
-            torch.cuda.empty_cache()
-        fit = alpha_beta_fit(lines, n)
+            log(f"sweep {1 << lg} B done")
+        fit = alpha_beta_fit(lines, N_RANKS)
         if fit:
             f.write(json.dumps(fit) + "\n")
     return lines
+
+
+def compact_sweep(torch, ar, dev, reps=20):
+    """The size curve of the metric in the default run: N = 8 fp32 sum, 64 KiB ... 1 GiB per rank, the four
+    one-pass orders (the round-per-launch schedules and the sizes in between are in --sweep)."""
+    out = []
+    for S in (64 << 10, 1 << 20, 16 << 20, 64 << 20, 256 << 20, 1 << 30):
+        for rec in sweep_points(torch, ar, dev, S, ("ring", "fused", "rhd", "tree"), reps, graph_max=1 << 20):
+            out.append({k: rec[k] for k in ("bytes_per_rank", "algo", "us_p50", "algbw_GBps", "busbw_GBps",
+                                            "hbm_GBps", "frac_of_peak", "buffer_sets", "graph_us_per_call")})
+        log(f"compact sweep {S} B done")
+    return out
 
 
 def main():
@@ -640,6 +701,9 @@ def main():
     achieved = alg_bytes / t_kernel / GB
     sources = ["ar_collapsed.hip", "ar_device.h"]
     traffic = _load_traffic("ring_front_kernel<bf16,avg,8>", sources)
+    traffic_source = (f"profiles/hbm_counters.json: rocprofv3 FETCH_SIZE and WRITE_SIZE of this kernel, taken in an "
+                      f"earlier profiled run of the same sources (sha256 {_sources_digest(sources)[:16]}), not "
+                      f"measured in this run") if traffic else None
     result = {
         "metric": METRIC,
         "value": algbw * bus_factor(N_RANKS),
@@ -651,27 +715,42 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "f32",
+        "dtype": "bf16",
         "data": "synthetic",
         "config": {"workload": "ring all-reduce, N=8 simulated ranks (separate HBM buffers), 134,217,728 bf16 "
                                "per rank (256 MiB), fp32 sum in ring order, /8, bf16 out to all 8",
-                   "nranks": N_RANKS, "count_per_rank": COUNT, "storage": "bf16", "op": "avg", "algo": "ring"},
+                   "nranks": N_RANKS, "count_per_rank": COUNT, "storage": "bf16", "accumulate": "fp32",
+                   "op": "avg", "algo": "ring"},
         "algbw_GBps": algbw,
         "busbw_GBps": algbw * bus_factor(N_RANKS),
         "hbm_GBps": achieved,
         "kernel_us": stats_us(ms),
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": PEAK_HBM_GBPS, "unit": "GB/s",
                      "frac": achieved / PEAK_HBM_GBPS,
-                     "traffic": traffic},
+                     "traffic": traffic, "traffic_source": traffic_source},
         # the counted HBM bytes of one launch over the same measured time (null while the counters are stale)
         "hbm_counter_GBps": traffic / (float(np.mean(ms)) * 1e-3) / GB if traffic else None,
     }
     if not args.headline_only:
         result["copy_ceiling_GBps"] = copy_ceiling(torch, ins, outs)
         result["write_ceiling_GBps"] = write_ceiling(torch, ins)
+        halves = fold_halves(torch, ins, outs)
+        if halves:
+            rd, wr = halves
+            half = alg_bytes / 2  # N*S read and N*S written
+            bound = mix_bound(rd, wr, half, half)
+            result["fold_read_only_GBps"], result["fold_write_only_GBps"] = rd, wr
+            result["roofline"]["mix_bound_GBps"] = bound
+            result["roofline"]["frac_of_mix_bound"] = achieved / bound
+            result["roofline"]["mix_bound"] = (
+                "bytes / (read bytes / R + written bytes / W): R = reading the 8 rank buffers, W = writing 8 buffers, "
+                "each alone with the fold's launch shape and access order (libar_ceiling.so), measured in this run")
+        log("compact sweep")
+        size_curve = compact_sweep(torch, ar, dev)
         log("overlap row")
         result["overlap"] = overlap_rows(torch, ar, ins, outs, dev)
         result["rows"] = other_rows(torch, ar, inputs, ins, outs, dev, reps=max(5, args.steps // 2), host=host)
+        result["rows"]["sweep"] = size_curve
         del ins, outs
         torch.cuda.empty_cache()
         log("timing the CPU oracle")

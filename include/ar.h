@@ -126,6 +126,13 @@ enum ar_algo {
  * a bad nranks or dtype. Pure host function. */
 int ar_auto_algo(int nranks, size_t count, int dtype);
 
+/* The balanced split every ring-order entry point uses ([G] "Ring-AllReduceの仕組み" and [W] "Ring AllReduce", 基本设定:
+ * the buffer is divided evenly into N chunks; where N does not divide count, the first count % N chunks take one
+ * element more): lo[c] = c * (count / N) + min(c, count % N) for c = 0..N, so chunk c is [lo[c], lo[c+1]).
+ *   lo: host array of nranks + 1 int64, written by the call. Pure host function, no HIP call.
+ * Errors: AR_ERR_INVALID (lo NULL, nranks outside 1..AR_MAX_RANKS, count above INT64_MAX). */
+int ar_chunk_bounds(int nranks, size_t count, int64_t* lo);
+
 /* All-reduce of N rank buffers ([P] opening definition: every process contributes a buffer, buffers are
  * combined element-wise and the result is copied back to all; [V] section "All-Reduceは全rankの値を集約して全rankへ返す").
  *   in_bufs, out_bufs: host arrays of nranks device pointers, each to `count` elements of `dtype`.
@@ -169,10 +176,16 @@ int ar_reduce_scatter(const void* const* in_bufs, void* const* out_bufs, int nra
 int ar_all_gather(const void* const* in_bufs, void* const* out_bufs, int nranks, size_t count, int dtype,
                   void* stream);
 
-/* Bytes of device workspace ar_allreduce_ws needs for this call (0 when none). Host only, no HIP call. */
+/* Bytes of device workspace ar_allreduce_ws needs for this call (0 when none). Host only, no HIP call. Only the
+ * round-per-launch schedules on bf16/f16 need any: [W] "Ring AllReduce" (阶段一 Reduce-Scatter) has every round
+ * leave each rank's partial for the next round to read, and with partials kept in fp32 between hops (the
+ * accumulation reading above) a 2-byte rank buffer cannot hold them, so the partials go to an fp32 mirror of every
+ * rank: nranks * roundup(count, 64) * 4 bytes. */
 int ar_allreduce_workspace_size(int nranks, size_t count, int dtype, int op, int algo, size_t* bytes);
 
-/* ar_allreduce with a caller workspace: `workspace` is a device pointer to at least
+/* ar_allreduce with a caller workspace (the fp32 mirror of the partials that the rounds of [W] "Ring AllReduce",
+ * [G] "Ring-AllReduceの仕組み" and the halving and tree schedules pass between launches): `workspace` is a device
+ * pointer to at least
  * ar_allreduce_workspace_size() bytes, 256-byte aligned, disjoint from every rank buffer; its contents on
  * entry do not matter and are clobbered. A NULL workspace is accepted when 0 bytes are needed. */
 int ar_allreduce_ws(const void* const* in_bufs, void* const* out_bufs, int nranks, size_t count, int dtype, int op,
@@ -250,8 +263,11 @@ int ar_bucket_pack(const ar_copy_desc* d_descs, int ndescs, int dtype, void* str
 int ar_bucket_unpack(const ar_copy_desc* d_descs, int ndescs, int dtype, void* stream);
 
 /* ------------------------------------------------------------------------------------------------ */
-/* FP8 E4M3 block codec (the quantization AR_ALGO_RING_FP8 applies on every hop; format: OCP 8-bit
- * floating point, E4M3, bias 7, largest finite 448, NaN = S.1111.111).
+/* FP8 E4M3 block codec: the quantization AR_ALGO_RING_FP8 applies to every message ([G] "勾配圧縮技術", FP8
+ * quantization of gradients, and the NCCL feature list's FP8 all-reduce, which halves the bytes against FP16;
+ * [V] "data typeと圧縮は品質だけの問題ではない": lower-precision data cuts traffic but its error has to be
+ * controlled, hence one fp32 scale per block). Format: OCP 8-bit floating point, E4M3, bias 7, largest finite
+ * 448, NaN = S.1111.111 (the OCP specification, not the pages). Block rule as AR_ALGO_RING_FP8 above.
  *   ar_fp8_quant: blocks of AR_FP8_BLOCK elements tile [0, count) from the start (the last may be
  *     partial). in: device, count elements of in_dtype (AR_F32 or AR_BF16). codes: device uint8[count].
  *     scales: device float[ceil(count / AR_FP8_BLOCK)].

@@ -47,6 +47,21 @@ def test_binding_constants_match_header():
     assert ar.AR_AUTO_LINK_GBPS == int(re.search(r"#define AR_AUTO_LINK_GBPS (\d+)", text).group(1))
 
 
+def test_chunk_bounds_match_the_oracle():
+    """The library's balanced split (which the binding uses to size reduce-scatter / all-gather chunks) against the
+    oracle's, including counts below N (empty chunks), ragged counts and counts beyond 2^31."""
+    for n in (1, 2, 3, 4, 5, 7, 8, 16, 63, 64):
+        for count in (0, 1, 2, n - 1, n, n + 1, 1000, 4099, 134_217_728, (1 << 31) + 1001, (1 << 40) + 3):
+            if count < 0:
+                continue
+            np.testing.assert_array_equal(ar.ar_chunk_bounds(n, count), oracle.chunk_bounds(count, n))
+    assert ar.chunk_bounds(2, 4) == [0, 1, 2, 2, 2]  # the worked example: chunks {0}, {1}, empty, empty
+    for bad in ((0, 10), (65, 10)):
+        with pytest.raises(ar.ArError):
+            ar.ar_chunk_bounds(*bad)
+    assert ar.lib().ar_chunk_bounds(4, 10, None) == ar.AR_ERR_INVALID
+
+
 def test_status_strings():
     for s in range(6):
         assert ar.ar_status_string(s).startswith(["AR_OK", "AR_ERR_INVALID", "AR_ERR_UNSUPPORTED", "AR_ERR_ALIAS",

@@ -8,7 +8,8 @@
 - largest sweep point: 8 ranks x 268,435,456 fp32 (1 GiB each): ring and ring-stepwise, every element; the
   rank-order and halving-doubling variants (which do not depend on chunk positions) on 2^20 sampled elements,
   for which the oracle is evaluated on exactly those elements.
-- buckets: 300 fp32 tensors per rank (log-uniform 1K..16M elements, 2.07 GB per rank), 25 MiB buckets, avg:
+- buckets: 300 fp32 tensors per rank (log-uniform 1K..16M elements, 604,529,495 elements = 2,418,117,980 B per
+  rank), 25 MiB buckets, avg:
   every tensor of every rank, through pack + per-bucket rings + unpack and through the fused tensor path.
 - the switch between the two builds of the one-pass kernels at 1 GiB of traffic: ring, rank order and trees on
   both sides of it (fp32, bf16, f16, int32; N = 2, 3, 4, 8, 16; ragged counts), and one shared segment launch of
