@@ -5,7 +5,8 @@ the hipStream_t, and a non-zero ar_status becomes an :class:`ArError`. Every ste
 the library's HIP kernels. There is no CPU fallback: if ``libar.so`` is missing or cannot be loaded, every
 call raises.
 
-Entry points (same names as ``include/ar.h``): ar_allreduce, ar_allreduce_ws, ar_allreduce_workspace_size,
+Entry points (same names as ``include/ar.h``): ar_allreduce, ar_allreduce_ws, ar_allreduce_noalloc,
+ar_allreduce_workspace_size,
 ar_allreduce_buckets, ar_allreduce_tensors, ar_reduce_scatter, ar_all_gather, ar_bucket_plan, ar_bucket_pack,
 ar_bucket_unpack, ar_fp8_quant, ar_fp8_dequant, ar_auto_algo, ar_chunk_bounds, ar_status_string, ar_last_call,
 ar_version. Helpers: chunk_bounds, make_copy_descs, BucketedAllReduce.
@@ -23,8 +24,8 @@ __all__ = [
     "AR_F32", "AR_BF16", "AR_F16", "AR_I32", "AR_SUM", "AR_AVG", "AR_MIN", "AR_MAX",
     "AR_ALGO_RING", "AR_ALGO_FUSED", "AR_ALGO_RHD", "AR_ALGO_RING_STEPWISE", "AR_ALGO_RHD_STEPWISE",
     "AR_ALGO_RING_FP8", "AR_ALGO_TREE", "AR_ALGO_TREE_STEPWISE", "AR_ALGO_AUTO", "AR_AUTO_STEP_NS",
-    "AR_AUTO_LINK_GBPS", "AR_MAX_RANKS", "AR_FP8_BLOCK", "ArError", "lib", "lib_path", "ar_auto_algo",
-    "ar_allreduce", "ar_allreduce_ws", "ar_allreduce_workspace_size", "ar_allreduce_buckets",
+    "AR_AUTO_LINK_GBPS", "AR_MAX_RANKS", "AR_FP8_BLOCK", "AR_NOALLOC_WS_BYTES", "ArError", "lib", "lib_path", "ar_auto_algo",
+    "ar_allreduce", "ar_allreduce_ws", "ar_allreduce_noalloc", "ar_allreduce_workspace_size", "ar_allreduce_buckets",
     "ar_allreduce_tensors", "ar_reduce_scatter", "ar_all_gather", "ar_chunk_bounds", "chunk_bounds",
     "ar_bucket_plan",
     "ar_bucket_pack",
@@ -40,6 +41,7 @@ AR_ALGO_TREE, AR_ALGO_TREE_STEPWISE, AR_ALGO_AUTO = 6, 7, 8
 AR_AUTO_STEP_NS, AR_AUTO_LINK_GBPS = 1900, 153
 AR_MAX_RANKS = 64
 AR_FP8_BLOCK = 128
+AR_NOALLOC_WS_BYTES = 64 << 20
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _LIB_PATH = os.path.join(_HERE, "libar.so")
@@ -73,6 +75,7 @@ def lib():
         vp, sz, i32 = ctypes.c_void_p, ctypes.c_size_t, ctypes.c_int
         L.ar_allreduce.argtypes = [vp, vp, i32, sz, i32, i32, i32, vp]
         L.ar_allreduce_ws.argtypes = [vp, vp, i32, sz, i32, i32, i32, vp, sz, vp]
+        L.ar_allreduce_noalloc.argtypes = [vp, vp, i32, sz, i32, i32, i32, vp]
         L.ar_allreduce_workspace_size.argtypes = [i32, sz, i32, i32, i32, ctypes.POINTER(sz)]
         L.ar_allreduce_buckets.argtypes = [vp, vp, i32, vp, i32, i32, i32, i32, vp]
         L.ar_allreduce_tensors.argtypes = [vp, vp, vp, i32, i32, i32, i32, i32, vp]
@@ -88,7 +91,8 @@ def lib():
         L.ar_status_string.argtypes = [i32]
         L.ar_status_string.restype = ctypes.c_char_p
         L.ar_last_call.argtypes = [ctypes.POINTER(_CallRecord)]
-        for name in ("ar_allreduce", "ar_allreduce_ws", "ar_allreduce_workspace_size", "ar_allreduce_buckets",
+        for name in ("ar_allreduce", "ar_allreduce_ws", "ar_allreduce_noalloc", "ar_allreduce_workspace_size",
+                     "ar_allreduce_buckets",
                      "ar_allreduce_tensors", "ar_reduce_scatter", "ar_all_gather", "ar_bucket_plan", "ar_bucket_pack",
                      "ar_bucket_unpack", "ar_fp8_quant", "ar_fp8_dequant", "ar_last_call", "ar_version",
                      "ar_auto_algo", "ar_chunk_bounds"):
@@ -202,6 +206,16 @@ def ar_allreduce_ws(ins, outs, op=AR_SUM, algo=AR_ALGO_RING, workspace=None, str
     with _on(dev):
         _check(lib().ar_allreduce_ws(arr_in, arr_out, n, count, dt, op, algo, wp, wb, _stream(stream, dev)),
                "ar_allreduce_ws")
+
+
+def ar_allreduce_noalloc(ins, outs, op=AR_SUM, algo=AR_ALGO_RING, stream=None):
+    """ar_allreduce_ws with the library's fixed per-GPU scratch instead of a caller workspace (allocates nothing;
+    calls that overlap on one GPU race on that scratch)."""
+    arr_in, arr_out, n, count, dt = _rank_arrays(ins, outs)
+    dev = ins[0].device
+    with _on(dev):
+        _check(lib().ar_allreduce_noalloc(arr_in, arr_out, n, count, dt, op, algo, _stream(stream, dev)),
+               "ar_allreduce_noalloc")
 
 
 def ar_allreduce_buckets(flat_ins, flat_outs, bucket_count, op=AR_SUM, algo=AR_ALGO_RING, stream=None):

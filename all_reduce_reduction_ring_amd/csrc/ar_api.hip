@@ -152,7 +152,8 @@ bool any_overlap(Range* r, int m) {
 }
 
 int allreduce_impl(const char* entry, const void* const* in_bufs, void* const* out_bufs, int nranks, size_t count,
-                   int dtype, int op, int algo, void* workspace, size_t ws_bytes, void* stream) {
+                   int dtype, int op, int algo, void* workspace, size_t ws_bytes, void* stream,
+                   bool library_scratch = false) {
   auto done = [&](int st) { return finish(entry, nranks, count, dtype, op, algo, st); };
   if (!valid_dtype(dtype) || !valid_op(op) || !valid_algo(algo)) return done(AR_ERR_INVALID);
   if (nranks < 1 || nranks > AR_MAX_RANKS) return done(AR_ERR_INVALID);
@@ -180,6 +181,11 @@ int allreduce_impl(const char* entry, const void* const* in_bufs, void* const* o
     if ((i | o) & 15u) vec = false;  // the round-per-launch and fp8 kernels take 16-byte slots from offset 0
   }
   const size_t need = workspace_bytes(nranks, count, dtype, algo);
+  if (need > 0 && library_scratch) {
+    if (need > AR_NOALLOC_WS_BYTES) return done(AR_ERR_WORKSPACE);
+    if (ar::noalloc_scratch(&workspace) != hipSuccess) return done(AR_ERR_HIP);
+    ws_bytes = AR_NOALLOC_WS_BYTES;
+  }
   if (need > 0) {
     if (!workspace || ws_bytes < need) return done(AR_ERR_WORKSPACE);
     const uintptr_t w = reinterpret_cast<uintptr_t>(workspace);
@@ -323,6 +329,12 @@ int ar_allreduce_ws(const void* const* in_bufs, void* const* out_bufs, int nrank
                     int algo, void* workspace, size_t ws_bytes, void* stream) {
   return allreduce_impl("ar_allreduce_ws", in_bufs, out_bufs, nranks, count, dtype, op, algo, workspace, ws_bytes,
                         stream);
+}
+
+int ar_allreduce_noalloc(const void* const* in_bufs, void* const* out_bufs, int nranks, size_t count, int dtype,
+                         int op, int algo, void* stream) {
+  return allreduce_impl("ar_allreduce_noalloc", in_bufs, out_bufs, nranks, count, dtype, op, algo, nullptr, 0, stream,
+                        true);
 }
 
 int ar_bucket_plan(const int64_t* numels, int ntensors, int dtype, int nranks, size_t cap_bytes, int32_t* bucket_of,

@@ -68,6 +68,9 @@ hipError_t launch_all_gather(const RankPtrs& p, int n, int64_t count, int esize,
 
 // Round-per-launch schedules. ws: fp32 partial mirror (n * ws_stride floats) for 16-bit types, else null.
 int64_t stepwise_ws_stride(int64_t count);
+// Device address of the current device's AR_NOALLOC_WS_BYTES of library scratch (resolved on the first call per
+// device, then cached). Allocates nothing.
+hipError_t noalloc_scratch(void** out);
 hipError_t launch_ring_stepwise(const RankPtrs& p, int n, int64_t count, int dtype, int op, float* ws, bool vec,
                                 hipStream_t s);
 hipError_t launch_rhd_stepwise(const RankPtrs& p, int n, int64_t count, int dtype, int op, float* ws, bool vec,

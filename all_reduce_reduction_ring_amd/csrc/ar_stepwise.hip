@@ -21,11 +21,18 @@
 // value); for BF16/F16 an fp32 mirror in the caller's workspace, rank r at ws + r * ws_stride, so partial
 // sums stay fp32 between rounds exactly as in the one-pass kernels. Within a round no rank writes anything
 // another rank reads in that round, so in-place buffers are safe.
+#include <mutex>
+
 #include "ar_device.h"
 #include "ar_internal.h"
 
 namespace ar {
 namespace {
+
+// The library's own fp32 mirror for callers that cannot allocate (ar_allreduce_noalloc): part of this file's code
+// object, so every GPU the library runs on holds one copy from the first use until the process ends. In host code
+// this name is only a handle for hipGetSymbolAddress; kernels get the device address that call returns.
+__device__ __align__(256) unsigned char scratch[AR_NOALLOC_WS_BYTES];
 
 constexpr int kThreads = 256;
 
@@ -344,6 +351,27 @@ hipError_t launch_rounds(const RankPtrs& p, int n, int64_t count, int dtype, int
 }  // namespace
 
 int64_t stepwise_ws_stride(int64_t count) { return (count + 63) / 64 * 64; }
+
+hipError_t noalloc_scratch(void** out) {
+  constexpr int kMaxDevices = 64;
+  static std::mutex mu;
+  static void* ptrs[kMaxDevices] = {};
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(mu);
+  if (!ptrs[dev]) {
+    // once per device, with that device current: this GPU's copy of the array
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    if (!p) return hipErrorInvalidSymbol;
+    ptrs[dev] = p;
+  }
+  *out = ptrs[dev];
+  return hipSuccess;
+}
 
 hipError_t launch_ring_stepwise(const RankPtrs& p, int n, int64_t count, int dtype, int op, float* ws, bool vec,
                                 hipStream_t s) {

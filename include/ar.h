@@ -191,6 +191,19 @@ int ar_allreduce_workspace_size(int nranks, size_t count, int dtype, int op, int
 int ar_allreduce_ws(const void* const* in_bufs, void* const* out_bufs, int nranks, size_t count, int dtype, int op,
                     int algo, void* workspace, size_t ws_bytes, void* stream);
 
+/* ar_allreduce_ws without a caller workspace, for callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid allocation): where the algorithm needs scratch (the
+ * round-per-launch schedules on bf16/f16), it uses the library's own fixed array of AR_NOALLOC_WS_BYTES, one per GPU,
+ * held from the first call on that GPU until the process ends. The call allocates nothing (no hipMalloc, no
+ * allocating library routine); the first call on each GPU looks up that GPU's array. Every call on one GPU shares the
+ * array, so calls that overlap in time on one GPU (different streams, or host threads) race on it and must be
+ * ordered by the caller; the array's contents on entry do not matter. Arguments, results and errors as
+ * ar_allreduce_ws, plus AR_ERR_WORKSPACE when ar_allreduce_workspace_size() exceeds AR_NOALLOC_WS_BYTES (nothing is
+ * enqueued) and AR_ERR_HIP when the array cannot be resolved on the current device. */
+#define AR_NOALLOC_WS_BYTES (64u << 20)
+int ar_allreduce_noalloc(const void* const* in_bufs, void* const* out_bufs, int nranks, size_t count, int dtype,
+                         int op, int algo, void* stream);
+
 /* ------------------------------------------------------------------------------------------------ */
 /* Bucketing ([G] "パフォーマンスチューニング": many small gradient tensors are packed into one bucket, 25 MB
  * by default, and all-reduced together; [V] "communicationとcomputeを重ねる条件": buckets that are too small
