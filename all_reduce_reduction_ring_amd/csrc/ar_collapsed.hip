@@ -474,7 +474,11 @@ hipError_t launch_front(CollapsedArgs& a, hipStream_t s) {
 // ones (whose upper slots end after them) go element by element. Same bits as the aligned kernels: every element still folds from its chunk's rank.
 struct SkewArgs {
   CollapsedArgs f;
-  int8_t im[AR_MAX_RANKS], om[AR_MAX_RANKS];  // elements past the 16-byte grid: each rank's input and output
+  // Elements past the 16-byte grid, each rank's input and output, and the input's grid itself (in[r] - im[r]
+  // elements). 32-bit entries: the kernel reads them with scalar loads (the rank rotation is wave-uniform), which
+  // never wait on the vector loads of the data.
+  int32_t im[AR_MAX_RANKS], om[AR_MAX_RANKS];
+  const char* ib[AR_MAX_RANKS];
 };
 static_assert(sizeof(SkewArgs) <= 4096, "kernel arguments must fit in 4 KiB");
 
@@ -492,6 +496,17 @@ __device__ __forceinline__ u32x4 shift_by(int m, const u32x4& x0, const u32x4& x
     case 6: return shift_concat<2, 6>(x0, x1);
     default: return shift_concat<2, 7>(x0, x1);
   }
+}
+
+// Lane i (< 63) receives lane i + 1's x; lane 63 keeps `last` (a DPP wave shift left by one lane, one VALU
+// operation per dword, no LDS traffic).
+[[maybe_unused]] __device__ __forceinline__ u32x4 from_next_lane(const u32x4& x, const u32x4& last) {
+  u32x4 r;
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+    r[i] = static_cast<uint32_t>(__builtin_amdgcn_update_dpp(static_cast<int>(last[i]), static_cast<int>(x[i]),
+                                                             0x130 /* wave_shl:1 */, 0xF, 0xF, false));
+  return r;
 }
 
 // storage bits of element k of a packed slot
@@ -548,7 +563,21 @@ __device__ __forceinline__ bool skew_vec_tile(const CollapsedArgs& a, int64_t w,
 // A wave walks a strip of kSkewStrip consecutive tiles and carries the previous tile's results into the next, so
 // the output slot shared by two tiles of a strip is stored whole by the later one; only slots at the ends of a
 // strip (or next to an element-path tile) are stored element by element.
-constexpr int kSkewStrip = 8;
+#ifndef AR_SKEW_STRIP
+#define AR_SKEW_STRIP 8
+#endif
+constexpr int kSkewStrip = AR_SKEW_STRIP;
+// Workgroups per CU, as a multiple of the one-pass kernels' count: each lane's shifts, lane exchanges and
+// assembled stores make a tile's work long enough that one wave per SIMD leaves the loads of the next tile waiting
+// on it; twice the waves hide that. N = 8, 256 MiB of bf16 per rank at odd per-rank offsets, one MI355X: 1,486 us
+// at 1x, 940 us at 2x, 951-956 us at 4x and 8x (ring; the binomial tree 1,378 / 912 / 915-975 us), 943 us at 4x
+// with strips of 32 tiles.
+#ifndef AR_SKEW_WORD_ALIGNED
+#define AR_SKEW_WORD_ALIGNED 0
+#endif
+#ifndef AR_SKEW_GRID_SCALE
+#define AR_SKEW_GRID_SCALE 2
+#endif
 
 template <int DT, int OP, int NR, int SHAPE>
 __global__ __launch_bounds__(kThreads) void skew_kernel(SkewArgs s) {
@@ -560,7 +589,10 @@ __global__ __launch_bounds__(kThreads) void skew_kernel(SkewArgs s) {
   const int64_t nwt = (a.count + 64 * V - 1) / (64 * V);
   const int64_t nstrips = (nwt + kSkewStrip - 1) / kSkewStrip;
   const int64_t nw = static_cast<int64_t>(gridDim.x) * (kThreads / 64);
-  const int64_t wv = static_cast<int64_t>(blockIdx.x) * (kThreads / 64) + (threadIdx.x >> 6);
+  // the wave index in a scalar register, so that everything derived from it (tile, chunk, rank rotation, per-rank
+  // pointers and shifts) is wave-uniform to the compiler too: scalar loads of the rank table, scalar branches on
+  // the shifts, and no wait on a vector load of a pointer between the data loads
+  const int64_t wv = static_cast<int64_t>(blockIdx.x) * (kThreads / 64) + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   for (int64_t sp = wv; sp < nstrips; sp += nw) {
     u32x4 prev = {0u, 0u, 0u, 0u};  // this lane's result in the previous tile of the strip
     bool prev_vec = false;           // the previous tile of the strip took the vector path
@@ -573,16 +605,22 @@ __global__ __launch_bounds__(kThreads) void skew_kernel(SkewArgs s) {
       const bool next_vec = k + 1 < kSkewStrip && skew_vec_tile<V, NR>(a, w + 1, &cn);
       const int64_t j = w * 64 + lane, e = j * V;
       if (cur_vec) {
-        const int start = a.rot ? c : 0;
+        const int start = __builtin_amdgcn_readfirstlane(a.rot ? c : 0);
+        // Lane j needs the aligned slots j and j + 1 of every rank; slot j + 1 is the next lane's slot j, so only
+        // the last lane loads it, and the others take it from their neighbour with a wave shift.
         u32x4 x0[NR], x1[NR];
 #pragma unroll
         for (int q = 0; q < NR; ++q) {
           int rr = start + q;
           rr = rr >= NR ? rr - NR : rr;
-          const char* base = static_cast<const char*>(a.p.in[rr]) - s.im[rr] * ES + j * 16;
+          const char* base = s.ib[rr] + j * 16;
           x0[q] = ld16(base);
-          x1[q] = ld16(base + 16);
+          // (not a copy of x0: that would wait for its load before the next one is issued)
+          x1[q] = u32x4{0u, 0u, 0u, 0u};
+          if (lane == 63) x1[q] = ld16(base + 16);
         }
+#pragma unroll
+        for (int q = 0; q < NR; ++q) x1[q] = from_next_lane(x0[q], x1[q]);
         typename S::Acc acc[V];
         if constexpr (SHAPE == kLinear) {
           typename S::Acc t[V];
@@ -605,12 +643,12 @@ __global__ __launch_bounds__(kThreads) void skew_kernel(SkewArgs s) {
 #pragma unroll
         for (int i = 0; i < V; ++i) acc[i] = finalize<OP>(acc[i], NR);
         const u32x4 o = S::pack(acc);
-        u32x4 nx, last;  // the next lane's result; the previous tile's last lane
+        // the next lane's result (lane 63's is never used) and the previous tile's last lane
+        const u32x4 nx = from_next_lane(o, o);
+        u32x4 last;
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          nx[i] = static_cast<uint32_t>(__shfl_down(static_cast<int>(o[i]), 1));
-          last[i] = static_cast<uint32_t>(__shfl(static_cast<int>(prev[i]), 63));
-        }
+        for (int i = 0; i < 4; ++i)
+          last[i] = static_cast<uint32_t>(__builtin_amdgcn_readlane(static_cast<int>(prev[i]), 63));
 #pragma unroll
         for (int r = 0; r < NR; ++r) {
           const int m = s.om[r];
@@ -655,7 +693,7 @@ hipError_t launch_skew(SkewArgs& s, hipStream_t st) {
   constexpr int V = Traits<DT>::kVec;
   const int64_t tiles = (s.f.count + 64 * V - 1) / (64 * V);
   const int64_t strips = (tiles + kSkewStrip - 1) / kSkewStrip;
-  int64_t g = static_cast<int64_t>(cu_count()) * blocks_per_cu<NR>();
+  int64_t g = static_cast<int64_t>(cu_count()) * blocks_per_cu<NR>() * AR_SKEW_GRID_SCALE;
   const int64_t need = (strips + kThreads / 64 - 1) / (kThreads / 64);
   if (g > need) g = need;
   if (g < 1) g = 1;
@@ -711,12 +749,13 @@ bool plan_skew(const RankPtrs& p, int n, int64_t count, int algo, SkewArgs& s) {
     if (i % ES || o % ES) return false;
     differ = differ || i % 16 != r0 || o % 16 != r0;
     words = words && i % 4 == 0 && o % 4 == 0;
-    s.im[r] = static_cast<int8_t>((i % 16) / ES);
-    s.om[r] = static_cast<int8_t>((o % 16) / ES);
+    s.im[r] = static_cast<int32_t>((i % 16) / ES);
+    s.om[r] = static_cast<int32_t>((o % 16) / ES);
+    s.ib[r] = static_cast<const char*>(p.in[r]) - (i % 16);
   }
   // addresses that are all multiples of 4 bytes keep the one-front kernel with 16-byte accesses at 4-byte
   // alignment, which measured faster (N = 8, 256 MiB of bf16, rank r at 2r elements: 938 us against 1,354 us)
-  return differ && !words;
+  return differ && (AR_SKEW_WORD_ALIGNED || !words);
 }
 
 // ------------------------------------------------------------------------------------------ launch

@@ -50,7 +50,10 @@ hipError_t launch_segments_dt(const RankPtrs& p, int n, const int64_t* counts, i
 // plus N writes of `elems` elements of `esize` bytes per rank), except the ring on 2 or 4 ranks, which stays on
 // the small build (bf16 avg, one MI355X, two runs: N = 2 at 512 MiB per rank 439-455 us against 459-465 us, N = 4 at
 // 256 MiB 399-404 against 416-418; the trees there ran 4-12% faster on the large build, N = 16 level or faster).
-constexpr int64_t kLargeTrafficBytes = int64_t(1) << 30;
+#ifndef AR_LARGE_TRAFFIC_BYTES
+#define AR_LARGE_TRAFFIC_BYTES (int64_t(1) << 30)
+#endif
+constexpr int64_t kLargeTrafficBytes = AR_LARGE_TRAFFIC_BYTES;
 template <int DT> constexpr int kElemSize = (DT == AR_BF16 || DT == AR_F16) ? 2 : 4;
 inline bool large_launch(int n, int64_t elems, int esize, int algo) {
   if (algo == AR_ALGO_RING && n <= 4) return false;

@@ -9,18 +9,24 @@
 // same bits as pack -> ring per bucket -> unpack, with N reads + N writes per element instead of three times
 // that. (Bucket pads are zeros that never mix with other elements, so they need not exist.)
 //
-// Work: tiles of 256 16-byte slots of one tensor, dealt out round-robin over a grid sized to the GPU (tile g to
-// block g mod G). Each block stages 256 tensor descriptors at a time in LDS and prefix-sums their tile counts.
+// Work: tiles of kThreads 16-byte slots of one tensor, dealt out round-robin over a grid sized to the GPU (tile g to
+// block g mod G). Each block stages kThreads tensor descriptors at a time in LDS and prefix-sums their tile counts.
 // A tile normally lies inside one bucket chunk, so the rank rotation is uniform across the block; a tile
 // that crosses a chunk boundary is processed as uniform sub-ranges.
+#ifndef AR_TENSOR_THREADS
+#define AR_TENSOR_THREADS 256
+#endif
+#ifndef AR_TENSOR_BLOCKS_PER_CU
+#define AR_TENSOR_BLOCKS_PER_CU 1
+#endif
 #include "ar_device.h"
 #include "ar_internal.h"
 
 namespace ar {
 namespace {
 
-constexpr int kThreads = 256;
-constexpr int kBatch = 256;
+constexpr int kThreads = AR_TENSOR_THREADS;
+constexpr int kBatch = kThreads;
 // each thread stages one descriptor and one entry of the tile-count prefix sum
 static_assert(kBatch == kThreads, "the descriptor batch is one per thread");
 
@@ -33,9 +39,12 @@ struct TensorArgs {
   int rot;  // 1: ring order; 0: rank order from 0
 };
 
-// Workgroups per CU of the persistent grid: 4 for every rank count (an A/B over 1, 2, 4 and 8 per CU on the
-// 300-tensor, 8-rank workload put 4 ahead by 5-15%).
-template <int NR> constexpr int tensor_blocks_per_cu() { return 4; }
+// Workgroups per CU of the persistent grid: one 256-thread workgroup (4 waves) for every rank count. On the
+// 300-tensor, 8-rank fp32 workload (one MI355X, same run): 7,486-7,491 us (ring order) against 7,752-7,817 us with
+// 4 per CU, 7,722 us with 128-thread workgroups at 2 per CU, 7,766 us with 512-thread ones at 1 per CU, 7,540 us
+// with default-policy loads. One per CU needs the cursor and the register copy of the rank pointers below: without
+// them (a search and a pointer reload per tile) one per CU ran 10,551 us, which is why 4 per CU had been chosen.
+template <int NR> constexpr int tensor_blocks_per_cu() { return AR_TENSOR_BLOCKS_PER_CU; }
 
 // Fold shapes: rank order from `start` (ring, fused), the halving tree (RHD), the binomial tree.
 enum Shape { kLinear = 0, kHalving = 1, kBinomial = 2 };
@@ -138,6 +147,7 @@ __global__ __launch_bounds__(kThreads) void tensor_kernel(TensorArgs a) {
   constexpr int64_t TE = static_cast<int64_t>(kThreads) * V;  // elements per tile
   __shared__ int64_t s_numel[kBatch], s_off[kBatch], s_clen[kBatch], pre[kBatch];
   const int n = NR > 0 ? NR : a.n;
+  constexpr int NT = NR > 0 ? NR : 1;
   const int64_t G = gridDim.x, b = blockIdx.x;
   const int t = threadIdx.x;
   int64_t base = 0;
@@ -160,25 +170,43 @@ __global__ __launch_bounds__(kThreads) void tensor_kernel(TensorArgs a) {
       __syncthreads();
     }
     const int64_t batch_tiles = pre[kBatch - 1];
+    // A block's tiles come in increasing order, so the batch entry that holds the current tile only moves forward
+    // (a cursor instead of a search per tile), and a tensor's rank pointers, loaded once when the block reaches it,
+    // stay in registers for all of its tiles that the block takes.
+    int lo = 0, cur = -1;
+    const void* const* ipg = nullptr;  // the tensor's rank pointers in the caller's table (element path)
+    void* const* opg = nullptr;
+    const void* ipv[NT];  // the same, in registers (vector path, rank count known at compile time)
+    void* opv[NT];
+    bool vec = false;
+    int64_t numel = 0, boff = 0, clen = 0, tile0 = 0;
     for (int64_t g = base + ((b - base % G) % G + G) % G; g < base + batch_tiles; g += G) {
       const int64_t lt = g - base;
-      int lo = 0, hi = m - 1;
-      while (lo < hi) {
-        const int mid = (lo + hi) >> 1;
-        if (pre[mid] > lt) hi = mid;
-        else lo = mid + 1;
-      }
+      while (pre[lo] <= lt) ++lo;  // stops below m: pre[m - 1] = batch_tiles > lt
       const int ti = __builtin_amdgcn_readfirstlane(b0 + lo);
-      const int64_t numel = s_numel[lo], boff = s_off[lo], clen = s_clen[lo];
-      const int64_t e0 = (lt - (lo > 0 ? pre[lo - 1] : 0)) * TE;
+      if (ti != cur) {
+        cur = ti;
+        numel = s_numel[lo];
+        boff = s_off[lo];
+        clen = s_clen[lo];
+        tile0 = lo > 0 ? pre[lo - 1] : 0;
+        ipg = a.in + static_cast<int64_t>(ti) * n;
+        opg = a.out + static_cast<int64_t>(ti) * n;
+        uintptr_t anyp = 0;
+        for (int r = 0; r < n; ++r) anyp |= reinterpret_cast<uintptr_t>(ipg[r]) | reinterpret_cast<uintptr_t>(opg[r]);
+        // the halving tree for a runtime rank count is evaluated per element
+        // 16-byte accesses need 4-byte alignment only (a tensor at another offset straddles cache lines)
+        vec = (anyp & 3u) == 0 && !(SHAPE == kHalving && NR == 0);
+        if constexpr (NR > 0) {
+#pragma unroll
+          for (int r = 0; r < NR; ++r) {
+            ipv[r] = ipg[r];
+            opv[r] = opg[r];
+          }
+        }
+      }
+      const int64_t e0 = (lt - tile0) * TE;
       const int64_t e1 = e0 + TE < numel ? e0 + TE : numel;
-      const void* const* ip = a.in + static_cast<int64_t>(ti) * n;
-      void* const* op = a.out + static_cast<int64_t>(ti) * n;
-      uintptr_t anyp = 0;
-      for (int r = 0; r < n; ++r) anyp |= reinterpret_cast<uintptr_t>(ip[r]) | reinterpret_cast<uintptr_t>(op[r]);
-      // the halving tree for a runtime rank count is evaluated per element
-      // 16-byte accesses need 4-byte alignment only (a tensor at another offset straddles cache lines)
-      const bool vec = (anyp & 3u) == 0 && !(SHAPE == kHalving && NR == 0);
       // uniform sub-ranges [s0, s1) of the tile that lie in one bucket chunk
       int64_t s0 = e0;
       while (s0 < e1) {
@@ -198,13 +226,19 @@ __global__ __launch_bounds__(kThreads) void tensor_kernel(TensorArgs a) {
         const int64_t v0 = s0 / V, v1 = vsub ? s1 / V : v0;
         const int64_t v = v0 + t;
         if (v < v1) {
-          const u32x4 w = fold_slot<DT, OP, NR, SHAPE>(ip, n, start, v * 16);
-          for (int r = 0; r < n; ++r) st16(static_cast<char*>(op[r]) + v * 16, w);
+          if constexpr (NR > 0) {
+            const u32x4 w = fold_slot<DT, OP, NR, SHAPE>(ipv, n, start, v * 16);
+#pragma unroll
+            for (int r = 0; r < NR; ++r) st16(static_cast<char*>(opv[r]) + v * 16, w);
+          } else {
+            const u32x4 w = fold_slot<DT, OP, NR, SHAPE>(ipg, n, start, v * 16);
+            for (int r = 0; r < n; ++r) st16(static_cast<char*>(opg[r]) + v * 16, w);
+          }
         }
         const int64_t tail0 = vsub ? v1 * V : s0;
         for (int64_t e = tail0 + t; e < s1; e += kThreads) {
-          const uint32_t bits = fold_elem<DT, OP, SHAPE>(ip, n, start, e);
-          for (int r = 0; r < n; ++r) store_elem<DT>(op[r], e, bits);
+          const uint32_t bits = fold_elem<DT, OP, SHAPE>(ipg, n, start, e);
+          for (int r = 0; r < n; ++r) store_elem<DT>(opg[r], e, bits);
         }
         s0 = s1;
       }

@@ -13,6 +13,7 @@ CPU oracle timed on this host on the same inputs; and, beside the headline, ever
 buckets over 300 tensors, the fp8 codec and compressed ring) with its own algorithmic-bytes roofline.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--headline-only] [--fp8-only] [--copy-calibration]
+                       [--ring-bytes-per-rank S] [--sweep OUT.jsonl]
 """
 from __future__ import annotations
 
@@ -155,8 +156,9 @@ def write_ceiling(torch, ins, reps=10):
 def fold_halves(torch, ins, outs, reps=10):
     """The headline fold's two halves on their own, with its launch shape and access order (libar_ceiling.so, the
     benchmark's measurement kernels): reading the N rank buffers with nothing written, and writing N buffers with
-    nothing read, each N*S bytes; median of 10 after warm-up calls. Returns (read GB/s, write GB/s), or None when
-    the measurement library is not built."""
+    nothing read, each N*S bytes; with the fold's large launch shape (the headline's) and its small one; and the
+    fastest plain write pattern measured for these bytes (one-shot blocks, 16 KiB of one buffer each). Median of 10
+    after warm-up calls. Returns {name: GB/s}, or None when the measurement library is not built."""
     path = os.path.join(ROOT, "all_reduce_reduction_ring_amd", "libar_ceiling.so")
     if not os.path.exists(path):
         return None
@@ -175,15 +177,18 @@ def fold_halves(torch, ins, outs, reps=10):
         if rc != 0:
             raise RuntimeError(f"libar_ceiling call failed ({rc})")
 
-    read = lambda: check(L.arc_read(rin, n, nbytes, 0x9E3779B9, sink.data_ptr(), 1, stream()))
-    write = lambda: check(L.arc_write(rout, n, nbytes, 1, stream()))
-    rates = []
-    for fn in (read, write):
+    calls = {"read_fold_large": lambda: check(L.arc_read(rin, n, nbytes, 0x9E3779B9, sink.data_ptr(), 1, stream())),
+             "read_fold_small": lambda: check(L.arc_read(rin, n, nbytes, 0x9E3779B9, sink.data_ptr(), 0, stream())),
+             "write_fold_large": lambda: check(L.arc_write(rout, n, nbytes, 1, stream())),
+             "write_fold_small": lambda: check(L.arc_write(rout, n, nbytes, 0, stream())),
+             "write_blocks": lambda: check(L.arc_write(rout, n, nbytes, 2, stream()))}
+    rates = {}
+    for name, fn in calls.items():
         for _ in range(3):
             fn()
         ms = Timer(torch).run(fn, reps)
-        rates.append(n * nbytes / (np.median(ms) * 1e-3) / GB)
-    return rates[0], rates[1]
+        rates[name] = n * nbytes / (np.median(ms) * 1e-3) / GB
+    return rates
 
 
 def mix_bound(read_gbps, write_gbps, read_bytes, write_bytes):
@@ -643,6 +648,8 @@ def main():
     p.add_argument("--fp8-only", action="store_true",
                    help="time only the compressed ring on its workload (8 x 67,108,864 bf16, 0.1%% outliers; for "
                         "profiler runs)")
+    p.add_argument("--ring-bytes-per-rank", type=int, metavar="S",
+                   help="time only the ring on N = 8 fp32 ranks of S bytes each, sum (for profiler runs at one size)")
     p.add_argument("--sweep", metavar="OUT.jsonl", help="run only the message-size sweep, one JSON line per point")
     p.add_argument("--sweep-max-log2", type=int, default=30)
     args = p.parse_args()
@@ -664,6 +671,23 @@ def main():
 
     if args.sweep:
         sweep(torch, ar, dev, args.sweep, max_log2=args.sweep_max_log2)
+        return
+
+    if args.ring_bytes_per_rank:
+        S = args.ring_bytes_per_rank
+        g = torch.Generator(device=dev)
+        g.manual_seed(4000)
+        rin = [torch.rand(S // 4, generator=g, device=dev).mul_(2).sub_(1) for _ in range(N_RANKS)]
+        rout = [torch.empty_like(t) for t in rin]
+        step = lambda: ar.ar_allreduce(rin, rout, ar.AR_SUM, ar.AR_ALGO_RING)
+        for _ in range(args.warmup):
+            step()
+        torch.cuda.synchronize()
+        ms = Timer(torch).run(step, args.steps)
+        t = float(np.mean(ms)) * 1e-3
+        print(json.dumps({"ring_f32": {"bytes_per_rank": S, "kernel_us": stats_us(ms),
+                                       "hbm_GBps": ring_bytes(N_RANKS, S // 4, 4) / t / GB,
+                                       "steps": args.steps, "warmup": args.warmup}}))
         return
 
     if args.fp8_only:
@@ -736,15 +760,19 @@ def main():
         result["write_ceiling_GBps"] = write_ceiling(torch, ins)
         halves = fold_halves(torch, ins, outs)
         if halves:
-            rd, wr = halves
             half = alg_bytes / 2  # N*S read and N*S written
-            bound = mix_bound(rd, wr, half, half)
-            result["fold_read_only_GBps"], result["fold_write_only_GBps"] = rd, wr
+            bound = mix_bound(halves["read_fold_large"], halves["write_fold_large"], half, half)
+            best = mix_bound(max(halves["read_fold_large"], halves["read_fold_small"]), max(
+                halves["write_fold_large"], halves["write_fold_small"], halves["write_blocks"]), half, half)
+            result["read_write_alone_GBps"] = halves
             result["roofline"]["mix_bound_GBps"] = bound
             result["roofline"]["frac_of_mix_bound"] = achieved / bound
+            result["roofline"]["mix_bound_best_GBps"] = best
+            result["roofline"]["frac_of_mix_bound_best"] = achieved / best
             result["roofline"]["mix_bound"] = (
-                "bytes / (read bytes / R + written bytes / W): R = reading the 8 rank buffers, W = writing 8 buffers, "
-                "each alone with the fold's launch shape and access order (libar_ceiling.so), measured in this run")
+                "bytes / (read bytes / R + written bytes / W), R and W measured alone in this run (libar_ceiling.so): "
+                "mix_bound with the headline kernel's own launch shape and access order, mix_bound_best with the "
+                "fastest read and write patterns measured for the same bytes")
         log("compact sweep")
         size_curve = compact_sweep(torch, ar, dev)
         log("overlap row")
