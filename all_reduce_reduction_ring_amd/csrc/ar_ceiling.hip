@@ -1,7 +1,8 @@
 // ar_ceiling.hip -- measurement kernels, built into libar_ceiling.so beside libar and loaded only by the benchmark:
 // the read half and the write half of the one-pass all-reduce on their own, each with the fold's launch shape and
 // access order, so that the time the fold would need if its reads and writes cost what they cost alone (and mixing
-// them cost nothing) can be measured on the GPU at hand.
+// them cost nothing) can be measured on the GPU at hand; and the fastest plain write pattern measured for the same
+// bytes, for the bound with the best reads and writes this GPU offers.
 //
 // The one-pass ring (ring_front_kernel) reads one 16-byte slot from each of N rank buffers per thread and tile,
 // folds, and stores one slot to each of N buffers; tiles of kThreads slots go round-robin to a grid of
@@ -60,6 +61,20 @@ __global__ __launch_bounds__(THREADS) void write_kernel(Bufs b, int64_t nslots, 
   }
 }
 
+// The fastest write pattern measured for these bytes on MI355X: a one-shot grid (no persistent workgroups) in which
+// block b writes 1024 consecutive slots (16 KiB) of buffer b % 8 at tile b / 8, default-policy stores, the way a plain
+// device fill kernel writes.
+__global__ __launch_bounds__(256) void write_blocks_kernel(Bufs b, int64_t nslots, uint32_t value) {
+  const u32x4 w = {value, value, value, value};
+  const int64_t tile = blockIdx.x / 8;
+  u32x4* dst = gptr<u32x4>(b.p[blockIdx.x % 8]);
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int64_t v = tile * 1024 + i * 256 + threadIdx.x;
+    if (v < nslots) dst[v] = w;
+  }
+}
+
 int grid_for(int threads, int64_t nslots) {
   int dev = 0, cus = 256;
   if (hipGetDevice(&dev) != hipSuccess || hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) !=
@@ -84,9 +99,10 @@ bool fill(Bufs& b, const void* const* bufs, int n, size_t bytes) {
 
 extern "C" {
 
-// Read `bytes` (a multiple of 16) from each of n = 8 device buffers (16-byte aligned) with the one-pass fold's loads.
-// sink: a device uint32 that is written only if the XOR of everything read equals `magic`. 0 on success, 1 for bad
-// arguments, 2 for a launch error.
+// Read `bytes` (a multiple of 16) from each of n = 8 device buffers (16-byte aligned) with the one-pass fold's loads
+// (large = 1: default-policy loads, the large launch shape; 0: non-temporal loads, the small one). sink: a device
+// uint32 that is written only if the XOR of everything read equals `magic`. 0 on success, 1 for bad arguments, 2 for
+// a launch error.
 int arc_read(const void* const* bufs, int n, size_t bytes, uint32_t magic, uint32_t* sink, int large, void* stream) {
   Bufs b = {};
   if (!fill(b, bufs, n, bytes) || !sink) return 1;
@@ -101,16 +117,25 @@ int arc_read(const void* const* bufs, int n, size_t bytes, uint32_t magic, uint3
   return hipGetLastError() == hipSuccess ? 0 : 2;
 }
 
-// Write `bytes` (a multiple of 16) of a constant to each of n = 8 device buffers with the fold's non-temporal stores.
-int arc_write(void* const* bufs, int n, size_t bytes, int large, void* stream) {
+// Write `bytes` (a multiple of 16) of a constant to each of n = 8 device buffers. shape 1 and 0: the fold's
+// non-temporal stores with the large and small launch shapes; shape 2: write_blocks_kernel.
+int arc_write(void* const* bufs, int n, size_t bytes, int shape, void* stream) {
   Bufs b = {};
   if (!fill(b, const_cast<const void* const*>(bufs), n, bytes)) return 1;
   const int64_t nslots = static_cast<int64_t>(bytes / 16);
   hipStream_t s = static_cast<hipStream_t>(stream);
-  if (large)
+  if (shape == 1) {
     hipLaunchKernelGGL((write_kernel<128, 8>), dim3(grid_for(128, nslots)), dim3(128), 0, s, b, nslots, 0x3F003F00u);
-  else
+  } else if (shape == 0) {
     hipLaunchKernelGGL((write_kernel<256, 8>), dim3(grid_for(256, nslots)), dim3(256), 0, s, b, nslots, 0x3F003F00u);
+  } else if (shape == 2) {
+    const int64_t blocks = (nslots + 1023) / 1024 * 8;
+    if (blocks > 0x7FFFFFFF) return 1;
+    hipLaunchKernelGGL(write_blocks_kernel, dim3(static_cast<unsigned>(blocks)), dim3(256), 0, s, b, nslots,
+                       0x3F003F00u);
+  } else {
+    return 1;
+  }
   return hipGetLastError() == hipSuccess ? 0 : 2;
 }
 
