@@ -509,6 +509,16 @@ __device__ __forceinline__ u32x4 shift_by(int m, const u32x4& x0, const u32x4& x
   return r;
 }
 
+// Lane i (> 0) receives lane i - 1's x; lane 0 keeps `first` (a DPP wave shift right by one lane).
+[[maybe_unused]] __device__ __forceinline__ u32x4 from_prev_lane(const u32x4& x, const u32x4& first) {
+  u32x4 r;
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+    r[i] = static_cast<uint32_t>(__builtin_amdgcn_update_dpp(static_cast<int>(first[i]), static_cast<int>(x[i]),
+                                                             0x138 /* wave_shr:1 */, 0xF, 0xF, false));
+  return r;
+}
+
 // storage bits of element k of a packed slot
 template <int DT>
 __device__ __forceinline__ uint32_t slot_elem(const u32x4& v, int k) {
@@ -572,9 +582,6 @@ constexpr int kSkewStrip = AR_SKEW_STRIP;
 // on it; twice the waves hide that. N = 8, 256 MiB of bf16 per rank at odd per-rank offsets, one MI355X: 1,486 us
 // at 1x, 940 us at 2x, 951-956 us at 4x and 8x (ring; the binomial tree 1,378 / 912 / 915-975 us), 943 us at 4x
 // with strips of 32 tiles.
-#ifndef AR_SKEW_WORD_ALIGNED
-#define AR_SKEW_WORD_ALIGNED 0
-#endif
 #ifndef AR_SKEW_GRID_SCALE
 #define AR_SKEW_GRID_SCALE 2
 #endif
@@ -643,12 +650,13 @@ __global__ __launch_bounds__(kThreads) void skew_kernel(SkewArgs s) {
 #pragma unroll
         for (int i = 0; i < V; ++i) acc[i] = finalize<OP>(acc[i], NR);
         const u32x4 o = S::pack(acc);
-        // the next lane's result (lane 63's is never used) and the previous tile's last lane
-        const u32x4 nx = from_next_lane(o, o);
+        // The previous lane's result; lane 0 takes the previous tile's last lane (used only when that tile took this
+        // path, so its result is the one carried in `prev`).
         u32x4 last;
 #pragma unroll
         for (int i = 0; i < 4; ++i)
           last[i] = static_cast<uint32_t>(__builtin_amdgcn_readlane(static_cast<int>(prev[i]), 63));
+        const u32x4 pv = from_prev_lane(o, last);
 #pragma unroll
         for (int r = 0; r < NR; ++r) {
           const int m = s.om[r];
@@ -656,15 +664,13 @@ __global__ __launch_bounds__(kThreads) void skew_kernel(SkewArgs s) {
           if (m == 0) {
             st16(ob + j * 16, o);
           } else {
-            // aligned slot j + 1: the last m elements of this lane, then the first V - m of the next
-            const u32x4 up = shift_by<ES>(V - m, o, nx);
-            if (lane < 63) st16(ob + (j + 1) * 16, up);
-            if (lane == 0) {
-              if (prev_vec) {
-                st16(ob + j * 16, shift_by<ES>(V - m, last, o));  // slot j: the previous tile's last m, then ours
-              } else {
-                for (int q = 0; q < V - m; ++q) store_elem<DT>(a.p.out[r], e + q, slot_elem<DT>(o, q));
-              }
+            // Aligned slot j: the previous lane's last m elements, then this lane's first V - m. The wave's slots
+            // j0 .. j0 + 63 go out in one store instruction over whole lines (a separate store for the tile's first
+            // slot made every line there a second, partial write).
+            if (lane > 0 || prev_vec) {
+              st16(ob + j * 16, shift_by<ES>(V - m, pv, o));
+            } else {
+              for (int q = 0; q < V - m; ++q) store_elem<DT>(a.p.out[r], e + q, slot_elem<DT>(o, q));
             }
             if (lane == 63 && !next_vec)
               for (int q = V - m; q < V; ++q) store_elem<DT>(a.p.out[r], e + q, slot_elem<DT>(o, q));
@@ -754,8 +760,9 @@ bool plan_skew(const RankPtrs& p, int n, int64_t count, int algo, SkewArgs& s) {
     s.ib[r] = static_cast<const char*>(p.in[r]) - (i % 16);
   }
   // addresses that are all multiples of 4 bytes keep the one-front kernel with 16-byte accesses at 4-byte
-  // alignment, which measured faster (N = 8, 256 MiB of bf16, rank r at 2r elements: 938 us against 1,354 us)
-  return differ && (AR_SKEW_WORD_ALIGNED || !words);
+  // alignment, which measured faster (N = 8, 256 MiB of bf16, rank r at 2r elements: 922-924 us against 980-992 us
+  // with the skewed kernel at its current launch shape)
+  return differ && !words;
 }
 
 // ------------------------------------------------------------------------------------------ launch

@@ -13,7 +13,7 @@ CPU oracle timed on this host on the same inputs; and, beside the headline, ever
 buckets over 300 tensors, the fp8 codec and compressed ring) with its own algorithmic-bytes roofline.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--headline-only] [--fp8-only] [--copy-calibration]
-                       [--ring-bytes-per-rank S] [--sweep OUT.jsonl]
+                       [--ring-bytes-per-rank S] [--per-rank-offsets-only] [--sweep OUT.jsonl]
 """
 from __future__ import annotations
 
@@ -135,6 +135,7 @@ def copy_ceiling(torch, ins, outs, reps=10):
     ms = Timer(torch).run(lambda: dst.copy_(src), reps)
     nbytes = 2 * src.numel() * src.element_size()
     del src, dst
+    torch.cuda.empty_cache()  # later rank buffers must not be carved out of these segments (see sweep_points)
     return nbytes / (np.mean(ms) * 1e-3) / GB
 
 
@@ -150,6 +151,7 @@ def write_ceiling(torch, ins, reps=10):
     ms = Timer(torch).run(write, reps)
     nbytes = dst.numel() * dst.element_size()
     del dst
+    torch.cuda.empty_cache()
     return nbytes / (np.median(ms) * 1e-3) / GB
 
 
@@ -577,6 +579,10 @@ def sweep_points(torch, ar, dev, S, names, reps=20, graph_max=16 << 20):
     n = N_RANKS
     count = S // 4
     sets = int(min(64, max(1, -(-(1 << 30) // (2 * n * S)))))
+    # Every rank buffer its own allocation, as separate tensors normally are: rank buffers cut from one large cached
+    # segment sit at fixed physical strides, which measured 4-13% slower on MI355X (N = 8, 256 MiB fp32 per rank:
+    # 784-800 us separate, 815-820 us at a 256 MiB stride in one allocation, 890-896 us at 256 MiB + 2 MiB).
+    torch.cuda.empty_cache()
     g = torch.Generator(device=dev)
     g.manual_seed(4000 + int(np.log2(S)))
     bufs = [([torch.rand(count, generator=g, device=dev).mul_(2).sub_(1) for _ in range(n)],
@@ -650,6 +656,9 @@ def main():
                         "profiler runs)")
     p.add_argument("--ring-bytes-per-rank", type=int, metavar="S",
                    help="time only the ring on N = 8 fp32 ranks of S bytes each, sum (for profiler runs at one size)")
+    p.add_argument("--per-rank-offsets-only", action="store_true",
+                   help="time only the headline workload with rank r's buffers r elements past an aligned address "
+                        "(the skewed kernel; for profiler runs)")
     p.add_argument("--sweep", metavar="OUT.jsonl", help="run only the message-size sweep, one JSON line per point")
     p.add_argument("--sweep-max-log2", type=int, default=30)
     args = p.parse_args()
@@ -671,6 +680,24 @@ def main():
 
     if args.sweep:
         sweep(torch, ar, dev, args.sweep, max_log2=args.sweep_max_log2)
+        return
+
+    if args.per_rank_offsets_only:
+        g = torch.Generator(device=dev)
+        g.manual_seed(2)
+        vin = [torch.empty(COUNT + N_RANKS, dtype=torch.bfloat16, device=dev)[r:r + COUNT] for r in range(N_RANKS)]
+        vout = [torch.empty(COUNT + N_RANKS, dtype=torch.bfloat16, device=dev)[r:r + COUNT] for r in range(N_RANKS)]
+        for v in vin:
+            v.copy_(torch.randn(COUNT, generator=g, device=dev).mul_(1e-3))
+        step = lambda: ar.ar_allreduce(vin, vout, ar.AR_AVG, ar.AR_ALGO_RING)
+        for _ in range(args.warmup):
+            step()
+        torch.cuda.synchronize()
+        ms = Timer(torch).run(step, args.steps)
+        t = float(np.mean(ms)) * 1e-3
+        print(json.dumps({"ring_per_rank_offsets": {"kernel_us": stats_us(ms),
+                                                    "hbm_GBps": ring_bytes(N_RANKS, COUNT, 2) / t / GB,
+                                                    "steps": args.steps, "warmup": args.warmup}}))
         return
 
     if args.ring_bytes_per_rank:
