@@ -479,6 +479,7 @@ struct SkewArgs {
   // never wait on the vector loads of the data.
   int32_t im[AR_MAX_RANKS], om[AR_MAX_RANKS];
   const char* ib[AR_MAX_RANKS];
+  int strip;  // tiles per strip (set by the launcher)
 };
 static_assert(sizeof(SkewArgs) <= 4096, "kernel arguments must fit in 4 KiB");
 
@@ -570,13 +571,13 @@ __device__ __forceinline__ bool skew_vec_tile(const CollapsedArgs& a, int64_t w,
   return c == cl;
 }
 
-// A wave walks a strip of kSkewStrip consecutive tiles and carries the previous tile's results into the next, so
+// A wave walks a strip of consecutive tiles and carries the previous tile's results into the next, so
 // the output slot shared by two tiles of a strip is stored whole by the later one; only slots at the ends of a
 // strip (or next to an element-path tile) are stored element by element.
-#ifndef AR_SKEW_STRIP
-#define AR_SKEW_STRIP 8
-#endif
-constexpr int kSkewStrip = AR_SKEW_STRIP;
+// Strips are long (32 tiles) when every wave of the grid still gets several of them, else 8 tiles: each strip end
+// leaves one 16-byte slot per rank written in two parts by two waves, whose 2-byte stores each cost a partial-line
+// fill read (with strips of 8, FETCH_SIZE counted 3.3% more than the algorithmic reads on the 8 x 256 MiB bf16 case).
+constexpr int kSkewStripLong = 32, kSkewStripShort = 8;
 // Workgroups per CU, as a multiple of the one-pass kernels' count: each lane's shifts, lane exchanges and
 // assembled stores make a tile's work long enough that one wave per SIMD leaves the loads of the next tile waiting
 // on it; twice the waves hide that. N = 8, 256 MiB of bf16 per rank at odd per-rank offsets, one MI355X: 1,486 us
@@ -594,7 +595,8 @@ __global__ __launch_bounds__(kThreads) void skew_kernel(SkewArgs s) {
   const CollapsedArgs& a = s.f;
   const int lane = threadIdx.x & 63;
   const int64_t nwt = (a.count + 64 * V - 1) / (64 * V);
-  const int64_t nstrips = (nwt + kSkewStrip - 1) / kSkewStrip;
+  const int strip = s.strip;
+  const int64_t nstrips = (nwt + strip - 1) / strip;
   const int64_t nw = static_cast<int64_t>(gridDim.x) * (kThreads / 64);
   // the wave index in a scalar register, so that everything derived from it (tile, chunk, rank rotation, per-rank
   // pointers and shifts) is wave-uniform to the compiler too: scalar loads of the rank table, scalar branches on
@@ -604,12 +606,12 @@ __global__ __launch_bounds__(kThreads) void skew_kernel(SkewArgs s) {
     u32x4 prev = {0u, 0u, 0u, 0u};  // this lane's result in the previous tile of the strip
     bool prev_vec = false;           // the previous tile of the strip took the vector path
     int c = 0;
-    bool cur_vec = skew_vec_tile<V, NR>(a, sp * kSkewStrip, &c);
-    for (int k = 0; k < kSkewStrip; ++k) {
-      const int64_t w = sp * kSkewStrip + k;
+    bool cur_vec = skew_vec_tile<V, NR>(a, sp * strip, &c);
+    for (int k = 0; k < strip; ++k) {
+      const int64_t w = sp * strip + k;
       if (w >= nwt) break;
       int cn = 0;
-      const bool next_vec = k + 1 < kSkewStrip && skew_vec_tile<V, NR>(a, w + 1, &cn);
+      const bool next_vec = k + 1 < strip && skew_vec_tile<V, NR>(a, w + 1, &cn);
       const int64_t j = w * 64 + lane, e = j * V;
       if (cur_vec) {
         const int start = __builtin_amdgcn_readfirstlane(a.rot ? c : 0);
@@ -698,8 +700,11 @@ template <int DT, int OP, int NR, int SHAPE>
 hipError_t launch_skew(SkewArgs& s, hipStream_t st) {
   constexpr int V = Traits<DT>::kVec;
   const int64_t tiles = (s.f.count + 64 * V - 1) / (64 * V);
-  const int64_t strips = (tiles + kSkewStrip - 1) / kSkewStrip;
-  int64_t g = static_cast<int64_t>(cu_count()) * blocks_per_cu<NR>() * AR_SKEW_GRID_SCALE;
+  const int64_t gmax = static_cast<int64_t>(cu_count()) * blocks_per_cu<NR>() * AR_SKEW_GRID_SCALE;
+  // long strips once every wave of the full grid gets at least one
+  s.strip = tiles >= static_cast<int64_t>(kSkewStripLong) * gmax * (kThreads / 64) ? kSkewStripLong : kSkewStripShort;
+  const int64_t strips = (tiles + s.strip - 1) / s.strip;
+  int64_t g = gmax;
   const int64_t need = (strips + kThreads / 64 - 1) / (kThreads / 64);
   if (g > need) g = need;
   if (g < 1) g = 1;

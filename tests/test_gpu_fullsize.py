@@ -1,8 +1,10 @@
 """GPU parity at the workloads' full sizes, in the launch configuration the benchmark times, against the oracle.
 
 - headline: 8 ranks x 134,217,728 bf16 (256 MiB each), fp32 ring-order sum, /8, bf16 out: every element of
-  every rank, bit for bit; the same inputs through reduce-scatter + all-gather and through the binomial tree.
-- compressed ring: 8 ranks x 67,108,864 bf16 with 0.1% outliers x100, E4M3 blocks of 128: every element.
+  every rank, bit for bit; the same inputs through reduce-scatter + all-gather and through the binomial tree, and
+  with every rank's input and output at its own odd element offset (the skewed kernel), ring and tree.
+- compressed ring: 8 ranks x 67,108,864 bf16 with 0.1% outliers x100, E4M3 blocks of 128: every element; and
+  8 ranks x (67,108,864 + 13) fp32 with avg (chunk starts off the 16-byte grid).
 - beyond 2^31 elements: 3 ranks x (2^31 + 1001) bf16 in place (ring, tree, rank order, a common offset and
   per-rank offsets), sampled against the oracle.
 - largest sweep point: 8 ranks x 268,435,456 fp32 (1 GiB each): ring and ring-stepwise, every element; the
@@ -62,6 +64,28 @@ def test_headline_eight_ranks_256MiB_bf16_avg():
     _same_on_all_ranks(outs)
     for r in range(n):
         np.testing.assert_array_equal(_down_bits(outs[r]), want[r])
+
+
+@pytest.mark.timeout(600)
+def test_headline_size_at_odd_per_rank_offsets():
+    """The headline workload with rank r's input r elements and its output 2r + 1 elements past an aligned address:
+    the skewed kernel at the size where it walks long strips (32 tiles per wave), in ring order and as the binomial
+    tree, every element of every rank against the oracle."""
+    n, count = 8, 134_217_728
+    host = _par(lambda r: inputs.normal_bf16((2, r), count), range(n))
+    ibase = [torch.empty(count + 16, dtype=torch.bfloat16, device=DEV) for _ in range(n)]
+    obase = [torch.empty(count + 16, dtype=torch.bfloat16, device=DEV) for _ in range(n)]
+    ins = [b[r:r + count] for r, b in enumerate(ibase)]
+    outs = [b[2 * r + 1:2 * r + 1 + count] for r, b in enumerate(obase)]
+    for t, h in zip(ins, _up(host, torch.bfloat16)):
+        t.copy_(h)
+    torch.cuda.synchronize()
+    for algo, fn in ((ar.AR_ALGO_RING, oracle.ring_allreduce), (ar.AR_ALGO_TREE, oracle.tree_allreduce)):
+        ar.ar_allreduce(ins, outs, ar.AR_AVG, algo)
+        torch.cuda.synchronize()
+        want = fn(host, oracle.BF16, oracle.AVG)
+        for r in range(n):
+            np.testing.assert_array_equal(_down_bits(outs[r]), want[r], err_msg=f"algo {algo} rank {r}")
 
 
 @pytest.mark.timeout(600)
@@ -162,6 +186,26 @@ def test_fp8_ring_eight_ranks_128MiB_bf16():
         exact += oracle.bf16_to_f32(h)
     got = oracle.bf16_to_f32(want[0]).astype(np.float64)
     print(f"fp8 ring: max |err| = {np.max(np.abs(got - exact)):.3e}, mean |exact| = {np.mean(np.abs(exact)):.3e}")
+
+
+@pytest.mark.timeout(600)
+def test_fp8_ring_eight_ranks_fp32_avg_ragged():
+    """The compressed ring on fp32 inputs with avg, at the same element count plus 13 (chunk starts off the 16-byte
+    grid, so the shifted fp32 vector path and its lane-assembled stores run at scale): every element of the first
+    and last rank, and all ranks equal."""
+    n, count = 8, 67_108_864 + 13
+    host = _par(lambda r: inputs.normal_f32((5, r, 32), count, 1e-3), range(n))
+    for h in host:
+        h[::997] *= np.float32(100)
+    ins = _up(host, torch.float32)
+    outs = [torch.empty_like(t) for t in ins]
+    ar.ar_allreduce(ins, outs, ar.AR_AVG, ar.AR_ALGO_RING_FP8)
+    torch.cuda.synchronize()
+    del ins
+    want = oracle.fp8_ring_allreduce(host, oracle.F32, oracle.AVG)
+    _same_on_all_ranks(outs)
+    np.testing.assert_array_equal(_down_bits(outs[0]), np.asarray(want[0]).view(np.uint32))
+    np.testing.assert_array_equal(_down_bits(outs[n - 1]), np.asarray(want[n - 1]).view(np.uint32))
 
 
 @pytest.mark.timeout(900)
