@@ -243,6 +243,28 @@ __device__ __forceinline__ void finish(float (&p)[kPerLane], int n) {
   for (int e = 0; e < kPerLane; ++e) p[e] = d[e] * s.scale;
 }
 
+// Lane i (> 0) receives lane i - 1's x; lane 0 keeps `first` (a DPP wave shift right by one lane: one VALU operation
+// per dword, no LDS traffic). All 64 lanes of the wave must be active.
+__device__ __forceinline__ u32x4 from_prev_lane(const u32x4& x, const u32x4& first) {
+  u32x4 r;
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+    r[i] = static_cast<uint32_t>(__builtin_amdgcn_update_dpp(static_cast<int>(first[i]), static_cast<int>(x[i]),
+                                                             0x138 /* wave_shr:1 */, 0xF, 0xF, false));
+  return r;
+}
+
+// Lane i (< 63) receives lane i + 1's x; lane 63 keeps `last` (a DPP wave shift left by one lane). All 64 lanes of
+// the wave must be active.
+__device__ __forceinline__ u32x4 from_next_lane(const u32x4& x, const u32x4& last) {
+  u32x4 r;
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+    r[i] = static_cast<uint32_t>(__builtin_amdgcn_update_dpp(static_cast<int>(last[i]), static_cast<int>(x[i]),
+                                                             0x130 /* wave_shl:1 */, 0xF, 0xF, false));
+  return r;
+}
+
 // 8 elements of a 16-byte bf16 slot, or of two fp32 slots, already loaded.
 template <int DT> struct Raw8;
 template <> struct Raw8<AR_BF16> {
@@ -267,9 +289,10 @@ template <> struct Raw8<AR_F32> {
 
 // bf16 chunks that start m elements past the 16-byte grid (0 < m < 8: counts that are not a multiple of 8 N).
 // Every lane's 8 elements then sit m elements into the aligned slot at A = e0 - m, with the same m across the
-// wave task (it never spans two chunks). The lane loads the aligned slots at A and A + 8 and shifts; after the
-// fold, the aligned output slot [A + 8, A + 16) holds the lane's last m elements and the next lane's first 8 - m
-// (a lane shuffle), so every store is one aligned 16-byte store except at the edges of a strip of tasks.
+// wave task (it never spans two chunks). The lane loads the aligned slot at A, takes the one at A + 8 from the
+// next lane (whose A it is) and shifts; after the fold, the aligned output slot [A, A + 8) holds the previous
+// lane's last m elements and this lane's first 8 - m, so every store is one aligned 16-byte store except at the
+// edges of a strip of tasks.
 template <int M, int NR>
 __device__ __forceinline__ void shift_ranks(const u32x4 (&x0)[NR], const u32x4 (&x1)[NR], u32x4 (&w)[NR]) {
 #pragma unroll
@@ -390,7 +413,7 @@ __global__ __launch_bounds__(kThreads) void fp8_ring_kernel(Fp8RingArgs a) {
         for (int r = 0; r < NR; ++r) store8<DT>(a.p.out[r], e0, kPerLane, true, p);
       } else if (shifted && DT == AR_F32) {
         // fp32: a lane's 8 elements start m (1..3) past the grid and span three aligned slots. The slot wholly
-        // inside the lane ([A + 4, A + 8)) is stored as it is; the one above takes the next lane's first 4 - m.
+        // inside the lane ([A + 4, A + 8)) is stored as it is; the one at A takes the previous lane's last m.
         constexpr int NT = NR > 0 ? NR : 1;
         const int64_t A = e0 - mis;  // a multiple of 4 elements; A + 12 <= count, so all three slots are in the buffer
         u32x4 x0[NT], x1[NT], x2[NT];
@@ -401,8 +424,12 @@ __global__ __launch_bounds__(kThreads) void fp8_ring_kernel(Fp8RingArgs a) {
           const float* base = static_cast<const float*>(a.p.in[rr]) + A;
           x0[k] = ld16(base);
           x1[k] = ld16(base + 4);
-          x2[k] = ld16(base + 8);
+          // the third slot is the next lane's first one: only the last lane loads it
+          x2[k] = u32x4{0u, 0u, 0u, 0u};
+          if (lane == 63) x2[k] = ld16(base + 8);
         }
+#pragma unroll
+        for (int k = 0; k < NT; ++k) x2[k] = from_next_lane(x0[k], x2[k]);
         auto widen8 = [&](int k, float (&v)[kPerLane]) {
           const u32x4 lo4 = shift4_by(mis, x0[k], x1[k]), hi4 = shift4_by(mis, x1[k], x2[k]);
 #pragma unroll
@@ -419,30 +446,24 @@ __global__ __launch_bounds__(kThreads) void fp8_ring_kernel(Fp8RingArgs a) {
           hop(p, own);
         }
         finish<OP>(p, NT);
-        u32x4 o0, o1, nx0, last;  // our two halves; the next lane's first half; the previous task's last lane
+        u32x4 o0, o1, last;  // our two halves; the previous task's last lane (its upper half)
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
           o0[i] = __float_as_uint(p[i]);
           o1[i] = __float_as_uint(p[i + 4]);
+          last[i] = static_cast<uint32_t>(__builtin_amdgcn_readlane(static_cast<int>(prev[i]), 63));
         }
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          nx0[i] = static_cast<uint32_t>(__shfl_down(static_cast<int>(o0[i]), 1));
-          last[i] = static_cast<uint32_t>(__shfl(static_cast<int>(prev[i]), 63));
-        }
+        const u32x4 pv1 = from_prev_lane(o1, last);      // lane i: lane i - 1's upper half; lane 0: `last`
+        const u32x4 low = shift4_by(4 - mis, pv1, o0);  // [A, A + 4): the previous lane's last m, then our first
         const u32x4 mid = shift4_by(4 - mis, o0, o1);   // [A + 4, A + 8)
-        const u32x4 up = shift4_by(4 - mis, o1, nx0);   // [A + 8, A + 12): our last m, the next lane's first 4 - m
-        const u32x4 low = shift4_by(4 - mis, last, o0); // [A, A + 4): the previous task's last m, then our first
 #pragma unroll
         for (int r = 0; r < NT; ++r) {
           float* out = static_cast<float*>(a.p.out[r]);
+          // both of a lane's aligned slots, each in one store instruction for the whole wave
+          if (lane > 0 || carried) st16(out + A, low);
+          else  // [A + m, A + 4): the rest of the slot below belongs to the previous task
+            for (int q = 0; q < 4 - mis; ++q) store_elem<AR_F32>(out, e0 + q, __float_as_uint(p[q]));
           st16(out + A + 4, mid);
-          if (lane < 63) st16(out + A + 8, up);
-          if (lane == 0) {
-            if (carried) st16(out + A, low);
-            else  // [A + m, A + 4): the rest of the slot below belongs to the previous task
-              for (int q = 0; q < 4 - mis; ++q) store_elem<AR_F32>(out, e0 + q, __float_as_uint(p[q]));
-          }
           if (lane == 63 && !next_shifted)  // [A + 8, A + 8 + m): the rest of the slot above is the next task's
             for (int q = 8 - mis; q < kPerLane; ++q) store_elem<AR_F32>(out, e0 + q, __float_as_uint(p[q]));
         }
@@ -456,8 +477,12 @@ __global__ __launch_bounds__(kThreads) void fp8_ring_kernel(Fp8RingArgs a) {
           int rr = start + k;
           rr = rr >= NT ? rr - NT : rr;
           x0[k] = ld16(static_cast<const uint16_t*>(a.p.in[rr]) + A);
-          x1[k] = ld16(static_cast<const uint16_t*>(a.p.in[rr]) + A + 8);
+          // the upper slot is the next lane's lower one: only the last lane loads it
+          x1[k] = u32x4{0u, 0u, 0u, 0u};
+          if (lane == 63) x1[k] = ld16(static_cast<const uint16_t*>(a.p.in[rr]) + A + 8);
         }
+#pragma unroll
+        for (int k = 0; k < NT; ++k) x1[k] = from_next_lane(x0[k], x1[k]);
         shift_ranks_by<NT>(mis, x0, x1, w);
         Slot<AR_BF16>::unpack(w[0], p);
 #pragma unroll
@@ -468,24 +493,20 @@ __global__ __launch_bounds__(kThreads) void fp8_ring_kernel(Fp8RingArgs a) {
         }
         finish<OP>(p, NT);
         const u32x4 o = Slot<AR_BF16>::pack(p);
-        u32x4 nx, last;  // the next lane's result; the previous task's last lane
+        u32x4 last;  // the previous task's last lane
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          nx[i] = static_cast<uint32_t>(__shfl_down(static_cast<int>(o[i]), 1));
-          last[i] = static_cast<uint32_t>(__shfl(static_cast<int>(prev[i]), 63));
-        }
-        u32x4 one[1] = {o}, two[1] = {nx}, slot[1], lst[1] = {last}, low[1];
-        shift_ranks_by<1>(8 - mis, one, two, slot);  // slot [A + 8, A + 16): our last m, the next lane's first 8 - m
-        shift_ranks_by<1>(8 - mis, lst, one, low);   // slot [A, A + 8): the previous task's last m, then our first
+        for (int i = 0; i < 4; ++i)
+          last[i] = static_cast<uint32_t>(__builtin_amdgcn_readlane(static_cast<int>(prev[i]), 63));
+        // slot [A, A + 8): the previous lane's last m, then our first 8 - m (lane 0: the previous task's last lane)
+        u32x4 pv[1] = {from_prev_lane(o, last)}, one[1] = {o}, low[1];
+        shift_ranks_by<1>(8 - mis, pv, one, low);
 #pragma unroll
         for (int r = 0; r < NT; ++r) {
           uint16_t* out = static_cast<uint16_t*>(a.p.out[r]);
-          if (lane < 63) st16(out + A + 8, slot[0]);
-          if (lane == 0) {
-            if (carried) st16(out + A, low[0]);
-            else  // [A + m, A + 8): the rest of the slot below belongs to the previous task
-              for (int q = 0; q < 8 - mis; ++q) store_elem<AR_BF16>(out, e0 + q, narrow<AR_BF16>(p[q]));
-          }
+          // the wave's slots of this rank in one store instruction over whole lines
+          if (lane > 0 || carried) st16(out + A, low[0]);
+          else  // [A + m, A + 8): the rest of the slot below belongs to the previous task
+            for (int q = 0; q < 8 - mis; ++q) store_elem<AR_BF16>(out, e0 + q, narrow<AR_BF16>(p[q]));
           if (lane == 63 && !next_shifted)  // [A + 8, A + 8 + m): the rest of the slot above is the next task's
             for (int q = 8 - mis; q < kPerLane; ++q) store_elem<AR_BF16>(out, e0 + q, narrow<AR_BF16>(p[q]));
         }
