@@ -74,6 +74,8 @@ def lib():
         L.oracle_fp8_quant.restype = i32
         L.oracle_fp8_dequant.argtypes = [vp, vp, i64, vp, i32]
         L.oracle_fp8_dequant.restype = i32
+        L.oracle_epilogue.argtypes = [vp, vp, i64, i32, i32, i32]
+        L.oracle_epilogue.restype = i32
         L.oracle_bucket_plan.argtypes = [vp, i32, i32, i32, i64, vp, vp, vp, ctypes.POINTER(ctypes.c_int)]
         L.oracle_bucket_plan.restype = i32
         L.oracle_bucketed_allreduce.argtypes = [pp, pp, i32, i32, vp, i32, i32, i64]
@@ -219,6 +221,15 @@ def fp8_dequant(codes, scales, dtype=F32):
     out = np.empty(codes.size, dtype=NP_DTYPE[dtype])
     _check(lib().oracle_fp8_dequant(codes.ctypes.data, scales.ctypes.data, codes.size, out.ctypes.data, dtype),
            "fp8_dequant")
+    return out
+
+
+def epilogue(acc, dtype=F32, op=SUM, n=1):
+    """The owner's finishing step on fp32 partial results (int32 for I32): avg divides by n, then the value is
+    rounded into `dtype`."""
+    acc = np.ascontiguousarray(acc, dtype=np.int32 if dtype == I32 else np.float32)
+    out = np.empty(acc.size, dtype=NP_DTYPE[dtype])
+    _check(lib().oracle_epilogue(acc.ctypes.data, out.ctypes.data, acc.size, dtype, op, n), "epilogue")
     return out
 
 

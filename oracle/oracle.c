@@ -249,6 +249,16 @@ static int check_common(int n, int64_t count, int dt, int op) {
     return OR_OK;
 }
 
+/* The owner's epilogue on its own ([W] "Ring AllReduce", end of 阶段一: each rank then holds one fully
+ * reduced chunk; avg: [W] "在 DDP 中的角色"): out[e] = finalize(acc[e]) rounded into dt. acc holds fp32
+ * partial results (int32 for OT_I32), one per element; out holds count elements of dt. */
+int oracle_epilogue(const uint32_t* acc, void* out, int64_t count, int dt, int op, int n) {
+    if (check_common(n, count, dt, op)) return OR_BAD;
+    int isint = dt == OT_I32;
+    for (int64_t e = 0; e < count; ++e) narrow_store(out, dt, e, finalize(acc[e], isint, op, n));
+    return OR_OK;
+}
+
 static uint32_t** alloc_work(int n, int64_t count) {
     uint32_t** w = (uint32_t**)calloc((size_t)n, sizeof(uint32_t*));
     if (!w) return NULL;

@@ -59,6 +59,8 @@ MUTANTS = {
     "bucket counts left unpadded": [("bucket_count[b] = (fill + g * n - 1) / (g * n) * (g * n);",
                                      "bucket_count[b] = fill;", 2)],
     "bucket closed when it reaches the cap": [("(fill + pad) * es > cap_bytes", "(fill + pad) * es >= cap_bytes", 1)],
+    "standalone epilogue skips the average": [("narrow_store(out, dt, e, finalize(acc[e], isint, op, n));",
+                                               "narrow_store(out, dt, e, acc[e]);", 1)],
 }
 
 

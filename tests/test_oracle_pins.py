@@ -364,6 +364,35 @@ def test_f16_matches_numpy_conversion():
     assert np.all(np.isnan(got[~ok]))
 
 
+@pytest.mark.parametrize("n", [1, 2, 3, 7, 64])
+def test_epilogue_is_one_division_then_one_rounding(n):
+    """The owner's finishing step on its own: avg is one fp32 division by n (numpy's IEEE quotient), then one
+    rounding into the storage type (torch's bf16 conversion, numpy's f16 conversion); the other ops pass the value
+    through; NaN becomes the canonical pattern; int32 avg truncates toward zero."""
+    x = _special_f32()
+    with np.errstate(over="ignore", under="ignore"):
+        q = (x / np.float32(n)).astype(np.float32)
+    for op in (oracle.SUM, oracle.AVG, oracle.MIN, oracle.MAX):
+        v = q if op == oracle.AVG else x
+        np.testing.assert_array_equal(oracle.epilogue(x, oracle.F32, op, n).view(np.uint32), v.view(np.uint32))
+        want_bf = torch.from_numpy(v.copy()).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+        np.testing.assert_array_equal(oracle.epilogue(x, oracle.BF16, op, n), want_bf)
+        with np.errstate(over="ignore"):
+            want_h = v.astype(np.float16).view(np.uint16)
+        np.testing.assert_array_equal(oracle.epilogue(x, oracle.F16, op, n), want_h)
+    nans = np.array([0x7FC00000, 0xFFC00000, 0x7F800001, 0xFFFFFFFF, 0x7FA00000], np.uint32).view(np.float32)
+    for op in (oracle.SUM, oracle.AVG):
+        assert np.all(oracle.epilogue(nans, oracle.BF16, op, n) == 0x7FC0)
+        assert np.all(oracle.epilogue(nans, oracle.F16, op, n) == 0x7E00)
+    rng = np.random.default_rng(11)
+    i = np.concatenate([np.array([0, 1, -1, n - 1, -(n - 1), n, -n, 2 ** 31 - 1, -2 ** 31], np.int64),
+                        rng.integers(-2 ** 31, 2 ** 31, 10_000)]).astype(np.int32)
+    wide = i.astype(np.int64)
+    trunc = np.where(wide < 0, -((-wide) // n), wide // n).astype(np.int32)
+    np.testing.assert_array_equal(oracle.epilogue(i, oracle.I32, oracle.AVG, n), trunc)
+    np.testing.assert_array_equal(oracle.epilogue(i, oracle.I32, oracle.SUM, n), i)
+
+
 def test_e4m3_fixed_points():
     with open(os.path.join(GOLDEN, "e4m3_points.txt")) as f:
         rows = [ln.split() for ln in f if ln.strip() and not ln.startswith("#")]
