@@ -88,6 +88,7 @@ def lib():
         L.ar_fp8_dequant.argtypes = [vp, vp, sz, vp, i32, vp]
         L.ar_auto_algo.argtypes = [i32, sz, i32]
         L.ar_chunk_bounds.argtypes = [i32, sz, vp]
+        L.ar_epilogue.argtypes = [vp, vp, sz, i32, i32, i32, vp]
         L.ar_status_string.argtypes = [i32]
         L.ar_status_string.restype = ctypes.c_char_p
         L.ar_last_call.argtypes = [ctypes.POINTER(_CallRecord)]
@@ -95,7 +96,7 @@ def lib():
                      "ar_allreduce_buckets",
                      "ar_allreduce_tensors", "ar_reduce_scatter", "ar_all_gather", "ar_bucket_plan", "ar_bucket_pack",
                      "ar_bucket_unpack", "ar_fp8_quant", "ar_fp8_dequant", "ar_last_call", "ar_version",
-                     "ar_auto_algo", "ar_chunk_bounds"):
+                     "ar_auto_algo", "ar_chunk_bounds", "ar_epilogue"):
             getattr(L, name).restype = i32
         _lib = L
     return _lib
@@ -370,6 +371,20 @@ def ar_fp8_dequant(codes, scales, out, stream=None):
         _check(lib().ar_fp8_dequant(ctypes.c_void_p(codes.data_ptr()), ctypes.c_void_p(scales.data_ptr()),
                                     out.numel(), ctypes.c_void_p(out.data_ptr()), dtype_code(out.dtype),
                                     _stream(stream, dev)), "ar_fp8_dequant")
+
+
+def ar_epilogue(acc, out, op=AR_SUM, nranks=1, stream=None):
+    """acc: float32 GPU tensor of partial results (int32 when `out` is int32); out: GPU tensor of as many elements,
+    whose dtype is the output type (may be acc itself for float32/int32)."""
+    import torch
+    dev = _gpu_tensor(acc, "acc").device
+    _gpu_tensor(out, "out", None, dev)
+    _gpu_tensor(acc, "acc", torch.int32 if out.dtype == torch.int32 else torch.float32)
+    if out.numel() != acc.numel():
+        raise ValueError("acc and out must hold the same number of elements")
+    with _on(dev):
+        _check(lib().ar_epilogue(ctypes.c_void_p(acc.data_ptr()), ctypes.c_void_p(out.data_ptr()), acc.numel(),
+                                 dtype_code(out.dtype), op, nranks, _stream(stream, dev)), "ar_epilogue")
 
 
 def ar_auto_algo(nranks, count, dtype) -> int:

@@ -24,7 +24,8 @@ CEILING_SRC = "ar_ceiling.hip"
 CEILING_LIB = os.path.join(HERE, "libar_ceiling.so")
 ARCH = "gfx950"
 
-SOURCES = ["ar_api.hip", "ar_collapsed.hip", "ar_stepwise.hip", "ar_bucket.hip", "ar_fp8.hip", "ar_tensors.hip", "ar_rsag.hip"]
+SOURCES = ["ar_api.hip", "ar_collapsed.hip", "ar_stepwise.hip", "ar_bucket.hip", "ar_fp8.hip", "ar_tensors.hip",
+           "ar_rsag.hip", "ar_epilogue.hip"]
 # ar_collapsed.hip holds several hundred kernel instances; it is compiled once per element type (AR_F32 = 0 ..
 # AR_I32 = 3) and per build of its launch shape and load policy (AR_COLLAPSED_LARGE = 0, 1), so the eight parts
 # build in parallel.

@@ -5,6 +5,8 @@
 #include <algorithm>
 #include <atomic>
 #include <cstdint>
+#include <cstdio>
+#include <cstdlib>
 #include <cstring>
 #include <mutex>
 
@@ -98,6 +100,16 @@ thread_local ar_call_record g_last;
 thread_local bool g_has_last = false;
 thread_local uint64_t g_seq = 0;
 
+// AR_LOG set to anything but "" or "0" in the environment (read once, at the first call): one line per call on
+// stderr, written when the call returns (its work may still be queued).
+bool log_calls() {
+  static const bool on = [] {
+    const char* v = std::getenv("AR_LOG");
+    return v != nullptr && v[0] != '\0' && std::strcmp(v, "0") != 0;
+  }();
+  return on;
+}
+
 int finish(const char* entry, int nranks, size_t count, int dtype, int op, int algo, int status) {
   g_last.seq = ++g_seq;
   g_last.entry = entry;
@@ -108,6 +120,9 @@ int finish(const char* entry, int nranks, size_t count, int dtype, int op, int a
   g_last.algo = algo;
   g_last.status = status;
   g_has_last = true;
+  if (log_calls())
+    std::fprintf(stderr, "ar: seq=%llu %s nranks=%d count=%zu dtype=%d op=%d algo=%d status=%d\n",
+                 static_cast<unsigned long long>(g_last.seq), entry, nranks, count, dtype, op, algo, status);
   return status;
 }
 
@@ -279,6 +294,24 @@ int ar_all_gather(const void* const* in_bufs, void* const* out_bufs, int nranks,
                   void* stream) {
   return rsag_impl("ar_all_gather", const_cast<const void* const*>(out_bufs), in_bufs, nranks, count, dtype, AR_SUM,
                    false, out_bufs, nullptr, stream);
+}
+
+int ar_epilogue(const void* acc, void* out, size_t count, int dtype, int op, int nranks, void* stream) {
+  auto done = [&](int st) { return finish("ar_epilogue", nranks, count, dtype, op, -1, st); };
+  if (!valid_dtype(dtype) || !valid_op(op) || nranks < 1 || nranks > AR_MAX_RANKS) return done(AR_ERR_INVALID);
+  if (count == 0) return done(AR_OK);
+  if (!acc || !out || count > (SIZE_MAX / 2) / 4) return done(AR_ERR_INVALID);
+  const size_t es = static_cast<size_t>(esize_of(dtype));
+  const uintptr_t a = reinterpret_cast<uintptr_t>(acc), o = reinterpret_cast<uintptr_t>(out);
+  if (a % 4 != 0 || o % es != 0) return done(AR_ERR_INVALID);
+  if (a > UINTPTR_MAX - 4 * count || o > UINTPTR_MAX - es * count) return done(AR_ERR_INVALID);
+  // in place only element for element (4-byte types); a 2-byte output over its own partials would overwrite
+  // partials other threads have not read yet
+  const bool in_place = a == o && es == 4;
+  if (!in_place && a < o + es * count && o < a + 4 * count) return done(AR_ERR_ALIAS);
+  const hipError_t e = ar::launch_epilogue(acc, out, static_cast<int64_t>(count), dtype, op, nranks,
+                                           static_cast<hipStream_t>(stream));
+  return done(e == hipSuccess ? AR_OK : AR_ERR_HIP);
 }
 
 int ar_version(void) { return AR_VERSION; }

@@ -84,6 +84,9 @@ hipError_t launch_tree_stepwise(const RankPtrs& p, int n, int64_t count, int dty
 // Batched copy with zero padding (bucket pack/unpack).
 hipError_t launch_batched_copy(const ar_copy_desc* d_descs, int ndescs, int esize, hipStream_t s);
 
+// The owner's epilogue over `count` fp32 partials (int32 for AR_I32) at acc (4-byte aligned), into out.
+hipError_t launch_epilogue(const void* acc, void* out, int64_t count, int dtype, int op, int n, hipStream_t s);
+
 // FP8 E4M3 block codec and the compressed ring.
 hipError_t launch_fp8_quant(const void* in, int dtype, int64_t count, uint8_t* codes, float* scales, hipStream_t s);
 hipError_t launch_fp8_dequant(const uint8_t* codes, const float* scales, int64_t count, void* out, int dtype,

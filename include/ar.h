@@ -30,6 +30,8 @@
  *   - AR_MIN / AR_MAX on floats: any NaN gives the quiet NaN 0x7FC00000 (bf16 0x7FC0, f16 0x7E00), and -0
  *     orders below +0. Rounding to bf16/f16 maps every NaN to those same canonical patterns.
  *   - All calls are re-entrant. The only state is a per-thread record of the last call (ar_last_call).
+ *   - With AR_LOG set in the environment (to anything but "" or "0"; read at the first call), every call prints
+ *     one line with its ar_call_record fields to stderr as it returns.
  */
 #ifndef AR_H
 #define AR_H
@@ -175,6 +177,19 @@ int ar_reduce_scatter(const void* const* in_bufs, void* const* out_bufs, int nra
  *     in_bufs[r] == out_bufs[r] + (start of chunk r); any other overlap -> AR_ERR_ALIAS. */
 int ar_all_gather(const void* const* in_bufs, void* const* out_bufs, int nranks, size_t count, int dtype,
                   void* stream);
+
+/* The owner's epilogue on its own ([W] "Ring AllReduce", end of 阶段一 Reduce-Scatter: each rank then holds one
+ * fully reduced chunk, which its owner finishes; the average: [W] "在 DDP 中的角色"). For e < count:
+ * out[e] = round_dtype(finalize(acc[e])), where finalize divides by nranks for AR_AVG (the rule above) and passes
+ * the value through for the other ops, and round_dtype is the rounding every entry point applies to its results
+ * (nearest even, canonical NaN; none for AR_F32 and AR_I32). The all-reduce kernels apply the same two functions
+ * in registers; this call applies them to partial results in memory.
+ *   acc: device pointer to `count` fp32 values (int32 when dtype is AR_I32), 4-byte aligned.
+ *   out: device pointer to `count` elements of dtype, aligned to the element size. In place (out == acc) only
+ *     when dtype is 4 bytes wide; any other overlap -> AR_ERR_ALIAS.
+ *   nranks: the divisor of AR_AVG, 1..AR_MAX_RANKS.
+ * Errors: AR_ERR_INVALID (enum, nranks, NULL, alignment), AR_ERR_ALIAS, AR_ERR_HIP. count == 0 enqueues nothing. */
+int ar_epilogue(const void* acc, void* out, size_t count, int dtype, int op, int nranks, void* stream);
 
 /* Bytes of device workspace ar_allreduce_ws needs for this call (0 when none). Host only, no HIP call. Only the
  * round-per-launch schedules on bf16/f16 need any: [W] "Ring AllReduce" (阶段一 Reduce-Scatter) has every round

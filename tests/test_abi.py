@@ -380,3 +380,55 @@ def test_binding_checks_codec_and_descriptor_tensors():
                                 2, 2, ar.AR_F32)
     with pytest.raises(ValueError, match=r"\[ndescs, 4\]"):
         ar.ar_bucket_pack(_StubTensor(12, torch.int64, shape=(3, 4, 1)), ar.AR_F32)
+
+
+def test_epilogue_validation():
+    L = ar.lib()
+    base = 0x20000000
+
+    def ep(acc, out, count, dt=ar.AR_BF16, op=ar.AR_SUM, n=1):
+        return L.ar_epilogue(ctypes.c_void_p(acc) if acc else None, ctypes.c_void_p(out) if out else None, count,
+                             dt, op, n, None)
+
+    assert ep(None, None, 0) == ar.AR_OK  # nothing to do, nothing enqueued
+    assert ep(base, base + 4096, 10, dt=7) == ar.AR_ERR_INVALID
+    assert ep(base, base + 4096, 10, op=9) == ar.AR_ERR_INVALID
+    assert ep(base, base + 4096, 10, n=0) == ar.AR_ERR_INVALID
+    assert ep(base, base + 4096, 10, n=65) == ar.AR_ERR_INVALID
+    assert ep(None, base + 4096, 10) == ar.AR_ERR_INVALID
+    assert ep(base, None, 10) == ar.AR_ERR_INVALID
+    assert ep(base + 2, base + 4096, 10) == ar.AR_ERR_INVALID  # partials not 4-byte aligned
+    assert ep(base, base + 4097, 10) == ar.AR_ERR_INVALID  # bf16 output at an odd address
+    assert ep(base, base + 4098, 10, dt=ar.AR_F32) == ar.AR_ERR_INVALID
+    # in place only for 4-byte outputs; any other overlap is rejected
+    assert ep(base, base, 10) == ar.AR_ERR_ALIAS
+    assert ep(base, base + 38, 10) == ar.AR_ERR_ALIAS
+    assert ep(base + 16, base, 10) == ar.AR_ERR_ALIAS
+    assert ep(base, base + 36, 10, dt=ar.AR_F32) == ar.AR_ERR_ALIAS
+    rec = ar.ar_last_call()
+    assert rec["entry"] == "ar_epilogue" and rec["count"] == 10 and rec["dtype"] == ar.AR_F32
+    assert rec["status"] == ar.AR_ERR_ALIAS
+
+
+def test_ar_log_prints_one_line_per_call():
+    import subprocess
+    import sys
+    code = ("import all_reduce_reduction_ring_amd as ar\n"
+            "L = ar.lib()\n"
+            "L.ar_allreduce(None, None, 2, 10, 7, 0, 0, None)\n"
+            "L.ar_epilogue(None, None, 0, 1, 1, 4, None)\n"
+            "ar.ar_bucket_plan([10, 20], ar.AR_F32, 2)\n")
+    for value, lines in (("1", 3), ("0", 0), ("", 0), (None, 0)):
+        env = dict(os.environ)
+        env.pop("AR_LOG", None)
+        if value is not None:
+            env["AR_LOG"] = value
+        r = subprocess.run([sys.executable, "-c", code], cwd=ROOT, env=env, capture_output=True, text=True,
+                           timeout=120)
+        assert r.returncode == 0, r.stderr
+        got = [ln for ln in r.stderr.splitlines() if ln.startswith("ar: ")]
+        assert len(got) == lines, (value, r.stderr)
+        if lines:
+            assert got[0] == "ar: seq=1 ar_allreduce nranks=2 count=10 dtype=7 op=0 algo=0 status=1"
+            assert got[1] == "ar: seq=2 ar_epilogue nranks=4 count=0 dtype=1 op=1 algo=-1 status=0"
+            assert got[2].startswith("ar: seq=3 ar_bucket_plan nranks=2 count=2 ") and got[2].endswith("status=0")
