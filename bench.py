@@ -364,6 +364,17 @@ def other_rows(torch, ar, inputs, ins, outs, dev, reps, host):
     rows["all_gather"] = row_entry("all_gather", timer.run(fn, reps), (N_RANKS + 1) * S, S, N_RANKS,
                                    factor=(N_RANKS - 1) / N_RANKS)
     del parts
+    # the owner's epilogue on its own (ar_epilogue): one rank's count of fp32 partials -> avg by N -> bf16, 4 bytes
+    # read and 2 written per element; no link traffic, so no busbw
+    acc = ins[0].float()
+    fn = lambda: ar.ar_epilogue(acc, outs[0], ar.AR_AVG, N_RANKS)
+    fn()
+    rows["epilogue"] = row_entry("epilogue", timer.run(fn, reps), 6 * COUNT, S, 1, {"count": COUNT}, factor=0.0)
+    n_s = COUNT // N_RANKS
+    acc_h = _o.bf16_to_f32(host[0][:n_s])
+    rows["epilogue"]["cpu_oracle"] = cpu_row(oracle_time(_o.epilogue, acc_h, _o.BF16, _o.AVG, N_RANKS), n_s * 2, 1,
+                                             f"the first {n_s:,} fp32 partials of one rank, one call")
+    del acc, acc_h
     ws = torch.empty(ar.ar_allreduce_workspace_size(N_RANKS, COUNT, ar.AR_BF16, ar.AR_AVG, ar.AR_ALGO_RING_STEPWISE),
                      dtype=torch.uint8, device=dev)
     levels = int(np.ceil(np.log2(N_RANKS)))
