@@ -145,7 +145,8 @@ int ar_chunk_bounds(int nranks, size_t count, int64_t* lo);
  *   multiple of 256 bytes (buffers of 1 MiB or more) or of 16 bytes, the rest in vectors. Pointers that differ
  *   modulo 16 but are all multiples of 4 use vectors from element 0 (slower: they straddle cache lines). 2-byte
  *   types at odd per-rank offsets use aligned vectors shifted per rank for RING, FUSED, RHD and TREE with nranks
- *   2, 4, 8 or 16 (slower still). RING_FP8 uses vectors when every pointer is 16-byte aligned, for any count
+ *   2, 4, 8 or 16 (also slower; both cost least when every rank's data starts in the first 16 bytes of a
+ *   128-byte line). RING_FP8 uses vectors when every pointer is 16-byte aligned, for any count
  *   (chunk starts off the 16-byte grid take shifted vectors); the other algorithms use vectors only when every
  *   pointer is 16-byte aligned. Otherwise element by element.
  * Errors: AR_ERR_INVALID (enum, nranks, NULL), AR_ERR_UNSUPPORTED (RHD with N not a power of two; FP8
