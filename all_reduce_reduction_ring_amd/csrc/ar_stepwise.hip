@@ -19,7 +19,8 @@
 //
 // Where partials live: for F32/I32 the output buffers themselves (the value in flight is the stored
 // value); for BF16/F16 an fp32 mirror in the caller's workspace, rank r at ws + r * ws_stride, so partial
-// sums stay fp32 between rounds exactly as in the one-pass kernels. Within a round no rank writes anything
+// sums stay fp32 between rounds exactly as in the one-pass kernels (each 8-element slot's partials split into two
+// halves, ws_stride / 2 apart, see Partial). Within a round no rank writes anything
 // another rank reads in that round, so in-place buffers are safe.
 #include <mutex>
 
@@ -77,10 +78,16 @@ template <int DT> struct Partial {
   static constexpr int V = Traits<DT>::kVec;
   static constexpr bool kMirror = Traits<DT>::kSize == 2;
 
+  // The mirror of rank r holds slot v's first four partials at 4v and its last four at half the stride further
+  // (element e of slot e / 8 at mirror_index), so each 16-byte mirror access of a wave covers whole lines.
+  __device__ __forceinline__ static int64_t mirror_index(const StepArgs& a, int r, int64_t e) {
+    const int64_t v = e >> 3, k = e & 7;
+    return r * a.ws_stride + (k < 4 ? 4 * v + k : (a.ws_stride >> 1) + 4 * v + (k - 4));
+  }
   __device__ __forceinline__ static void load(const StepArgs& a, int r, int64_t v, Acc (&x)[V]) {
     if constexpr (kMirror) {
-      const float* w = a.ws + r * a.ws_stride + v * V;
-      u32x4 lo = ld16(w), hi = ld16(w + 4);
+      const float* w = a.ws + r * a.ws_stride + 4 * v;
+      u32x4 lo = ld16(w), hi = ld16(w + (a.ws_stride >> 1));
 #pragma unroll
       for (int k = 0; k < 4; ++k) {
         x[k] = __uint_as_float(lo[k]);
@@ -92,7 +99,7 @@ template <int DT> struct Partial {
   }
   __device__ __forceinline__ static void store(const StepArgs& a, int r, int64_t v, const Acc (&x)[V]) {
     if constexpr (kMirror) {
-      float* w = a.ws + r * a.ws_stride + v * V;
+      float* w = a.ws + r * a.ws_stride + 4 * v;
       u32x4 lo, hi;
 #pragma unroll
       for (int k = 0; k < 4; ++k) {
@@ -100,17 +107,17 @@ template <int DT> struct Partial {
         hi[k] = __float_as_uint(x[k + 4]);
       }
       st16(w, lo);
-      st16(w + 4, hi);
+      st16(w + (a.ws_stride >> 1), hi);
     } else {
       st16(static_cast<char*>(a.p.out[r]) + v * 16, Slot<DT>::pack(x));
     }
   }
   __device__ __forceinline__ static Acc load_e(const StepArgs& a, int r, int64_t e) {
-    if constexpr (kMirror) return a.ws[r * a.ws_stride + e];
+    if constexpr (kMirror) return a.ws[mirror_index(a, r, e)];
     else return widen<DT>(load_elem<DT>(a.p.out[r], e));
   }
   __device__ __forceinline__ static void store_e(const StepArgs& a, int r, int64_t e, Acc x) {
-    if constexpr (kMirror) a.ws[r * a.ws_stride + e] = x;
+    if constexpr (kMirror) a.ws[mirror_index(a, r, e)] = x;
     else store_elem<DT>(a.p.out[r], e, narrow<DT>(x));
   }
 };
