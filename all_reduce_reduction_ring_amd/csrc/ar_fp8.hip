@@ -141,6 +141,50 @@ __global__ __launch_bounds__(kThreads) void quant_kernel(const void* in, int64_t
   const int64_t nwaves = (static_cast<int64_t>(gridDim.x) * kThreads) >> 6;
   for (int64_t w = wave; w * 4 < nblocks; w += nwaves) {  // uniform per wave: DPP sees all lanes
     const int64_t blk = w * 4 + row;
+    if constexpr (DT == AR_F32) {
+      // fp32: the lane holds [f, f + 4) and [f + 64, f + 68) of its block (f = block start + 4 l16), so that each
+      // 16-byte load of the wave covers whole lines (two adjacent slots per lane took every other 16 bytes)
+      const int64_t f = blk * kBlock + l16 * 4;
+      const bool whole = vec && blk < nblocks && (blk + 1) * kBlock <= count;
+      float v[kPerLane];
+      if (whole) {
+        const u32x4 x = ld16_cached(static_cast<const float*>(in) + f);
+        const u32x4 y = ld16_cached(static_cast<const float*>(in) + f + kBlock / 2);
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+          v[k] = __uint_as_float(x[k]);
+          v[k + 4] = __uint_as_float(y[k]);
+        }
+      } else {
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+          const int64_t e = f + k, e2 = e + kBlock / 2;
+          v[k] = blk < nblocks && e < count ? static_cast<const float*>(in)[e] : 0.0f;
+          v[k + 4] = blk < nblocks && e2 < count ? static_cast<const float*>(in)[e2] : 0.0f;
+        }
+      }
+      const BlockScale s = block_scale(v);
+      float q[kPerLane], r[kPerLane];
+#pragma unroll
+      for (int k = 0; k < kPerLane; ++k) q[k] = v[k] * s.inv;
+      uint32_t w0, w1;
+      e4m3_round4(q, r, &w0);
+      e4m3_round4(q + 4, r + 4, &w1);
+      w0 = canonical_nan_codes(w0);
+      w1 = canonical_nan_codes(w1);
+      if (whole) {
+        __builtin_nontemporal_store(w0, reinterpret_cast<uint32_t*>(codes + f));
+        __builtin_nontemporal_store(w1, reinterpret_cast<uint32_t*>(codes + f + kBlock / 2));
+      } else {
+        for (int k = 0; k < 4; ++k) {
+          if (blk < nblocks && f + k < count) codes[f + k] = static_cast<uint8_t>((w0 >> (8 * k)) & 0xFFu);
+          if (blk < nblocks && f + kBlock / 2 + k < count)
+            codes[f + kBlock / 2 + k] = static_cast<uint8_t>((w1 >> (8 * k)) & 0xFFu);
+        }
+      }
+      if (l16 == 0 && blk < nblocks) scales[blk] = s.scale;
+      continue;
+    }
     const int64_t e0 = blk * kBlock + l16 * kPerLane;
     int64_t nv = blk < nblocks ? count - e0 : 0;
     const int nvalid = nv <= 0 ? 0 : (nv >= kPerLane ? kPerLane : static_cast<int>(nv));
@@ -168,9 +212,43 @@ __global__ __launch_bounds__(kThreads) void quant_kernel(const void* in, int64_t
   }
 }
 
+// fp32 output: wave tasks of 512 elements, lane i decoding [4i, 4i + 4) and [256 + 4i, 256 + 4i + 4), so that each
+// 16-byte store of the wave covers whole lines (8 consecutive elements per lane stored every other 16 bytes).
+__device__ __forceinline__ void dequant4_f32(const uint8_t* codes, const float* scales, int64_t count, float* out,
+                                             int64_t e, bool whole) {
+  const float sc = scales[e / kBlock];
+  if (whole) {
+    const uint32_t w = *reinterpret_cast<const uint32_t*>(codes + e);
+    const f32x2 lo = __builtin_amdgcn_cvt_pk_f32_fp8(static_cast<int>(w), false);
+    const f32x2 hi = __builtin_amdgcn_cvt_pk_f32_fp8(static_cast<int>(w), true);
+    const u32x4 o = {__float_as_uint(lo[0] * sc), __float_as_uint(lo[1] * sc), __float_as_uint(hi[0] * sc),
+                     __float_as_uint(hi[1] * sc)};
+    st16(out + e, o);
+  } else {
+    for (int k = 0; k < 4 && e + k < count; ++k) {
+      const f32x2 d = __builtin_amdgcn_cvt_pk_f32_fp8(static_cast<int>(codes[e + k]), false);
+      out[e + k] = d[0] * sc;
+    }
+  }
+}
+
 template <int DT>
 __global__ __launch_bounds__(kThreads) void dequant_kernel(const uint8_t* codes, const float* scales, int64_t count,
                                                            void* out, int vec) {
+  if constexpr (DT == AR_F32) {
+    constexpr int64_t kTask = 64 * kPerLane;
+    const int lane = threadIdx.x & 63;
+    const int64_t ntasks = (count + kTask - 1) / kTask;
+    const int64_t nwaves = static_cast<int64_t>(gridDim.x) * (kThreads / 64);
+    for (int64_t t = static_cast<int64_t>(blockIdx.x) * (kThreads / 64) + (threadIdx.x >> 6); t < ntasks;
+         t += nwaves) {
+      const bool whole = vec && (t + 1) * kTask <= count;  // wave-uniform
+      const int64_t e0 = t * kTask + 4 * lane;
+      dequant4_f32(codes, scales, count, static_cast<float*>(out), e0, whole);
+      dequant4_f32(codes, scales, count, static_cast<float*>(out), e0 + kTask / 2, whole);
+    }
+    return;
+  }
   const int64_t tid = static_cast<int64_t>(blockIdx.x) * kThreads + threadIdx.x;
   const int64_t nth = static_cast<int64_t>(gridDim.x) * kThreads;
   const int64_t ngroups = (count + kPerLane - 1) / kPerLane;
@@ -591,7 +669,8 @@ hipError_t launch_fp8_dequant(const uint8_t* codes, const float* scales, int64_t
   const int64_t cap = static_cast<int64_t>(cu_count()) * 16;
   if (blocks > cap) blocks = cap;
   if (blocks < 1) blocks = 1;
-  const int vec = ((reinterpret_cast<uintptr_t>(out) & 15u) == 0) ? 1 : 0;
+  // the vector path reads 4 or 8 codes at a time too, so the codes need the alignment as well
+  const int vec = (((reinterpret_cast<uintptr_t>(out) | reinterpret_cast<uintptr_t>(codes)) & 15u) == 0) ? 1 : 0;
   if (dtype == AR_BF16)
     hipLaunchKernelGGL((dequant_kernel<AR_BF16>), dim3(blocks), dim3(kThreads), 0, s, codes, scales, count, out, vec);
   else

@@ -448,6 +448,33 @@ def test_fp8_quant_dequant_match_oracle(count):
     np.testing.assert_array_equal(scales.cpu().numpy().view(np.uint32), ws.view(np.uint32))
 
 
+@pytest.mark.parametrize("x_off,c_off,o_off", [(1, 0, 0), (0, 3, 0), (0, 0, 1), (3, 5, 2)])
+def test_fp8_codec_at_unaligned_offsets(x_off, c_off, o_off):
+    """Inputs, codes and outputs as views off the 16-byte grid (element offsets for fp32 and bf16, byte offsets for
+    codes): the element-by-element paths of both codec kernels, against the oracle."""
+    count = 128 * 37 + 51
+    x = _special_fp32(count, 23)
+    xb_all = torch.empty(count + 8, dtype=torch.float32, device=DEV)
+    xd = xb_all[x_off:x_off + count]
+    xd.copy_(torch.from_numpy(x))
+    cb = torch.empty(count + 16, dtype=torch.uint8, device=DEV)
+    codes = cb[c_off:c_off + count]
+    scales = torch.empty((count + 127) // 128, dtype=torch.float32, device=DEV)
+    ar.ar_fp8_quant(xd, codes, scales)
+    ob = torch.empty(count + 8, dtype=torch.float32, device=DEV)
+    out = ob[o_off:o_off + count]
+    ar.ar_fp8_dequant(codes, scales, out)
+    obb = torch.empty(count + 8, dtype=torch.bfloat16, device=DEV)
+    outb = obb[o_off:o_off + count]
+    ar.ar_fp8_dequant(codes, scales, outb)
+    torch.cuda.synchronize()
+    wc, ws = oracle.fp8_quant(x, oracle.F32)
+    np.testing.assert_array_equal(codes.cpu().numpy(), wc)
+    np.testing.assert_array_equal(scales.cpu().numpy().view(np.uint32), ws.view(np.uint32))
+    _f32_bits_equal_nan_aware(out.cpu().numpy(), oracle.fp8_dequant(wc, ws, oracle.F32))
+    np.testing.assert_array_equal(from_dev(outb, ar.AR_BF16), oracle.fp8_dequant(wc, ws, oracle.BF16))
+
+
 def test_fp8_encoder_dense_sweep_of_fp32_patterns():
     """Every 997th fp32 bit pattern with |v| <= 448, quantized in blocks whose amax is exactly 448 (scale 1), so
     the E4M3 encoder sees raw values across all binades, ties included."""
