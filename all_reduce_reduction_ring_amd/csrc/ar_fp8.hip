@@ -343,6 +343,23 @@ __device__ __forceinline__ u32x4 from_next_lane(const u32x4& x, const u32x4& las
   return r;
 }
 
+// Within each 16-lane row: lane i (< 15) receives lane i + 1's x and lane 15 keeps `last` (row_shl:1); lane i (> 0)
+// receives lane i - 1's x and lane 0 keeps `first` (row_shr:1); and the row rotated by one lane either way
+// (row_ror:15, lane i <- lane i + 1 mod 16; row_ror:1, lane i <- lane i - 1 mod 16). All 64 lanes must be active.
+template <int CTRL>
+__device__ __forceinline__ u32x4 dpp4(const u32x4& old, const u32x4& x) {
+  u32x4 r;
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+    r[i] = static_cast<uint32_t>(
+        __builtin_amdgcn_update_dpp(static_cast<int>(old[i]), static_cast<int>(x[i]), CTRL, 0xF, 0xF, false));
+  return r;
+}
+__device__ __forceinline__ u32x4 from_next_in_row(const u32x4& x, const u32x4& last) { return dpp4<0x101>(last, x); }
+__device__ __forceinline__ u32x4 from_prev_in_row(const u32x4& x, const u32x4& first) { return dpp4<0x111>(first, x); }
+__device__ __forceinline__ u32x4 rot_row_left(const u32x4& x) { return dpp4<0x12F>(x, x); }
+__device__ __forceinline__ u32x4 rot_row_right(const u32x4& x) { return dpp4<0x121>(x, x); }
+
 // A lane's 8 elements in the aligned path, loaded and stored in 16-byte slots: bf16, one slot (elements
 // [s, s + 8), s = block start + 8 l16); fp32, two slots half a block apart (elements [s, s + 4) and [s + 64, s + 68),
 // s = block start + 4 l16). Either way a row of 16 lanes holds its whole 128-element block, and each load or store
@@ -512,30 +529,39 @@ __global__ __launch_bounds__(kThreads) void fp8_ring_kernel(Fp8RingArgs a) {
 #pragma unroll
         for (int r = 0; r < NR; ++r) Raw8<DT>::store(a.p.out[r], s, p);
       } else if (shifted && DT == AR_F32) {
-        // fp32: a lane's 8 elements start m (1..3) past the grid and span three aligned slots. The slot wholly
-        // inside the lane ([A + 4, A + 8)) is stored as it is; the one at A takes the previous lane's last m.
+        // fp32 with the chunk start m (1..3) elements past the grid, in the aligned path's lane layout: the lane's
+        // groups [F, F + 4) and [F + 64, F + 68) each span two aligned slots, the one at or below the group (loaded
+        // by the lane) and the next (the following group's, taken from its lane with DPP: within the row the next
+        // lane's; after the row's last lane, the group half a block on, or the next row's first). Each load and
+        // store instruction of the wave then covers 256-byte runs instead of every other 16 bytes.
         constexpr int NT = NR > 0 ? NR : 1;
-        const int64_t A = e0 - mis;  // a multiple of 4 elements; A + 12 <= count, so all three slots are in the buffer
-        u32x4 x0[NT], x1[NT], x2[NT];
+        const int64_t F = lo + bic * kBlock + l16 * 4, G = F + kBlock / 2;
+        const int64_t A1 = F - mis, A2 = G - mis;  // multiples of 4; lane 63 reads to A2 + 8 <= count
+        u32x4 y1[NT], y2[NT], n1[NT], n2[NT];
 #pragma unroll
         for (int k = 0; k < NT; ++k) {
           int rr = start + k;
           rr = rr >= NT ? rr - NT : rr;
-          const float* base = static_cast<const float*>(a.p.in[rr]) + A;
-          x0[k] = ld16(base);
-          x1[k] = ld16(base + 4);
-          // the third slot is the next lane's first one: only the last lane loads it
-          x2[k] = u32x4{0u, 0u, 0u, 0u};
-          if (lane == 63) x2[k] = ld16(base + 8);
+          const float* base = static_cast<const float*>(a.p.in[rr]);
+          y1[k] = ld16(base + A1);
+          y2[k] = ld16(base + A2);
+          // the slot after the task's last group begins the next task: only the last lane loads it
+          n2[k] = u32x4{0u, 0u, 0u, 0u};
+          if (lane == 63) n2[k] = ld16(base + A2 + 4);
         }
 #pragma unroll
-        for (int k = 0; k < NT; ++k) x2[k] = from_next_lane(x0[k], x2[k]);
+        for (int k = 0; k < NT; ++k) {
+          // row lane 15: the slot after its first group is lane 0's second slot; after its second, the next row's
+          // (or, for lane 63, the next task's) first slot
+          n1[k] = from_next_in_row(y1[k], rot_row_left(y2[k]));
+          n2[k] = from_next_in_row(y2[k], from_next_lane(y1[k], n2[k]));
+        }
         auto widen8 = [&](int k, float (&v)[kPerLane]) {
-          const u32x4 lo4 = shift4_by(mis, x0[k], x1[k]), hi4 = shift4_by(mis, x1[k], x2[k]);
+          const u32x4 g1 = shift4_by(mis, y1[k], n1[k]), g2 = shift4_by(mis, y2[k], n2[k]);
 #pragma unroll
           for (int i = 0; i < 4; ++i) {
-            v[i] = __uint_as_float(lo4[i]);
-            v[i + 4] = __uint_as_float(hi4[i]);
+            v[i] = __uint_as_float(g1[i]);
+            v[i + 4] = __uint_as_float(g2[i]);
           }
         };
         widen8(0, p);
@@ -546,28 +572,30 @@ __global__ __launch_bounds__(kThreads) void fp8_ring_kernel(Fp8RingArgs a) {
           hop(p, own);
         }
         finish<OP>(p, NT);
-        u32x4 o0, o1, last;  // our two halves; the previous task's last lane (its upper half)
+        u32x4 o1, o2, last;  // our two groups; the previous task's last group (lane 63's second)
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-          o0[i] = __float_as_uint(p[i]);
-          o1[i] = __float_as_uint(p[i + 4]);
+          o1[i] = __float_as_uint(p[i]);
+          o2[i] = __float_as_uint(p[i + 4]);
           last[i] = static_cast<uint32_t>(__builtin_amdgcn_readlane(static_cast<int>(prev[i]), 63));
         }
-        const u32x4 pv1 = from_prev_lane(o1, last);      // lane i: lane i - 1's upper half; lane 0: `last`
-        const u32x4 low = shift4_by(4 - mis, pv1, o0);  // [A, A + 4): the previous lane's last m, then our first
-        const u32x4 mid = shift4_by(4 - mis, o0, o1);   // [A + 4, A + 8)
+        // the group before each of ours: within the row the previous lane's; before the row's lane 0, the previous
+        // row's last second group (the previous task's, carried, for lane 0) or this row's lane 15 first group
+        const u32x4 b1 = from_prev_in_row(o1, from_prev_lane(o2, last));
+        const u32x4 b2 = from_prev_in_row(o2, rot_row_right(o1));
+        const u32x4 s1 = shift4_by(4 - mis, b1, o1);  // [A1, A1 + 4)
+        const u32x4 s2 = shift4_by(4 - mis, b2, o2);  // [A2, A2 + 4)
 #pragma unroll
         for (int r = 0; r < NT; ++r) {
           float* out = static_cast<float*>(a.p.out[r]);
-          // both of a lane's aligned slots, each in one store instruction for the whole wave
-          if (lane > 0 || carried) st16(out + A, low);
-          else  // [A + m, A + 4): the rest of the slot below belongs to the previous task
-            for (int q = 0; q < 4 - mis; ++q) store_elem<AR_F32>(out, e0 + q, __float_as_uint(p[q]));
-          st16(out + A + 4, mid);
-          if (lane == 63 && !next_shifted)  // [A + 8, A + 8 + m): the rest of the slot above is the next task's
-            for (int q = 8 - mis; q < kPerLane; ++q) store_elem<AR_F32>(out, e0 + q, __float_as_uint(p[q]));
+          if (lane > 0 || carried) st16(out + A1, s1);
+          else  // [F, A1 + 4): the rest of the slot below belongs to the previous task
+            for (int q = 0; q < 4 - mis; ++q) store_elem<AR_F32>(out, F + q, __float_as_uint(p[q]));
+          st16(out + A2, s2);
+          if (lane == 63 && !next_shifted)  // [A2 + 4, G + 4): the rest of the slot above is the next task's
+            for (int q = 4 - mis; q < 4; ++q) store_elem<AR_F32>(out, G + q, __float_as_uint(p[4 + q]));
         }
-        prev = o1;
+        prev = o2;
       } else if (shifted && DT == AR_BF16) {
         constexpr int NT = NR > 0 ? NR : 1;
         const int64_t A = e0 - mis;  // a multiple of 8 elements; A + 16 <= count, so both slots are in the buffer
