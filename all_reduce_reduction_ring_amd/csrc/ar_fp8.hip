@@ -321,31 +321,8 @@ __device__ __forceinline__ void finish(float (&p)[kPerLane], int n) {
   for (int e = 0; e < kPerLane; ++e) p[e] = d[e] * s.scale;
 }
 
-// Lane i (> 0) receives lane i - 1's x; lane 0 keeps `first` (a DPP wave shift right by one lane: one VALU operation
-// per dword, no LDS traffic). All 64 lanes of the wave must be active.
-__device__ __forceinline__ u32x4 from_prev_lane(const u32x4& x, const u32x4& first) {
-  u32x4 r;
-#pragma unroll
-  for (int i = 0; i < 4; ++i)
-    r[i] = static_cast<uint32_t>(__builtin_amdgcn_update_dpp(static_cast<int>(first[i]), static_cast<int>(x[i]),
-                                                             0x138 /* wave_shr:1 */, 0xF, 0xF, false));
-  return r;
-}
-
-// Lane i (< 63) receives lane i + 1's x; lane 63 keeps `last` (a DPP wave shift left by one lane). All 64 lanes of
-// the wave must be active.
-__device__ __forceinline__ u32x4 from_next_lane(const u32x4& x, const u32x4& last) {
-  u32x4 r;
-#pragma unroll
-  for (int i = 0; i < 4; ++i)
-    r[i] = static_cast<uint32_t>(__builtin_amdgcn_update_dpp(static_cast<int>(last[i]), static_cast<int>(x[i]),
-                                                             0x130 /* wave_shl:1 */, 0xF, 0xF, false));
-  return r;
-}
-
-// Within each 16-lane row: lane i (< 15) receives lane i + 1's x and lane 15 keeps `last` (row_shl:1); lane i (> 0)
-// receives lane i - 1's x and lane 0 keeps `first` (row_shr:1); and the row rotated by one lane either way
-// (row_ror:15, lane i <- lane i + 1 mod 16; row_ror:1, lane i <- lane i - 1 mod 16). All 64 lanes must be active.
+// Lane moves within a wave by DPP (one VALU operation per dword, no LDS traffic); a lane whose source lies outside
+// the wave or the row keeps the `old` operand. All 64 lanes of the wave must be active.
 template <int CTRL>
 __device__ __forceinline__ u32x4 dpp4(const u32x4& old, const u32x4& x) {
   u32x4 r;
@@ -355,6 +332,13 @@ __device__ __forceinline__ u32x4 dpp4(const u32x4& old, const u32x4& x) {
         __builtin_amdgcn_update_dpp(static_cast<int>(old[i]), static_cast<int>(x[i]), CTRL, 0xF, 0xF, false));
   return r;
 }
+// Across the wave: lane i receives lane i - 1's x and lane 0 keeps `first` (wave_shr:1), or lane i + 1's x and lane
+// 63 keeps `last` (wave_shl:1).
+__device__ __forceinline__ u32x4 from_prev_lane(const u32x4& x, const u32x4& first) { return dpp4<0x138>(first, x); }
+__device__ __forceinline__ u32x4 from_next_lane(const u32x4& x, const u32x4& last) { return dpp4<0x130>(last, x); }
+// Within each 16-lane row: lane i receives lane i + 1's x and lane 15 keeps `last` (row_shl:1), or lane i - 1's x
+// and lane 0 keeps `first` (row_shr:1); and the row rotated by one lane either way (row_ror:15, lane i <- lane
+// i + 1 mod 16; row_ror:1, lane i <- lane i - 1 mod 16).
 __device__ __forceinline__ u32x4 from_next_in_row(const u32x4& x, const u32x4& last) { return dpp4<0x101>(last, x); }
 __device__ __forceinline__ u32x4 from_prev_in_row(const u32x4& x, const u32x4& first) { return dpp4<0x111>(first, x); }
 __device__ __forceinline__ u32x4 rot_row_left(const u32x4& x) { return dpp4<0x12F>(x, x); }
