@@ -10,7 +10,8 @@ Reported: busbw (the JSON "value") = algbw * 2(N-1)/N with algbw = S / t and S t
 of the kernel = algorithmic bytes (N reads + N writes of S) / kernel time, against the 8 TB/s peak; the
 CPU oracle timed on this host on the same inputs; and, beside the headline, every other step of the path
 (rank-order and halving-doubling one-pass kernels, the round-per-launch schedules, bucketing with 25 MiB
-buckets over 300 tensors, the fp8 codec and compressed ring) with its own algorithmic-bytes roofline.
+buckets over 300 tensors, the fp8 codec and compressed ring, the owner's epilogue on its own) with its own
+algorithmic-bytes roofline.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--headline-only] [--fp8-only] [--copy-calibration]
                        [--ring-bytes-per-rank S] [--per-rank-offsets-only] [--sweep OUT.jsonl]
