@@ -288,8 +288,10 @@ struct Fp8RingArgs {
   int64_t tasks;       // total wave tasks
   int n;
   int vec;    // 1: every rank buffer starts on a 16-byte boundary
-  int strip;  // wave tasks per strip: kStrip when some chunk start is off the 16-byte grid (bf16 q % 8 or fp32
-              // q % 4 non-zero, or r != 0), else 1
+  int strip;  // wave tasks per strip: kStrip<DT> when some chunk start is off the 16-byte grid (bf16 q % 8 or fp32
+              // q % 4 non-zero, or r != 0), or, for bf16 with lrot, off the 128-byte line grid; else 1
+  int lrot;   // bf16: every output buffer sits at the same place in its 128-byte line, lmod elements in, so that the
+  int lmod;   //   shifted path can rotate its stores onto whole lines
 };
 
 // One hop: the sender's partial p goes out as E4M3 codes + block scale and comes back as d * scale; the
@@ -433,15 +435,24 @@ __device__ __forceinline__ TaskGeo task_geo(const Fp8RingArgs& a, int64_t w) {
   return g;
 }
 
-// The shifted path below takes task g: full, its chunk start off the 16-byte grid (m elements past it), and every
-// lane's aligned slots inside the buffers (bf16: two slots, 16 elements from the lower one's start; fp32: three
-// slots, 12 elements).
+// bf16 with lrot: the slot (0..7) within its 128-byte output line of the aligned slot at or below task g's first
+// element; the same for every task of a chunk (tasks are 1 KiB apart). 0 otherwise.
+template <int DT>
+__device__ __forceinline__ int line_slot(const Fp8RingArgs& a, const TaskGeo& g) {
+  if (DT != AR_BF16 || !a.lrot) return 0;
+  const int64_t a0 = g.lo - (g.lo & 7) + g.t * 4 * kBlock;
+  return static_cast<int>(((a.lmod + a0) >> 3) & 7);
+}
+
+// The shifted path below takes task g: full, its chunk start off the 16-byte grid (m elements past it) or, for
+// bf16, its first slot off the 128-byte line grid, and every lane's aligned slots inside the buffers (bf16: two
+// slots, 16 elements from the lower one's start, or one when m = 0; fp32: three slots, 12 elements).
 template <int DT, int NR>
 __device__ __forceinline__ bool shifted_task(const Fp8RingArgs& a, const TaskGeo& g) {
   if (!(NR > 0) || a.vec == 0 || !g.full) return false;
   const int mis = static_cast<int>(g.lo & (DT == AR_BF16 ? 7 : 3));
-  constexpr int kSpan = DT == AR_BF16 ? 16 : 12;
-  return mis != 0 && g.lo + g.t * 4 * kBlock + 63 * kPerLane - mis + kSpan <= a.count;
+  const int span = DT == AR_BF16 ? (mis ? 16 : 8) : 12;
+  return (mis != 0 || line_slot<DT>(a, g) != 0) && g.lo + g.t * 4 * kBlock + 63 * kPerLane - mis + span <= a.count;
 }
 
 // fp32 slots: x0 from element m on, continued into x1 (m wave-uniform, 0..3)
@@ -454,11 +465,14 @@ __device__ __forceinline__ u32x4 shift4_by(int m, const u32x4& x0, const u32x4& 
   }
 }
 
-// With chunk starts off the grid, a wave walks a strip of kStrip consecutive tasks, so that in the shifted path
-// the slot shared by two tasks of one chunk is stored whole by the later one, from the earlier one's last lane
-// carried over in registers (N = 8, 64 Mi + 7 bf16: 521 us against 645 us with single tasks). Otherwise a strip
-// is one task: consecutive tasks on consecutive waves ran 7% faster when nothing is carried (427 against 458 us).
-constexpr int kStrip = 8;
+// With chunk starts off the grid, a wave walks a strip of consecutive tasks, so that in the shifted path the slot
+// shared by two tasks of one chunk is stored whole by the later one, from the earlier one's last lane carried over
+// in registers (N = 8, 64 Mi + 7 bf16: 521 us against 645 us with single tasks). Longer strips spread the grid's
+// front through the buffers, which costs as well: N = 8, one box, two passes, strips of 2 / 4 / 8 / 32 tasks ran
+// 487 / 476 / 486 / 510 us for 64 Mi + 7 bf16 per rank, 460 / 443 / 452 / 494 us for 64 Mi + 64 bf16 and
+// 917 / 944 / 977 / 1,032 us for 64 Mi + 13 fp32. Otherwise a strip is one task: consecutive tasks on consecutive
+// waves ran 7% faster when nothing is carried (427 against 458 us).
+template <int DT> constexpr int kStrip = DT == AR_BF16 ? 4 : 2;
 
 template <int DT, int OP, int NR>
 __global__ __launch_bounds__(kThreads) void fp8_ring_kernel(Fp8RingArgs a) {
@@ -469,6 +483,7 @@ __global__ __launch_bounds__(kThreads) void fp8_ring_kernel(Fp8RingArgs a) {
   const int64_t nstrips = (a.tasks + a.strip - 1) / a.strip;
   for (int64_t sp = wave0; sp < nstrips; sp += nwaves) {
     u32x4 prev = {0u, 0u, 0u, 0u};  // this lane's result in the previous task (bf16: packed; fp32: upper half)
+    u32x4 prev_low = {0u, 0u, 0u, 0u};  // bf16: the aligned output slot this lane assembled in the previous task
     bool prev_shifted = false;       // that task took the shifted path (in the same chunk as the next one or not)
     int64_t prev_c = -1;
     TaskGeo gn = task_geo(a, sp * a.strip);
@@ -492,7 +507,7 @@ __global__ __launch_bounds__(kThreads) void fp8_ring_kernel(Fp8RingArgs a) {
       const bool full = g.full;
       const bool shifted = shifted_task<DT, NR>(a, g);
       float p[kPerLane];
-      if (NR > 0 && lane_vec && full) {
+      if (NR > 0 && lane_vec && full && !shifted) {
         // every lane holds 8 in-range, aligned elements: issue all N loads before any arithmetic
         const int64_t s = lo + bic * kBlock + l16 * Raw8<DT>::kLaneStep;
         Raw8<DT> raw[NR > 0 ? NR : 1];
@@ -591,11 +606,16 @@ __global__ __launch_bounds__(kThreads) void fp8_ring_kernel(Fp8RingArgs a) {
           x0[k] = ld16(static_cast<const uint16_t*>(a.p.in[rr]) + A);
           // the upper slot is the next lane's lower one: only the last lane loads it
           x1[k] = u32x4{0u, 0u, 0u, 0u};
-          if (lane == 63) x1[k] = ld16(static_cast<const uint16_t*>(a.p.in[rr]) + A + 8);
+          if (mis != 0 && lane == 63) x1[k] = ld16(static_cast<const uint16_t*>(a.p.in[rr]) + A + 8);
         }
+        if (mis != 0) {
 #pragma unroll
-        for (int k = 0; k < NT; ++k) x1[k] = from_next_lane(x0[k], x1[k]);
-        shift_ranks_by<NT>(mis, x0, x1, w);
+          for (int k = 0; k < NT; ++k) x1[k] = from_next_lane(x0[k], x1[k]);
+          shift_ranks_by<NT>(mis, x0, x1, w);
+        } else {
+#pragma unroll
+          for (int k = 0; k < NT; ++k) w[k] = x0[k];
+        }
         Slot<AR_BF16>::unpack(w[0], p);
 #pragma unroll
         for (int k = 1; k < NT; ++k) {
@@ -610,19 +630,38 @@ __global__ __launch_bounds__(kThreads) void fp8_ring_kernel(Fp8RingArgs a) {
         for (int i = 0; i < 4; ++i)
           last[i] = static_cast<uint32_t>(__builtin_amdgcn_readlane(static_cast<int>(prev[i]), 63));
         // slot [A, A + 8): the previous lane's last m, then our first 8 - m (lane 0: the previous task's last lane)
-        u32x4 pv[1] = {from_prev_lane(o, last)}, one[1] = {o}, low[1];
-        shift_ranks_by<1>(8 - mis, pv, one, low);
+        u32x4 low[1] = {o};
+        if (mis != 0) {
+          u32x4 pv[1] = {from_prev_lane(o, last)}, one[1] = {o};
+          shift_ranks_by<1>(8 - mis, pv, one, low);
+        }
+        // Rotated by kl lanes, each store instruction covers whole 128-byte lines: lane j stores lane j - kl's slot,
+        // lanes j < kl the previous task's last kl slots (which it held back), and this task's last kl slots wait
+        // for the next task. Partial lines written by two waves cost far more than straddled reads.
+        const int kl = line_slot<DT>(a, g);
+        const int src = ((lane - kl) & 63) << 2;
+        u32x4 rot;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int cur = __builtin_amdgcn_ds_bpermute(src, static_cast<int>(low[0][i]));
+          const int old = __builtin_amdgcn_ds_bpermute(src, static_cast<int>(prev_low[i]));
+          rot[i] = static_cast<uint32_t>(lane >= kl ? cur : old);
+        }
+        const int64_t As = A - 8 * kl;  // the slot this lane stores: lane j - kl's
 #pragma unroll
         for (int r = 0; r < NT; ++r) {
           uint16_t* out = static_cast<uint16_t*>(a.p.out[r]);
-          // the wave's slots of this rank in one store instruction over whole lines
-          if (lane > 0 || carried) st16(out + A, low[0]);
-          else  // [A + m, A + 8): the rest of the slot below belongs to the previous task
-            for (int q = 0; q < 8 - mis; ++q) store_elem<AR_BF16>(out, e0 + q, narrow<AR_BF16>(p[q]));
+          if (lane > kl || carried || (lane == kl && mis == 0)) {
+            st16(out + As, rot);
+          } else if (lane == kl) {  // the task's first slot: [A + m, A + 8) is ours, the rest the previous task's
+            for (int q = mis; q < 8; ++q) store_elem<AR_BF16>(out, As + q, (rot[q >> 1] >> (16 * (q & 1))) & 0xFFFFu);
+          }
+          if (!next_shifted && lane >= 64 - kl) st16(out + A, low[0]);  // nothing will carry them: store them here
           if (lane == 63 && !next_shifted)  // [A + 8, A + 8 + m): the rest of the slot above is the next task's
             for (int q = 8 - mis; q < kPerLane; ++q) store_elem<AR_BF16>(out, e0 + q, narrow<AR_BF16>(p[q]));
         }
         prev = o;
+        prev_low = low[0];
       } else {
         load8<DT>(a.p.in[start], e0, nvalid, lane_vec, p);
         for (int k = 1; k < n; ++k) {
@@ -705,7 +744,23 @@ hipError_t launch_fp8_ring(const RankPtrs& p, int n, int64_t count, int dtype, i
   // chunk starts off the 16-byte grid are handled per wave task in the kernel
   a.vec = vec ? 1 : 0;
   // chunk starts on the 16-byte grid: q a multiple of 8 bf16 or 4 fp32 elements (and no remainder)
-  a.strip = (vec && !(a.r == 0 && a.q % (dtype == AR_BF16 ? 8 : 4) == 0)) ? kStrip : 1;
+  const int strip = dtype == AR_BF16 ? kStrip<AR_BF16> : kStrip<AR_F32>;
+  a.strip = (vec && !(a.r == 0 && a.q % (dtype == AR_BF16 ? 8 : 4) == 0)) ? strip : 1;
+  // bf16 outputs all at one place in their 128-byte lines: the shifted path rotates its stores onto whole lines,
+  // which needs strips wherever a chunk starts off the line grid
+  a.lrot = 0;
+  a.lmod = 0;
+  if (vec && dtype == AR_BF16) {
+    const uintptr_t m0 = reinterpret_cast<uintptr_t>(p.out[0]) % 128;
+    bool same = true;
+    for (int r = 1; r < n; ++r) same = same && reinterpret_cast<uintptr_t>(p.out[r]) % 128 == m0;
+    if (same) {
+      a.lrot = 1;
+      a.lmod = static_cast<int>(m0 / 2);
+      for (int c = 0; c < n && a.strip == 1; ++c)
+        if ((a.lmod + c * a.q + (c < a.r ? c : a.r)) % 64 != 0) a.strip = strip;
+    }
+  }
   if (dtype == AR_BF16) return op == AR_AVG ? ring_n<AR_BF16, AR_AVG>(a, s) : ring_n<AR_BF16, AR_SUM>(a, s);
   return op == AR_AVG ? ring_n<AR_F32, AR_AVG>(a, s) : ring_n<AR_F32, AR_SUM>(a, s);
 }
