@@ -478,6 +478,9 @@ struct SkewArgs {
   // elements). 32-bit entries: the kernel reads them with scalar loads (the rank rotation is wave-uniform), which
   // never wait on the vector loads of the data.
   int32_t im[AR_MAX_RANKS], om[AR_MAX_RANKS];
+  // the 16-byte slot (0..7) within its 128-byte line of the output's slot 0: tile windows of 64 slots start there
+  int32_t ok[AR_MAX_RANKS];
+  int any_kl;  // some ok[r] != 0
   const char* ib[AR_MAX_RANKS];
   int strip;  // tiles per strip (set by the launcher)
 };
@@ -659,21 +662,58 @@ __global__ __launch_bounds__(kThreads) void skew_kernel(SkewArgs s) {
         for (int i = 0; i < 4; ++i)
           last[i] = static_cast<uint32_t>(__builtin_amdgcn_readlane(static_cast<int>(prev[i]), 63));
         const u32x4 pv = from_prev_lane(o, last);
-#pragma unroll
-        for (int r = 0; r < NR; ++r) {
+        // Aligned slot j of an output at m elements past its grid: the previous lane's last m elements, then this
+        // lane's first V - m. The wave's slots j0 .. j0 + 63 go out in one store instruction (a separate store
+        // for the tile's first slot made every line there a second, partial write).
+        auto store_plain = [&](int r) {
           const int m = s.om[r];
           char* ob = static_cast<char*>(a.p.out[r]) - m * ES;  // the output's 16-byte grid
           if (m == 0) {
             st16(ob + j * 16, o);
+            return;
+          }
+          if (lane > 0 || prev_vec) {
+            st16(ob + j * 16, shift_by<ES>(V - m, pv, o));
           } else {
-            // Aligned slot j: the previous lane's last m elements, then this lane's first V - m. The wave's slots
-            // j0 .. j0 + 63 go out in one store instruction over whole lines (a separate store for the tile's first
-            // slot made every line there a second, partial write).
-            if (lane > 0 || prev_vec) {
-              st16(ob + j * 16, shift_by<ES>(V - m, pv, o));
-            } else {
-              for (int q = 0; q < V - m; ++q) store_elem<DT>(a.p.out[r], e + q, slot_elem<DT>(o, q));
+            for (int q = 0; q < V - m; ++q) store_elem<DT>(a.p.out[r], e + q, slot_elem<DT>(o, q));
+          }
+          if (lane == 63 && !next_vec)
+            for (int q = V - m; q < V; ++q) store_elem<DT>(a.p.out[r], e + q, slot_elem<DT>(o, q));
+        };
+        if (!s.any_kl) {
+#pragma unroll
+          for (int r = 0; r < NR; ++r) store_plain(r);
+        } else {
+          // Some output's tile windows start kl > 0 slots into a 128-byte line. Partial lines written by two
+          // waves cost far more than anything else here, so its slots are rotated by kl lanes: lane i stores lane
+          // i - kl's slot, lanes i < kl the previous tile's last kl slots (held back by it), and every store
+          // instruction covers whole lines except at strip ends. One rank at a time (not unrolled): the
+          // temporaries then stay within 128 VGPRs for the rank-order fold, 4 waves per SIMD.
+#pragma unroll 1
+          for (int r = 0; r < NR; ++r) {
+            const int m = s.om[r], kl = s.ok[r];
+            if (kl == 0) {
+              store_plain(r);
+              continue;
             }
+            char* ob = static_cast<char*>(a.p.out[r]) - m * ES;
+            const u32x4 cur = m == 0 ? o : shift_by<ES>(V - m, pv, o);  // this lane's aligned slot j
+            // its slot in the previous tile (lanes 1..63 are used, so lane 0's neighbour does not matter)
+            const u32x4 old = m == 0 ? prev : shift_by<ES>(V - m, from_prev_lane(prev, prev), prev);
+            const int src = ((lane - kl) & 63) << 2;
+            u32x4 rot;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+              const int rc = __builtin_amdgcn_ds_bpermute(src, static_cast<int>(cur[i]));
+              const int ro = __builtin_amdgcn_ds_bpermute(src, static_cast<int>(old[i]));
+              rot[i] = static_cast<uint32_t>(lane >= kl ? rc : ro);
+            }
+            if (lane > kl || prev_vec || (lane == kl && m == 0)) {
+              st16(ob + (j - kl) * 16, rot);
+            } else if (lane == kl) {  // the tile's first slot: its first m elements are the previous tile's
+              for (int q = m; q < V; ++q) store_elem<DT>(a.p.out[r], (j - kl) * V + q - m, slot_elem<DT>(rot, q));
+            }
+            if (!next_vec && lane >= 64 - kl) st16(ob + j * 16, cur);  // held back for a tile that will not come
             if (lane == 63 && !next_vec)
               for (int q = V - m; q < V; ++q) store_elem<DT>(a.p.out[r], e + q, slot_elem<DT>(o, q));
           }
@@ -743,9 +783,11 @@ hipError_t skew_op(SkewArgs& s, int op, int algo, hipStream_t st) {
   }
 }
 
-// The skewed-buffer kernel takes a call when the 2N addresses are element-aligned, not all equal modulo 16 and
-// not all multiples of 4 bytes (2-byte types at odd offsets), the rank count is 2, 4, 8 or 16, the algorithm is
-// a one-pass one, and there are a few wave tiles of work; it fills the per-rank offsets.
+// The skewed-buffer kernel takes a call of 2-byte elements when the 2N addresses are element-aligned and not all
+// equal modulo 16 (views at different offsets), the rank count is 2, 4, 8 or 16, the algorithm is a one-pass one,
+// and there are a few wave tiles of work; it fills the per-rank offsets. Addresses that are all multiples of 4
+// bytes come here too rather than to the one-front kernel's 16-byte accesses at 4-byte alignment, whose store
+// windows straddle lines.
 template <int DT>
 bool plan_skew(const RankPtrs& p, int n, int64_t count, int algo, SkewArgs& s) {
   constexpr int ES = Traits<DT>::kSize, V = Traits<DT>::kVec;
@@ -753,21 +795,20 @@ bool plan_skew(const RankPtrs& p, int n, int64_t count, int algo, SkewArgs& s) {
       !(n == 2 || n == 4 || n == 8 || n == 16))
     return false;
   if (count < 4 * 64 * V) return false;
-  bool differ = false, words = true;
+  bool differ = false;
+  s.any_kl = 0;
   const uintptr_t r0 = reinterpret_cast<uintptr_t>(p.in[0]) % 16;
   for (int r = 0; r < n; ++r) {
     const uintptr_t i = reinterpret_cast<uintptr_t>(p.in[r]), o = reinterpret_cast<uintptr_t>(p.out[r]);
     if (i % ES || o % ES) return false;
     differ = differ || i % 16 != r0 || o % 16 != r0;
-    words = words && i % 4 == 0 && o % 4 == 0;
     s.im[r] = static_cast<int32_t>((i % 16) / ES);
     s.om[r] = static_cast<int32_t>((o % 16) / ES);
+    s.ok[r] = static_cast<int32_t>(((o - o % 16) % 128) / 16);
+    s.any_kl = s.any_kl || s.ok[r] != 0;
     s.ib[r] = static_cast<const char*>(p.in[r]) - (i % 16);
   }
-  // addresses that are all multiples of 4 bytes keep the one-front kernel with 16-byte accesses at 4-byte
-  // alignment, which measured faster (N = 8, 256 MiB of bf16, rank r at 2r elements: 922-924 us against 980-992 us
-  // with the skewed kernel at its current launch shape)
-  return differ && !words;
+  return differ;
 }
 
 // ------------------------------------------------------------------------------------------ launch

@@ -142,11 +142,11 @@ int ar_chunk_bounds(int nranks, size_t count, int64_t* lo);
  *   count == 0 returns AR_OK and enqueues nothing. nranks == 1 copies (avg divides by 1).
  *   Alignment: any. RING, FUSED, RHD and TREE work in 16-byte vectors whenever all 2N pointers share one address
  *   modulo 16 (a multiple of the element size): the first few elements of every buffer go one by one, up to a
- *   multiple of 256 bytes (buffers of 1 MiB or more) or of 16 bytes, the rest in vectors. Pointers that differ
- *   modulo 16 but are all multiples of 4 use vectors from element 0 (slower: they straddle cache lines). 2-byte
- *   types at odd per-rank offsets use aligned vectors shifted per rank for RING, FUSED, RHD and TREE with nranks
- *   2, 4, 8 or 16 (also slower; both cost least when every rank's data starts in the first 16 bytes of a
- *   128-byte line). RING_FP8 uses vectors when every pointer is 16-byte aligned, for any count
+ *   multiple of 256 bytes (buffers of 1 MiB or more) or of 16 bytes, the rest in vectors. Where the pointers
+ *   differ modulo 16, 4-byte types use vectors from element 0 (slower: they straddle cache lines), and 2-byte
+ *   types use aligned vectors shifted per rank, with the stores rotated onto whole 128-byte lines, for RING,
+ *   FUSED, RHD and TREE with nranks 2, 4, 8 or 16 (also slower, least when every rank's data starts in the first
+ *   16 bytes of a line), else element by element. RING_FP8 uses vectors when every pointer is 16-byte aligned, for any count
  *   (chunk starts off the 16-byte grid take shifted vectors); the other algorithms use vectors only when every
  *   pointer is 16-byte aligned. Otherwise element by element.
  * Errors: AR_ERR_INVALID (enum, nranks, NULL), AR_ERR_UNSUPPORTED (RHD with N not a power of two; FP8

@@ -242,13 +242,41 @@ def test_skewed_rank_buffers_every_residue(n, dt, algo):
             assert_bitwise([from_dev(t, dt) for t in ins], want, f"skewed in place n={n} dt={dt} count={count}")
 
 
+@pytest.mark.parametrize("n", [2, 4, 8, 16])
+@pytest.mark.parametrize("algo", [ar.AR_ALGO_RING, ar.AR_ALGO_FUSED, ar.AR_ALGO_RHD, ar.AR_ALGO_TREE])
+@pytest.mark.parametrize("dt", [ar.AR_BF16, ar.AR_F16])
+def test_skewed_outputs_at_every_line_slot(n, algo, dt):
+    """2-byte rank buffers whose views start anywhere in their 128-byte lines (output rank r at 9r + 3 elements
+    past a line, input at 5r + 1, both modulo 64): the skewed kernel's stores rotated per output rank onto whole
+    lines, with the held-back slots carried between the tiles of a strip and stored at strip ends; every element
+    against the oracle, nothing written outside the views, out of place and in place, sum and max."""
+    count = 64 * 8 * 53 + 7 * n + 5
+    xs = _inputs(dt, n, count, 28)
+    in_off = [(5 * r + 1) % 64 for r in range(n)]
+    out_off = [(9 * r + 3) % 64 for r in range(n)]
+    for op in (ar.AR_SUM, ar.AR_MAX):
+        want = expect(xs, dt, op, algo)
+        ins = [to_dev(x, dt, offset=in_off[r], guard=64)[1] for r, x in enumerate(xs)]
+        outs = [empty_like_dev(count, dt, offset=out_off[r], guard=64) for r in range(n)]
+        ar.ar_allreduce(ins, [o[1] for o in outs], op, algo)
+        torch.cuda.synchronize()
+        assert_bitwise([from_dev(o[1], dt) for o in outs], want, f"line slots n={n} algo={algo} op={op}")
+        for r, (base, _) in enumerate(outs):
+            bits = from_dev(base, dt)
+            lo = 64 + out_off[r]
+            full = np.iinfo(bits.dtype).max
+            assert np.all(bits[:lo] == full) and np.all(bits[lo + count:] == full), f"guard band rank {r}"
+        ar.ar_allreduce(ins, ins, op, algo)
+        torch.cuda.synchronize()
+        assert_bitwise([from_dev(t, dt) for t in ins], want, f"line slots in place n={n} algo={algo} op={op}")
+
+
 @pytest.mark.parametrize("algo", ONE_PASS)
 @pytest.mark.parametrize("dt,step", [(ar.AR_F32, 1), (ar.AR_BF16, 2), (ar.AR_BF16, 1), (ar.AR_I32, 3)])
 @pytest.mark.parametrize("count", [300_001, 5_000_011])
 def test_rank_buffers_at_different_offsets(algo, dt, step, count):
-    """Rank r at r*step elements past an aligned address: addresses that differ modulo 16 but are multiples of 4
-    (fp32 and int32 at any offset, bf16 at even ones) take 16-byte slots at 4-byte alignment; bf16 at odd offsets
-    goes element by element. Small calls and one-front-sized ones, in place."""
+    """Rank r at r*step elements past an aligned address: 4-byte types take 16-byte slots at 4-byte alignment,
+    bf16 (even offsets among them) the skewed kernel. Small calls and one-front-sized ones, in place."""
     n = 8
     xs = _inputs(dt, n, count, 26)
     ins = [to_dev(x, dt, offset=r * step)[1] for r, x in enumerate(xs)]
