@@ -146,9 +146,9 @@ int ar_chunk_bounds(int nranks, size_t count, int64_t* lo);
  *   differ modulo 16, 4-byte types use vectors from element 0 (slower: they straddle cache lines), and 2-byte
  *   types use aligned vectors shifted per rank, with the stores rotated onto whole 128-byte lines, for RING,
  *   FUSED, RHD and TREE with nranks 2, 4, 8 or 16 (also slower, least when every rank's data starts in the first
- *   16 bytes of a line), else element by element. RING_FP8 uses vectors when every pointer is 16-byte aligned, for any count
- *   (chunk starts off the 16-byte grid take shifted vectors); the other algorithms use vectors only when every
- *   pointer is 16-byte aligned. Otherwise element by element.
+ *   16 bytes of a line), else element by element. RING_FP8 uses vectors when every pointer is 16-byte aligned,
+ *   for any count (chunk starts off the 16-byte grid take shifted vectors); the other algorithms use vectors only
+ *   when every pointer is 16-byte aligned. Otherwise element by element.
  * Errors: AR_ERR_INVALID (enum, nranks, NULL), AR_ERR_UNSUPPORTED (RHD with N not a power of two; FP8
  *   with a dtype other than F32/BF16 or an op other than SUM/AVG), AR_ERR_ALIAS, AR_ERR_WORKSPACE (the
  *   stepwise algorithms on bf16/f16 need ar_allreduce_ws), AR_ERR_HIP. AR_ALGO_AUTO is resolved first, so
