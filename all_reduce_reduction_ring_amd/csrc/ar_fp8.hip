@@ -289,8 +289,8 @@ struct Fp8RingArgs {
   int n;
   int vec;    // 1: every rank buffer starts on a 16-byte boundary
   int strip;  // wave tasks per strip: kStrip<DT> when some chunk start is off the 16-byte grid (bf16 q % 8 or fp32
-              // q % 4 non-zero, or r != 0), or, for bf16 with lrot, off the 128-byte line grid; else 1
-  int lrot;   // bf16: every output buffer sits at the same place in its 128-byte line, lmod elements in, so that the
+              // q % 4 non-zero, or r != 0), or, with lrot, off the 128-byte line grid; else 1
+  int lrot;   // every output buffer sits at the same place in its 128-byte line, lmod elements in, so that the
   int lmod;   //   shifted path can rotate its stores onto whole lines
 };
 
@@ -435,23 +435,24 @@ __device__ __forceinline__ TaskGeo task_geo(const Fp8RingArgs& a, int64_t w) {
   return g;
 }
 
-// bf16 with lrot: the slot (0..7) within its 128-byte output line of the aligned slot at or below task g's first
-// element; the same for every task of a chunk (tasks are 1 KiB apart). 0 otherwise.
+// With lrot: the slot (0..7) within its 128-byte output line of the aligned slot at or below task g's first
+// element; the same for every task of a chunk (tasks are whole lines apart). 0 otherwise.
 template <int DT>
 __device__ __forceinline__ int line_slot(const Fp8RingArgs& a, const TaskGeo& g) {
-  if (DT != AR_BF16 || !a.lrot) return 0;
-  const int64_t a0 = g.lo - (g.lo & 7) + g.t * 4 * kBlock;
-  return static_cast<int>(((a.lmod + a0) >> 3) & 7);
+  if (!a.lrot) return 0;
+  constexpr int kVecElems = DT == AR_BF16 ? 8 : 4;
+  const int64_t a0 = g.lo - (g.lo & (kVecElems - 1)) + g.t * 4 * kBlock;
+  return static_cast<int>(((a.lmod + a0) / kVecElems) & 7);
 }
 
-// The shifted path below takes task g: full, its chunk start off the 16-byte grid (m elements past it) or, for
-// bf16, its first slot off the 128-byte line grid, and every lane's aligned slots inside the buffers (bf16: two
-// slots, 16 elements from the lower one's start, or one when m = 0; fp32: three slots, 12 elements).
+// The shifted path below takes task g: full, its chunk start off the 16-byte grid (m elements past it) or its
+// first slot off the 128-byte line grid, and every lane's aligned slots inside the buffers (bf16: two slots, 16
+// elements from the lower one's start; fp32: three slots, 12 elements; 8 when m = 0).
 template <int DT, int NR>
 __device__ __forceinline__ bool shifted_task(const Fp8RingArgs& a, const TaskGeo& g) {
   if (!(NR > 0) || a.vec == 0 || !g.full) return false;
   const int mis = static_cast<int>(g.lo & (DT == AR_BF16 ? 7 : 3));
-  const int span = DT == AR_BF16 ? (mis ? 16 : 8) : 12;
+  const int span = mis ? (DT == AR_BF16 ? 16 : 12) : 8;
   return (mis != 0 || line_slot<DT>(a, g) != 0) && g.lo + g.t * 4 * kBlock + 63 * kPerLane - mis + span <= a.count;
 }
 
@@ -483,7 +484,7 @@ __global__ __launch_bounds__(kThreads) void fp8_ring_kernel(Fp8RingArgs a) {
   const int64_t nstrips = (a.tasks + a.strip - 1) / a.strip;
   for (int64_t sp = wave0; sp < nstrips; sp += nwaves) {
     u32x4 prev = {0u, 0u, 0u, 0u};  // this lane's result in the previous task (bf16: packed; fp32: upper half)
-    u32x4 prev_low = {0u, 0u, 0u, 0u};  // bf16: the aligned output slot this lane assembled in the previous task
+    u32x4 prev_low = {0u, 0u, 0u, 0u};  // the (last) aligned output slot this lane assembled in the previous task
     bool prev_shifted = false;       // that task took the shifted path (in the same chunk as the next one or not)
     int64_t prev_c = -1;
     TaskGeo gn = task_geo(a, sp * a.strip);
@@ -528,11 +529,11 @@ __global__ __launch_bounds__(kThreads) void fp8_ring_kernel(Fp8RingArgs a) {
 #pragma unroll
         for (int r = 0; r < NR; ++r) Raw8<DT>::store(a.p.out[r], s, p);
       } else if (shifted && DT == AR_F32) {
-        // fp32 with the chunk start m (1..3) elements past the grid, in the aligned path's lane layout: the lane's
-        // groups [F, F + 4) and [F + 64, F + 68) each span two aligned slots, the one at or below the group (loaded
-        // by the lane) and the next (the following group's, taken from its lane with DPP: within the row the next
-        // lane's; after the row's last lane, the group half a block on, or the next row's first). Each load and
-        // store instruction of the wave then covers 256-byte runs instead of every other 16 bytes.
+        // fp32 with the chunk start m (0..3) elements past the grid, in the aligned path's lane layout: the lane's
+        // groups [F, F + 4) and [F + 64, F + 68) each span two aligned slots (one when m = 0), the one at or below
+        // the group (loaded by the lane) and the next (the following group's, taken from its lane with DPP: within
+        // the row the next lane's; after the row's last lane, the group half a block on, or the next row's first).
+        // Each load and store instruction of the wave then covers 256-byte runs instead of every other 16 bytes.
         constexpr int NT = NR > 0 ? NR : 1;
         const int64_t F = lo + bic * kBlock + l16 * 4, G = F + kBlock / 2;
         const int64_t A1 = F - mis, A2 = G - mis;  // multiples of 4; lane 63 reads to A2 + 8 <= count
@@ -546,17 +547,20 @@ __global__ __launch_bounds__(kThreads) void fp8_ring_kernel(Fp8RingArgs a) {
           y2[k] = ld16(base + A2);
           // the slot after the task's last group begins the next task: only the last lane loads it
           n2[k] = u32x4{0u, 0u, 0u, 0u};
-          if (lane == 63) n2[k] = ld16(base + A2 + 4);
+          if (mis != 0 && lane == 63) n2[k] = ld16(base + A2 + 4);
         }
+        if (mis != 0) {
 #pragma unroll
-        for (int k = 0; k < NT; ++k) {
-          // row lane 15: the slot after its first group is lane 0's second slot; after its second, the next row's
-          // (or, for lane 63, the next task's) first slot
-          n1[k] = from_next_in_row(y1[k], rot_row_left(y2[k]));
-          n2[k] = from_next_in_row(y2[k], from_next_lane(y1[k], n2[k]));
+          for (int k = 0; k < NT; ++k) {
+            // row lane 15: the slot after its first group is lane 0's second slot; after its second, the next
+            // row's (or, for lane 63, the next task's) first slot
+            n1[k] = from_next_in_row(y1[k], rot_row_left(y2[k]));
+            n2[k] = from_next_in_row(y2[k], from_next_lane(y1[k], n2[k]));
+          }
         }
         auto widen8 = [&](int k, float (&v)[kPerLane]) {
-          const u32x4 g1 = shift4_by(mis, y1[k], n1[k]), g2 = shift4_by(mis, y2[k], n2[k]);
+          const u32x4 g1 = mis ? shift4_by(mis, y1[k], n1[k]) : y1[k];
+          const u32x4 g2 = mis ? shift4_by(mis, y2[k], n2[k]) : y2[k];
 #pragma unroll
           for (int i = 0; i < 4; ++i) {
             v[i] = __uint_as_float(g1[i]);
@@ -580,21 +584,45 @@ __global__ __launch_bounds__(kThreads) void fp8_ring_kernel(Fp8RingArgs a) {
         }
         // the group before each of ours: within the row the previous lane's; before the row's lane 0, the previous
         // row's last second group (the previous task's, carried, for lane 0) or this row's lane 15 first group
-        const u32x4 b1 = from_prev_in_row(o1, from_prev_lane(o2, last));
-        const u32x4 b2 = from_prev_in_row(o2, rot_row_right(o1));
-        const u32x4 s1 = shift4_by(4 - mis, b1, o1);  // [A1, A1 + 4)
-        const u32x4 s2 = shift4_by(4 - mis, b2, o2);  // [A2, A2 + 4)
+        u32x4 s1 = o1, s2 = o2;  // [A1, A1 + 4) and [A2, A2 + 4)
+        if (mis != 0) {
+          s1 = shift4_by(4 - mis, from_prev_in_row(o1, from_prev_lane(o2, last)), o1);
+          s2 = shift4_by(4 - mis, from_prev_in_row(o2, rot_row_right(o1)), o2);
+        }
+        // Rotated by kl slots onto whole 128-byte lines (as in the bf16 path): a row's first-group instruction
+        // stores its 16 slots from kl slots earlier, the first kl of them the previous row's last second-group
+        // slots (row 0: the previous task's, held back by it); its second-group instruction stores the rest of
+        // the row's run, the first kl of them from the row's own first-group slots.
+        const int kl = line_slot<DT>(a, g);
+        const int src1 = ((lane - kl) & 63) << 2;
+        const int src2 = (l16 >= kl ? lane - kl : lane + 16 - kl) << 2;
+        u32x4 r1, r2;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int s1c = __builtin_amdgcn_ds_bpermute(src1, static_cast<int>(s1[i]));
+          const int s2p = __builtin_amdgcn_ds_bpermute(src1, static_cast<int>(s2[i]));
+          const int s2o = __builtin_amdgcn_ds_bpermute(src1, static_cast<int>(prev_low[i]));
+          r1[i] = static_cast<uint32_t>(l16 >= kl ? s1c : (row > 0 ? s2p : s2o));
+          const int s2c = __builtin_amdgcn_ds_bpermute(src2, static_cast<int>(s2[i]));
+          const int s1r = __builtin_amdgcn_ds_bpermute(src2, static_cast<int>(s1[i]));
+          r2[i] = static_cast<uint32_t>(l16 >= kl ? s2c : s1r);
+        }
+        const int64_t R1 = A1 - 4 * kl, R2 = A2 - 4 * kl;  // the slots this lane stores
 #pragma unroll
         for (int r = 0; r < NT; ++r) {
           float* out = static_cast<float*>(a.p.out[r]);
-          if (lane > 0 || carried) st16(out + A1, s1);
-          else  // [F, A1 + 4): the rest of the slot below belongs to the previous task
-            for (int q = 0; q < 4 - mis; ++q) store_elem<AR_F32>(out, F + q, __float_as_uint(p[q]));
-          st16(out + A2, s2);
+          if (row > 0 || lane > kl || carried || (lane == kl && mis == 0)) {
+            st16(out + R1, r1);
+          } else if (lane == kl) {  // the task's first slot: [F, A1 + 4) is ours, the rest the previous task's
+            for (int q = mis; q < 4; ++q) store_elem<AR_F32>(out, R1 + q, r1[q]);
+          }
+          st16(out + R2, r2);
+          if (!next_shifted && lane >= 64 - kl) st16(out + A2, s2);  // nothing will carry them: store them here
           if (lane == 63 && !next_shifted)  // [A2 + 4, G + 4): the rest of the slot above is the next task's
             for (int q = 4 - mis; q < 4; ++q) store_elem<AR_F32>(out, G + q, __float_as_uint(p[4 + q]));
         }
         prev = o2;
+        prev_low = s2;
       } else if (shifted && DT == AR_BF16) {
         constexpr int NT = NR > 0 ? NR : 1;
         const int64_t A = e0 - mis;  // a multiple of 8 elements; A + 16 <= count, so both slots are in the buffer
@@ -746,19 +774,20 @@ hipError_t launch_fp8_ring(const RankPtrs& p, int n, int64_t count, int dtype, i
   // chunk starts on the 16-byte grid: q a multiple of 8 bf16 or 4 fp32 elements (and no remainder)
   const int strip = dtype == AR_BF16 ? kStrip<AR_BF16> : kStrip<AR_F32>;
   a.strip = (vec && !(a.r == 0 && a.q % (dtype == AR_BF16 ? 8 : 4) == 0)) ? strip : 1;
-  // bf16 outputs all at one place in their 128-byte lines: the shifted path rotates its stores onto whole lines,
+  // outputs all at one place in their 128-byte lines: the shifted path rotates its stores onto whole lines,
   // which needs strips wherever a chunk starts off the line grid
   a.lrot = 0;
   a.lmod = 0;
-  if (vec && dtype == AR_BF16) {
+  if (vec) {
+    const int es = dtype == AR_BF16 ? 2 : 4;
     const uintptr_t m0 = reinterpret_cast<uintptr_t>(p.out[0]) % 128;
     bool same = true;
     for (int r = 1; r < n; ++r) same = same && reinterpret_cast<uintptr_t>(p.out[r]) % 128 == m0;
     if (same) {
       a.lrot = 1;
-      a.lmod = static_cast<int>(m0 / 2);
+      a.lmod = static_cast<int>(m0 / es);
       for (int c = 0; c < n && a.strip == 1; ++c)
-        if ((a.lmod + c * a.q + (c < a.r ? c : a.r)) % 64 != 0) a.strip = strip;
+        if ((a.lmod + c * a.q + (c < a.r ? c : a.r)) % (128 / es) != 0) a.strip = strip;
     }
   }
   if (dtype == AR_BF16) return op == AR_AVG ? ring_n<AR_BF16, AR_AVG>(a, s) : ring_n<AR_BF16, AR_SUM>(a, s);

@@ -559,24 +559,27 @@ def test_fp8_ring_chunks_off_the_16_byte_grid(n, extra, dt):
 
 
 @pytest.mark.parametrize("n", [2, 4, 8])
-@pytest.mark.parametrize("q", [4096 + 8, 4096 + 24, 4096 + 64 + 56, 4096 + 3])
+@pytest.mark.parametrize("q", [4096 + 8, 4096 + 24, 4096 + 64 + 56, 4096 + 3, 4096 + 4, 4096 + 13])
 @pytest.mark.parametrize("out_offs", ["aligned", "common_16B", "common_80B", "mixed"])
-def test_fp8_ring_chunk_starts_off_the_line_grid(n, q, out_offs):
-    """bf16 chunk starts on the 16-byte grid but off the 128-byte line grid (q = 4104, 4120, 4216 elements per
-    chunk), or off both (4099), with every output buffer at the same place in its line (aligned, 16 or 80 bytes
-    in: the rotated aligned stores) or at different places (rank r at 16 (r % 2) bytes: unrotated): bitwise
-    against the oracle, every element of every rank."""
+@pytest.mark.parametrize("dt", [ar.AR_BF16, ar.AR_F32])
+def test_fp8_ring_chunk_starts_off_the_line_grid(n, q, out_offs, dt):
+    """Chunk starts on the 16-byte grid but off the 128-byte line grid (bf16: q = 4104, 4120, 4216 elements per
+    chunk; fp32: also 4100), or off both (4099, 4109), with every output buffer at the same place in its line
+    (aligned, 16 or 80 bytes in: the rotated aligned stores) or at different places (rank r at 16 (r % 2) bytes:
+    unrotated): bitwise against the oracle, every element of every rank."""
     count = n * q
-    xs = inputs.rank_inputs("outlier_bf16", n, count, cfg=7, extra=(n, q))
-    offs = {"aligned": [0] * n, "common_16B": [8] * n, "common_80B": [40] * n,
-            "mixed": [8 * (r % 2) for r in range(n)]}[out_offs]
-    ins = [to_dev(x, ar.AR_BF16)[1] for x in xs]
-    outs = [empty_like_dev(count, ar.AR_BF16, offset=o, guard=64)[1] for o in offs]
+    kind = "outlier_bf16" if dt == ar.AR_BF16 else "uniform_f32"
+    xs = inputs.rank_inputs(kind, n, count, cfg=7, extra=(n, q))
+    per16 = 8 if dt == ar.AR_BF16 else 4  # elements in 16 bytes
+    offs = {"aligned": [0] * n, "common_16B": [per16] * n, "common_80B": [5 * per16] * n,
+            "mixed": [per16 * (r % 2) for r in range(n)]}[out_offs]
+    ins = [to_dev(x, dt)[1] for x in xs]
+    outs = [empty_like_dev(count, dt, offset=o, guard=64)[1] for o in offs]
     for op in (ar.AR_SUM, ar.AR_AVG):
         ar.ar_allreduce(ins, outs, op, ar.AR_ALGO_RING_FP8)
         torch.cuda.synchronize()
-        assert_bitwise([from_dev(o, ar.AR_BF16) for o in outs], expect(xs, ar.AR_BF16, op, ar.AR_ALGO_RING_FP8),
-                       f"fp8 ring n={n} q={q} outputs {out_offs}")
+        assert_bitwise([from_dev(o, dt) for o in outs], expect(xs, dt, op, ar.AR_ALGO_RING_FP8),
+                       f"fp8 ring n={n} q={q} dt={dt} outputs {out_offs}")
 
 
 @pytest.mark.parametrize("n", [1, 2, 3, 5, 8])
