@@ -413,6 +413,19 @@ __device__ __forceinline__ void shift_ranks_by(int m, const u32x4 (&x0)[NR], con
   }
 }
 
+// Elements [b, e) of the aligned slot of 8 bf16 at s, from its packed value v: a 4-byte store for each pair inside
+// the range, a 2-byte store for a pair it cuts (b and e wave-uniform, so the choice costs no vector instructions;
+// the element loop it replaces indexed registers by a varying q, which took 4% of the time of a ragged N = 8 call).
+__device__ __forceinline__ void store_bf16_part(uint16_t* s, const u32x4& v, int b, int e) {
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const bool lo = 2 * i >= b && 2 * i < e, hi = 2 * i + 1 >= b && 2 * i + 1 < e;
+    if (lo && hi) *gptr<uint32_t>(s + 2 * i) = v[i];
+    else if (lo) *gptr<uint16_t>(s + 2 * i) = static_cast<uint16_t>(v[i]);
+    else if (hi) *gptr<uint16_t>(s + 2 * i + 1) = static_cast<uint16_t>(v[i] >> 16);
+  }
+}
+
 // Wave task w: its chunk c, its index t in the chunk (tasks run 4 blocks of 128 elements from the chunk start),
 // the chunk bounds, and whether every lane holds 8 elements of the chunk (full). Wave-uniform.
 struct TaskGeo {
@@ -614,12 +627,17 @@ __global__ __launch_bounds__(kThreads) void fp8_ring_kernel(Fp8RingArgs a) {
           if (row > 0 || lane > kl || carried || (lane == kl && mis == 0)) {
             st16(out + R1, r1);
           } else if (lane == kl) {  // the task's first slot: [F, A1 + 4) is ours, the rest the previous task's
-            for (int q = mis; q < 4; ++q) store_elem<AR_F32>(out, R1 + q, r1[q]);
+#pragma unroll
+            for (int q = 0; q < 4; ++q)  // fixed indices, wave-uniform conditions
+              if (q >= mis) store_elem<AR_F32>(out, R1 + q, r1[q]);
           }
           st16(out + R2, r2);
           if (!next_shifted && lane >= 64 - kl) st16(out + A2, s2);  // nothing will carry them: store them here
-          if (lane == 63 && !next_shifted)  // [A2 + 4, G + 4): the rest of the slot above is the next task's
-            for (int q = 4 - mis; q < 4; ++q) store_elem<AR_F32>(out, G + q, __float_as_uint(p[4 + q]));
+          if (lane == 63 && !next_shifted) {  // [A2 + 4, G + 4): the rest of the slot above is the next task's
+#pragma unroll
+            for (int q = 1; q < 4; ++q)
+              if (q >= 4 - mis) store_elem<AR_F32>(out, G + q, __float_as_uint(p[4 + q]));
+          }
         }
         prev = o2;
         prev_low = s2;
@@ -676,17 +694,24 @@ __global__ __launch_bounds__(kThreads) void fp8_ring_kernel(Fp8RingArgs a) {
           rot[i] = static_cast<uint32_t>(lane >= kl ? cur : old);
         }
         const int64_t As = A - 8 * kl;  // the slot this lane stores: lane j - kl's
+        // [A + 8, A + 8 + m): lane 63's last m elements, at the start of the slot above, which the next task stores
+        // whole when it is in the strip; else lane 63 stores them here
+        const bool tail = !next_shifted && mis != 0;
+        u32x4 top[1] = {o};
+        if (tail) {
+          const u32x4 one[1] = {o};
+          shift_ranks_by<1>(8 - mis, one, one, top);
+        }
 #pragma unroll
         for (int r = 0; r < NT; ++r) {
           uint16_t* out = static_cast<uint16_t*>(a.p.out[r]);
           if (lane > kl || carried || (lane == kl && mis == 0)) {
             st16(out + As, rot);
           } else if (lane == kl) {  // the task's first slot: [A + m, A + 8) is ours, the rest the previous task's
-            for (int q = mis; q < 8; ++q) store_elem<AR_BF16>(out, As + q, (rot[q >> 1] >> (16 * (q & 1))) & 0xFFFFu);
+            store_bf16_part(out + As, rot, mis, 8);
           }
           if (!next_shifted && lane >= 64 - kl) st16(out + A, low[0]);  // nothing will carry them: store them here
-          if (lane == 63 && !next_shifted)  // [A + 8, A + 8 + m): the rest of the slot above is the next task's
-            for (int q = 8 - mis; q < kPerLane; ++q) store_elem<AR_BF16>(out, e0 + q, narrow<AR_BF16>(p[q]));
+          if (tail && lane == 63) store_bf16_part(out + A + 8, top[0], 0, mis);
         }
         prev = o;
         prev_low = low[0];

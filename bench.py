@@ -666,6 +666,9 @@ def main():
     p.add_argument("--fp8-only", action="store_true",
                    help="time only the compressed ring on its workload (8 x 67,108,864 bf16, 0.1%% outliers; for "
                         "profiler runs)")
+    p.add_argument("--fp8-extra", type=int, default=0, metavar="E",
+                   help="with --fp8-only: E more elements per rank (a count off the multiples of 8 N puts chunk "
+                        "starts inside 16-byte slots, the compressed ring's shifted path)")
     p.add_argument("--ring-bytes-per-rank", type=int, metavar="S",
                    help="time only the ring on N = 8 fp32 ranks of S bytes each, sum (for profiler runs at one size)")
     p.add_argument("--per-rank-offsets-only", action="store_true",
@@ -730,7 +733,7 @@ def main():
         return
 
     if args.fp8_only:
-        n8 = 67_108_864
+        n8 = 67_108_864 + args.fp8_extra
         log("generating the compressed-ring inputs")
         h8 = _gen_parallel(lambda r: inputs.outlier_bf16((5, r), n8), range(N_RANKS))
         i8 = _upload(torch, h8, torch.bfloat16, dev)
@@ -741,7 +744,8 @@ def main():
         torch.cuda.synchronize()
         ms = Timer(torch).run(step, args.steps)
         t = float(np.mean(ms)) * 1e-3
-        print(json.dumps({"fp8_ring": {"kernel_us": stats_us(ms), "hbm_GBps": ring_bytes(N_RANKS, n8, 2) / t / GB,
+        print(json.dumps({"fp8_ring": {"count": n8, "kernel_us": stats_us(ms),
+                                       "hbm_GBps": ring_bytes(N_RANKS, n8, 2) / t / GB,
                                        "busbw_GBps": n8 * 2 / t / GB * bus_factor(N_RANKS),
                                        "steps": args.steps, "warmup": args.warmup}}))
         return
