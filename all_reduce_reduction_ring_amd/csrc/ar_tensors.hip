@@ -10,7 +10,8 @@
 // that. (Bucket pads are zeros that never mix with other elements, so they need not exist.)
 //
 // Work: tiles of kThreads 16-byte slots of one tensor, dealt out round-robin over a grid sized to the GPU (tile g to
-// block g mod G). Each block stages kThreads tensor descriptors at a time in LDS and prefix-sums their tile counts.
+// block g mod G). Each block stages kThreads tensor descriptors at a time in LDS (with their rank pointers for up
+// to 8 ranks) and prefix-sums their tile counts.
 // A tile normally lies inside one bucket chunk, so the rank rotation is uniform across the block; a tile
 // that crosses a chunk boundary is processed as uniform sub-ranges.
 #ifndef AR_TENSOR_THREADS
@@ -141,11 +142,25 @@ __device__ __forceinline__ uint32_t fold_elem(const void* const* ip, int n, int 
   return narrow<DT>(finalize<OP>(acc, n));
 }
 
+// A value the whole wave holds alike, moved to scalar registers.
+__device__ __forceinline__ int64_t uniform64(int64_t v) {
+  const uint32_t lo = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(v));
+  const uint32_t hi = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(static_cast<uint64_t>(v) >> 32));
+  return static_cast<int64_t>((static_cast<uint64_t>(hi) << 32) | lo);
+}
+
 template <int DT, int OP, int NR, int SHAPE>
 __global__ __launch_bounds__(kThreads) void tensor_kernel(TensorArgs a) {
   constexpr int V = Traits<DT>::kVec;
   constexpr int64_t TE = static_cast<int64_t>(kThreads) * V;  // elements per tile
   __shared__ int64_t s_numel[kBatch], s_off[kBatch], s_clen[kBatch], pre[kBatch];
+  // the batch's rank pointers, in and out, and whether all of a tensor's are 4-byte aligned (NR <= 8: up to
+  // 32 KiB; larger and runtime rank counts read the caller's table at each tensor the block reaches)
+  constexpr bool kStage = NR > 0 && NR <= 8;
+  constexpr int NS = kStage ? NR : 1;
+  __shared__ const void* s_ip[kStage ? kBatch * NS : 1];
+  __shared__ void* s_op[kStage ? kBatch * NS : 1];
+  __shared__ int s_vec[kBatch];
   const int n = NR > 0 ? NR : a.n;
   constexpr int NT = NR > 0 ? NR : 1;
   const int64_t G = gridDim.x, b = blockIdx.x;
@@ -160,6 +175,21 @@ __global__ __launch_bounds__(kThreads) void tensor_kernel(TensorArgs a) {
       s_off[t] = d.bucket_offset;
       s_clen[t] = d.chunk_len;
       nt = d.numel > 0 ? (d.numel + TE - 1) / TE : 0;
+      const void* const* ipt = a.in + static_cast<int64_t>(b0 + t) * n;
+      void* const* opt = a.out + static_cast<int64_t>(b0 + t) * n;
+      uintptr_t anyp = 0;
+      for (int r = 0; r < n; ++r) {
+        const void* ip = ipt[r];
+        void* op = opt[r];
+        anyp |= reinterpret_cast<uintptr_t>(ip) | reinterpret_cast<uintptr_t>(op);
+        if constexpr (kStage) {
+          s_ip[t * NS + r] = ip;
+          s_op[t * NS + r] = op;
+        }
+      }
+      // 16-byte accesses need 4-byte alignment only (a tensor at another offset straddles cache lines); the
+      // halving tree for a runtime rank count is evaluated per element
+      s_vec[t] = (anyp & 3u) == 0 && !(SHAPE == kHalving && NR == 0);
     }
     pre[t] = nt;
     __syncthreads();
@@ -174,30 +204,38 @@ __global__ __launch_bounds__(kThreads) void tensor_kernel(TensorArgs a) {
     // (a cursor instead of a search per tile), and a tensor's rank pointers, loaded once when the block reaches it,
     // stay in registers for all of its tiles that the block takes.
     int lo = 0, cur = -1;
+    int64_t lim = pre[0];  // the first tile past the batch entry lo
     const void* const* ipg = nullptr;  // the tensor's rank pointers in the caller's table (element path)
     void* const* opg = nullptr;
     const void* ipv[NT];  // the same, in registers (vector path, rank count known at compile time)
     void* opv[NT];
     bool vec = false;
     int64_t numel = 0, boff = 0, clen = 0, tile0 = 0;
+    // the bucket chunk holding the current position of the tensor, and the tensor element where the next begins
+    // (the block's positions in a tensor only increase, so the division runs once per chunk crossed)
+    int c = 0;
+    int64_t cb = -1;
     for (int64_t g = base + ((b - base % G) % G + G) % G; g < base + batch_tiles; g += G) {
       const int64_t lt = g - base;
-      while (pre[lo] <= lt) ++lo;  // stops below m: pre[m - 1] = batch_tiles > lt
+      while (lim <= lt) lim = pre[++lo];  // stops below m: pre[m - 1] = batch_tiles > lt
       const int ti = __builtin_amdgcn_readfirstlane(b0 + lo);
       if (ti != cur) {
         cur = ti;
-        numel = s_numel[lo];
-        boff = s_off[lo];
-        clen = s_clen[lo];
-        tile0 = lo > 0 ? pre[lo - 1] : 0;
+        numel = uniform64(s_numel[lo]);
+        boff = uniform64(s_off[lo]);
+        clen = uniform64(s_clen[lo]);
+        tile0 = uniform64(lo > 0 ? pre[lo - 1] : 0);
         ipg = a.in + static_cast<int64_t>(ti) * n;
         opg = a.out + static_cast<int64_t>(ti) * n;
-        uintptr_t anyp = 0;
-        for (int r = 0; r < n; ++r) anyp |= reinterpret_cast<uintptr_t>(ipg[r]) | reinterpret_cast<uintptr_t>(opg[r]);
-        // the halving tree for a runtime rank count is evaluated per element
-        // 16-byte accesses need 4-byte alignment only (a tensor at another offset straddles cache lines)
-        vec = (anyp & 3u) == 0 && !(SHAPE == kHalving && NR == 0);
-        if constexpr (NR > 0) {
+        vec = __builtin_amdgcn_readfirstlane(s_vec[lo]) != 0;
+        cb = -1;
+        if constexpr (kStage) {
+#pragma unroll
+          for (int r = 0; r < NR; ++r) {
+            ipv[r] = reinterpret_cast<const void*>(uniform64(reinterpret_cast<int64_t>(s_ip[lo * NS + r])));
+            opv[r] = reinterpret_cast<void*>(uniform64(reinterpret_cast<int64_t>(s_op[lo * NS + r])));
+          }
+        } else if constexpr (NR > 0) {
 #pragma unroll
           for (int r = 0; r < NR; ++r) {
             ipv[r] = ipg[r];
@@ -213,11 +251,13 @@ __global__ __launch_bounds__(kThreads) void tensor_kernel(TensorArgs a) {
         int start = 0;
         int64_t s1 = e1;
         if (SHAPE == kLinear && a.rot && clen > 0) {
-          int64_t c = (boff + s0) / clen;
-          c = c < 0 ? 0 : (c < n ? c : n - 1);
-          start = static_cast<int>(c);
-          const int64_t bnd = (c + 1) * clen - boff;  // next chunk boundary, in tensor elements
-          s1 = bnd < e1 ? bnd : e1;
+          if (s0 >= cb) {
+            const int64_t q = (boff + s0) / clen;
+            c = static_cast<int>(q < 0 ? 0 : (q < n ? q : n - 1));
+            cb = (c + 1) * clen - boff;  // next chunk boundary, in tensor elements
+          }
+          start = c;
+          s1 = cb < e1 ? cb : e1;
           if (s1 <= s0) s1 = e1;  // only a malformed descriptor gets here; always make progress
         }
         // whole slots (tile starts and, for a valid plan, chunk boundaries are slot-aligned); the tensor's
