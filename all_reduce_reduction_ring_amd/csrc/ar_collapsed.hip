@@ -736,11 +736,19 @@ __global__ __launch_bounds__(kThreads) void skew_kernel(SkewArgs s) {
   }
 }
 
+// Workgroups per CU before the scale above: the one-pass kernels' count, and for the rank counts the skewed kernel
+// alone builds (3, 5, 6, 7; ring and rank order) that of the next power of two, whose loads in flight per thread
+// they come closest to. (With 3 and 4 ranks more workgroups are asked for than fit at once; capping the grid at
+// the resident count measured 4-8% slower at 64 MiB of bf16 per rank and level at 256 MiB.)
+template <int NR> constexpr int skew_blocks_per_cu() {
+  return NR == 3 ? blocks_per_cu<4>() : (NR > 4 && NR < 8) ? blocks_per_cu<8>() : blocks_per_cu<NR>();
+}
+
 template <int DT, int OP, int NR, int SHAPE>
 hipError_t launch_skew(SkewArgs& s, hipStream_t st) {
   constexpr int V = Traits<DT>::kVec;
   const int64_t tiles = (s.f.count + 64 * V - 1) / (64 * V);
-  const int64_t gmax = static_cast<int64_t>(cu_count()) * blocks_per_cu<NR>() * AR_SKEW_GRID_SCALE;
+  const int64_t gmax = static_cast<int64_t>(cu_count()) * skew_blocks_per_cu<NR>() * AR_SKEW_GRID_SCALE;
   // long strips once every wave of the full grid gets at least one
   s.strip = tiles >= static_cast<int64_t>(kSkewStripLong) * gmax * (kThreads / 64) ? kSkewStripLong : kSkewStripShort;
   const int64_t strips = (tiles + s.strip - 1) / s.strip;
@@ -759,8 +767,18 @@ hipError_t skew_n(SkewArgs& s, hipStream_t st) {
     case 4: return launch_skew<DT, OP, 4, SHAPE>(s, st);
     case 8: return launch_skew<DT, OP, 8, SHAPE>(s, st);
     case 16: return launch_skew<DT, OP, 16, SHAPE>(s, st);
-    default: return hipErrorInvalidValue;
+    default: break;
   }
+  if constexpr (SHAPE == kLinear) {  // the trees need a power-of-two rank count here
+    switch (s.f.n) {
+      case 3: return launch_skew<DT, OP, 3, SHAPE>(s, st);
+      case 5: return launch_skew<DT, OP, 5, SHAPE>(s, st);
+      case 6: return launch_skew<DT, OP, 6, SHAPE>(s, st);
+      case 7: return launch_skew<DT, OP, 7, SHAPE>(s, st);
+      default: break;
+    }
+  }
+  return hipErrorInvalidValue;
 }
 
 template <int DT, int OP>
@@ -784,16 +802,17 @@ hipError_t skew_op(SkewArgs& s, int op, int algo, hipStream_t st) {
 }
 
 // The skewed-buffer kernel takes a call of 2-byte elements when the 2N addresses are element-aligned and not all
-// equal modulo 16 (views at different offsets), the rank count is 2, 4, 8 or 16, the algorithm is a one-pass one,
-// and there are a few wave tiles of work; it fills the per-rank offsets. Addresses that are all multiples of 4
+// equal modulo 16 (views at different offsets), the algorithm is a one-pass one with a rank count of 2, 4, 8 or 16,
+// or the ring or rank order with 3, 5, 6 or 7 ranks, and there are a few wave tiles of work; it fills the per-rank
+// offsets. Addresses that are all multiples of 4
 // bytes come here too rather than to the one-front kernel's 16-byte accesses at 4-byte alignment, whose store
 // windows straddle lines.
 template <int DT>
 bool plan_skew(const RankPtrs& p, int n, int64_t count, int algo, SkewArgs& s) {
   constexpr int ES = Traits<DT>::kSize, V = Traits<DT>::kVec;
-  if (!(algo == AR_ALGO_RING || algo == AR_ALGO_FUSED || algo == AR_ALGO_RHD || algo == AR_ALGO_TREE) ||
-      !(n == 2 || n == 4 || n == 8 || n == 16))
-    return false;
+  const bool linear = algo == AR_ALGO_RING || algo == AR_ALGO_FUSED;
+  if (!(linear || algo == AR_ALGO_RHD || algo == AR_ALGO_TREE)) return false;
+  if (!(n == 2 || n == 4 || n == 8 || n == 16 || (linear && (n == 3 || n == 5 || n == 6 || n == 7)))) return false;
   if (count < 4 * 64 * V) return false;
   bool differ = false;
   s.any_kl = 0;

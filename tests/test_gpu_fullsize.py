@@ -89,6 +89,29 @@ def test_headline_size_at_odd_per_rank_offsets():
 
 
 @pytest.mark.timeout(600)
+@pytest.mark.parametrize("n,count", [(3, 134_217_737), (7, 40_000_003)])
+def test_odd_per_rank_offsets_three_and_seven_ranks_long_strips(n, count):
+    """The skewed kernel's builds for rank counts that are not a power of two, at sizes where it walks long strips
+    (32 tiles per wave): rank r's input r elements and its output 3r + 2 elements past an aligned address, ragged
+    chunks, ring order and rank order, every element of every rank against the oracle."""
+    host = _par(lambda r: inputs.normal_bf16((7, n, r), count), range(n))
+    ibase = [torch.empty(count + 32, dtype=torch.bfloat16, device=DEV) for _ in range(n)]
+    obase = [torch.empty(count + 32, dtype=torch.bfloat16, device=DEV) for _ in range(n)]
+    ins = [b[r:r + count] for r, b in enumerate(ibase)]
+    outs = [b[3 * r + 2:3 * r + 2 + count] for r, b in enumerate(obase)]
+    for t, h in zip(ins, _up(host, torch.bfloat16)):
+        t.copy_(h)
+    torch.cuda.synchronize()
+    for algo, fn in ((ar.AR_ALGO_RING, oracle.ring_allreduce), (ar.AR_ALGO_FUSED, oracle.fused_allreduce)):
+        print(f"case n={n} count={count} algo={algo}", flush=True)
+        ar.ar_allreduce(ins, outs, ar.AR_SUM, algo)
+        torch.cuda.synchronize()
+        want = fn(host, oracle.BF16, oracle.SUM)
+        for r in range(n):
+            np.testing.assert_array_equal(_down_bits(outs[r]), want[r], err_msg=f"algo {algo} rank {r}")
+
+
+@pytest.mark.timeout(600)
 def test_headline_size_reduce_scatter_all_gather_and_tree():
     """The headline inputs through reduce-scatter then all-gather (must equal the ring all-reduce, every element)
     and through the binomial tree (against its own oracle, every element)."""

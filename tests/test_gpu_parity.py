@@ -210,9 +210,16 @@ def test_inputs_and_outputs_at_different_offsets(algo, in_off, out_off):
     assert_bitwise([from_dev(o, dt) for o in outs], expect(xs, dt, ar.AR_MAX, algo), f"{in_off}/{out_off} {algo}")
 
 
-@pytest.mark.parametrize("n", [2, 4, 8, 16])
+# Rank counts and one-pass orders for buffers at per-rank offsets: the skewed kernel's builds (2, 4, 8, 16 for every
+# order; 3, 5, 6, 7 for the ring and rank order, the trees there going element by element) and halving-doubling
+# only where it is defined (a power of two).
+SKEW_CASES = [(n, algo) for n in (2, 3, 4, 5, 6, 7, 8, 16)
+              for algo in (ar.AR_ALGO_RING, ar.AR_ALGO_FUSED, ar.AR_ALGO_RHD, ar.AR_ALGO_TREE)
+              if not (algo == ar.AR_ALGO_RHD and n & (n - 1))]
+
+
+@pytest.mark.parametrize("n,algo", SKEW_CASES)
 @pytest.mark.parametrize("dt", [ar.AR_F32, ar.AR_BF16, ar.AR_F16, ar.AR_I32])
-@pytest.mark.parametrize("algo", [ar.AR_ALGO_RING, ar.AR_ALGO_FUSED, ar.AR_ALGO_RHD, ar.AR_ALGO_TREE])
 def test_skewed_rank_buffers_every_residue(n, dt, algo):
     """Every rank's input and output at an element offset of its own (residues modulo 16 bytes all over, inputs
     and outputs different). 2-byte types (odd offsets among them): aligned loads shifted per rank, aligned stores
@@ -242,8 +249,7 @@ def test_skewed_rank_buffers_every_residue(n, dt, algo):
             assert_bitwise([from_dev(t, dt) for t in ins], want, f"skewed in place n={n} dt={dt} count={count}")
 
 
-@pytest.mark.parametrize("n", [2, 4, 8, 16])
-@pytest.mark.parametrize("algo", [ar.AR_ALGO_RING, ar.AR_ALGO_FUSED, ar.AR_ALGO_RHD, ar.AR_ALGO_TREE])
+@pytest.mark.parametrize("n,algo", SKEW_CASES)
 @pytest.mark.parametrize("dt", [ar.AR_BF16, ar.AR_F16])
 def test_skewed_outputs_at_every_line_slot(n, algo, dt):
     """2-byte rank buffers whose views start anywhere in their 128-byte lines (output rank r at 9r + 3 elements
