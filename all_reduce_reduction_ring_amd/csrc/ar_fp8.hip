@@ -463,7 +463,7 @@ __device__ __forceinline__ int line_slot(const Fp8RingArgs& a, const TaskGeo& g)
 // elements from the lower one's start; fp32: three slots, 12 elements; 8 when m = 0).
 template <int DT, int NR>
 __device__ __forceinline__ bool shifted_task(const Fp8RingArgs& a, const TaskGeo& g) {
-  if (!(NR > 0) || a.vec == 0 || !g.full) return false;
+  if (a.vec == 0 || !g.full) return false;
   const int mis = static_cast<int>(g.lo & (DT == AR_BF16 ? 7 : 3));
   const int span = mis ? (DT == AR_BF16 ? 16 : 12) : 8;
   return (mis != 0 || line_slot<DT>(a, g) != 0) && g.lo + g.t * 4 * kBlock + 63 * kPerLane - mis + span <= a.count;
@@ -550,44 +550,72 @@ __global__ __launch_bounds__(kThreads) void fp8_ring_kernel(Fp8RingArgs a) {
         constexpr int NT = NR > 0 ? NR : 1;
         const int64_t F = lo + bic * kBlock + l16 * 4, G = F + kBlock / 2;
         const int64_t A1 = F - mis, A2 = G - mis;  // multiples of 4; lane 63 reads to A2 + 8 <= count
-        u32x4 y1[NT], y2[NT], n1[NT], n2[NT];
-#pragma unroll
-        for (int k = 0; k < NT; ++k) {
-          int rr = start + k;
-          rr = rr >= NT ? rr - NT : rr;
-          const float* base = static_cast<const float*>(a.p.in[rr]);
-          y1[k] = ld16(base + A1);
-          y2[k] = ld16(base + A2);
-          // the slot after the task's last group begins the next task: only the last lane loads it
-          n2[k] = u32x4{0u, 0u, 0u, 0u};
-          if (mis != 0 && lane == 63) n2[k] = ld16(base + A2 + 4);
-        }
-        if (mis != 0) {
-#pragma unroll
+        if constexpr (NR > 0) {
+          u32x4 y1[NT], y2[NT], n1[NT], n2[NT];
+  #pragma unroll
           for (int k = 0; k < NT; ++k) {
-            // row lane 15: the slot after its first group is lane 0's second slot; after its second, the next
-            // row's (or, for lane 63, the next task's) first slot
-            n1[k] = from_next_in_row(y1[k], rot_row_left(y2[k]));
-            n2[k] = from_next_in_row(y2[k], from_next_lane(y1[k], n2[k]));
+            int rr = start + k;
+            rr = rr >= NT ? rr - NT : rr;
+            const float* base = static_cast<const float*>(a.p.in[rr]);
+            y1[k] = ld16(base + A1);
+            y2[k] = ld16(base + A2);
+            // the slot after the task's last group begins the next task: only the last lane loads it
+            n2[k] = u32x4{0u, 0u, 0u, 0u};
+            if (mis != 0 && lane == 63) n2[k] = ld16(base + A2 + 4);
+          }
+          if (mis != 0) {
+  #pragma unroll
+            for (int k = 0; k < NT; ++k) {
+              // row lane 15: the slot after its first group is lane 0's second slot; after its second, the next
+              // row's (or, for lane 63, the next task's) first slot
+              n1[k] = from_next_in_row(y1[k], rot_row_left(y2[k]));
+              n2[k] = from_next_in_row(y2[k], from_next_lane(y1[k], n2[k]));
+            }
+          }
+          auto widen8 = [&](int k, float (&v)[kPerLane]) {
+            const u32x4 g1 = mis ? shift4_by(mis, y1[k], n1[k]) : y1[k];
+            const u32x4 g2 = mis ? shift4_by(mis, y2[k], n2[k]) : y2[k];
+  #pragma unroll
+            for (int i = 0; i < 4; ++i) {
+              v[i] = __uint_as_float(g1[i]);
+              v[i + 4] = __uint_as_float(g2[i]);
+            }
+          };
+          widen8(0, p);
+  #pragma unroll
+          for (int k = 1; k < NT; ++k) {
+            float own[kPerLane];
+            widen8(k, own);
+            hop(p, own);
+          }
+        } else {
+          // a rank count known only at run time: each rank's groups loaded, moved and shifted in turn
+          auto rank_groups = [&](int rr, float (&v)[kPerLane]) {
+            const float* base = static_cast<const float*>(a.p.in[rr]);
+            u32x4 g1 = ld16(base + A1), g2 = ld16(base + A2), n2 = u32x4{0u, 0u, 0u, 0u};
+            if (mis != 0 && lane == 63) n2 = ld16(base + A2 + 4);
+            if (mis != 0) {
+              const u32x4 n1 = from_next_in_row(g1, rot_row_left(g2));
+              n2 = from_next_in_row(g2, from_next_lane(g1, n2));
+              g1 = shift4_by(mis, g1, n1);
+              g2 = shift4_by(mis, g2, n2);
+            }
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+              v[i] = __uint_as_float(g1[i]);
+              v[i + 4] = __uint_as_float(g2[i]);
+            }
+          };
+          rank_groups(start, p);
+          for (int k = 1; k < n; ++k) {
+            int rr = start + k;
+            rr = rr >= n ? rr - n : rr;
+            float own[kPerLane];
+            rank_groups(rr, own);
+            hop(p, own);
           }
         }
-        auto widen8 = [&](int k, float (&v)[kPerLane]) {
-          const u32x4 g1 = mis ? shift4_by(mis, y1[k], n1[k]) : y1[k];
-          const u32x4 g2 = mis ? shift4_by(mis, y2[k], n2[k]) : y2[k];
-#pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            v[i] = __uint_as_float(g1[i]);
-            v[i + 4] = __uint_as_float(g2[i]);
-          }
-        };
-        widen8(0, p);
-#pragma unroll
-        for (int k = 1; k < NT; ++k) {
-          float own[kPerLane];
-          widen8(k, own);
-          hop(p, own);
-        }
-        finish<OP>(p, NT);
+        finish<OP>(p, n);
         u32x4 o1, o2, last;  // our two groups; the previous task's last group (lane 63's second)
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
@@ -622,7 +650,7 @@ __global__ __launch_bounds__(kThreads) void fp8_ring_kernel(Fp8RingArgs a) {
         }
         const int64_t R1 = A1 - 4 * kl, R2 = A2 - 4 * kl;  // the slots this lane stores
 #pragma unroll
-        for (int r = 0; r < NT; ++r) {
+        for (int r = 0; r < n; ++r) {
           float* out = static_cast<float*>(a.p.out[r]);
           if (row > 0 || lane > kl || carried || (lane == kl && mis == 0)) {
             st16(out + R1, r1);
@@ -644,32 +672,54 @@ __global__ __launch_bounds__(kThreads) void fp8_ring_kernel(Fp8RingArgs a) {
       } else if (shifted && DT == AR_BF16) {
         constexpr int NT = NR > 0 ? NR : 1;
         const int64_t A = e0 - mis;  // a multiple of 8 elements; A + 16 <= count, so both slots are in the buffer
-        u32x4 x0[NT], x1[NT], w[NT];
-#pragma unroll
-        for (int k = 0; k < NT; ++k) {
-          int rr = start + k;
-          rr = rr >= NT ? rr - NT : rr;
-          x0[k] = ld16(static_cast<const uint16_t*>(a.p.in[rr]) + A);
-          // the upper slot is the next lane's lower one: only the last lane loads it
-          x1[k] = u32x4{0u, 0u, 0u, 0u};
-          if (mis != 0 && lane == 63) x1[k] = ld16(static_cast<const uint16_t*>(a.p.in[rr]) + A + 8);
-        }
-        if (mis != 0) {
-#pragma unroll
-          for (int k = 0; k < NT; ++k) x1[k] = from_next_lane(x0[k], x1[k]);
-          shift_ranks_by<NT>(mis, x0, x1, w);
+        if constexpr (NR > 0) {
+          u32x4 x0[NT], x1[NT], w[NT];
+  #pragma unroll
+          for (int k = 0; k < NT; ++k) {
+            int rr = start + k;
+            rr = rr >= NT ? rr - NT : rr;
+            x0[k] = ld16(static_cast<const uint16_t*>(a.p.in[rr]) + A);
+            // the upper slot is the next lane's lower one: only the last lane loads it
+            x1[k] = u32x4{0u, 0u, 0u, 0u};
+            if (mis != 0 && lane == 63) x1[k] = ld16(static_cast<const uint16_t*>(a.p.in[rr]) + A + 8);
+          }
+          if (mis != 0) {
+  #pragma unroll
+            for (int k = 0; k < NT; ++k) x1[k] = from_next_lane(x0[k], x1[k]);
+            shift_ranks_by<NT>(mis, x0, x1, w);
+          } else {
+  #pragma unroll
+            for (int k = 0; k < NT; ++k) w[k] = x0[k];
+          }
+          Slot<AR_BF16>::unpack(w[0], p);
+  #pragma unroll
+          for (int k = 1; k < NT; ++k) {
+            float own[kPerLane];
+            Slot<AR_BF16>::unpack(w[k], own);
+            hop(p, own);
+          }
         } else {
-#pragma unroll
-          for (int k = 0; k < NT; ++k) w[k] = x0[k];
+          // a rank count known only at run time: each rank's slot loaded, moved and shifted in turn
+          auto rank_slot = [&](int rr, float (&v)[kPerLane]) {
+            const uint16_t* base = static_cast<const uint16_t*>(a.p.in[rr]);
+            u32x4 x0[1] = {ld16(base + A)}, x1[1] = {u32x4{0u, 0u, 0u, 0u}}, w[1] = {x0[0]};
+            if (mis != 0 && lane == 63) x1[0] = ld16(base + A + 8);
+            if (mis != 0) {
+              x1[0] = from_next_lane(x0[0], x1[0]);
+              shift_ranks_by<1>(mis, x0, x1, w);
+            }
+            Slot<AR_BF16>::unpack(w[0], v);
+          };
+          rank_slot(start, p);
+          for (int k = 1; k < n; ++k) {
+            int rr = start + k;
+            rr = rr >= n ? rr - n : rr;
+            float own[kPerLane];
+            rank_slot(rr, own);
+            hop(p, own);
+          }
         }
-        Slot<AR_BF16>::unpack(w[0], p);
-#pragma unroll
-        for (int k = 1; k < NT; ++k) {
-          float own[kPerLane];
-          Slot<AR_BF16>::unpack(w[k], own);
-          hop(p, own);
-        }
-        finish<OP>(p, NT);
+        finish<OP>(p, n);
         const u32x4 o = Slot<AR_BF16>::pack(p);
         u32x4 last;  // the previous task's last lane
 #pragma unroll
@@ -703,7 +753,7 @@ __global__ __launch_bounds__(kThreads) void fp8_ring_kernel(Fp8RingArgs a) {
           shift_ranks_by<1>(8 - mis, one, one, top);
         }
 #pragma unroll
-        for (int r = 0; r < NT; ++r) {
+        for (int r = 0; r < n; ++r) {
           uint16_t* out = static_cast<uint16_t*>(a.p.out[r]);
           if (lane > kl || carried || (lane == kl && mis == 0)) {
             st16(out + As, rot);

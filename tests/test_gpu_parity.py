@@ -546,14 +546,16 @@ def test_fp8_ring_matches_oracle(n, count):
                 assert_bitwise(got, want, f"fp8 ring n={n} count={count} dt={dt}")
 
 
-@pytest.mark.parametrize("n", [2, 3, 4, 8])
+@pytest.mark.parametrize("n", [2, 3, 4, 5, 6, 7, 8, 12])
 @pytest.mark.parametrize("extra", [1, 3, 5, 7, 26, 4096 * 3 + 5])
 @pytest.mark.parametrize("dt", [ar.AR_BF16, ar.AR_F32])
 def test_fp8_ring_chunks_off_the_16_byte_grid(n, extra, dt):
     """Counts that are not a multiple of 8 N (bf16) or 4 N (fp32) put chunk starts 1..7 (1..3) elements past the
     16-byte grid (n = 8, extra = 7 gives every bf16 one); chunks of several 512-element wave tasks take shifted
     vector loads and lane-exchanged aligned stores carried along strips of tasks, the chunk ends and the last
-    slots of the buffer element by element. Bitwise against the oracle, out of place and in place."""
+    slots of the buffer element by element. Rank counts other than 2, 4, 8 run the build whose rank count is known
+    only at run time, which loads and shifts one rank after another. Bitwise against the oracle, out of place and in
+    place."""
     count = n * 4096 + extra
     kind = "outlier_bf16" if dt == ar.AR_BF16 else "uniform_f32"
     xs = inputs.rank_inputs(kind, n, count, cfg=6, extra=(n, count))
@@ -564,7 +566,7 @@ def test_fp8_ring_chunks_off_the_16_byte_grid(n, extra, dt):
                        f"fp8 ring in place n={n} count={count} dt={dt}")
 
 
-@pytest.mark.parametrize("n", [2, 4, 8])
+@pytest.mark.parametrize("n", [2, 3, 4, 6, 8])
 @pytest.mark.parametrize("q", [4096 + 8, 4096 + 24, 4096 + 64 + 56, 4096 + 3, 4096 + 4, 4096 + 13])
 @pytest.mark.parametrize("out_offs", ["aligned", "common_16B", "common_80B", "mixed"])
 @pytest.mark.parametrize("dt", [ar.AR_BF16, ar.AR_F32])
