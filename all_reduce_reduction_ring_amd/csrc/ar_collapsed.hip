@@ -561,6 +561,22 @@ __device__ __forceinline__ void binomial_vals(const Acc (&v)[NV][V], Acc (&acc)[
   }
 }
 
+// The binomial tree for any rank count: T(lo, n) = T(lo, h) (+) T(lo + h, n - h), h the largest power of two below
+// n (binomial_fold's association), over the same values.
+template <int OP, int NR, int LO, typename Acc, int V, int NV>
+__device__ __forceinline__ void binomial_vals_any(const Acc (&v)[NV][V], Acc (&acc)[V]) {
+  if constexpr ((NR & (NR - 1)) == 0) {
+    binomial_vals<OP, NR, LO>(v, acc);
+  } else {
+    constexpr int H = below_pow2<NR>();
+    Acc b[V];
+    binomial_vals<OP, H, LO>(v, acc);
+    binomial_vals_any<OP, NR - H, LO + H>(v, b);
+#pragma unroll
+    for (int e = 0; e < V; ++e) acc[e] = combine<OP>(acc[e], b[e]);
+  }
+}
+
 // A wave tile takes the vector path when it lies in one chunk and both aligned slots of every lane lie inside the
 // buffers: tile 0's lower slots would start before them, and the upper slots of a tile need V more elements.
 template <int V, int NR>
@@ -650,7 +666,7 @@ __global__ __launch_bounds__(kThreads) void skew_kernel(SkewArgs s) {
 #pragma unroll
           for (int r = 0; r < NR; ++r) S::unpack(shift_by<ES>(s.im[r], x0[r], x1[r]), v[r]);
           if constexpr (SHAPE == kHalving) halving_vals<OP, NR, 1, 0>(v, acc);
-          else binomial_vals<OP, NR, 0>(v, acc);
+          else binomial_vals_any<OP, NR, 0>(v, acc);
         }
 #pragma unroll
         for (int i = 0; i < V; ++i) acc[i] = finalize<OP>(acc[i], NR);
@@ -737,9 +753,9 @@ __global__ __launch_bounds__(kThreads) void skew_kernel(SkewArgs s) {
 }
 
 // Workgroups per CU before the scale above: the one-pass kernels' count, and for the rank counts the skewed kernel
-// alone builds (3, 5, 6, 7; ring and rank order) that of the next power of two, whose loads in flight per thread
-// they come closest to. (With 3 and 4 ranks more workgroups are asked for than fit at once; capping the grid at
-// the resident count measured 4-8% slower at 64 MiB of bf16 per rank and level at 256 MiB.)
+// alone builds (3, 5, 6, 7; ring, rank order and binomial tree) that of the next power of two, whose loads in
+// flight per thread they come closest to. (With 3 and 4 ranks more workgroups are asked for than fit at once;
+// capping the grid at the resident count measured 4-8% slower at 64 MiB of bf16 per rank and level at 256 MiB.)
 template <int NR> constexpr int skew_blocks_per_cu() {
   return NR == 3 ? blocks_per_cu<4>() : (NR > 4 && NR < 8) ? blocks_per_cu<8>() : blocks_per_cu<NR>();
 }
@@ -769,7 +785,7 @@ hipError_t skew_n(SkewArgs& s, hipStream_t st) {
     case 16: return launch_skew<DT, OP, 16, SHAPE>(s, st);
     default: break;
   }
-  if constexpr (SHAPE == kLinear) {  // the trees need a power-of-two rank count here
+  if constexpr (SHAPE != kHalving) {  // halving-doubling needs a power-of-two rank count
     switch (s.f.n) {
       case 3: return launch_skew<DT, OP, 3, SHAPE>(s, st);
       case 5: return launch_skew<DT, OP, 5, SHAPE>(s, st);
@@ -803,16 +819,16 @@ hipError_t skew_op(SkewArgs& s, int op, int algo, hipStream_t st) {
 
 // The skewed-buffer kernel takes a call of 2-byte elements when the 2N addresses are element-aligned and not all
 // equal modulo 16 (views at different offsets), the algorithm is a one-pass one with a rank count of 2, 4, 8 or 16,
-// or the ring or rank order with 3, 5, 6 or 7 ranks, and there are a few wave tiles of work; it fills the per-rank
-// offsets. Addresses that are all multiples of 4
+// or the ring, rank order or binomial tree with 3, 5, 6 or 7 ranks, and there are a few wave tiles of work; it
+// fills the per-rank offsets. Addresses that are all multiples of 4
 // bytes come here too rather than to the one-front kernel's 16-byte accesses at 4-byte alignment, whose store
 // windows straddle lines.
 template <int DT>
 bool plan_skew(const RankPtrs& p, int n, int64_t count, int algo, SkewArgs& s) {
   constexpr int ES = Traits<DT>::kSize, V = Traits<DT>::kVec;
-  const bool linear = algo == AR_ALGO_RING || algo == AR_ALGO_FUSED;
-  if (!(linear || algo == AR_ALGO_RHD || algo == AR_ALGO_TREE)) return false;
-  if (!(n == 2 || n == 4 || n == 8 || n == 16 || (linear && (n == 3 || n == 5 || n == 6 || n == 7)))) return false;
+  if (!(algo == AR_ALGO_RING || algo == AR_ALGO_FUSED || algo == AR_ALGO_RHD || algo == AR_ALGO_TREE)) return false;
+  if (!(n == 2 || n == 4 || n == 8 || n == 16 || (algo != AR_ALGO_RHD && (n == 3 || n == 5 || n == 6 || n == 7))))
+    return false;
   if (count < 4 * 64 * V) return false;
   bool differ = false;
   s.any_kl = 0;

@@ -145,8 +145,8 @@ int ar_chunk_bounds(int nranks, size_t count, int64_t* lo);
  *   multiple of 256 bytes (buffers of 1 MiB or more) or of 16 bytes, the rest in vectors. Where the pointers
  *   differ modulo 16, 4-byte types use vectors from element 0 (slower: they straddle cache lines), and 2-byte
  *   types use aligned vectors shifted per rank, with the stores rotated onto whole 128-byte lines, for RING,
- *   FUSED, RHD and TREE with nranks 2, 4, 8 or 16 and for RING and FUSED with nranks 3, 5, 6 or 7 (also slower,
- *   least when every rank's data starts in the first 16 bytes of a line), else element by element. RING_FP8 uses vectors when every pointer is 16-byte aligned,
+ *   FUSED, RHD and TREE with nranks 2, 4, 8 or 16 and for RING, FUSED and TREE with nranks 3, 5, 6 or 7 (also
+ *   slower, least when every rank's data starts in the first 16 bytes of a line), else element by element. RING_FP8 uses vectors when every pointer is 16-byte aligned,
  *   for any count (chunk starts off the 16-byte grid take shifted vectors); the other algorithms use vectors only
  *   when every pointer is 16-byte aligned. Otherwise element by element.
  * Errors: AR_ERR_INVALID (enum, nranks, NULL), AR_ERR_UNSUPPORTED (RHD with N not a power of two; FP8

@@ -93,7 +93,7 @@ def test_headline_size_at_odd_per_rank_offsets():
 def test_odd_per_rank_offsets_three_and_seven_ranks_long_strips(n, count):
     """The skewed kernel's builds for rank counts that are not a power of two, at sizes where it walks long strips
     (32 tiles per wave): rank r's input r elements and its output 3r + 2 elements past an aligned address, ragged
-    chunks, ring order and rank order, every element of every rank against the oracle."""
+    chunks, ring order, rank order and the binomial tree, every element of every rank against the oracle."""
     host = _par(lambda r: inputs.normal_bf16((7, n, r), count), range(n))
     ibase = [torch.empty(count + 32, dtype=torch.bfloat16, device=DEV) for _ in range(n)]
     obase = [torch.empty(count + 32, dtype=torch.bfloat16, device=DEV) for _ in range(n)]
@@ -102,7 +102,8 @@ def test_odd_per_rank_offsets_three_and_seven_ranks_long_strips(n, count):
     for t, h in zip(ins, _up(host, torch.bfloat16)):
         t.copy_(h)
     torch.cuda.synchronize()
-    for algo, fn in ((ar.AR_ALGO_RING, oracle.ring_allreduce), (ar.AR_ALGO_FUSED, oracle.fused_allreduce)):
+    for algo, fn in ((ar.AR_ALGO_RING, oracle.ring_allreduce), (ar.AR_ALGO_FUSED, oracle.fused_allreduce),
+                     (ar.AR_ALGO_TREE, oracle.tree_allreduce)):
         print(f"case n={n} count={count} algo={algo}", flush=True)
         ar.ar_allreduce(ins, outs, ar.AR_SUM, algo)
         torch.cuda.synchronize()
