@@ -486,6 +486,12 @@ hipError_t launch_front(CollapsedArgs& a, hipStream_t s) {
   const int64_t nslots = a.count > a.head ? (a.count - a.head) / V : 0;
   const int64_t ntiles = (nslots + TS - 1) / TS;
   int64_t g = static_cast<int64_t>(cu_count()) * blocks_per_cu<NR>();
+  // N = 16 keeps all 16 loads of a thread in flight; on launches that give every workgroup four tiles or more, a
+  // quarter of the workgroups measured faster (one process, base and new interleaved: 64 MiB per rank 4.97-4.99 ->
+  // 5.66-5.67 TB/s bf16 and 4.91-4.92 -> 5.36-5.41 fp32; 16 MiB 4.75-4.77 -> 5.18-5.27 and 4.02-4.09 -> 4.79-4.86;
+  // 256 MiB 5.64-5.65 -> 5.91-5.93 and 5.80-5.81 -> 5.84), while at 4 MiB, one tile per workgroup, it ran 7-11%
+  // slower. The rank-order and tree kernels at N = 16 keep theirs: for fp32 they ran 15-25% slower with a quarter.
+  if (NR == 16 && ntiles >= 4 * g) g /= 4;
   // up to two tiles per workgroup: one workgroup per tile instead, so no workgroup walks two in turn (N = 8,
   // 2 MiB of fp32 per rank: 7.8 us against 9.7 us of device time; from four tiles per workgroup up it gained nothing)
   if (ntiles <= 2 * g) g = ntiles;
