@@ -336,6 +336,10 @@ THRESHOLD_CASES = [
     (2, ar.AR_I32, (1 << 26) + 5),
     (4, ar.AR_F16, (1 << 26) + 3),
     (16, ar.AR_F16, (1 << 24) + 9),
+    # N = 16 on the small build with four tiles or more per workgroup: the one-front ring and the rank-order and
+    # tree kernels on a quarter of the workgroups, the latter with every load issued first
+    (16, ar.AR_BF16, (1 << 23) + 5),
+    (16, ar.AR_F32, (1 << 22) + 3),
 ]
 
 
