@@ -363,6 +363,16 @@ def test_one_pass_builds_on_both_sides_of_the_switch(n, dt, count):
             want = ofn(xs, ORACLE_DT[dt], ORACLE_OP[op])[0]
             got = from_dev(outs[0], dt)
             assert np.array_equal(got, np.asarray(want).view(got.dtype)), f"algo={algo} op={op}"
+    if n == 16:  # in place on the quarter grid (every load of a slot issued before its stores)
+        for algo, ofn in ((ar.AR_ALGO_RING, oracle.ring_allreduce), (ar.AR_ALGO_TREE, oracle.tree_allreduce)):
+            work = [t.clone() for t in ins]
+            ar.ar_allreduce(work, work, ar.AR_AVG, algo)
+            torch.cuda.synchronize()
+            _same_on_all_ranks(work)
+            want = ofn(xs, ORACLE_DT[dt], ORACLE_OP[ar.AR_AVG])[0]
+            got = from_dev(work[0], dt)
+            assert np.array_equal(got, np.asarray(want).view(got.dtype)), f"in place algo={algo}"
+            del work
     del ins, outs
     torch.cuda.empty_cache()
 
