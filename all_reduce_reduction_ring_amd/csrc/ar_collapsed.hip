@@ -54,8 +54,9 @@ constexpr int kLarge = AR_COLLAPSED_LARGE;
 constexpr int kThreads = kLarge ? 128 : 256;
 
 // Launch shape, measured on MI355X: HBM3E streams writes best with few concurrent writers, while reads need
-// bytes in flight. Each thread keeps about eight independent 16-byte loads in flight (U slots x N ranks,
-// U = 8/N for small N), and the grid is a small number of waves per CU in total (split over the chunks): four
+// bytes in flight. Each thread folds U slots x N ranks (U = 8/N for small N; how many of those loads the compiler
+// keeps in flight at once is its choice, see kAllLoadsFirst), and the grid is a small number of waves per CU in
+// total (split over the chunks): four
 // for N = 8 (one 256-thread workgroup, or two 128-thread ones in the large build), more where a thread has
 // fewer loads in flight or writes fewer streams. More bytes in flight (longer tiles, a second tile's loads
 // issued before the first tile's stores, more workgroups) measured slower. On large launches 128-thread
